@@ -1,0 +1,201 @@
+"""Benchmark of the block-scaled FP8 attention forward on one MI355X.
+
+One step = the whole hot path on one batch of synthetic inputs already resident in HBM:
+QKV quantisation (fp8attn_quantize_qkv) + attention forward (fp8attn_forward). The metric is
+the attention forward's dense-equivalent FLOP count 4 * N^2 * D * H * B divided by the step
+time (TFLOP/s). The attention kernel's own time (HIP events around its launches on the stream
+it runs on) gives the roofline fraction against the FP8 dense MFMA peak. The CPU oracle is
+timed on a bounded sample of the same workload as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 attn fwd TFLOP/s (4·N²·D·H, dense-equiv) + % of MI355X FP8 MFMA peak"
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (no sparsity)
+
+WORKLOADS = {
+    # name: (workloads.py config, sparse, vsmooth+expcast, description)
+    "wan14b": ("wan14b", False, False,
+               "Wan-14B-720p-shaped dense FP8 attention, B=1 H=40 N=75600 (21x45x80) D=128, "
+               "Q/K E4M3 per-64-token block scales, V per-channel scale, S=256, reverse KV order"),
+    "wan14b_sparse": ("wan14b", True, False,
+                      "Wan-14B-720p-shaped STA block-sparse: grid 21x45x80 padded to 24x48x80, "
+                      "tiles (6,8,8), Chebyshev radius 1, N'=92160, H=40, D=128, S=256, reverse"),
+    "wan13b": ("wan13b", False, False,
+               "Wan-1.3B-480p-shaped dense FP8 attention, B=1 H=12 N=32760 (21x30x52) D=128 with "
+               "4 outlier channels x8 per head and tensor, S=256, reverse KV order"),
+    "vsmooth": ("vsmooth", False, True,
+                "V-Smooth + ExpCast, B=1 H=24 N=49152 D=128, 5% token outliers x20 in V, "
+                "16-cluster k-means permutation (reused, not timed), S=256, reverse KV order"),
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path runs per GPU on its own heads with no "
+              "communication, so only --gpus 1 is supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_attention_video_qkv_amd as fa
+    import workloads
+
+    cfg_name, sparse, vs, desc = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    q, k, v = workloads.workload(cfg_name)
+    B, N, H, D = q.shape
+    log(f"inputs {args.workload} B={B} N={N} H={H} D={D} generated in {time.time() - t0:.1f}s")
+
+    perm_q = perm_kv = sp = out_rows = None
+    n_layout, n_out = N, N
+    if sparse:
+        lay = fa.sta_build(21, 45, 80, 6, 8, 8, 1, 1, 1)
+        perm_q = torch.from_numpy(lay["perm"]).to(dev)
+        perm_kv = perm_q
+        sp = fa.sparse_to_device(lay, dev)
+        out_rows = perm_q
+        n_layout = lay["perm"].shape[0]
+    if vs:
+        # A per-head shuffle stands in for the cluster order: the step gathers through whatever
+        # permutation it is given, and the clustering itself is reused across steps (not timed).
+        g = torch.Generator("cpu").manual_seed(55)
+        perm_kv = torch.stack([torch.randperm(N, generator=g) for _ in range(H)]).view(1, H, N)
+        perm_kv = perm_kv.to(torch.int32).to(dev)
+
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    del q, k, v
+    qz = fa.alloc_quantized(B, n_layout, H, vs, dev)
+    ws_q = fa.quantize_workspace(B, n_layout, H, vs, dev)
+    ws_f = fa.forward_workspace(B, n_layout, H, vs, dev)
+    out = torch.zeros((B, n_out, H, D), dtype=torch.bfloat16, device=dev)
+    pcast = fa.FP8ATTN_PCAST_EXPCAST if vs else fa.FP8ATTN_PCAST_RNE
+
+    def step(ev=None):
+        fa.quantize_qkv(qd, kd, vd, perm_q=perm_q, perm_kv=perm_kv, vsmooth=vs, n_layout=n_layout,
+                        out=qz, workspace=ws_q)
+        if ev is not None:
+            ev[0].record()
+        fa.forward(qz, p_scale=256.0, kv_order=fa.FP8ATTN_KV_REVERSE, pcast=pcast, sparse=sp,
+                   out_rows=out_rows, n_out=n_out, out=out, workspace=ws_f)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    ms_attn = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    dense_flops = 4.0 * N * N * D * H * B
+    value = dense_flops / (ms_step * 1e-3) / 1e12
+    if sparse:
+        tl = lay["tile_len"].astype(np.int64)
+        rp, ci = lay["row_ptr"], lay["col_idx"]
+        pairs = sum(int(tl[u]) * int(tl[ci[rp[u]:rp[u + 1]]].sum()) for u in range(len(tl)))
+        attn_flops = 4.0 * pairs * D * H * B   # algorithmic work of the sparse kernel
+    else:
+        attn_flops = dense_flops
+    achieved = attn_flops / (ms_attn * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms, attention kernel {ms_attn:.3f} ms, quantize {ms_step - ms_attn:.3f} ms")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": desc, "global_batch": B, "seq_len": N, "heads": H, "head_dim": D,
+                   "parallelism": "none (one GPU)", "name": args.workload},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_fwd", "kernel_ms": round(ms_attn, 4),
+                     "algorithmic_flop_per_launch": attn_flops},
+    }
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(args, cfg_name, sparse, vs)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, cfg_name, sparse, vs):
+    """The oracle as it stands on the host cores: quantisation of one head plus the attention
+    of a bounded sample of that head's query rows, scaled to TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    oracle._load()
+    q, k, v = workloads.workload(cfg_name, heads=1)
+    B, N, H, D = q.shape
+    bq, bk, bv = workloads.bits(q), workloads.bits(k), workloads.bits(v)
+    rows_n = args.cpu_rows or 16384
+    t0 = time.time()
+    if sparse:
+        lay = oracle.sta_layout(21, 45, 80, 6, 8, 8, 1, 1, 1)
+        qz = oracle.quantize(bq, bk, bv, perm_q=lay["perm"], perm_kv=lay["perm"])
+    else:
+        lay = None
+        qz = oracle.quantize(bq, bk, bv, vsmooth=vs, perm_kv=None)
+    t_quant = time.time() - t0
+    Nl = qz["N"]
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(Nl, rows_n, replace=False)).astype(np.int32)
+    t1 = time.time()
+    oracle.attention_fp8(qz, rows=rows, kv_reverse=True, expcast=vs, sparse=lay)
+    t_attn = time.time() - t1
+    flops = 4.0 * rows_n * N * D            # dense-equivalent work of the sampled rows
+    return {"value": round(flops / t_attn / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"1 head of {cfg_name}: quantisation of the head ({t_quant:.2f} s, not in "
+                      f"value) + attention of {rows_n} random query rows over all {N} keys "
+                      f"({t_attn:.2f} s); value = 4*rows*N*D / attention time"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,231 @@
+"""Python binding of libfp8attn (block-scaled FP8 attention forward for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libfp8attn.so``; PyTorch supplies device memory and the current HIP stream. The entry points
+mirror the C ABI in ``include/fp8attn.h``:
+
+* ``quantize_qkv``  -> ``fp8attn_quantize_qkv``
+* ``forward``       -> ``fp8attn_forward``
+* ``sta_build``     -> ``fp8attn_sta_build`` (host helper)
+
+There is no fallback: if the library is missing or the device is not gfx950 these calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8attn.so")
+
+FP8ATTN_KV_FORWARD, FP8ATTN_KV_REVERSE = 0, 1
+FP8ATTN_PCAST_RNE, FP8ATTN_PCAST_EXPCAST = 0, 1
+HEAD_DIM = 128
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or device", 3: "HIP runtime error"}
+
+
+class Fp8AttnError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+class _QuantArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("N_src", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("D", ctypes.c_int32), ("perm_q", ctypes.c_void_p),
+                ("perm_kv", ctypes.c_void_p), ("perm_kv_per_head", ctypes.c_int32),
+                ("vsmooth", ctypes.c_int32)]
+
+
+class _Sparse(ctypes.Structure):
+    _fields_ = [("tile_tokens", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
+                ("tile_len", ctypes.c_void_p), ("row_ptr", ctypes.c_void_p),
+                ("col_idx", ctypes.c_void_p)]
+
+
+class _FwdOpts(ctypes.Structure):
+    _fields_ = [("softmax_scale", ctypes.c_float), ("p_scale", ctypes.c_float),
+                ("kv_order", ctypes.c_int), ("pcast", ctypes.c_int),
+                ("sparse", ctypes.POINTER(_Sparse)), ("out_rows", ctypes.c_void_p),
+                ("n_out", ctypes.c_int32), ("underflow", ctypes.c_void_p)]
+
+
+_lib = None
+
+EXPORTED = ("fp8attn_quantize_qkv", "fp8attn_quantize_workspace_bytes", "fp8attn_forward",
+            "fp8attn_forward_workspace_bytes", "fp8attn_sta_build", "fp8attn_status_string")
+
+
+def lib():
+    """The loaded libfp8attn (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fp8attn_quantize_qkv.restype = ctypes.c_int
+        L.fp8attn_quantize_qkv.argtypes = [ctypes.POINTER(_QuantArgs)] + [ctypes.c_void_p] * 11 + [
+            ctypes.c_size_t, ctypes.c_void_p]
+        L.fp8attn_quantize_workspace_bytes.restype = ctypes.c_size_t
+        L.fp8attn_quantize_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+        L.fp8attn_forward.restype = ctypes.c_int
+        L.fp8attn_forward.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 7 + [
+            ctypes.POINTER(_FwdOpts), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.c_void_p]
+        L.fp8attn_forward_workspace_bytes.restype = ctypes.c_size_t
+        L.fp8attn_forward_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+        L.fp8attn_sta_build.restype = ctypes.c_int
+        L.fp8attn_sta_build.argtypes = [ctypes.c_int32] * 9 + [ctypes.c_void_p] * 4 + [
+            ctypes.c_int32, ctypes.c_void_p]
+        L.fp8attn_status_string.restype = ctypes.c_char_p
+        L.fp8attn_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Fp8AttnError(fn, status)
+
+
+@dataclass
+class Quantized:
+    """Output of quantize_qkv (device tensors, layout described in include/fp8attn.h)."""
+    q8: torch.Tensor
+    k8: torch.Tensor
+    v8t: torch.Tensor
+    q_scale: torch.Tensor
+    k_scale: torch.Tensor
+    v_scale: torch.Tensor
+    v_mean: torch.Tensor | None
+    B: int
+    N: int
+    H: int
+
+
+def alloc_quantized(B, N, H, vsmooth, device):
+    NB = (N + 63) // 64
+    N64 = NB * 64
+    NB128 = (N + 127) // 128
+    u8 = dict(dtype=torch.uint8, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    return Quantized(
+        q8=torch.empty((B, H, N64, HEAD_DIM), **u8), k8=torch.empty((B, H, N64, HEAD_DIM), **u8),
+        v8t=torch.empty((B, H, HEAD_DIM, N64), **u8), q_scale=torch.empty((B, H, NB), **f32),
+        k_scale=torch.empty((B, H, NB), **f32), v_scale=torch.empty((B, H, HEAD_DIM), **f32),
+        v_mean=torch.empty((B, H, NB128, HEAD_DIM), dtype=torch.int16, device=device) if vsmooth else None,
+        B=B, N=N, H=H)
+
+
+def quantize_workspace(B, N, H, vsmooth, device):
+    n = lib().fp8attn_quantize_workspace_bytes(B, N, H, HEAD_DIM, 1 if vsmooth else 0)
+    return torch.empty(max(int(n), 256), dtype=torch.uint8, device=device)
+
+
+def quantize_qkv(q, k, v, perm_q=None, perm_kv=None, vsmooth=False, n_layout=None, out=None,
+                 workspace=None):
+    """q, k, v: bf16 device tensors [B, N_src, H, 128]. perm_q: int32 device [N] or None;
+    perm_kv: int32 device [N] (shared by heads) or [B, H, N] or None. Returns Quantized."""
+    B, Nsrc, H, D = q.shape
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.shape != q.shape:
+            raise ValueError("q, k, v must be contiguous bf16 tensors of one shape")
+    per_head = 0
+    if perm_kv is not None:
+        per_head = 1 if perm_kv.dim() == 3 else 0
+    if n_layout is None:
+        n_layout = perm_q.shape[0] if perm_q is not None else (
+            perm_kv.shape[-1] if perm_kv is not None else Nsrc)
+    N = int(n_layout)
+    qz = out if out is not None else alloc_quantized(B, N, H, vsmooth, q.device)
+    ws = workspace if workspace is not None else quantize_workspace(B, N, H, vsmooth, q.device)
+    args = _QuantArgs(B, Nsrc, N, H, D, _ptr(perm_q), _ptr(perm_kv), per_head, 1 if vsmooth else 0)
+    st = lib().fp8attn_quantize_qkv(
+        ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(qz.q8), _ptr(qz.k8), _ptr(qz.v8t),
+        _ptr(qz.q_scale), _ptr(qz.k_scale), _ptr(qz.v_scale), _ptr(qz.v_mean) if vsmooth else None,
+        _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(q.device))
+    _check("fp8attn_quantize_qkv", st)
+    return qz
+
+
+@dataclass
+class Sparse:
+    """STA descriptor with device arrays (see fp8attn_sparse)."""
+    tile_tokens: int
+    n_tiles: int
+    tile_len: torch.Tensor
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+
+    def _c(self):
+        return _Sparse(self.tile_tokens, self.n_tiles, self.tile_len.data_ptr(),
+                       self.row_ptr.data_ptr(), self.col_idx.data_ptr())
+
+
+def sta_build(T, Hg, W, tt, th, tw, rt, rh, rw):
+    """Host layout helper -> dict of numpy int32 arrays (perm, tile_len, row_ptr, col_idx)."""
+    gt, gh, gw = -(-T // tt), -(-Hg // th), -(-W // tw)
+    n_tiles, tile = gt * gh * gw, tt * th * tw
+    perm = np.zeros(n_tiles * tile, np.int32)
+    tile_len = np.zeros(n_tiles, np.int32)
+    row_ptr = np.zeros(n_tiles + 1, np.int32)
+    nnz = ctypes.c_int32(0)
+    L = lib()
+    st = L.fp8attn_sta_build(T, Hg, W, tt, th, tw, rt, rh, rw, perm.ctypes.data, tile_len.ctypes.data,
+                             row_ptr.ctypes.data, None, 0, ctypes.byref(nnz))
+    col_idx = np.zeros(max(nnz.value, 1), np.int32)
+    st = L.fp8attn_sta_build(T, Hg, W, tt, th, tw, rt, rh, rw, perm.ctypes.data, tile_len.ctypes.data,
+                             row_ptr.ctypes.data, col_idx.ctypes.data, nnz.value, ctypes.byref(nnz))
+    _check("fp8attn_sta_build", st)
+    return dict(perm=perm, tile_len=tile_len, row_ptr=row_ptr, col_idx=col_idx[:nnz.value],
+                tile_tokens=tile, n_tiles=n_tiles)
+
+
+def sparse_to_device(layout, device):
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return Sparse(int(layout["tile_tokens"]), int(layout["n_tiles"]), to(layout["tile_len"]),
+                  to(layout["row_ptr"]), to(layout["col_idx"]))
+
+
+def forward_workspace(B, N, H, vsmooth, device):
+    n = int(lib().fp8attn_forward_workspace_bytes(B, N, H, HEAD_DIM, 1 if vsmooth else 0))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def forward(qz: Quantized, softmax_scale=1.0 / math.sqrt(HEAD_DIM), p_scale=256.0,
+            kv_order=FP8ATTN_KV_REVERSE, pcast=FP8ATTN_PCAST_RNE, sparse: Sparse | None = None,
+            out_rows=None, n_out=None, underflow=None, out=None, workspace=None):
+    """Attention forward on quantised operands. Returns bf16 [B, n_out, H, 128] (``out`` when
+    given; rows the call does not own keep their previous contents)."""
+    B, N, H = qz.B, qz.N, qz.H
+    dev = qz.q8.device
+    if n_out is None:
+        n_out = N
+    if out is None:
+        out = torch.zeros((B, n_out, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    vs = qz.v_mean is not None
+    ws = workspace if workspace is not None else forward_workspace(B, N, H, vs, dev)
+    sp = sparse._c() if sparse is not None else None
+    opts = _FwdOpts(float(softmax_scale), float(p_scale), int(kv_order), int(pcast),
+                    ctypes.pointer(sp) if sp is not None else None, _ptr(out_rows), int(n_out),
+                    _ptr(underflow))
+    st = lib().fp8attn_forward(
+        B, N, H, HEAD_DIM, _ptr(qz.q8), _ptr(qz.k8), _ptr(qz.v8t), _ptr(qz.q_scale),
+        _ptr(qz.k_scale), _ptr(qz.v_scale), _ptr(qz.v_mean), ctypes.byref(opts), _ptr(out),
+        _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel()), _stream(dev))
+    _check("fp8attn_forward", st)
+    return out

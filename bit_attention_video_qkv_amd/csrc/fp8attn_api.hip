@@ -1,0 +1,234 @@
+// C ABI of libfp8attn: argument validation, workspace carving and kernel launches.
+// The operations are specified in include/fp8attn.h next to each declaration.
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "fp8attn.h"
+#include "fp8attn_common.h"
+#include "fp8attn_internal.h"
+
+namespace {
+
+using fp8attn::kHeadDim;
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Per-device result of the gfx950 check (0 unknown, 1 gfx950, 2 other). Written once per device.
+std::atomic<int> g_arch_ok[64];
+
+fp8attn_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8ATTN_EHIP;
+  if (dev < 0 || dev >= 64) return FP8ATTN_EUNSUPPORTED;
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8ATTN_EHIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? FP8ATTN_OK : FP8ATTN_EUNSUPPORTED;
+}
+
+fp8attn_status from_hip(hipError_t e) { return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8attn_status_string(fp8attn_status s) {
+  switch (s) {
+    case FP8ATTN_OK: return "ok";
+    case FP8ATTN_EINVAL: return "invalid argument";
+    case FP8ATTN_EUNSUPPORTED: return "unsupported shape or device";
+    case FP8ATTN_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t fp8attn_quantize_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D, int32_t vsmooth) {
+  (void)vsmooth;
+  if (B < 1 || N < 1 || H < 1 || D != kHeadDim) return 0;
+  const size_t bh = static_cast<size_t>(B) * H;
+  return round_up(bh * cdiv(N, 128) * kHeadDim * sizeof(float)) + round_up(bh * kHeadDim * sizeof(float));
+}
+
+fp8attn_status fp8attn_quantize_qkv(const fp8attn_quant_args* a, const void* q, const void* k,
+                                    const void* v, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                                    float* q_scale, float* k_scale, float* v_scale,
+                                    uint16_t* v_mean, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  if (!a) return FP8ATTN_EINVAL;
+  if (a->B < 1 || a->N < 1 || a->H < 1 || a->N_src < 1 || a->D < 1) return FP8ATTN_EINVAL;
+  if (a->D != kHeadDim) return FP8ATTN_EUNSUPPORTED;
+  if (static_cast<int64_t>(a->B) * a->H > 65535) return FP8ATTN_EUNSUPPORTED;
+  if (!a->perm_q && a->N != a->N_src) return FP8ATTN_EINVAL;
+  if (!a->perm_kv && a->N != a->N_src) return FP8ATTN_EINVAL;
+  if (a->perm_kv_per_head != 0 && a->perm_kv_per_head != 1) return FP8ATTN_EINVAL;
+  if (a->vsmooth != 0 && a->vsmooth != 1) return FP8ATTN_EINVAL;
+  const void* p16[] = {q, k, v, q8, k8, v8t, v_scale, workspace};
+  for (const void* ptr : p16)
+    if (!ptr || !aligned(ptr, 16)) return FP8ATTN_EINVAL;
+  if (!q_scale || !k_scale || !aligned(q_scale, 4) || !aligned(k_scale, 4)) return FP8ATTN_EINVAL;
+  if ((a->perm_q && !aligned(a->perm_q, 4)) || (a->perm_kv && !aligned(a->perm_kv, 4))) return FP8ATTN_EINVAL;
+  if (a->vsmooth && (!v_mean || !aligned(v_mean, 16))) return FP8ATTN_EINVAL;
+  const size_t need = fp8attn_quantize_workspace_bytes(a->B, a->N, a->H, a->D, a->vsmooth);
+  if (workspace_bytes < need) return FP8ATTN_EINVAL;
+  const fp8attn_status dev = check_device();
+  if (dev != FP8ATTN_OK) return dev;
+
+  fp8attn::QuantParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.perm_q = a->perm_q;
+  p.perm_kv = a->perm_kv;
+  p.q8 = q8;
+  p.k8 = k8;
+  p.v8t = v8t;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.v_mean = a->vsmooth ? v_mean : nullptr;
+  p.B = a->B;
+  p.H = a->H;
+  p.Nsrc = a->N_src;
+  p.N = a->N;
+  p.NB = cdiv(a->N, 64);
+  p.N64 = p.NB * 64;
+  p.NB128 = cdiv(a->N, 128);
+  p.perm_kv_per_head = a->perm_kv_per_head;
+  p.vsmooth = a->vsmooth;
+  const size_t bh = static_cast<size_t>(a->B) * a->H;
+  p.ws_partial = static_cast<float*>(workspace);
+  p.ws_inv = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      round_up(bh * p.NB128 * kHeadDim * sizeof(float)));
+  return from_hip(fp8attn::launch_quantize(p, stream));
+}
+
+size_t fp8attn_forward_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D, int32_t vsmooth) {
+  if (B < 1 || N < 1 || H < 1 || D != kHeadDim || !vsmooth) return 0;
+  return round_up(static_cast<size_t>(B) * H * cdiv(N, 128) * kHeadDim * sizeof(float));
+}
+
+fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const uint8_t* q8,
+                               const uint8_t* k8, const uint8_t* v8t, const float* q_scale,
+                               const float* k_scale, const float* v_scale,
+                               const uint16_t* v_mean, const fp8attn_fwd_opts* o, void* out,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!o || B < 1 || N < 1 || H < 1 || D < 1) return FP8ATTN_EINVAL;
+  if (D != kHeadDim) return FP8ATTN_EUNSUPPORTED;
+  const int64_t total_bh = static_cast<int64_t>(B) * H;
+  if (total_bh > 65535) return FP8ATTN_EUNSUPPORTED;
+  const void* p16[] = {q8, k8, v8t, v_scale};
+  for (const void* ptr : p16)
+    if (!ptr || !aligned(ptr, 16)) return FP8ATTN_EINVAL;
+  if (!q_scale || !k_scale || !aligned(q_scale, 4) || !aligned(k_scale, 4)) return FP8ATTN_EINVAL;
+  if (!out || !aligned(out, 16)) return FP8ATTN_EINVAL;
+  if (!(o->softmax_scale > 0.0f) || !isfinite(o->softmax_scale)) return FP8ATTN_EINVAL;
+  if (!(o->p_scale > 0.0f) || !(o->p_scale <= 448.0f)) return FP8ATTN_EINVAL;
+  if (o->kv_order != FP8ATTN_KV_FORWARD && o->kv_order != FP8ATTN_KV_REVERSE) return FP8ATTN_EINVAL;
+  if (o->pcast != FP8ATTN_PCAST_RNE && o->pcast != FP8ATTN_PCAST_EXPCAST) return FP8ATTN_EINVAL;
+  const bool vsmooth = v_mean != nullptr;
+  const bool sparse = o->sparse != nullptr;
+  if (vsmooth && (sparse || !aligned(v_mean, 16))) return FP8ATTN_EINVAL;
+  if (o->underflow && (o->pcast != FP8ATTN_PCAST_RNE || !aligned(o->underflow, 8))) return FP8ATTN_EINVAL;
+  if (o->out_rows ? (o->n_out < 1 || !aligned(o->out_rows, 4)) : (o->n_out != N)) return FP8ATTN_EINVAL;
+  if (sparse) {
+    const fp8attn_sparse* s = o->sparse;
+    if (s->tile_tokens <= 0 || s->tile_tokens % 64 != 0 || s->n_tiles < 1) return FP8ATTN_EINVAL;
+    if (static_cast<int64_t>(s->tile_tokens) * s->n_tiles != N) return FP8ATTN_EINVAL;
+    if (!s->tile_len || !s->row_ptr || !s->col_idx) return FP8ATTN_EINVAL;
+  }
+  const size_t need = fp8attn_forward_workspace_bytes(B, N, H, D, vsmooth ? 1 : 0);
+  if (need && (!workspace || !aligned(workspace, 16) || workspace_bytes < need)) return FP8ATTN_EINVAL;
+  const fp8attn_status dev = check_device();
+  if (dev != FP8ATTN_OK) return dev;
+
+  fp8attn::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q8 = q8;
+  p.k8 = k8;
+  p.v8t = v8t;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.v_mean = v_mean;
+  p.mu_f = vsmooth ? static_cast<float*>(workspace) : nullptr;
+  p.out = static_cast<uint16_t*>(out);
+  p.out_rows = o->out_rows;
+  p.underflow = o->underflow;
+  p.N = N;
+  p.NB = cdiv(N, 64);
+  p.N64 = p.NB * 64;
+  p.NB128 = cdiv(N, 128);
+  p.n_out = o->n_out;
+  p.B = B;
+  p.H = H;
+  p.logit_scale = static_cast<float>(static_cast<double>(o->softmax_scale) * 1.4426950408889634);
+  p.log2S = static_cast<float>(log2(static_cast<double>(o->p_scale)));
+  p.reverse = o->kv_order == FP8ATTN_KV_REVERSE ? 1 : 0;
+  int variant = 0;
+  if (o->pcast == FP8ATTN_PCAST_EXPCAST) variant |= fp8attn::kVarExpCast;
+  if (vsmooth) variant |= fp8attn::kVarVSmooth;
+  if (o->underflow) variant |= fp8attn::kVarStats;
+  if (sparse) {
+    variant |= fp8attn::kVarSparse;
+    p.tile_tokens = o->sparse->tile_tokens;
+    p.tile_len = o->sparse->tile_len;
+    p.row_ptr = o->sparse->row_ptr;
+    p.col_idx = o->sparse->col_idx;
+  }
+  return from_hip(fp8attn::launch_attention(p, variant, stream));
+}
+
+// Host-side tile layout. Each token's tile follows from its raster coordinates; tokens are
+// bucketed per tile in raster order (valid first), then padded with -1; the neighbour list of a
+// tile is every tile whose tile coordinates are within the per-axis Chebyshev radius.
+fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, int32_t th,
+                                 int32_t tw, int32_t rt, int32_t rh, int32_t rw, int32_t* perm,
+                                 int32_t* tile_len, int32_t* row_ptr, int32_t* col_idx,
+                                 int32_t capacity, int32_t* nnz) {
+  if (T < 1 || Hg < 1 || W < 1 || tt < 1 || th < 1 || tw < 1 || rt < 0 || rh < 0 || rw < 0)
+    return FP8ATTN_EINVAL;
+  if (!perm || !tile_len || !row_ptr || !nnz || capacity < 0 || (capacity > 0 && !col_idx))
+    return FP8ATTN_EINVAL;
+  const int64_t gt = cdiv(T, tt), gh = cdiv(Hg, th), gw = cdiv(W, tw);
+  const int64_t n_tiles = gt * gh * gw, tile = static_cast<int64_t>(tt) * th * tw;
+  if (n_tiles * tile > INT32_MAX) return FP8ATTN_EINVAL;
+  for (int64_t u = 0; u < n_tiles; u++) tile_len[u] = 0;
+  for (int64_t t = 0; t < T; t++)
+    for (int64_t y = 0; y < Hg; y++)
+      for (int64_t x = 0; x < W; x++) {
+        const int64_t u = ((t / tt) * gh + (y / th)) * gw + (x / tw);
+        perm[u * tile + tile_len[u]++] = static_cast<int32_t>((t * Hg + y) * W + x);
+      }
+  for (int64_t u = 0; u < n_tiles; u++)
+    for (int64_t i = tile_len[u]; i < tile; i++) perm[u * tile + i] = -1;
+  int64_t count = 0;
+  for (int64_t u = 0; u < n_tiles; u++) {
+    row_ptr[u] = static_cast<int32_t>(count);
+    const int64_t ut = u / (gh * gw), uy = (u / gw) % gh, ux = u % gw;
+    for (int64_t a = ut - rt; a <= ut + rt; a++)
+      for (int64_t c = uy - rh; c <= uy + rh; c++)
+        for (int64_t e = ux - rw; e <= ux + rw; e++) {
+          if (a < 0 || a >= gt || c < 0 || c >= gh || e < 0 || e >= gw) continue;
+          if (count < capacity) col_idx[count] = static_cast<int32_t>((a * gh + c) * gw + e);
+          count++;
+        }
+  }
+  row_ptr[n_tiles] = static_cast<int32_t>(count);
+  *nnz = static_cast<int32_t>(count);
+  return count <= capacity ? FP8ATTN_OK : FP8ATTN_EINVAL;
+}
+
+}  // extern "C"

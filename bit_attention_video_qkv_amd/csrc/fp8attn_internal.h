@@ -1,0 +1,66 @@
+// Internal launch interfaces of libfp8attn (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8attn {
+
+struct QuantParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* perm_q;
+  const int32_t* perm_kv;
+  uint8_t* q8;
+  uint8_t* k8;
+  uint8_t* v8t;
+  float* q_scale;
+  float* k_scale;
+  float* v_scale;
+  uint16_t* v_mean;
+  float* ws_partial;  // [B*H, NB128, 128] per-block channel amax
+  float* ws_inv;      // [B*H, 128] 448 / channel amax
+  int64_t B, H, Nsrc, N, N64, NB, NB128;
+  int perm_kv_per_head;
+  int vsmooth;
+};
+
+struct AttnParams {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8t;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  const uint16_t* v_mean;   // V-Smooth block means (bf16) or null
+  float* mu_f;              // V-Smooth: [B*H, NB128, 128] mean * (1 / s_r) workspace
+  uint16_t* out;            // bf16 [B, n_out, H, 128]
+  const int32_t* out_rows;  // [N] or null
+  unsigned long long* underflow;  // [B*H] or null
+  const int32_t* tile_len;  // sparse descriptor (device) or null
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t N, N64, NB, NB128, n_out;
+  int B, H;
+  int tile_tokens;
+  int n_qtiles;    // query tiles per (b, h)
+  int total_work;  // B * H * n_qtiles
+  float logit_scale;  // softmax_scale * log2(e)
+  float log2S;
+  int reverse;
+};
+
+hipError_t launch_quantize(const QuantParams& p, hipStream_t stream);
+
+enum AttnVariant : int {
+  kVarExpCast = 1,
+  kVarVSmooth = 2,
+  kVarSparse = 4,
+  kVarStats = 8,
+};
+
+// Launches the attention forward for the variant bits; p.n_qtiles / p.total_work are filled in.
+hipError_t launch_attention(AttnParams p, int variant, hipStream_t stream);
+
+}  // namespace fp8attn

@@ -1,0 +1,189 @@
+/*
+ * fp8attn.h — C ABI of libfp8attn, block-scaled FP8 (OCP E4M3) attention forward for MI355X
+ * (gfx950).
+ *
+ * Operations and the passages that define them:
+ *  - QKV preparation: TeleFuser blog "FP8 Sol-Attn: H100 视频 DiT 的量化稀疏注意力", section
+ *    "面向注意力的 FP8 Preparation" (equations s_q, s_k, s_v; V in token-contiguous storage);
+ *    FPSAttention write-up, section 3.1 (Q/K per block, V per channel).
+ *  - Attention mainloop: same blog, section "SM90 CuTe Mainloop" (E4M3 QK, online softmax,
+ *    P cast to E4M3, E4M3 PV, V channel scale after all PV, BF16 out); "FP8 P-Cast Precision
+ *    in Attention: Sink-Induced Collapse and the Optimality of S=2^8", sections 二/三 (KV
+ *    iteration order, static P scale S).
+ *  - Sliding-tile sparsity: FPSAttention write-up, sections 2.2 (neighbourhood W(u)) and 3.1.
+ *  - V-Smooth and ExpCast: VC-Attention article, sections 二 and 三.
+ *
+ * Conventions shared by every entry point:
+ *  - Device pointers are caller-owned device memory; the library never allocates device
+ *    memory, never synchronises, and keeps no mutable global state (thread-safe).
+ *  - Work is enqueued on the caller's `stream`; outputs are valid when the stream reaches it.
+ *  - Argument checks are synchronous and happen before any launch: on error nothing is
+ *    enqueued and FP8ATTN_EINVAL / FP8ATTN_EUNSUPPORTED is returned. A failed launch returns
+ *    FP8ATTN_EHIP. No call ever falls back to another implementation.
+ *  - Shapes: B batch, N tokens in the layout order, H heads, D = 128 channels.
+ *    NB = ceil(N / 64), N64 = 64 * NB, NB128 = ceil(N / 128).
+ *  - Indices and offsets are 64-bit inside the library; B*H*N64*128 may exceed 2^31.
+ */
+#ifndef FP8ATTN_H_
+#define FP8ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8attn_status {
+  FP8ATTN_OK = 0,
+  FP8ATTN_EINVAL = 1,        /* bad argument, shape or pointer */
+  FP8ATTN_EUNSUPPORTED = 2,  /* valid but not supported (D != 128, device not gfx950, ...) */
+  FP8ATTN_EHIP = 3           /* a HIP call or launch failed */
+} fp8attn_status;
+
+typedef enum fp8attn_kv_order {
+  FP8ATTN_KV_FORWARD = 0,  /* key blocks visited 0 .. NB-1 */
+  FP8ATTN_KV_REVERSE = 1   /* key blocks visited NB-1 .. 0 (sink block last) */
+} fp8attn_kv_order;
+
+typedef enum fp8attn_pcast {
+  FP8ATTN_PCAST_RNE = 0,     /* P8 = E4M3_RNE(S * exp(x - m)) */
+  FP8ATTN_PCAST_EXPCAST = 1  /* P8 byte = clamp(rint(8 z + 56 - 0.35), 0, 126), z = log2(S p) */
+} fp8attn_pcast;
+
+/* ------------------------------------------------------------------------------------------
+ * fp8attn_quantize_qkv — QKV preparation.
+ *
+ * Q and K: one FP32 scale per (b, h, 64-token block) of the layout order,
+ *   scale = fl32(amax / 448), code = E4M3_RNE(fl32(x * fl32(448 / amax))), amax = max |x|
+ *   over the block's valid tokens; an all-zero block has scale 0 and codes 0.
+ * V: one FP32 scale per (b, h, channel) over all valid tokens, same rule; codes written
+ *   token-contiguous.
+ * Gathers: perm_q[i] / perm_kv[...] is the source token of layout position i, or -1 for a
+ *   padding position (zero vector, excluded from every amax and mean). K and V share perm_kv.
+ * V-Smooth (vsmooth = 1): per 128-row block j of the permuted V', mu_j = mean of the valid
+ *   rows (FP64 sum / count, rounded to FP32 then BF16 = v_mean), R = fl32(V' - mu_hat_j), and
+ *   R is quantised per channel in place of V (v_scale then holds the residual scales).
+ *
+ * Arguments (device pointers unless noted):
+ *   args      host pointer; B, N_src, N, H, D (= 128), perm_q [N] or NULL (identity; then
+ *             N == N_src), perm_kv [N] (perm_kv_per_head = 0) or [B*H*N] (= 1) or NULL,
+ *             vsmooth 0/1.
+ *   q, k, v   bf16 [B, N_src, H, D] (row-major, 16-byte aligned).
+ *   q8, k8    E4M3 [B, H, N64, D]; rows >= N are written as code 0.
+ *   v8t       E4M3 [B, H, D, N64]; columns >= N and padding positions are code 0.
+ *   q_scale, k_scale   FP32 [B, H, NB].      v_scale   FP32 [B, H, D].
+ *   v_mean    bf16 [B, H, NB128, D] when vsmooth, else ignored (may be NULL).
+ *   workspace device scratch of at least fp8attn_quantize_workspace_bytes(...) bytes,
+ *             16-byte aligned; its contents are overwritten.
+ * Errors: EINVAL on null/misaligned pointers, non-positive sizes, N != N_src without
+ *   perm_q, too-small workspace; EUNSUPPORTED on D != 128 or a device other than gfx950.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct fp8attn_quant_args {
+  int32_t B, N_src, N, H, D;
+  const int32_t* perm_q;
+  const int32_t* perm_kv;
+  int32_t perm_kv_per_head;
+  int32_t vsmooth;
+} fp8attn_quant_args;
+
+size_t fp8attn_quantize_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D,
+                                        int32_t vsmooth);
+
+fp8attn_status fp8attn_quantize_qkv(const fp8attn_quant_args* args, const void* q,
+                                    const void* k, const void* v, uint8_t* q8, uint8_t* k8,
+                                    uint8_t* v8t, float* q_scale, float* k_scale,
+                                    float* v_scale, uint16_t* v_mean, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Sliding-tile (STA) block-sparse descriptor (FPSAttention 2.2 / 3.1). The layout is
+ * tile-major: n_tiles tiles of tile_tokens positions (a multiple of 64), the valid tokens of a
+ * tile first, padding last. Query tile u attends to the key tiles
+ * col_idx[row_ptr[u] .. row_ptr[u+1]), listed in ascending order. All arrays are DEVICE
+ * pointers. N must equal n_tiles * tile_tokens.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct fp8attn_sparse {
+  int32_t tile_tokens;
+  int32_t n_tiles;
+  const int32_t* tile_len;  /* [n_tiles] valid tokens per tile, 1 .. tile_tokens */
+  const int32_t* row_ptr;   /* [n_tiles + 1] */
+  const int32_t* col_idx;   /* [row_ptr[n_tiles]] */
+} fp8attn_sparse;
+
+/* ------------------------------------------------------------------------------------------
+ * fp8attn_sta_build — HOST helper that lays a raster latent grid (T, Hg, W) out in tiles
+ * (tt, th, tw) (the grid is padded up to whole tiles; tiles numbered in raster order over the
+ * tile grid; inside a tile valid tokens first in raster order, then padding) and lists, for
+ * each tile, the tiles within Chebyshev radius (rt, rh, rw) in tile coordinates.
+ * All pointers are HOST pointers: perm [n_tiles * tile] (source token or -1), tile_len
+ * [n_tiles], row_ptr [n_tiles + 1], col_idx [capacity]; *nnz receives the entry count.
+ * Returns EINVAL on bad sizes or when capacity < nnz (then *nnz still holds the need).
+ * ------------------------------------------------------------------------------------------ */
+fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, int32_t th,
+                                 int32_t tw, int32_t rt, int32_t rh, int32_t rw, int32_t* perm,
+                                 int32_t* tile_len, int32_t* row_ptr, int32_t* col_idx,
+                                 int32_t capacity, int32_t* nnz);
+
+/* ------------------------------------------------------------------------------------------
+ * fp8attn_forward — attention forward on the output of fp8attn_quantize_qkv.
+ *
+ * Per query row, key blocks of 64 are visited in `kv_order` (dense) or along the sparse
+ * row; per block: x = (q8 . k8) * s_q * s_k * softmax_scale; m' = max(m, max x);
+ * p = exp(x - m'); l = exp(m - m') l + sum p; P8 = E4M3(S p) (or the ExpCast byte, whose
+ * l increment is sum decode(P8) / S); acc = exp(m - m') acc + P8 . V8. Masked keys (>= N or
+ * sparse padding) have p = 0. End: O = acc * v_scale / (S l), rounded to BF16.
+ * V-Smooth (v_mean != NULL): the block's row sum r restores the mean, O = ((s_r / S) acc +
+ * sum r mu_hat_j) / l, j the 128-row V block of each key block.
+ *
+ * Arguments (device pointers unless noted):
+ *   q8, k8, v8t, q_scale, k_scale, v_scale, v_mean   as written by fp8attn_quantize_qkv
+ *             (v_mean non-NULL iff the V was quantised with vsmooth = 1).
+ *   opts      host pointer:
+ *     softmax_scale  > 0 (1/sqrt(128) for the usual attention);
+ *     p_scale        S, 0 < S <= 448 (256 recommended);
+ *     kv_order, pcast;
+ *     sparse         host pointer to a descriptor (device arrays) or NULL for dense;
+ *     out_rows       device int32 [N] destination row of each layout row (-1 = not written)
+ *                    or NULL (identity); lets a gathered layout write O in source order;
+ *     n_out          number of rows of `out` (N when out_rows is NULL);
+ *     underflow      device uint64 [B*H] or NULL; when non-NULL the counts of keys whose
+ *                    p > 0 but whose P code is 0 are ADDED to it (RNE mode only; slower).
+ *   out       bf16 [B, n_out, H, D]; rows a query does not own are left untouched.
+ *   workspace device scratch of fp8attn_forward_workspace_bytes(...) bytes (may be 0 / NULL
+ *             when that is 0).
+ * Errors: EINVAL on bad pointers/sizes, S outside (0, 448], sparse with V-Smooth, sparse
+ *   N != n_tiles * tile_tokens or tile_tokens not a multiple of 64, ExpCast with underflow
+ *   counting; EUNSUPPORTED on D != 128 or a device other than gfx950.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct fp8attn_fwd_opts {
+  float softmax_scale;
+  float p_scale;
+  fp8attn_kv_order kv_order;
+  fp8attn_pcast pcast;
+  const fp8attn_sparse* sparse;
+  const int32_t* out_rows;
+  int32_t n_out;
+  unsigned long long* underflow;
+} fp8attn_fwd_opts;
+
+size_t fp8attn_forward_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D,
+                                       int32_t vsmooth);
+
+fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const uint8_t* q8,
+                               const uint8_t* k8, const uint8_t* v8t, const float* q_scale,
+                               const float* k_scale, const float* v_scale,
+                               const uint16_t* v_mean, const fp8attn_fwd_opts* opts,
+                               void* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* fp8attn_status_string(fp8attn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8ATTN_H_ */

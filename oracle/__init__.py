@@ -157,11 +157,14 @@ def _sparse_args(sparse):
 
 
 def attention_fp8(qz, rows=None, softmax_scale=1.0 / math.sqrt(128.0), p_scale=256.0,
-                  kv_reverse=False, expcast=False, sparse=None):
+                  kv_reverse=False, expcast=False, sparse=None, return_amb=False):
     """Full FP8 path (TeleFuser "SM90 CuTe Mainloop" + the P-cast paper's order/scale +
     VC-Attention's V-Smooth restore and ExpCast codes) on the output of ``quantize``.
     Returns (out f64 [B,H,R,D], out_bf16 uint16 [B,H,R,D], underflow int64 [B,H,R],
-    row_valid uint8 [B,H,R])."""
+    row_valid uint8 [B,H,R]) and, with return_amb, amb_bound f64 [B,H,R,D]: per output element,
+    the largest change that P codes lying within the evaluation error of a rounding boundary
+    (FP32 and the E4M3 matrix-core contraction) and the contraction's own truncation can
+    explain."""
     B, H, N64, D = qz["q8"].shape
     N = qz["N"]
     rows = np.arange(N, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
@@ -170,16 +173,17 @@ def attention_fp8(qz, rows=None, softmax_scale=1.0 / math.sqrt(128.0), p_scale=2
     ob = np.zeros((B, H, R, D), np.uint16)
     uf = np.zeros((B, H, R), np.int64)
     rv = np.zeros((B, H, R), np.uint8)
+    amb = np.zeros((B, H, R, D), np.float64) if return_amb else None
     tt, nt, tl, rp, ci, _keep = _sparse_args(sparse)
     rc = _load().orc_attention(
         MODE_FP8, B, N, H, D, None, None, None, _p(qz["q8"]), _p(qz["k8"]), _p(qz["v8t"]),
         _p(qz["q_scale"]), _p(qz["k_scale"]), _p(qz["v_scale"]),
         _p(qz["v_mean"]) if qz.get("vsmooth") else None, ctypes.c_double(softmax_scale),
         ctypes.c_double(p_scale), 1 if kv_reverse else 0, 1 if expcast else 0, tt, nt, _p(tl),
-        _p(rp), _p(ci), _p(rows), ctypes.c_int64(R), _p(out), _p(ob), _p(uf), _p(rv))
+        _p(rp), _p(ci), _p(rows), ctypes.c_int64(R), _p(out), _p(ob), _p(uf), _p(rv), _p(amb))
     if rc != 0:
         raise ValueError("oracle attention: invalid arguments")
-    return out, ob, uf, rv
+    return (out, ob, uf, rv, amb) if return_amb else (out, ob, uf, rv)
 
 
 def attention_ref(mode, q, k, v, rows=None, softmax_scale=1.0 / math.sqrt(128.0),
@@ -201,7 +205,7 @@ def attention_ref(mode, q, k, v, rows=None, softmax_scale=1.0 / math.sqrt(128.0)
         int(mode), B, N, H, D, _p(q), _p(k), _p(v), None, None, None, None, None, None, None,
         ctypes.c_double(softmax_scale), ctypes.c_double(p_scale), 1 if kv_reverse else 0,
         1 if expcast else 0, tt, nt, _p(tl), _p(rp), _p(ci), _p(rows), ctypes.c_int64(R),
-        _p(out), None, _p(uf), _p(rv))
+        _p(out), None, _p(uf), _p(rv), None)
     if rc != 0:
         raise ValueError("oracle attention_ref: invalid arguments")
     return out, uf, rv

@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports every entry
+point declared in include/fp8attn.h, argument validation rejects bad calls before any HIP
+call, and the host STA layout helper agrees with the oracle's independent implementation."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "fp8attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8attn_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    import bit_attention_video_qkv_amd as m
+    m.lib()
+    return m
+
+
+def test_exports_every_declared_symbol(m):
+    names = _declared()
+    assert len(names) >= 6
+    for n in names:
+        assert hasattr(m.lib(), n), n
+    assert set(names) == set(m.EXPORTED)
+
+
+def test_status_strings(m):
+    L = m.lib()
+    for s in range(4):
+        assert L.fp8attn_status_string(s)
+    assert L.fp8attn_status_string(99) == b"unknown status"
+
+
+def _fake(n=0x10000):
+    return ctypes.c_void_p(n)   # never dereferenced: validation fails first
+
+
+def test_quantize_rejects_bad_arguments(m):
+    L = m.lib()
+    A = m._QuantArgs
+    ptrs = [_fake()] * 10
+    ws = ctypes.c_size_t(1 << 20)
+    call = lambda a, p=ptrs: L.fp8attn_quantize_qkv(ctypes.byref(a), *p, _fake(), ws, None)
+    assert call(A(1, 64, 64, 2, 64, None, None, 0, 0)) == 2            # D != 128
+    assert call(A(0, 64, 64, 2, 128, None, None, 0, 0)) == 1           # B < 1
+    assert call(A(1, 64, 65, 2, 128, None, None, 0, 0)) == 1           # N != N_src, no perm
+    bad = list(ptrs)
+    bad[0] = None
+    assert call(A(1, 64, 64, 2, 128, None, None, 0, 0), bad) == 1      # null q
+    bad = list(ptrs)
+    bad[3] = _fake(0x10001)
+    assert call(A(1, 64, 64, 2, 128, None, None, 0, 0), bad) == 1      # misaligned q8
+    assert L.fp8attn_quantize_qkv(ctypes.byref(A(1, 64, 64, 2, 128, None, None, 0, 0)), *ptrs,
+                                  _fake(), ctypes.c_size_t(16), None) == 1   # workspace too small
+    assert call(A(1, 64, 64, 2, 128, None, None, 0, 1), ptrs[:9] + [None]) == 1  # vsmooth, no mean
+    assert L.fp8attn_quantize_qkv(None, *ptrs, _fake(), ws, None) == 1
+
+
+def _opts(m, **kw):
+    o = dict(softmax_scale=0.088, p_scale=256.0, kv_order=1, pcast=0, sparse=None, out_rows=None,
+             n_out=256, underflow=None)
+    o.update(kw)
+    return m._FwdOpts(o["softmax_scale"], o["p_scale"], o["kv_order"], o["pcast"], o["sparse"],
+                      o["out_rows"], o["n_out"], o["underflow"])
+
+
+def test_forward_rejects_bad_arguments(m):
+    L = m.lib()
+    P = [_fake()] * 7
+
+    def call(opts, D=128, N=256, v_mean=None, ws=0):
+        args = P[:6] + [v_mean]
+        return L.fp8attn_forward(1, N, 2, D, *args, ctypes.byref(opts), _fake(), None,
+                                 ctypes.c_size_t(ws), None)
+
+    assert call(_opts(m), D=64) == 2
+    assert call(_opts(m, p_scale=500.0)) == 1
+    assert call(_opts(m, p_scale=0.0)) == 1
+    assert call(_opts(m, p_scale=float("nan"))) == 1
+    assert call(_opts(m, softmax_scale=-1.0)) == 1
+    assert call(_opts(m, kv_order=3)) == 1
+    assert call(_opts(m, pcast=2)) == 1
+    assert call(_opts(m, n_out=100)) == 1                               # n_out != N without out_rows
+    assert call(_opts(m, pcast=1, underflow=_fake())) == 1              # ExpCast + counting
+    sp = m._Sparse(64, 3, _fake(), _fake(), _fake())                    # 3 * 64 != 256
+    assert call(_opts(m, sparse=ctypes.pointer(sp))) == 1
+    sp = m._Sparse(96, 2, _fake(), _fake(), _fake())                    # not a multiple of 64
+    assert call(_opts(m, sparse=ctypes.pointer(sp)), N=192) == 1
+    sp = m._Sparse(128, 2, _fake(), _fake(), _fake())
+    assert call(_opts(m, sparse=ctypes.pointer(sp)), v_mean=_fake()) == 1   # sparse + V-Smooth
+    assert call(_opts(m), v_mean=_fake(), ws=0) == 1                    # V-Smooth needs workspace
+
+
+@pytest.mark.parametrize("grid", [(21, 45, 80, 6, 8, 8, 1, 1, 1), (5, 7, 9, 2, 4, 8, 1, 1, 0),
+                                  (3, 5, 8, 2, 4, 8, 9, 9, 9), (4, 4, 4, 4, 4, 4, 0, 0, 0)])
+def test_sta_build_matches_oracle(m, orc, grid):
+    a = m.sta_build(*grid)
+    b = orc.sta_layout(*grid)
+    for key in ("perm", "tile_len", "row_ptr", "col_idx"):
+        assert np.array_equal(a[key], b[key]), key
+    assert a["tile_tokens"] == b["tile_tokens"] and a["n_tiles"] == b["n_tiles"]
+
+
+def test_sta_build_capacity_error(m):
+    L = m.lib()
+    perm = np.zeros(92160, np.int32)
+    tl = np.zeros(240, np.int32)
+    rp = np.zeros(241, np.int32)
+    ci = np.zeros(10, np.int32)
+    nnz = ctypes.c_int32(0)
+    st = L.fp8attn_sta_build(21, 45, 80, 6, 8, 8, 1, 1, 1, perm.ctypes.data, tl.ctypes.data,
+                             rp.ctypes.data, ci.ctypes.data, 10, ctypes.byref(nnz))
+    assert st == 1 and nnz.value == 4480
+
+
+def test_workspace_sizes(m):
+    L = m.lib()
+    assert L.fp8attn_quantize_workspace_bytes(1, 75600, 40, 128, 0) >= 40 * 591 * 128 * 4
+    assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0) == 0
+    assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1) == 24 * 384 * 128 * 4
+    assert L.fp8attn_quantize_workspace_bytes(1, 100, 2, 64, 0) == 0

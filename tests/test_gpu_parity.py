@@ -1,0 +1,346 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: quantisation codes, scales and V-Smooth means bit-exact; attention outputs within
+max-abs 1e-2 and rel-L2 5e-3 of the oracle's FP8-path output on the compared rows (cosine
+against FP64 unquantised attention is checked >= 0.995 where the inputs are unstructured).
+Small cases run every row across several tiles and ragged tails; the full-size workloads run
+the same launch configuration as the benchmark and compare sampled rows of sampled heads.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL_L2, COS_MIN = 1e-2, 5e-3, 0.995
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_attention_video_qkv_amd as m
+    m.lib()
+    return m
+
+
+DEV = "cuda:0"
+
+
+def _bits(t):
+    return workloads.bits(t)
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _gpu_quantize(m, q, k, v, perm_q=None, perm_kv=None, vsmooth=False, n_layout=None):
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    pq = None if perm_q is None else torch.from_numpy(np.ascontiguousarray(perm_q)).to(DEV)
+    pkv = None if perm_kv is None else torch.from_numpy(np.ascontiguousarray(perm_kv)).to(DEV)
+    qz = m.quantize_qkv(qd, kd, vd, perm_q=pq, perm_kv=pkv, vsmooth=vsmooth, n_layout=n_layout)
+    torch.cuda.synchronize()
+    return qz
+
+
+def _compare_quant(qz, ref):
+    assert np.array_equal(_np(qz.q8), ref["q8"]), "q8"
+    assert np.array_equal(_np(qz.k8), ref["k8"]), "k8"
+    assert np.array_equal(_np(qz.v8t), ref["v8t"]), "v8t"
+    for key in ("q_scale", "k_scale", "v_scale"):
+        assert np.array_equal(_np(getattr(qz, key)).view(np.uint32), ref[key].view(np.uint32)), key
+    if ref.get("v_mean") is not None:
+        assert np.array_equal(_np(qz.v_mean).view(np.uint16), ref["v_mean"]), "v_mean"
+
+
+def _compare_out(gpu_rows, ref_rows, what, amb=None):
+    """gpu_rows (BF16 values), ref_rows: [B, H, R, D] float64 over the compared rows.
+
+    Per element the GPU must be within 1e-2 of the oracle, plus half a BF16 step of the value
+    (the output is BF16, 2^-8 |O| at most), plus amb: what the documented evaluation error of
+    the kernel can explain (P codes within that error of a rounding boundary, where either code
+    is correct, and the E4M3 matrix-core truncation; see the oracle). rel-L2 over all compared
+    elements must stay below 5e-3 with no allowance."""
+    diff = np.abs(gpu_rows - ref_rows)
+    amb = np.zeros(diff.shape) if amb is None else amb
+    bf16 = 2.0 ** -8 * np.abs(ref_rows)
+    excess = diff - (ATOL + bf16 + amb)
+    max_all = float(diff.max()) if diff.size else 0.0
+    within = float(np.mean(diff <= ATOL)) if diff.size else 1.0
+    rel = float(np.linalg.norm(gpu_rows - ref_rows) / max(np.linalg.norm(ref_rows), 1e-30))
+    say(f"{what}: max_abs {max_all:.3e}, {100 * within:.3f}% of elements within 1e-2, "
+        f"max allowance used {float(np.max(diff - ATOL - bf16, initial=0)):.3e} "
+        f"(median amb {float(np.median(amb)) if amb.size else 0:.2e}), rel_l2 {rel:.3e}")
+    assert np.all(excess <= 0), (what, float(excess.max()))
+    assert rel <= RTOL_L2, (what, rel)
+    return max_all, rel
+
+
+def _cos(a, b):
+    return float(np.sum(a * b) / math.sqrt(np.sum(a * a) * np.sum(b * b)))
+
+
+def _gpu_rows(out, rows):
+    """GPU out [B, N, H, D] bf16 -> [B, H, R, D] float64 at the given source rows."""
+    o = out.float().cpu().numpy()[:, rows]
+    return np.ascontiguousarray(o.transpose(0, 2, 1, 3)).astype(np.float64)
+
+
+# ------------------------------------------------------------------------------------------
+# Quantisation: bit-exact
+# ------------------------------------------------------------------------------------------
+QUANT_CASES = [
+    ("dense512", dict(B=1, N=512, H=2, seed=1)),
+    ("ragged1000", dict(B=1, N=1000, H=3, seed=2)),
+    ("tiny37", dict(B=2, N=37, H=1, seed=3)),
+]
+
+
+@pytest.mark.parametrize("name,c", QUANT_CASES)
+@pytest.mark.parametrize("vsmooth", [False, True])
+def test_quantize_bit_exact(m, orc, name, c, vsmooth):
+    say("quantize", name, "vsmooth", vsmooth)
+    q, k, v = workloads.make_qkv(c["B"], c["N"], c["H"], c["seed"], kind="channel_outliers")
+    ref = orc.quantize(_bits(q), _bits(k), _bits(v), vsmooth=vsmooth)
+    qz = _gpu_quantize(m, q, k, v, vsmooth=vsmooth)
+    _compare_quant(qz, ref)
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_quantize_gather_bit_exact(m, orc, per_head):
+    say("quantize gather, per_head", per_head)
+    rng = np.random.default_rng(5)
+    Nsrc, N, H = 300, 384, 2
+    q, k, v = workloads.make_qkv(1, Nsrc, H, 7, kind="token_outliers")
+    perm_q = rng.permutation(N).astype(np.int32)
+    perm_q = np.where(perm_q >= Nsrc, -1, perm_q).astype(np.int32)
+    if per_head:
+        pkv = np.stack([rng.permutation(N) for _ in range(H)])[None].astype(np.int32)
+    else:
+        pkv = rng.permutation(N).astype(np.int32)
+    pkv = np.where(pkv >= Nsrc, -1, pkv).astype(np.int32)
+    for vs in (False, True):
+        ref = orc.quantize(_bits(q), _bits(k), _bits(v), perm_q=perm_q, perm_kv=pkv, vsmooth=vs)
+        qz = _gpu_quantize(m, q, k, v, perm_q=perm_q, perm_kv=pkv, vsmooth=vs, n_layout=N)
+        _compare_quant(qz, ref)
+
+
+def test_quantize_encoder_boundaries(m, orc):
+    """Every Q/K block holds 448 so its scale is 1 and codes are E4M3(x) itself: the values sit
+    on and around every rounding boundary of the E4M3 grid (the device conversion against
+    the oracle's round-to-nearest-even)."""
+    say("quantize boundaries")
+    grid = orc.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = (grid[:-1] + grid[1:]) / 2
+    vals = np.concatenate([grid, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9)])
+    vals = torch.tensor(np.concatenate([vals, -vals]), dtype=torch.float32)
+    # keep only values exactly representable in bf16 (the inputs are bf16)
+    vals = vals[vals.to(torch.bfloat16).float() == vals]
+    n_per_row = 127
+    rows = -(-vals.numel() // n_per_row)
+    N = ((rows + 63) // 64) * 64
+    x = torch.zeros((1, N, 1, 128), dtype=torch.float32)
+    flat = torch.zeros(N * n_per_row)
+    flat[: vals.numel()] = vals
+    x[0, :, 0, 1:] = flat.view(N, n_per_row)
+    x[0, :, 0, 0] = 448.0
+    xb = x.to(torch.bfloat16)
+    ref = orc.quantize(_bits(xb), _bits(xb), _bits(xb))
+    assert np.all(ref["q_scale"] == 1.0)
+    qz = _gpu_quantize(m, xb, xb, xb)
+    _compare_quant(qz, ref)
+
+
+# ------------------------------------------------------------------------------------------
+# Attention: small cases, every row
+# ------------------------------------------------------------------------------------------
+def _run_attn(m, qz, **kw):
+    out = m.forward(qz, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("N,H,reverse,S", [
+    (512, 2, True, 256.0), (512, 2, False, 256.0), (512, 2, False, 1.0), (512, 2, True, 448.0),
+    (1000, 3, True, 256.0), (1000, 3, False, 448.0), (37, 2, False, 256.0), (64, 1, True, 1.0),
+    (2500, 2, False, 256.0)])
+def test_attention_dense_small(m, orc, N, H, reverse, S):
+    say("dense", N, H, "reverse" if reverse else "forward", S)
+    q, k, v = workloads.make_qkv(1, N, H, seed=N + H)
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb)
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, p_scale=S, kv_reverse=reverse, return_amb=True)
+    qz = _gpu_quantize(m, q, k, v)
+    out = _run_attn(m, qz, p_scale=S, kv_order=int(reverse))
+    got = _gpu_rows(out, np.arange(N))
+    _compare_out(got, ref, f"dense N={N}", amb)
+    tr = lambda a: np.ascontiguousarray(orc.bf16_decode(a).transpose(0, 2, 1, 3))
+    ex, _, _ = orc.attention_ref(orc.MODE_EXACT, tr(qb), tr(kb), tr(vb))
+    c = _cos(got, ex)
+    say(f"cosine vs FP64 exact {c:.6f}")
+    assert c >= COS_MIN
+
+
+@pytest.mark.parametrize("N,reverse", [(512, True), (1000, False)])
+def test_attention_expcast_small(m, orc, N, reverse):
+    say("expcast", N, reverse)
+    q, k, v = workloads.make_qkv(1, N, 2, seed=11 + N)
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref, _, _, _, amb = orc.attention_fp8(orc.quantize(qb, kb, vb), kv_reverse=reverse,
+                                          expcast=True, return_amb=True)
+    qz = _gpu_quantize(m, q, k, v)
+    out = _run_attn(m, qz, kv_order=int(reverse), pcast=m.FP8ATTN_PCAST_EXPCAST)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, "expcast", amb)
+
+
+@pytest.mark.parametrize("N,reverse,expcast", [(1000, True, False), (768, False, True),
+                                               (300, False, False)])
+def test_attention_vsmooth_small(m, orc, N, reverse, expcast):
+    say("vsmooth", N, reverse, expcast)
+    H = 2
+    q, k, v = workloads.make_qkv(1, N, H, seed=21 + N, kind="token_outliers")
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    perm = orc.vsmooth_perm(vb)                         # [1, H, N], an input to both sides
+    ref_q = orc.quantize(qb, kb, vb, perm_kv=perm, vsmooth=True)
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=reverse, expcast=expcast,
+                                          return_amb=True)
+    qz = _gpu_quantize(m, q, k, v, perm_kv=perm, vsmooth=True)
+    _compare_quant(qz, ref_q)
+    out = _run_attn(m, qz, kv_order=int(reverse),
+                    pcast=m.FP8ATTN_PCAST_EXPCAST if expcast else m.FP8ATTN_PCAST_RNE)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, "vsmooth", amb)
+
+
+def test_vsmooth_constant_value_exact(m, orc):
+    say("vsmooth constant")
+    N, H = 700, 2
+    q, k, _ = workloads.make_qkv(1, N, H, seed=31)
+    c = torch.randn(128, generator=torch.Generator().manual_seed(3)) * 4
+    v = c.view(1, 1, 1, 128).expand(1, N, H, 128).contiguous().to(torch.bfloat16)
+    qz = _gpu_quantize(m, q, k, v, vsmooth=True)
+    for rev, pc in ((True, 0), (False, 1)):
+        out = _run_attn(m, qz, kv_order=int(rev), pcast=pc)
+        want = v.to(DEV)
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+
+
+def _sparse_case(m, orc, grid, H, seed, reverse, expcast=False):
+    T, Hg, W, tt, th, tw, rt, rh, rw = grid
+    lay = orc.sta_layout(*grid)
+    perm = lay["perm"]
+    n_src = T * Hg * W
+    q, k, v = workloads.make_qkv(1, n_src, H, seed=seed)
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb, perm_q=perm, perm_kv=perm)
+    ref, _, _, rv, amb = orc.attention_fp8(ref_q, kv_reverse=reverse, expcast=expcast, sparse=lay,
+                                           return_amb=True)
+    qz = _gpu_quantize(m, q, k, v, perm_q=perm, perm_kv=perm)
+    _compare_quant(qz, ref_q)
+    sp = m.sparse_to_device(m.sta_build(*grid), DEV)
+    out_rows = torch.from_numpy(perm).to(DEV)
+    out = _run_attn(m, qz, kv_order=int(reverse), sparse=sp, out_rows=out_rows, n_out=n_src,
+                    pcast=m.FP8ATTN_PCAST_EXPCAST if expcast else m.FP8ATTN_PCAST_RNE)
+    valid = perm >= 0
+    got = _gpu_rows(out, perm[valid])                    # GPU wrote O in source order
+    assert np.all(rv[0, 0][valid] == 1)
+    _compare_out(got, ref[:, :, valid], f"sparse {grid[:3]}", amb[:, :, valid])
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_attention_sparse_small(m, orc, reverse):
+    say("sparse (10,20,20) tiles (6,8,8)", reverse)
+    _sparse_case(m, orc, (10, 20, 20, 6, 8, 8, 1, 1, 1), H=2, seed=41, reverse=reverse)
+
+
+def test_attention_sparse_expcast_and_odd_tiles(m, orc):
+    say("sparse expcast; 64-token tiles")
+    _sparse_case(m, orc, (10, 20, 20, 6, 8, 8, 1, 1, 1), H=1, seed=42, reverse=True, expcast=True)
+    _sparse_case(m, orc, (5, 7, 9, 2, 4, 8, 1, 1, 0), H=2, seed=43, reverse=False)
+    _sparse_case(m, orc, (9, 10, 11, 3, 8, 8, 1, 0, 1), H=1, seed=44, reverse=True)
+
+
+@pytest.mark.parametrize("delta,S,reverse", [(7, 1.0, False), (7, 256.0, True), (9, 256.0, False)])
+def test_underflow_counter(m, orc, delta, S, reverse):
+    say("underflow", delta, S, reverse)
+    q, k, v = workloads.workload("sink4096", delta=delta, heads=2)
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb)
+    ref, _, uf, _, amb = orc.attention_fp8(ref_q, p_scale=S, kv_reverse=reverse, return_amb=True)
+    qz = _gpu_quantize(m, q, k, v)
+    cnt = torch.zeros(2, dtype=torch.int64, device=DEV)
+    out = _run_attn(m, qz, p_scale=S, kv_order=int(reverse), underflow=cnt)
+    _compare_out(_gpu_rows(out, np.arange(4096)), ref, "sink", amb)
+    g = _np(cnt).astype(np.float64)
+    o = uf.sum(axis=2)[0].astype(np.float64)
+    say("underflow gpu", g, "oracle", o)
+    total = 4096 * 4096
+    assert np.all(np.abs(g - o) <= 1e-4 * total + 1e-3 * o)
+
+
+# ------------------------------------------------------------------------------------------
+# Full-size workloads (benchmark launch configuration), sampled heads and rows
+# ------------------------------------------------------------------------------------------
+def _slice_heads(t, heads):
+    return t[:, :, heads, :].contiguous()
+
+
+@pytest.mark.parametrize("name", ["wan13b", "wan14b", "vsmooth"])
+def test_full_size_sampled(m, orc, name):
+    say("full size", name)
+    q, k, v = workloads.workload(name)
+    B, N, H, _ = q.shape
+    heads = [0, H - 1]
+    vs = name == "vsmooth"
+    perm = None
+    if vs:
+        perm_s = orc.vsmooth_perm(_bits(_slice_heads(v, heads)))     # [1, 2, N]
+        perm = np.zeros((1, H, N), np.int32)
+        perm[:] = np.arange(N, dtype=np.int32)
+        perm[0, heads] = perm_s[0]
+    qz = _gpu_quantize(m, q, k, v, perm_kv=perm, vsmooth=vs)
+    out = _run_attn(m, qz, kv_order=1, pcast=m.FP8ATTN_PCAST_EXPCAST if vs else m.FP8ATTN_PCAST_RNE)
+    qs, ks, vsl = (_bits(_slice_heads(t, heads)) for t in (q, k, v))
+    ref_q = orc.quantize(qs, ks, vsl, perm_kv=None if perm is None else perm[:, heads], vsmooth=vs)
+    for key in ("q8", "k8", "v8t"):
+        assert np.array_equal(_np(getattr(qz, key)[:, heads]), ref_q[key]), key
+    for key in ("q_scale", "k_scale", "v_scale"):
+        assert np.array_equal(_np(getattr(qz, key)[:, heads]), ref_q[key]), key
+    rows = workloads.sample_rows(N, 48, seed=7)
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, rows=rows, kv_reverse=True, expcast=vs,
+                                          return_amb=True)
+    got = _gpu_rows(out[:, :, heads], rows)
+    _compare_out(got, ref, name, amb)
+
+
+def test_full_size_sparse_sampled(m, orc):
+    say("full size wan14b sparse")
+    q, k, v = workloads.workload("wan14b")
+    B, N, H, _ = q.shape
+    grid = (21, 45, 80, 6, 8, 8, 1, 1, 1)
+    lay = m.sta_build(*grid)
+    perm = lay["perm"]
+    qz = _gpu_quantize(m, q, k, v, perm_q=perm, perm_kv=perm)
+    sp = m.sparse_to_device(lay, DEV)
+    out = _run_attn(m, qz, kv_order=1, sparse=sp, out_rows=torch.from_numpy(perm).to(DEV), n_out=N)
+    heads = [0, H - 1]
+    qs, ks, vsl = (_bits(_slice_heads(t, heads)) for t in (q, k, v))
+    ref_q = orc.quantize(qs, ks, vsl, perm_q=perm, perm_kv=perm)
+    assert np.array_equal(_np(qz.k8[:, heads]), ref_q["k8"])
+    valid_pos = np.flatnonzero(perm >= 0)
+    rng = np.random.default_rng(9)
+    pos = np.unique(np.concatenate([valid_pos[:2], valid_pos[-2:], rng.choice(valid_pos, 96)]))
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, rows=pos.astype(np.int32), kv_reverse=True,
+                                          sparse=orc.sta_layout(*grid), return_amb=True)
+    got = _gpu_rows(out[:, :, heads], perm[pos])
+    _compare_out(got, ref, "wan14b sparse", amb)

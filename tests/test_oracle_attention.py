@@ -370,3 +370,29 @@ def test_vsmooth_perm_properties(orc):
         ids = [c for c in range(16) if np.any(lab == c)]
         d2 = ((f[:, None, :] - cent[None]) ** 2).sum(axis=2)
         assert np.array_equal(np.array(ids)[d2.argmin(axis=1)], lab)
+
+
+def test_ambiguity_bound_flags_a_midpoint(orc):
+    # Two keys on exactly representable operands (all scales 1); the softmax scale puts S p of
+    # the second key exactly on the midpoint 248 between the E4M3 values 240 and 256 (S = 256),
+    # so either code is a correct FP32 outcome and the bound must cover one grid step.
+    D = 128
+    qb = np.zeros((1, 2, 1, D), np.float32)
+    kb = np.zeros((1, 2, 1, D), np.float32)
+    vb = np.zeros((1, 2, 1, D), np.float32)
+    qb[0, :, 0, 0] = 448.0
+    kb[0, 0, 0, 0] = 448.0
+    kb[0, 1, 0, 0] = 416.0
+    vb[0, 1, 0, :] = 448.0
+    to = lambda a: torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    qz = orc.quantize(to(qb), to(kb), to(vb))
+    x_gap = 448.0 * 32.0                                  # logit gap of the two keys, code units
+    sc = -math.log(248.0 / 256.0) / x_gap                 # exp(-gap * sc) = 248 / 256
+    rows = np.array([0], np.int32)
+    _, _, _, _, amb = orc.attention_fp8(qz, rows=rows, softmax_scale=sc, return_amb=True)
+    l = 1.0 + 248.0 / 256.0
+    flip = 16.0 * 448.0 / (256.0 * l)                     # one grid step of key 2, |V_2| = 448
+    # plus the matrix-core truncation allowance (2^-11 of the largest P8 V of the key group)
+    assert flip <= amb[0, 0, 0].min() and amb[0, 0, 0].max() <= flip * 1.03
+    _, _, _, _, amb2 = orc.attention_fp8(qz, rows=rows, softmax_scale=sc * 1.3, return_amb=True)
+    assert amb2[0, 0, 0].max() < 0.03 * flip              # no ambiguous code: truncation only
