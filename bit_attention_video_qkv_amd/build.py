@@ -35,6 +35,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed building libfp8attn")
     if verbose:
         sys.stderr.write(res.stderr)
+    # every kernel launch stub must resolve (a toolchain quirk can leave them undefined)
+    import ctypes
+    ctypes.CDLL(tmp, mode=ctypes.RTLD_GLOBAL | os.RTLD_NOW)
     os.replace(tmp, LIB)
     return LIB
 
