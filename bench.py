@@ -53,6 +53,8 @@ def main():
     ap.add_argument("--workload", default="wan14b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -65,6 +67,10 @@ def main():
 
     import bit_attention_video_qkv_amd as fa
     import workloads
+
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
 
     cfg_name, sparse, vs, desc = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -160,6 +166,18 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, cfg_name, sparse, vs)
     print(json.dumps(result), flush=True)
+
+
+def calibrate_copy(torch, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE readings per
+    dispatch give the factor that turns those counters into HBM bytes for the other kernels."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def cpu_baseline(args, cfg_name, sparse, vs):

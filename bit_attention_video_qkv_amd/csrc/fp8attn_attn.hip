@@ -16,11 +16,17 @@
 //    [32h, 32h+32) of the block; the E4M3 P bytes of a lane are then exactly the B operand of
 //    O^T = V^T P^T, whose A operand is 32 contiguous key bytes of a token-contiguous V row.
 //  * O^T accumulators give every lane one query, so the softmax rescale is a per-lane scalar.
-//  * K and V tiles (8 KB each per 64 keys) are staged in LDS by direct global->LDS loads,
-//    double buffered, with XOR-swizzled 16-byte chunks for conflict-free operand reads.
-//  * One wave owns 64 queries (two 32-row sub-tiles sharing every K/V operand read); a
-//    workgroup has 4 waves (dense) or 2 waves (sparse, so a workgroup never straddles a
-//    384-token query tile). Workgroups are mapped XCD-major so each XCD streams one head's K/V.
+//  * One wave owns 64 queries as two 32-row sub-tiles A and B and runs alone on its SIMD. The
+//    two sub-tiles are software-pipelined inside the wave: while the VALU computes the softmax
+//    of one sub-tile, the matrix core runs the other sub-tile's QK of the same (or next) key
+//    block and its PV of the previous one, so the exp/convert work (the longer of the two on
+//    this chip) overlaps the MFMAs without a second wave or a barrier between them.
+//  * K and V tiles (8 KB each per 64 keys) reach LDS by direct global->LDS copies, three key
+//    blocks deep, in three separately declared slots so that the compiler can tell an operand
+//    read of one slot from a copy still landing in another. One barrier per key block.
+//  * Workgroups are mapped XCD-major so each XCD streams the K/V of few heads through its L2.
+#include <type_traits>
+
 #include "fp8attn_common.h"
 #include "fp8attn_internal.h"
 
@@ -67,43 +73,101 @@ __device__ __forceinline__ v8i load_op_lds(const uint8_t* base, int off0, int of
   return r;
 }
 
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm_lgkm() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
+// Waits until at most N vector-memory operations of this wave are outstanding (they complete
+// in issue order, so every older global->LDS copy has landed).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // Workgroup barrier without the release/acquire fence of __syncthreads(): that fence makes the
-// compiler wait for every outstanding global->LDS copy, including prefetches meant to stay in
-// flight across the barrier. Callers order their own LDS traffic with explicit waits; the
-// "memory" clobber keeps the compiler from moving memory operations across the barrier.
+// compiler wait for every outstanding global->LDS copy, including those meant to stay in flight
+// across the barrier. Callers order their own LDS traffic with explicit waits; the "memory"
+// clobber keeps the compiler from moving memory operations across the barrier.
 __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
-// Iteration state over the key blocks of one query tile.
+// Direct global->LDS copies (each lane: 16 or 4 bytes from gbase + voff to LDS lds_addr + 16 *
+// lane or + 4 * lane). Issued as opaque instructions: the compiler would otherwise treat every
+// later LDS read as possibly overlapping a copy still in flight and drain all of them first,
+// which would cost the copies' prefetch distance. The kernel orders them itself (explicit
+// vmcnt waits and barriers).
+__device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)p));
+}
+// A wave-uniform pointer as an SGPR pair (the copies take their base from scalar registers).
+__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(gbase)),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(gbase)),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+// Interleaving of one key block's softmax with the eight MFMAs of the wave (PV of the previous
+// block first, QK of the next block last) and the sixteen 16-byte operand reads of the next
+// pair: each MFMA is followed by a run of VALU work long enough to cover its 64-cycle issue on
+// the matrix core.
+__device__ __forceinline__ void interleave_block() {
+#ifndef FP8ATTN_NO_IGLP
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (PV)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 18, 0);  // VALU
+  }
+  __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // VALU
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (QK)
+    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
+  }
+#endif
+}
+
+// Dense/sparse key-block cursor of the copy engine.
 struct KvCursor {
-  int e;    // sparse: CSR entry; dense: block counter
-  int bt;   // sparse: block within the KV tile
+  int e;     // sparse: CSR entry; dense: block counter
+  int bt;    // sparse: block within the KV tile
+  int v;     // sparse: KV tile id col_idx[e]
+  int len;   // sparse: valid tokens of tile v
 };
 
-// One workgroup owns WAVES * 32 query rows of one (b, h); each wave owns 32 rows.
+// One workgroup owns WAVES * 32 query rows of one (b, h); each wave owns 32 of them.
 //
-// Schedule. Key block j is consumed in two phases per wave:
-//   M(j): PV of block j-1 (V^T P^T on the matrix cores) and QK of block j (K Q^T), on operands
-//         already in registers;
-//   V(j): online softmax of block j and its P cast (VALU), during which the wave reads the
-//         operands of the next pair from LDS.
-// LDS "pair" p (buffer p % 3) holds V tile p-1, K tile p, s_k of block p and its valid key
-// count (plus, for V-Smooth, the mean factors of V tile p-1's 128-row block). The first group
-// of waves stages pair j+2 by direct global->LDS copies right after its prefetch reads in V(j)
-// and waits for it at the end of M(j+1), so no LDS read ever follows a copy it does not need.
-// With GROUPS == 2 the second half of the waves runs one phase behind the first half; waves w
-// and w + WAVES/2 share a SIMD, so one wave's softmax overlaps the other wave's MFMAs. A barrier
-// closes every phase.
-template <int WAVES, int GROUPS, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd(AttnParams p) {
+// Schedule of key block j inside a wave (the operands named are already in registers):
+//   MFMA:  PV of block j-1 (V(j-1), P(j-1)) first, QK of block j+1 (K(j+1)) last
+//   VALU:  online softmax of block j on S(j), producing P(j), in between
+//   LDS:   the operands of the next block, V(j) and K(j+1), read from slot "pair j+1" after
+//          the MFMAs that consumed the previous values
+//   end:   rescale of O by alpha(j) (PV(j-1) long done), wait for pair j+2, barrier, copy
+//          pair j+4 into the slot just read.
+// Pair p (slot p % 3) holds the K tile of key block p with its s_k and valid-key count and the
+// V tile of key block p-1 (for V-Smooth, with the mean factors of that block's 128-row V block).
+// QK(j+1) writes its result into the registers the softmax of block j has just consumed, so a
+// wave needs one S tile of registers; two workgroups share each CU, so every SIMD runs two such
+// waves whose barriers and dependency stalls cover each other.
+template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd(AttnParams p) {
+  constexpr int kThreads = WAVES * 64;
   constexpr int kRowsPerWg = WAVES * 32;
-  constexpr int kLoaders = (WAVES / GROUPS) * 64;
-  constexpr int kMetaOff = 2 * kTileBytes;          // s_k (f32), valid keys (i32)
-  constexpr int kMeanOff = kMetaOff + 16;           // V-Smooth mean factors, 128 x f32
-  constexpr int kPairBytes = kMeanOff + (VSMOOTH ? kHeadDim * 4 : 0);
-  constexpr int kBufs = 3;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kBufs][kPairBytes];
+  constexpr int kChunks = 512 / kThreads;       // 16-byte chunks per thread of one 8 KB tile
+  constexpr int kMetaOff = 2 * kTileBytes;      // s_k (f32) and valid keys (i32) of the K block
+  constexpr int kMeanOff = kMetaOff + 16;       // V-Smooth mean factors, 128 x f32
+  constexpr int kSlotBytes = kMeanOff + (VSMOOTH ? kHeadDim * 4 : 0);  // multiple of 16
+  constexpr int kMeanLanes = 32 / WAVES;        // V-Smooth: lanes per wave copying the factors
+  constexpr int kCopies = 2 * kChunks + (VSMOOTH ? 1 : 0);  // copies per pair (wave 0: +1, s_k)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kSlotBytes];
+  auto slot = [&](int i) -> uint8_t* { return lds + i * kSlotBytes; };
 
   // ---- work item (XCD-major: dispatch round-robins workgroups over the 8 XCDs) ----
   const int per_xcd = (p.total_work + 7) / 8;
@@ -114,12 +178,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   const int64_t b = bh / p.H, h = bh % p.H;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lane = tid & 63;
-  const int lh = lane >> 5;   // lane half
+  const int lh = lane >> 5;  // lane half
   const int l32 = lane & 31;
-  const int group = (GROUPS == 2 && wave >= WAVES / 2) ? 1 : 0;
-  const bool loader = tid < kLoaders;
 
   // ---- sparse row of this query tile ----
   int e_begin = 0, e_end = 0, q_valid_len = 0;
@@ -130,31 +192,33 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     q_valid_len = p.tile_len[u];
     if (static_cast<int>(q0 % p.tile_tokens) >= q_valid_len) return;  // all padding rows
   }
+  const int per_tile = p.tile_tokens / kBlock;
+  auto nblk_of_len = [&](int len) -> int { return min((len + kBlock - 1) / kBlock, per_tile); };
 
   // ---- key-block sequence ----
-  auto nblk_of_tile = [&](int e) -> int {
-    const int v = p.col_idx[e];
-    return min((p.tile_len[v] + kBlock - 1) / kBlock, p.tile_tokens / kBlock);
-  };
   int n_iter = 0;
   if constexpr (SPARSE) {
-    for (int e = e_begin; e < e_end; e++) n_iter += nblk_of_tile(e);
+    for (int e = e_begin; e < e_end; e++) n_iter += nblk_of_len(p.tile_len[p.col_idx[e]]);
   } else {
     n_iter = static_cast<int>(p.NB);
   }
-  KvCursor lc;  // the loaders' cursor: the next K block to stage
+  if (n_iter == 0) return;  // a query tile without key blocks has no defined output
+
+  KvCursor lc;  // the copy engine's cursor: the next K block to stage
+  lc.e = 0;
+  lc.bt = 0;
+  lc.v = 0;
+  lc.len = 0;
   if constexpr (SPARSE) {
     lc.e = p.reverse ? e_end - 1 : e_begin;
-    lc.bt = (p.reverse && e_end > e_begin) ? nblk_of_tile(e_end - 1) - 1 : 0;
-  } else {
-    lc.e = 0;
-    lc.bt = 0;
+    lc.v = p.col_idx[lc.e];
+    lc.len = p.tile_len[lc.v];
+    lc.bt = p.reverse ? nblk_of_len(lc.len) - 1 : 0;
   }
   auto block_of = [&](const KvCursor& c, int& limit) -> int64_t {
     if constexpr (SPARSE) {
-      const int v = p.col_idx[c.e];
-      limit = min(kBlock, p.tile_len[v] - c.bt * kBlock);
-      return static_cast<int64_t>(v) * (p.tile_tokens / kBlock) + c.bt;
+      limit = min(kBlock, c.len - c.bt * kBlock);
+      return static_cast<int64_t>(c.v) * per_tile + c.bt;
     } else {
       const int64_t kb = p.reverse ? (p.NB - 1 - c.e) : c.e;
       limit = static_cast<int>(min<int64_t>(kBlock, p.N - kb * kBlock));
@@ -164,13 +228,21 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   auto advance = [&](KvCursor& c) {
     if constexpr (SPARSE) {
       if (!p.reverse) {
-        if (++c.bt >= nblk_of_tile(c.e)) {
+        if (++c.bt >= nblk_of_len(c.len)) {
           c.e++;
           c.bt = 0;
+          if (c.e < e_end) {
+            c.v = p.col_idx[c.e];
+            c.len = p.tile_len[c.v];
+          }
         }
       } else if (--c.bt < 0) {
         c.e--;
-        if (c.e >= e_begin) c.bt = nblk_of_tile(c.e) - 1;
+        if (c.e >= e_begin) {
+          c.v = p.col_idx[c.e];
+          c.len = p.tile_len[c.v];
+          c.bt = nblk_of_len(c.len) - 1;
+        }
       }
     } else {
       c.e++;
@@ -184,62 +256,56 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     return (kb >> 1) != (kn >> 1);
   };
 
-  // ---- staging of pair `pidx` (V tile pidx-1, K tile pidx) into buffer `buf` (loaders only) ----
-  // Each loader lane copies fixed 16-byte chunks: its byte offsets inside a K tile and inside a
-  // V tile are computed once; per pair only the wave-uniform tile base changes.
-  constexpr int kRounds = 512 / kLoaders;
+  // ---- staging of pair `pidx` into slot `sl` (every thread copies its fixed 16-byte chunks;
+  // per pair only the wave-uniform tile bases change) ----
   const uint8_t* kbase = p.k8 + bh * p.N64 * kHeadDim;
   const uint8_t* vbase = p.v8t + bh * kHeadDim * p.N64;
-  // fixed extent 4 (>= kRounds): an extent that depends on the template parameters makes the
+  // fixed extent 8 (>= kChunks): an extent that depends on the template parameters makes the
   // host pass of this toolchain drop the kernel launch stubs
-  static_assert(kRounds <= 4, "at least 128 loader threads");
-  uint32_t koff[4], voff[4];
+  static_assert(kChunks <= 8, "at least 64 threads");
+  uint32_t koff[8], voff[8];
 #pragma unroll
-  for (int r = 0; r < kRounds; r++) {
-    const int L = r * kLoaders + tid;
+  for (int r = 0; r < kChunks; r++) {
+    const int L = r * kThreads + tid;
     const int row = L >> 3;
     koff[r] = static_cast<uint32_t>(row * kHeadDim + (((L & 7) ^ swz_k(row)) * 16));
     const int d = L >> 2;
     voff[r] = static_cast<uint32_t>(d * p.N64 + (((L & 3) ^ swz_v(d)) * 16));
   }
   int64_t kb_prev = 0;  // K block of the previous pair (= the V tile of this pair)
-  auto stage_pair = [&](int pidx, int buf) {
-    uint8_t* lk = &lds[buf][0];
-    uint8_t* lv = &lds[buf][kTileBytes];
-    int64_t kb = 0;
+  auto stage = [&](int pidx, uint8_t* sl) {
+    int64_t kb = kb_prev;  // pair n_iter carries no K block: its K copy repeats a valid tile
+    int limit = kBlock;
     if (pidx < n_iter) {
-      int limit_k;
-      kb = block_of(lc, limit_k);
-      const uint8_t* kt = kbase + kb * kTileBytes;
-#pragma unroll
-      for (int r = 0; r < kRounds; r++)
-        __builtin_amdgcn_global_load_lds(kt + koff[r],
-                                         (__attribute__((address_space(3))) void*)(lk + (r * kLoaders + wave * 64) * 16),
-                                         16, 0, 0);
-      if (wave == 0 && lane == 0) {
-        __builtin_amdgcn_global_load_lds(p.k_scale + bh * p.NB + kb,
-                                         (__attribute__((address_space(3))) void*)(&lds[buf][kMetaOff]), 4, 0, 0);
-        *reinterpret_cast<int*>(&lds[buf][kMetaOff + 4]) = limit_k;
-      }
+      kb = block_of(lc, limit);
       advance(lc);
     }
-    if (pidx >= 1) {
-      const uint8_t* vt = vbase + kb_prev * kBlock;
+    const int64_t vb = pidx >= 1 ? kb_prev : kb;  // pair 0 carries no V block (same: a valid tile)
+    const uint8_t* kt = kbase + kb * kTileBytes;
+    const uint8_t* vt = vbase + vb * kBlock;
+    const uint32_t l0 = lds_addr_of(sl);
 #pragma unroll
-      for (int r = 0; r < kRounds; r++)
-        __builtin_amdgcn_global_load_lds(vt + voff[r],
-                                         (__attribute__((address_space(3))) void*)(lv + (r * kLoaders + wave * 64) * 16),
-                                         16, 0, 0);
-      if constexpr (VSMOOTH) {
-        if (wave == 0 && lane < 32)
-          __builtin_amdgcn_global_load_lds(p.mu_f + (bh * p.NB128 + (kb_prev >> 1)) * kHeadDim + 4 * lane,
-                                           (__attribute__((address_space(3))) void*)(&lds[buf][kMeanOff]), 16, 0, 0);
-      }
+    for (int r = 0; r < kChunks; r++) copy16_to_lds(kt, koff[r], l0 + (r * kThreads + wave * 64) * 16);
+#pragma unroll
+    for (int r = 0; r < kChunks; r++) copy16_to_lds(vt, voff[r], l0 + kTileBytes + (r * kThreads + wave * 64) * 16);
+    if constexpr (VSMOOTH) {
+      if (lane < kMeanLanes)
+        copy16_to_lds(p.mu_f + (bh * p.NB128 + (vb >> 1)) * kHeadDim, 16u * (wave * kMeanLanes + lane),
+                      l0 + kMeanOff + wave * kMeanLanes * 16);
+    }
+    if (wave == 0 && lane == 0) {
+      copy4_to_lds(p.k_scale + bh * p.NB + kb, 0u, l0 + kMetaOff);
+      *reinterpret_cast<int*>(sl + kMetaOff + 4) = limit;
     }
     kb_prev = kb;
   };
+  // Waits until only the copies of the newest staged pair may still be in flight.
+  auto wait_all_but_newest = [&]() {
+    if (wave == 0) wait_vmcnt<kCopies + 1>();
+    else wait_vmcnt<kCopies>();
+  };
 
-  // ---- Q operands (B operand of S^T = K Q^T), straight from HBM ----
+  // ---- Q operand (B operand of S^T = K Q^T), straight from HBM ----
   const int64_t qrow = q0 + 32 * wave + l32;  // this lane's query row
   v8i qop[2];
 #pragma unroll
@@ -251,113 +317,102 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
       qop[c][4] = bq.x; qop[c][5] = bq.y; qop[c][6] = bq.z; qop[c][7] = bq.w;
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; j++) qop[c][j] = 0;
+      for (int w = 0; w < 8; w++) qop[c][w] = 0;
     }
   }
   const int64_t qblk = (q0 + 32 * wave) / kBlock;  // the wave's 32 rows lie in one Q block
   const float s_q = qblk < p.NB ? p.q_scale[bh * p.NB + qblk] : 0.0f;
 
   // ---- per-wave state ----
-  v16f oacc[4];
+  v16f oacc[4], sacc[2];
 #pragma unroll
   for (int dt = 0; dt < 4; dt++)
 #pragma unroll
     for (int r = 0; r < 16; r++) oacc[dt][r] = 0.0f;
-  v16f sacc[2];
-  v8i pop;
+  v8i pop;  // E4M3 P bytes (B operand of O^T = V^T P^T)
 #pragma unroll
   for (int w = 0; w < 8; w++) pop[w] = 0;
   float m_run = -INFINITY;  // running max, log2 units
   float l_part = 0.0f;      // this lane's 32-key share of the S-scaled row sum
-  float r_cur = 0.0f;       // V-Smooth: S-scaled row sum of the open 128-row V block
-  float r_done = 0.0f;      // V-Smooth: closed V block awaiting its mean in the next M phase
-  bool mean_due = false;    // V-Smooth: r_done holds a closed block (uniform over the wave)
-  float s_k = 0.0f;
-  int limit = kBlock;
+  float r_cur = 0.0f;       // V-Smooth: S-scaled row sum of the open V block
   unsigned long long n_under = 0;
-
-  // Operands of the next M phase, read from LDS during the V phase before it.
   v8i kop[2][2], vop[4];
-  float s_k_next = 0.0f;
-  int limit_next = kBlock;
-  auto read_pair = [&](int pidx) {
-    const uint8_t* base = &lds[pidx % kBufs][0];
-    if (pidx >= 1) {
+  float sk_cur = 0.0f, sk_next = 0.0f;
+  int lim_cur = kBlock, lim_next = kBlock;
+
+  // Per-lane byte offsets of the 16-byte operand chunks inside a slot (K rows in the permuted
+  // order, swizzled chunks).
+  uint32_t kro[8], vro[8];
 #pragma unroll
-      for (int dt = 0; dt < 4; dt++) {
-        const int d = 32 * dt + l32;
-        const int sw = swz_v(d);
-        vop[dt] = load_op_lds(base + kTileBytes, d * kBlock + ((2 * lh) ^ sw) * 16,
-                              d * kBlock + ((2 * lh + 1) ^ sw) * 16);
-      }
+  for (int t = 0; t < 2; t++) {
+    const int row = k_row_of(t, l32);
+    const int sw = swz_k(row);
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      const int c0 = 4 * c + 2 * lh;
+      kro[4 * t + 2 * c] = static_cast<uint32_t>(row * kHeadDim + (c0 ^ sw) * 16);
+      kro[4 * t + 2 * c + 1] = static_cast<uint32_t>(row * kHeadDim + ((c0 + 1) ^ sw) * 16);
     }
-    if (pidx < n_iter) {
+  }
 #pragma unroll
-      for (int t = 0; t < 2; t++) {
-        const int row = k_row_of(t, l32);
-        const int sw = swz_k(row);
+  for (int dt = 0; dt < 4; dt++) {
+    const int d = 32 * dt + l32;
+    const int sw = swz_v(d);
+    vro[2 * dt] = static_cast<uint32_t>(kTileBytes + d * kBlock + ((2 * lh) ^ sw) * 16);
+    vro[2 * dt + 1] = static_cast<uint32_t>(kTileBytes + d * kBlock + ((2 * lh + 1) ^ sw) * 16);
+  }
+  auto read_k = [&](const uint8_t* base) {
 #pragma unroll
-        for (int c = 0; c < 2; c++) {
-          const int c0 = 4 * c + 2 * lh;
-          kop[t][c] = load_op_lds(base, row * kHeadDim + (c0 ^ sw) * 16, row * kHeadDim + ((c0 + 1) ^ sw) * 16);
-        }
-      }
-      s_k_next = *reinterpret_cast<const float*>(base + kMetaOff);
-      limit_next = *reinterpret_cast<const int*>(base + kMetaOff + 4);
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int c = 0; c < 2; c++) kop[t][c] = load_op_lds(base, kro[4 * t + 2 * c], kro[4 * t + 2 * c + 1]);
+  };
+  auto read_v = [&](const uint8_t* base) {
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) vop[dt] = load_op_lds(base, vro[2 * dt], vro[2 * dt + 1]);
+  };
+  auto read_meta = [&](const uint8_t* base) {
+    sk_next = *reinterpret_cast<const float*>(base + kMetaOff);
+    lim_next = *reinterpret_cast<const int*>(base + kMetaOff + 4);
+  };
+  auto qk = [&]() {
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      v16f z;
+#pragma unroll
+      for (int r = 0; r < 16; r++) z[r] = 0.0f;
+      sacc[t] = mfma_f8(kop[t][0], qop[0], z);
+      sacc[t] = mfma_f8(kop[t][1], qop[1], sacc[t]);
     }
   };
-
-  // M(j): PV of block j-1 and QK of block j on the prefetched operands of pair j.
-  auto phase_m = [&](int j) {
-    if constexpr (VSMOOTH) {
-      if (mean_due) {
-        const float* mu = reinterpret_cast<const float*>(&lds[j % kBufs][kMeanOff]);
+  auto pv = [&]() {
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-          for (int g = 0; g < 4; g++) {
-            const float4 m4 = *reinterpret_cast<const float4*>(mu + 32 * dt + 8 * g + 4 * lh);
-            oacc[dt][4 * g + 0] = __builtin_fmaf(r_done, m4.x, oacc[dt][4 * g + 0]);
-            oacc[dt][4 * g + 1] = __builtin_fmaf(r_done, m4.y, oacc[dt][4 * g + 1]);
-            oacc[dt][4 * g + 2] = __builtin_fmaf(r_done, m4.z, oacc[dt][4 * g + 2]);
-            oacc[dt][4 * g + 3] = __builtin_fmaf(r_done, m4.w, oacc[dt][4 * g + 3]);
-          }
-      }
-      r_done = 0.0f;
-      mean_due = false;
-    }
-    if (j >= 1) {
-#pragma unroll
-      for (int dt = 0; dt < 4; dt++) oacc[dt] = mfma_f8(vop[dt], pop, oacc[dt]);
-    }
-    if (j < n_iter) {
-      s_k = s_k_next;
-      limit = limit_next;
-#pragma unroll
-      for (int t = 0; t < 2; t++) {
-        v16f z;
-#pragma unroll
-        for (int r = 0; r < 16; r++) z[r] = 0.0f;
-        sacc[t] = mfma_f8(kop[t][0], qop[0], z);
-        sacc[t] = mfma_f8(kop[t][1], qop[1], sacc[t]);
-      }
-    }
+    for (int dt = 0; dt < 4; dt++) oacc[dt] = mfma_f8(vop[dt], pop, oacc[dt]);
   };
 
-  // V(j): online softmax of block j and its E4M3 P bytes.
-  auto phase_v = [&](int j) {
-    read_pair(j + 1);
-    if (loader && j + 2 <= n_iter) stage_pair(j + 2, (j + 2) % kBufs);
-    const float cs = fmaxf(s_q * s_k * p.logit_scale, 1e-30f);  // log2 units per MFMA unit
+  // Orders the QK MFMAs of key sub-tile t of the next block after the P bytes of sub-tile t of
+  // this block (a register dependency through an empty asm): the compiler would otherwise issue
+  // QK first and keep both S tiles alive, or sink the softmax past the end of the block.
+  // The row-sum partial rides along so that its adds stay in this block as well.
+  auto tie_k = [&](int t, float& lsum_part) {
+    asm volatile("" : "+v"(kop[t][0]), "+v"(kop[t][1]), "+v"(lsum_part) : "v"(pop[4 * t]), "v"(pop[4 * t + 1]),
+                 "v"(pop[4 * t + 2]), "v"(pop[4 * t + 3]));
+  };
+
+  // Online softmax of block j on the S^T accumulators: updates the running state, writes the
+  // E4M3 P bytes into pop and returns alpha.
+  auto softmax = [&](auto mask_tag) -> float {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    const float cs = fmaxf(s_q * sk_cur * p.logit_scale, 1e-30f);  // log2 units per MFMA unit
     float x[32];
 #pragma unroll
     for (int t = 0; t < 2; t++)
 #pragma unroll
       for (int r = 0; r < 16; r++) x[16 * t + r] = sacc[t][r];
-    if (limit < kBlock) {
+    if constexpr (kMask) {
+      const int nv = lim_cur - 32 * lh;  // valid keys among this lane's 32
 #pragma unroll
-      for (int q = 0; q < 32; q++)
-        if (32 * lh + q >= limit) x[q] = -INFINITY;
+      for (int q = 0; q < 32; q++) x[q] = q < nv ? x[q] : -INFINITY;
     }
     // two chains of three-input maxima
     float mlo = fmaxf(x[0], x[1]), mhi = fmaxf(x[2], x[3]);
@@ -374,7 +429,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_cand;
     float lsum;
-    uint32_t pk[8];
     if constexpr (EXPCAST) {
       const float c8 = 8.0f * cs;
       const float b8 = 8.0f * (p.log2S - m_new) + 55.65f;
@@ -388,78 +442,139 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
           const float code = fminf(fmaxf(__builtin_rintf(tq), 0.0f), 126.0f);
           word |= static_cast<uint32_t>(code) << (8 * q);
         }
-        pk[w] = word;
+        pop[w] = static_cast<int>(word);
         const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(word), false);
         const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(word), true);
         l4[w & 3] += (lo[0] + lo[1]) + (hi[0] + hi[1]);
       }
       lsum = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+      tie_k(0, lsum);
+      tie_k(1, lsum);
     } else {
       const float bias = p.log2S - m_new;
-      float pv[32];
+      // key sub-tile by key sub-tile (t = 0: x[0..15], t = 1: x[16..31]), so that the QK MFMAs of
+      // the next block can take over each sub-tile's accumulator registers as soon as its P bytes
+      // exist (see tie_k)
+      lsum = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 32; q++) pv[q] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[q], cs, bias));
-      // tree sum (eight independent chains) keeps the adds off one dependency chain
-      float l8[8];
+      for (int t = 0; t < 2; t++) {
+        float pv[16];
 #pragma unroll
-      for (int q = 0; q < 8; q++) l8[q] = (pv[q] + pv[q + 8]) + (pv[q + 16] + pv[q + 24]);
-      lsum = ((l8[0] + l8[1]) + (l8[2] + l8[3])) + ((l8[4] + l8[5]) + (l8[6] + l8[7]));
+        for (int q = 0; q < 16; q++) pv[q] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[16 * t + q], cs, bias));
+        // tree sum (four independent chains) keeps the adds off one dependency chain
+        float l4[4];
 #pragma unroll
-      for (int w = 0; w < 8; w++) pk[w] = e4m3x4(pv[4 * w], pv[4 * w + 1], pv[4 * w + 2], pv[4 * w + 3]);
-      if constexpr (STATS) {
-        if (qrow < p.N) {
+        for (int q = 0; q < 4; q++) l4[q] = (pv[q] + pv[q + 4]) + (pv[q + 8] + pv[q + 12]);
+        float lt = (l4[0] + l4[1]) + (l4[2] + l4[3]);
 #pragma unroll
-          for (int q = 0; q < 32; q++)
-            n_under += (pv[q] > 0.0f && ((pk[q >> 2] >> (8 * (q & 3))) & 0xFFu) == 0u) ? 1ull : 0ull;
+        for (int w = 0; w < 4; w++) {
+          // the previous block's P bytes are dead once PV(j-1) has issued: converting into them
+          // saves clearing the destination (each convert writes one half of the word)
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * w], pv[4 * w + 1], pop[4 * t + w], false);
+          pop[4 * t + w] = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * w + 2], pv[4 * w + 3], lo, true);
         }
-      }
-    }
+        if constexpr (STATS) {
+          const unsigned long long valid = qrow < p.N ? 1ull : 0ull;
 #pragma unroll
-    for (int w = 0; w < 8; w++) pop[w] = static_cast<int>(pk[w]);
-    l_part = alpha * l_part + lsum;
-    if constexpr (VSMOOTH) {
-      r_cur = alpha * r_cur + xsum(lsum);
-      r_done *= alpha;
-      if (closes_vblock(j)) {
-        r_done = r_cur;
-        r_cur = 0.0f;
-        mean_due = true;
+          for (int q = 0; q < 16; q++)
+            n_under += (pv[q] > 0.0f && ((static_cast<uint32_t>(pop[4 * t + (q >> 2)]) >> (8 * (q & 3))) & 0xFFu) == 0u)
+                           ? valid
+                           : 0ull;
+        }
+        tie_k(t, lt);
+        lsum += lt;
       }
     }
-    // rescale O only when some row's max moved (alpha == 1 leaves O bit-identical)
+    l_part = alpha * l_part + lsum;
+    if constexpr (VSMOOTH) r_cur = alpha * r_cur + xsum(lsum);
+    return alpha;
+  };
+
+  // One key block j; `sl` is the slot of pair j+1 (read here, then refilled with pair j+4).
+  // The masked copy serves blocks with fewer than 64 valid keys.
+  auto iteration = [&](auto mask_tag, int j, uint8_t* sl) {
+    pv();         // PV of block j-1 (zero P bytes before the first block)
+    read_v(sl);   // V(j)
+    read_k(sl);   // K(j+1)
+    read_meta(sl);
+    const float alpha = softmax(mask_tag);
+    qk();         // QK of block j+1 (a dummy K tile after the last block: unused)
+    interleave_block();
+    // alpha == 1 in every lane leaves O bit-identical: skip the multiplies
     if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int dt = 0; dt < 4; dt++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
     }
+    if constexpr (VSMOOTH) {
+      if (closes_vblock(j)) {
+        // rank-one mean restore of the V block that block j closes (its factors travel in pair
+        // j+1); O holds blocks up to j-1 in the units of the running max of block j, like r
+        const float* mu = reinterpret_cast<const float*>(sl + kMeanOff);
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+          for (int g = 0; g < 4; g++) {
+            const float4 m4 = *reinterpret_cast<const float4*>(mu + 32 * dt + 8 * g + 4 * lh);
+            oacc[dt][4 * g + 0] = __builtin_fmaf(r_cur, m4.x, oacc[dt][4 * g + 0]);
+            oacc[dt][4 * g + 1] = __builtin_fmaf(r_cur, m4.y, oacc[dt][4 * g + 1]);
+            oacc[dt][4 * g + 2] = __builtin_fmaf(r_cur, m4.z, oacc[dt][4 * g + 2]);
+            oacc[dt][4 * g + 3] = __builtin_fmaf(r_cur, m4.w, oacc[dt][4 * g + 3]);
+          }
+        r_cur = 0.0f;
+      }
+    }
+    // hand-off: every read of this slot is complete, pair j+2 has landed everywhere
+    wait_lgkm0();
+    if (j + 3 <= n_iter) wait_all_but_newest();
+    else wait_vmcnt<0>();
+    barrier_nofence();
+    sk_cur = sk_next;
+    lim_cur = lim_next;
+    if (j + 4 <= n_iter) stage(j + 4, sl);
   };
 
-  // ---- prologue: pairs 0 and 1 staged, operands of pair 0 in registers ----
-  if (loader && n_iter > 0) {
-    stage_pair(0, 0);
-    stage_pair(1, 1);
+  // ---- prologue: pairs 0..2 staged; K(0) read; QK of block 0; pair 3 staged ----
+  stage(0, slot(0));
+  stage(1, slot(1));
+  if (n_iter >= 2) {
+    stage(2, slot(2));
+    wait_all_but_newest();
+  } else {
+    wait_vmcnt<0>();
   }
-  wait_vm();
-  __syncthreads();
-  read_pair(0);
+  barrier_nofence();
+  read_k(slot(0));
+  read_v(slot(0));  // a valid tile; it only meets the zero P bytes of PV(-1)
+  read_meta(slot(0));
+  qk();
+  wait_lgkm0();
+  barrier_nofence();
+  sk_cur = sk_next;
+  lim_cur = lim_next;
+  if (n_iter >= 3) stage(3, slot(0));
 
-  // ---- phases. The second group passes one extra barrier first, so its phase k runs beside
-  // the first group's phase k + 1 (s_barrier counts arrivals, not program points). ----
-  // Hand-offs: a pair staged by the loaders in V(j-1) is complete (copies and the valid-count
-  // store) before the barrier that ends M(j); every LDS read of a buffer is consumed by an MFMA
-  // (so complete) at least one barrier before the loaders overwrite that buffer.
-  if (group == 1) barrier_nofence();
-  for (int j = 0; j < n_iter; j++) {
-    phase_m(j);
-    if (loader) wait_vm_lgkm();  // pair j+1, staged during V(j-1), has landed
-    barrier_nofence();
-    phase_v(j);
-    barrier_nofence();
+  // ---- mainloop. Dense: the one block with fewer than 64 valid keys (the last key block, first
+  // in reverse order) runs in a masked copy outside the loop. Sparse: partial blocks sit at the
+  // end of tiles anywhere in the sequence, so every block takes the (cheap) masked path. ----
+  using kNoMask = std::integral_constant<bool, false>;
+  using kMasked = std::integral_constant<bool, true>;
+  using kLoopMask = std::integral_constant<bool, SPARSE>;
+  const bool partial_tail = !SPARSE && (p.N % kBlock) != 0;
+  int j_begin = 0, j_end = n_iter, sidx = 1;  // sidx: slot of pair j+1
+  if (partial_tail && p.reverse) {
+    iteration(kMasked{}, 0, slot(1));
+    j_begin = 1;
+    sidx = 2;
   }
-  phase_m(n_iter);  // PV of the last block
-  __syncthreads();
-  if (GROUPS == 2 && group == 0) __syncthreads();
+  if (partial_tail && !p.reverse) j_end = n_iter - 1;
+  for (int j = j_begin; j < j_end; j++) {
+    iteration(kLoopMask{}, j, slot(sidx));
+    sidx = sidx == 2 ? 0 : sidx + 1;
+  }
+  if (partial_tail && !p.reverse) iteration(kMasked{}, n_iter - 1, slot(sidx));
+  pv();  // PV of the last block (vop = V(n_iter - 1))
 
   if constexpr (STATS) {
     unsigned long long tot = n_under;
@@ -509,14 +624,13 @@ __global__ __launch_bounds__(128) void vsmooth_mean_factors(AttnParams p) {
   p.mu_f[idx] = bf16_to_f32(p.v_mean[idx]) * f;
 }
 
-template <int WAVES, int GROUPS, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS>
+template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS>
 hipError_t launch_variant(AttnParams& p, hipStream_t stream) {
   const int rows = WAVES * 32;
   p.n_qtiles = static_cast<int>((p.N + rows - 1) / rows);
   p.total_work = p.B * p.H * p.n_qtiles;
   const unsigned grid = static_cast<unsigned>(((p.total_work + 7) / 8) * 8);
-  hipLaunchKernelGGL((attn_fwd<WAVES, GROUPS, SPARSE, EXPCAST, VSMOOTH, STATS>), dim3(grid), dim3(WAVES * 64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((attn_fwd<WAVES, SPARSE, EXPCAST, VSMOOTH, STATS>), dim3(grid), dim3(WAVES * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -531,26 +645,26 @@ hipError_t launch_attention(AttnParams p, int variant, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // Dense: 8 waves of 32 queries in two ping-pong groups. Sparse: a workgroup stays inside one
-  // query tile (128 or 64 rows) and runs a single group.
+  // Dense: 4 waves (128 queries) per workgroup. Sparse: a workgroup stays inside one query tile
+  // (128 or 64 rows).
   if (sp && p.tile_tokens % 128 == 0) {
-    if (st) return launch_variant<4, 1, true, false, false, true>(p, stream);
-    if (ec) return launch_variant<4, 1, true, true, false, false>(p, stream);
-    return launch_variant<4, 1, true, false, false, false>(p, stream);
+    if (st) return launch_variant<4, true, false, false, true>(p, stream);
+    if (ec) return launch_variant<4, true, true, false, false>(p, stream);
+    return launch_variant<4, true, false, false, false>(p, stream);
   }
   if (sp) {
-    if (st) return launch_variant<2, 1, true, false, false, true>(p, stream);
-    if (ec) return launch_variant<2, 1, true, true, false, false>(p, stream);
-    return launch_variant<2, 1, true, false, false, false>(p, stream);
+    if (st) return launch_variant<2, true, false, false, true>(p, stream);
+    if (ec) return launch_variant<2, true, true, false, false>(p, stream);
+    return launch_variant<2, true, false, false, false>(p, stream);
   }
   if (vs) {
-    if (st) return launch_variant<8, 2, false, false, true, true>(p, stream);
-    if (ec) return launch_variant<8, 2, false, true, true, false>(p, stream);
-    return launch_variant<8, 2, false, false, true, false>(p, stream);
+    if (st) return launch_variant<4, false, false, true, true>(p, stream);
+    if (ec) return launch_variant<4, false, true, true, false>(p, stream);
+    return launch_variant<4, false, false, true, false>(p, stream);
   }
-  if (st) return launch_variant<8, 2, false, false, false, true>(p, stream);
-  if (ec) return launch_variant<8, 2, false, true, false, false>(p, stream);
-  return launch_variant<8, 2, false, false, false, false>(p, stream);
+  if (st) return launch_variant<4, false, false, false, true>(p, stream);
+  if (ec) return launch_variant<4, false, true, false, false>(p, stream);
+  return launch_variant<4, false, false, false, false>(p, stream);
 }
 
 }  // namespace fp8attn
