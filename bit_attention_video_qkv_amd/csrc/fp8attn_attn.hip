@@ -39,10 +39,15 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kTileBytes = kBlock * kHeadDim;  // 8 KB: one 64-key K tile or V tile
 
-// Physical 16-byte chunk of logical chunk cc in row `row` of the K tile (8 chunks per row).
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | (((row >> 5) & 1) << 2); }
-// Same for the V tile (4 chunks per 64-byte channel row).
-__device__ __forceinline__ int swz_v(int d) { return (d >> 1) & 3; }
+// XOR swizzle of the 16-byte chunks of a K tile row (8 chunks per 128-byte row): logical chunk c
+// of row `row` sits at c ^ swz_k(row). Chosen so that each operand read (ds_read_b128, lanes in
+// the permuted row order of k_row_of) touches every bank once per group of 8 lanes over 32
+// banks and per group of 16 lanes over 64 banks.
+__device__ __forceinline__ int swz_k(int row) {
+  return ((row >> 1) & 1) | (((row ^ (row >> 2)) & 1) << 1) | (((row >> 5) & 1) << 2);
+}
+// Same for the V tile (4 chunks per 64-byte channel row), for reads of 32 consecutive channels.
+__device__ __forceinline__ int swz_v(int d) { return ((d >> 2) & 1) | ((((d >> 1) ^ (d >> 3)) & 1) << 1); }
 
 // Key (row of the K tile) that feeds A-operand row i of key sub-tile t: chosen so that the
 // S^T accumulator register r of lane half h holds key 32h + 16t + r.
@@ -113,25 +118,32 @@ __device__ __forceinline__ void copy4_to_lds(const void* gbase, uint32_t voff, u
                : "memory", "m0");
 }
 
-// Interleaving of one key block's softmax with the eight MFMAs of the wave (PV of the previous
-// block first, QK of the next block last) and the sixteen 16-byte operand reads of the next
-// pair: each MFMA is followed by a run of VALU work long enough to cover its 64-cycle issue on
-// the matrix core.
-__device__ __forceinline__ void interleave_block() {
+// Instruction interleaving inside one key block. The block is cut into three scheduling regions
+// (sched_barrier): (1) PV of the previous block with the operand reads, the row max and the
+// exp / convert of the first 32-key half, (2) QK of the next block's first key half with the
+// exp / convert of the second half, (3) QK of the second key half. Inside a region every MFMA
+// is followed by a run of VALU work long enough to cover its 64-cycle issue on the matrix
+// core, so the wave never queues behind its own MFMAs while it has VALU work left.
+__device__ __forceinline__ void interleave_region1() {
 #ifndef FP8ATTN_NO_IGLP
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (PV)
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
-    __builtin_amdgcn_sched_group_barrier(0x002, 18, 0);  // VALU
-  }
-  __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // VALU
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (QK)
-    __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (PV)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // VALU
   }
 #endif
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void interleave_region2() {
+#ifndef FP8ATTN_NO_IGLP
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (QK, first key half)
+    __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // VALU
+  }
+#endif
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Dense/sparse key-block cursor of the copy engine.
@@ -375,15 +387,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     sk_next = *reinterpret_cast<const float*>(base + kMetaOff);
     lim_next = *reinterpret_cast<const int*>(base + kMetaOff + 4);
   };
+  auto qk_half = [&](int t) {
+    v16f z;
+#pragma unroll
+    for (int r = 0; r < 16; r++) z[r] = 0.0f;
+    sacc[t] = mfma_f8(kop[t][0], qop[0], z);
+    sacc[t] = mfma_f8(kop[t][1], qop[1], sacc[t]);
+  };
   auto qk = [&]() {
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-      v16f z;
-#pragma unroll
-      for (int r = 0; r < 16; r++) z[r] = 0.0f;
-      sacc[t] = mfma_f8(kop[t][0], qop[0], z);
-      sacc[t] = mfma_f8(kop[t][1], qop[1], sacc[t]);
-    }
+    qk_half(0);
+    qk_half(1);
   };
   auto pv = [&]() {
 #pragma unroll
@@ -401,7 +414,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // Online softmax of block j on the S^T accumulators: updates the running state, writes the
   // E4M3 P bytes into pop and returns alpha.
-  auto softmax = [&](auto mask_tag) -> float {
+  auto softmax = [&](auto mask_tag, auto&& issue_qk_half) -> float {
     constexpr bool kMask = decltype(mask_tag)::value;
     const float cs = fmaxf(s_q * sk_cur * p.logit_scale, 1e-30f);  // log2 units per MFMA unit
     float x[32];
@@ -414,7 +427,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
       for (int q = 0; q < 32; q++) x[q] = q < nv ? x[q] : -INFINITY;
     }
-    // two chains of three-input maxima
+    // two chains of three-input maxima, first over the first key half (whose QK finished first)
     float mlo = fmaxf(x[0], x[1]), mhi = fmaxf(x[2], x[3]);
 #pragma unroll
     for (int q = 4; q < 32; q += 4) {
@@ -450,6 +463,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       lsum = (l4[0] + l4[1]) + (l4[2] + l4[3]);
       tie_k(0, lsum);
       tie_k(1, lsum);
+      interleave_region1();
+      issue_qk_half(0);
+      issue_qk_half(1);
     } else {
       const float bias = p.log2S - m_new;
       // key sub-tile by key sub-tile (t = 0: x[0..15], t = 1: x[16..31]), so that the QK MFMAs of
@@ -483,6 +499,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         }
         tie_k(t, lt);
         lsum += lt;
+        // QK of the next block's key half t takes over this half's registers
+        if (t == 0) interleave_region1();
+        else interleave_region2();
+        issue_qk_half(t);
       }
     }
     l_part = alpha * l_part + lsum;
@@ -497,9 +517,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     read_v(sl);   // V(j)
     read_k(sl);   // K(j+1)
     read_meta(sl);
-    const float alpha = softmax(mask_tag);
-    qk();         // QK of block j+1 (a dummy K tile after the last block: unused)
-    interleave_block();
+    // QK of block j+1 is issued inside the softmax, half by half (a dummy K tile after the last
+    // block: its result is unused)
+    const float alpha = softmax(mask_tag, qk_half);
     // alpha == 1 in every lane leaves O bit-identical: skip the multiplies
     if (__any(alpha != 1.0f)) {
 #pragma unroll
