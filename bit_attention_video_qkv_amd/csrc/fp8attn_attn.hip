@@ -59,9 +59,13 @@ __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// IEEE maximum (v_maximum3_f32 on gfx950): unlike fmaxf it needs no NaN canonicalisation of
+// its inputs; the logits carry no NaN.
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float xmax(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_ieee(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float xsum(float v) {
@@ -428,16 +432,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       for (int q = 0; q < 32; q++) x[q] = q < nv ? x[q] : -INFINITY;
     }
     // two chains of three-input maxima, first over the first key half (whose QK finished first)
-    float mlo = fmaxf(x[0], x[1]), mhi = fmaxf(x[2], x[3]);
+    float mlo = fmax_ieee(x[0], x[1]), mhi = fmax_ieee(x[2], x[3]);
 #pragma unroll
     for (int q = 4; q < 32; q += 4) {
-      mlo = fmaxf(fmaxf(mlo, x[q]), x[q + 1]);
-      mhi = fmaxf(fmaxf(mhi, x[q + 2]), x[q + 3]);
+      mlo = fmax_ieee(fmax_ieee(mlo, x[q]), x[q + 1]);
+      mhi = fmax_ieee(fmax_ieee(mhi, x[q + 2]), x[q + 3]);
     }
-    const float mloc = fmaxf(mlo, mhi);
+    const float mloc = fmax_ieee(mlo, mhi);
     // every visited block holds a valid key, so the max is finite after the first block; the
     // guard only keeps a fully masked first block from producing NaN
-    const float m_cand = fmaxf(m_run, xmax(mloc) * cs);
+    const float m_cand = fmax_ieee(m_run, xmax(mloc) * cs);
     const float m_new = m_cand == -INFINITY ? 0.0f : m_cand;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_cand;
