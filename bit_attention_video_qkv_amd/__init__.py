@@ -59,7 +59,8 @@ class _FwdOpts(ctypes.Structure):
 _lib = None
 
 EXPORTED = ("fp8attn_quantize_qkv", "fp8attn_quantize_workspace_bytes", "fp8attn_forward",
-            "fp8attn_forward_workspace_bytes", "fp8attn_sta_build", "fp8attn_status_string")
+            "fp8attn_forward_workspace_bytes", "fp8attn_sta_build", "fp8attn_status_string",
+            "fp8attn_vsmooth_cluster", "fp8attn_vsmooth_cluster_workspace_bytes")
 
 
 def lib():
@@ -85,6 +86,11 @@ def lib():
             ctypes.c_int32, ctypes.c_void_p]
         L.fp8attn_status_string.restype = ctypes.c_char_p
         L.fp8attn_status_string.argtypes = [ctypes.c_int]
+        L.fp8attn_vsmooth_cluster_workspace_bytes.restype = ctypes.c_size_t
+        L.fp8attn_vsmooth_cluster_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+        L.fp8attn_vsmooth_cluster.restype = ctypes.c_int
+        L.fp8attn_vsmooth_cluster.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] + [ctypes.c_int32] * 3 + [
+            ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -174,6 +180,23 @@ class Sparse:
     def _c(self):
         return _Sparse(self.tile_tokens, self.n_tiles, self.tile_len.data_ptr(),
                        self.row_ptr.data_ptr(), self.col_idx.data_ptr())
+
+
+def vsmooth_cluster(v, n_clusters=16, n_feat=8, iters=10, labels=False, workspace=None):
+    """fp8attn_vsmooth_cluster: V-Smooth token permutation of bf16 V [B, N, H, 128] on its device.
+    Returns perm int32 [B, H, N] (and labels int32 [B, H, N] when labels=True); pass perm as
+    perm_kv to quantize_qkv."""
+    B, N, H, D = v.shape
+    dev = v.device
+    perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    lab = torch.empty((B, H, N), dtype=torch.int32, device=dev) if labels else None
+    if workspace is None:
+        n = lib().fp8attn_vsmooth_cluster_workspace_bytes(B, N, H, D, n_feat)
+        workspace = torch.empty(max(int(n), 256), dtype=torch.uint8, device=dev)
+    _check("fp8attn_vsmooth_cluster", lib().fp8attn_vsmooth_cluster(
+        B, N, H, D, _ptr(v), n_clusters, n_feat, iters, _ptr(perm), _ptr(lab), _ptr(workspace),
+        workspace.numel(), _stream(dev)))
+    return (perm, lab) if labels else perm
 
 
 def sta_build(T, Hg, W, tt, th, tw, rt, rh, rw):

@@ -231,4 +231,46 @@ fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, i
   return count <= capacity ? FP8ATTN_OK : FP8ATTN_EINVAL;
 }
 
+
+size_t fp8attn_vsmooth_cluster_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D, int32_t n_feat) {
+  if (B < 1 || N < 1 || H < 1 || D != 128 || n_feat < 1 || n_feat > fp8attn::kMaxFeatures) return 0;
+  const int64_t bhn = static_cast<int64_t>(B) * H * N;
+  const size_t feat = static_cast<size_t>(bhn) * n_feat * sizeof(float);
+  return ((feat + 255) / 256) * 256 + static_cast<size_t>(bhn) * sizeof(int32_t);
+}
+
+fp8attn_status fp8attn_vsmooth_cluster(int32_t B, int32_t N, int32_t H, int32_t D, const void* v,
+                                       int32_t n_clusters, int32_t n_feat, int32_t iters, int32_t* perm,
+                                       int32_t* labels, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  if (B < 1 || N < 1 || H < 1 || D < 1) return FP8ATTN_EINVAL;
+  if (D != 128) return FP8ATTN_EUNSUPPORTED;
+  if (static_cast<int64_t>(B) * H > 65535) return FP8ATTN_EINVAL;
+  if (n_clusters < 1 || n_clusters > fp8attn::kMaxClusters || n_feat < 1 || n_feat > fp8attn::kMaxFeatures ||
+      iters < 0 || iters > 1000)
+    return FP8ATTN_EINVAL;
+  if (!v || !perm || !aligned(v, 16) || !aligned(perm, 4)) return FP8ATTN_EINVAL;
+  if (labels && !aligned(labels, 4)) return FP8ATTN_EINVAL;
+  const size_t need = fp8attn_vsmooth_cluster_workspace_bytes(B, N, H, D, n_feat);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FP8ATTN_EINVAL;
+  const fp8attn_status dev = check_device();
+  if (dev != FP8ATTN_OK) return dev;
+  fp8attn::ClusterParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.v = static_cast<const uint16_t*>(v);
+  p.perm = perm;
+  p.labels = labels;
+  const int64_t bhn = static_cast<int64_t>(B) * H * N;
+  const size_t feat = static_cast<size_t>(bhn) * n_feat * sizeof(float);
+  p.ws_feat = static_cast<float*>(workspace);
+  p.ws_labels = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + ((feat + 255) / 256) * 256);
+  p.N = N;
+  p.B = B;
+  p.H = H;
+  p.n_clusters = n_clusters;
+  p.n_feat = n_feat;
+  p.iters = iters;
+  return from_hip(fp8attn::launch_cluster(p, stream));
+}
+
 }  // extern "C"

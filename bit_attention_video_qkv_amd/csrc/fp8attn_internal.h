@@ -53,6 +53,22 @@ struct AttnParams {
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t stream);
 
+constexpr int kMaxClusters = 32;  // V-Smooth clustering limits (registers and LDS of the kernel)
+constexpr int kMaxFeatures = 16;
+
+struct ClusterParams {
+  const uint16_t* v;   // bf16 [B, N, H, 128]
+  int32_t* perm;       // [B, H, N]
+  int32_t* labels;     // [B, H, N] or null
+  float* ws_feat;      // [B*H, N, n_feat]
+  int32_t* ws_labels;  // [B*H, N]
+  int64_t N;
+  int B, H;
+  int n_clusters, n_feat, iters;
+};
+
+hipError_t launch_cluster(const ClusterParams& p, hipStream_t stream);
+
 enum AttnVariant : int {
   kVarExpCast = 1,
   kVarVSmooth = 2,

@@ -114,6 +114,31 @@ typedef struct fp8attn_sparse {
 } fp8attn_sparse;
 
 /* ------------------------------------------------------------------------------------------
+ * fp8attn_vsmooth_cluster — V-Smooth token permutation (VC-Attention article, section 二, first
+ * step: a light clustering of the value tokens on a few representative channels; tokens of a
+ * cluster are made contiguous so that each 128-row block of the permuted V is homogeneous; the
+ * permutation is computed once and reused across steps). Per (b, h):
+ *   features = the n_feat channels of V with the largest variance over the head's tokens (ties
+ *   to the lower channel), in ascending channel order; k-means with n_clusters centroids
+ *   initialised at tokens floor((2c+1) N / (2 n_clusters)), iters Lloyd rounds and a final
+ *   assignment, squared L2 distance in FP64 with ties to the lower cluster id (an empty cluster
+ *   keeps its centroid); perm = the head's tokens stably sorted by cluster id. The result is
+ *   deterministic. Pass perm as perm_kv (perm_kv_per_head = 1) to fp8attn_quantize_qkv.
+ * Arguments (device pointers): v bf16 [B, N, H, D] (D = 128); perm int32 [B, H, N] (out);
+ *   labels int32 [B, H, N] (out, cluster id of each source token) or NULL; workspace of at
+ *   least fp8attn_vsmooth_cluster_workspace_bytes(...) bytes, 16-byte aligned, overwritten.
+ * Errors: EINVAL on null/misaligned pointers, non-positive sizes, n_clusters outside [1, 32],
+ *   n_feat outside [1, 16], iters outside [0, 1000], B*H > 65535 or a too-small workspace;
+ *   EUNSUPPORTED on D != 128 or a device other than gfx950.
+ * ------------------------------------------------------------------------------------------ */
+size_t fp8attn_vsmooth_cluster_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D,
+                                               int32_t n_feat);
+fp8attn_status fp8attn_vsmooth_cluster(int32_t B, int32_t N, int32_t H, int32_t D, const void* v,
+                                       int32_t n_clusters, int32_t n_feat, int32_t iters,
+                                       int32_t* perm, int32_t* labels, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * fp8attn_sta_build — HOST helper that lays a raster latent grid (T, Hg, W) out in tiles
  * (tt, th, tw) (the grid is padded up to whole tiles; tiles numbered in raster order over the
  * tile grid; inside a tile valid tokens first in raster order, then padding) and lists, for

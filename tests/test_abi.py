@@ -127,3 +127,29 @@ def test_workspace_sizes(m):
     assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0) == 0
     assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1) == 24 * 384 * 128 * 4
     assert L.fp8attn_quantize_workspace_bytes(1, 100, 2, 64, 0) == 0
+
+
+def test_cluster_rejects_bad_arguments(m):
+    L = m.lib()
+    need = L.fp8attn_vsmooth_cluster_workspace_bytes(1, 100, 2, 128, 8)
+    assert need >= 100 * 2 * (8 * 4 + 4)
+    assert L.fp8attn_vsmooth_cluster_workspace_bytes(1, 100, 2, 64, 8) == 0
+    assert L.fp8attn_vsmooth_cluster_workspace_bytes(1, 100, 2, 128, 17) == 0
+    good = dict(B=1, N=100, H=2, D=128, v=_fake(), K=16, F=8, it=10, perm=_fake(), lab=None,
+                ws=_fake(), wsb=need)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return L.fp8attn_vsmooth_cluster(a["B"], a["N"], a["H"], a["D"], a["v"], a["K"], a["F"], a["it"],
+                                         a["perm"], a["lab"], a["ws"], a["wsb"], None)
+    EINVAL, EUNSUPPORTED = 1, 2
+    assert call(B=0) == EINVAL
+    assert call(N=0) == EINVAL
+    assert call(D=64) == EUNSUPPORTED
+    assert call(B=300, H=300) == EINVAL
+    assert call(K=0) == EINVAL and call(K=33) == EINVAL
+    assert call(F=0) == EINVAL and call(F=17) == EINVAL
+    assert call(it=-1) == EINVAL and call(it=1001) == EINVAL
+    assert call(v=None) == EINVAL and call(v=_fake(0x10008)) == EINVAL
+    assert call(perm=None) == EINVAL and call(lab=_fake(0x10002)) == EINVAL
+    assert call(ws=None) == EINVAL and call(wsb=need - 1) == EINVAL

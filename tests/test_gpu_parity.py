@@ -289,6 +289,42 @@ def test_underflow_counter(m, orc, delta, S, reverse):
 
 
 # ------------------------------------------------------------------------------------------
+# V-Smooth clustering (fp8attn_vsmooth_cluster) against the oracle's clustering
+# ------------------------------------------------------------------------------------------
+def _check_perm_valid(perm, labels):
+    """Every (b, h) row of perm is a permutation of its tokens, grouped by ascending cluster id,
+    in ascending token order inside a cluster (a stable sort)."""
+    B, H, N = perm.shape
+    for b in range(B):
+        for h in range(H):
+            p, lab = perm[b, h], labels[b, h]
+            assert np.array_equal(np.sort(p), np.arange(N))
+            key = lab[p].astype(np.int64) * N + p
+            assert np.all(np.diff(key) > 0)
+
+
+@pytest.mark.parametrize("N,H,K,F,iters", [(49152, 2, 16, 8, 10), (1000, 3, 16, 8, 10), (37, 1, 16, 8, 3),
+                                           (5, 1, 16, 4, 2), (3000, 1, 32, 16, 0)])
+def test_vsmooth_cluster_matches_oracle(m, orc, N, H, K, F, iters):
+    say("cluster", N, H, K, F, iters)
+    if N == 49152:
+        _, _, v = workloads.workload("vsmooth", heads=H)
+    else:
+        _, _, v = workloads.make_qkv(1, N, H, seed=N + K, kind="token_outliers", n_outlier_channels=8)
+    perm_g, lab_g = m.vsmooth_cluster(v.to(DEV), n_clusters=K, n_feat=F, iters=iters, labels=True)
+    torch.cuda.synchronize()
+    perm_g, lab_g = _np(perm_g), _np(lab_g)
+    perm_o, lab_o = orc.vsmooth_perm(_bits(v), n_clusters=K, n_feat=F, iters=iters, return_labels=True)
+    _check_perm_valid(perm_g, lab_g)
+    # the same deterministic algorithm: only the order of FP64 sums differs, which could move a
+    # token only if it were equidistant to two centroids to within rounding
+    agree = float(np.mean(lab_g == lab_o))
+    say(f"cluster labels agree with the oracle on {agree * 100:.4f}% of tokens")
+    assert np.array_equal(lab_g, lab_o)
+    assert np.array_equal(perm_g, perm_o)
+
+
+# ------------------------------------------------------------------------------------------
 # Full-size workloads (benchmark launch configuration), sampled heads and rows
 # ------------------------------------------------------------------------------------------
 def _slice_heads(t, heads):
