@@ -25,9 +25,22 @@ METRIC = "FP8 attn fwd TFLOP/s (4·N²·D·H, dense-equiv) + % of MI355X FP8 MFM
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (no sparsity)
 ATTN_SRC = os.path.join(ROOT, "bit_attention_video_qkv_amd", "csrc", "fp8attn_attn.hip")
 # HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) as measured by
-# rocprofv3 for the attention source with this sha256 prefix and workload; see profiles/.
-# Reported only while the source is unchanged.
-MEASURED_TRAFFIC = {("99046641749c", "wan14b"): 185797360753}
+# rocprofv3 for the attention source whose code (comments and blank lines dropped) has this
+# sha256 prefix, per workload; see profiles/. Reported only while that code is unchanged.
+MEASURED_TRAFFIC = {("cc21e70fa022", "wan14b"): 185797360753}
+
+
+def code_sha(path):
+    """sha256 prefix of a source file with // comments and blank lines removed."""
+    import hashlib
+    import re
+    lines = []
+    with open(path, encoding="utf-8") as fh:
+        for ln in fh.read().splitlines():
+            ln = re.sub(r"//.*$", "", ln).rstrip()
+            if ln.strip():
+                lines.append(ln)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:12]
 
 WORKLOADS = {
     # name: (workloads.py config, sparse, vsmooth+expcast, description)
@@ -154,10 +167,7 @@ def main():
     achieved = attn_flops / (ms_attn * 1e-3) / 1e12
     log(f"step {ms_step:.3f} ms, attention kernel {ms_attn:.3f} ms, quantize {ms_step - ms_attn:.3f} ms")
 
-    import hashlib
-    with open(ATTN_SRC, "rb") as fh:
-        src_sha = hashlib.sha256(fh.read()).hexdigest()[:12]
-    traffic = MEASURED_TRAFFIC.get((src_sha, args.workload))
+    traffic = MEASURED_TRAFFIC.get((code_sha(ATTN_SRC), args.workload))
 
     result = {
         "metric": METRIC,

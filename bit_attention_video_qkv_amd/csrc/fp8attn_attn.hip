@@ -16,15 +16,14 @@
 //    [32h, 32h+32) of the block; the E4M3 P bytes of a lane are then exactly the B operand of
 //    O^T = V^T P^T, whose A operand is 32 contiguous key bytes of a token-contiguous V row.
 //  * O^T accumulators give every lane one query, so the softmax rescale is a per-lane scalar.
-//  * One wave owns 64 queries as two 32-row sub-tiles A and B and runs alone on its SIMD. The
-//    two sub-tiles are software-pipelined inside the wave: while the VALU computes the softmax
-//    of one sub-tile, the matrix core runs the other sub-tile's QK of the same (or next) key
-//    block and its PV of the previous one, so the exp/convert work (the longer of the two on
-//    this chip) overlaps the MFMAs without a second wave or a barrier between them.
+//  * One wave owns 32 queries and software-pipelines them over the key blocks: the softmax of
+//    block j (VALU) overlaps the PV MFMAs of block j-1 and the QK MFMAs of block j+1, whose
+//    results take over the softmax's registers half by half. The kernel fits two waves per
+//    SIMD, so two 4-wave workgroups share every CU and cover each other's stalls.
 //  * K and V tiles (8 KB each per 64 keys) reach LDS by direct global->LDS copies, three key
-//    blocks deep, in three separately declared slots so that the compiler can tell an operand
-//    read of one slot from a copy still landing in another. One barrier per key block.
-//  * Workgroups are mapped XCD-major so each XCD streams the K/V of few heads through its L2.
+//    blocks deep; one barrier per key block. LDS chunks are XOR-swizzled so that every operand
+//    read is free of bank conflicts.
+//  * Workgroups are mapped XCD-major so each XCD works on few heads at a time.
 #include <type_traits>
 
 #include "fp8attn_common.h"
