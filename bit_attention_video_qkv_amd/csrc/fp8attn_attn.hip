@@ -426,9 +426,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
       for (int r = 0; r < 16; r++) x[16 * t + r] = sacc[t][r];
     if constexpr (kMask) {
-      const int nv = lim_cur - 32 * lh;  // valid keys among this lane's 32
+      // only blocks with padding keys pay for the selects; the empty asm keeps the compiler from
+      // hoisting the per-key compares out of the (uniform) branch
+      if (__builtin_amdgcn_readfirstlane(lim_cur) < kBlock) {
+        int nv = lim_cur - 32 * lh;  // valid keys among this lane's 32
+        asm volatile("" : "+v"(nv));
 #pragma unroll
-      for (int q = 0; q < 32; q++) x[q] = q < nv ? x[q] : -INFINITY;
+        for (int q = 0; q < 32; q++) x[q] = q < nv ? x[q] : -INFINITY;
+      }
     }
     // two chains of three-input maxima, first over the first key half (whose QK finished first)
     float mlo = fmax_ieee(x[0], x[1]), mhi = fmax_ieee(x[2], x[3]);
@@ -580,7 +585,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // ---- mainloop. Dense: the one block with fewer than 64 valid keys (the last key block, first
   // in reverse order) runs in a masked copy outside the loop. Sparse: partial blocks sit at the
-  // end of tiles anywhere in the sequence, so every block takes the (cheap) masked path. ----
+  // end of tiles anywhere in the sequence, so every block checks its valid-key count. ----
   using kNoMask = std::integral_constant<bool, false>;
   using kMasked = std::integral_constant<bool, true>;
   using kLoopMask = std::integral_constant<bool, SPARSE>;
