@@ -106,11 +106,14 @@ def bf16_decode(bits) -> np.ndarray:
 # Quantisation: TeleFuser "面向注意力的 FP8 Preparation" eq. s_q, s_k (per 64-token block),
 # s_v (per channel), V stored token-contiguous; VC-Attention 二 (V-Smooth residual).
 # ----------------------------------------------------------------------------------------
-def quantize(q, k, v, perm_q=None, perm_kv=None, vsmooth=False, n_layout=None):
+def quantize(q, k, v, perm_q=None, perm_kv=None, vsmooth=False, n_layout=None, smoothing=0,
+             v_bias_correction=False):
     """q, k, v: uint16 bf16 bits [B, Nsrc, H, D]. perm_q: int32 [N] or None; perm_kv: int32
-    [N] (shared) or [B, H, N] (per head) or None. Returns a dict of numpy arrays:
-    q8, k8 [B,H,N64,D] uint8; v8t [B,H,D,N64] uint8; q_scale, k_scale [B,H,NB] f32;
-    v_scale [B,H,D] f32; v_mean [B,H,ceil(N/128),D] uint16 (V-Smooth only)."""
+    [N] (shared) or [B, H, N] (per head) or None. smoothing: 0 none, 1 K, 2 K and V
+    (sequence-mean smoothing, TeleFuser MiniMax-H3 section); v_bias_correction only with 2.
+    Returns a dict of numpy arrays: q8, k8 [B,H,N64,D] uint8; v8t [B,H,D,N64] uint8;
+    q_scale, k_scale [B,H,NB] f32; v_scale [B,H,D] f32; v_mean [B,H,ceil(N/128),D] uint16
+    (V-Smooth only); v_shift [B,H,D] f32 (smoothing 2 only)."""
     q = np.ascontiguousarray(q, dtype=np.uint16)
     k = np.ascontiguousarray(k, dtype=np.uint16)
     v = np.ascontiguousarray(v, dtype=np.uint16)
@@ -137,11 +140,13 @@ def quantize(q, k, v, perm_q=None, perm_kv=None, vsmooth=False, n_layout=None):
         v8t=np.zeros((B, H, D, N64), np.uint8), q_scale=np.zeros((B, H, NB), np.float32),
         k_scale=np.zeros((B, H, NB), np.float32), v_scale=np.zeros((B, H, D), np.float32),
         v_mean=np.zeros((B, H, NB128, D), np.uint16) if vsmooth else None,
+        v_shift=np.zeros((B, H, D), np.float32) if smoothing == 2 else None,
         N=N, vsmooth=bool(vsmooth))
     rc = _load().orc_quantize(
         B, Nsrc, N, H, D, _p(q), _p(k), _p(v), _p(perm_q), _p(perm_kv), per_head,
         1 if vsmooth else 0, _p(out["q8"]), _p(out["k8"]), _p(out["v8t"]), _p(out["q_scale"]),
-        _p(out["k_scale"]), _p(out["v_scale"]), _p(out["v_mean"]))
+        _p(out["k_scale"]), _p(out["v_scale"]), _p(out["v_mean"]), int(smoothing),
+        1 if v_bias_correction else 0, _p(out["v_shift"]))
     if rc != 0:
         raise ValueError("oracle quantize: invalid arguments")
     return out
@@ -180,7 +185,8 @@ def attention_fp8(qz, rows=None, softmax_scale=1.0 / math.sqrt(128.0), p_scale=2
         _p(qz["q_scale"]), _p(qz["k_scale"]), _p(qz["v_scale"]),
         _p(qz["v_mean"]) if qz.get("vsmooth") else None, ctypes.c_double(softmax_scale),
         ctypes.c_double(p_scale), 1 if kv_reverse else 0, 1 if expcast else 0, tt, nt, _p(tl),
-        _p(rp), _p(ci), _p(rows), ctypes.c_int64(R), _p(out), _p(ob), _p(uf), _p(rv), _p(amb))
+        _p(rp), _p(ci), _p(rows), ctypes.c_int64(R), _p(out), _p(ob), _p(uf), _p(rv), _p(amb),
+        _p(qz.get("v_shift")))
     if rc != 0:
         raise ValueError("oracle attention: invalid arguments")
     return (out, ob, uf, rv, amb) if return_amb else (out, ob, uf, rv)
@@ -205,7 +211,7 @@ def attention_ref(mode, q, k, v, rows=None, softmax_scale=1.0 / math.sqrt(128.0)
         int(mode), B, N, H, D, _p(q), _p(k), _p(v), None, None, None, None, None, None, None,
         ctypes.c_double(softmax_scale), ctypes.c_double(p_scale), 1 if kv_reverse else 0,
         1 if expcast else 0, tt, nt, _p(tl), _p(rp), _p(ci), _p(rows), ctypes.c_int64(R),
-        _p(out), None, _p(uf), _p(rv), None)
+        _p(out), None, _p(uf), _p(rv), None, None)
     if rc != 0:
         raise ValueError("oracle attention_ref: invalid arguments")
     return out, uf, rv

@@ -156,19 +156,59 @@ void orc_bf16_encode(const float* x, uint16_t* out, int64_t n) {
 //    valid rows (stored as one 16-bit vector per block, BF16 here), R = V' - mu_hat_j, and R
 //    (not V) is quantised per channel.
 //
+//  * Sequence-mean smoothing ([TF] MiniMax-H3 section: K' = K - mean_T(K), V' = V - mean_T(V)
+//    per head, FP32 statistics; the K shift moves every logit of a query row by the same
+//    constant, and mean_T(V) is added back to the output because each softmax row sums to 1):
+//    smoothing 1 shifts K, 2 shifts K and V. The mean is seq_mean below; K' = fl32(K - mean) and
+//    V' = fl32(V - mean) are quantised by the usual rules. v_shift [B, H, D] receives the vector
+//    the attention adds to its output: mean_T(V), or with v_bias_correction (the page's
+//    compensation of the residual mean bias that rounding V' to E4M3 leaves) mean_T(V) - e,
+//    e = seq_mean of fl32(fl32(decode(code) * s_v) - V') over the valid rows.
+//
 // Shapes: q, k, v bf16 [B, Nsrc, H, D]; q8, k8 [B, H, N64, D]; v8t [B, H, D, N64];
-// q_scale, k_scale [B, H, NB]; v_scale [B, H, D]; v_mean bf16 [B, H, ceil(N/128), D].
-// N64 = 64 * NB, NB = ceil(N / 64). Padding rows/columns get code 0.
+// q_scale, k_scale [B, H, NB]; v_scale [B, H, D]; v_mean bf16 [B, H, ceil(N/128), D];
+// v_shift f32 [B, H, D]. N64 = 64 * NB, NB = ceil(N / 64). Padding rows/columns get code 0.
 // Returns 0, or 1 on an argument error.
 // ---------------------------------------------------------------------------------------
+
+// Mean over the valid layout rows of one channel, in FP32 ([TF] says the statistics are FP32;
+// the summation order is this reading): the valid values of each 64-position block of the
+// layout summed in ascending position, the block sums combined by a pairwise tree (level by
+// level s[i] = s[2i] + s[2i+1], an odd last element carried up unchanged), the total divided
+// by the number of valid rows. x[i * stride] is row i's value.
+float seq_mean(const float* x, int64_t stride, const std::vector<char>& valid, int64_t N) {
+  const int64_t NB = ceil_div(N, 64);
+  std::vector<float> s(NB, 0.0f);
+  int64_t count = 0;
+  for (int64_t blk = 0; blk < NB; blk++) {
+    float acc = 0.0f;
+    for (int64_t i = blk * 64; i < std::min<int64_t>(N, blk * 64 + 64); i++)
+      if (valid[i]) {
+        acc = acc + x[i * stride];
+        count++;
+      }
+    s[blk] = acc;
+  }
+  int64_t n = NB;
+  while (n > 1) {
+    for (int64_t i = 0; i < n / 2; i++) s[i] = s[2 * i] + s[2 * i + 1];
+    if (n % 2) s[n / 2] = s[n - 1];
+    n = (n + 1) / 2;
+  }
+  return count ? s[0] / static_cast<float>(count) : 0.0f;
+}
+
 int orc_quantize(int B, int Nsrc, int N, int H, int D, const uint16_t* q, const uint16_t* k,
                  const uint16_t* v, const int32_t* perm_q, const int32_t* perm_kv,
                  int perm_kv_per_head, int vsmooth, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
-                 float* q_scale, float* k_scale, float* v_scale, uint16_t* v_mean) {
+                 float* q_scale, float* k_scale, float* v_scale, uint16_t* v_mean,
+                 int smoothing, int v_bias_correction, float* v_shift) {
   if (B < 1 || N < 1 || H < 1 || D < 1 || Nsrc < 1) return 1;
   if (!perm_q && N != Nsrc) return 1;
   if (!perm_kv && N != Nsrc) return 1;
   if (vsmooth && !v_mean) return 1;
+  if (smoothing < 0 || smoothing > 2 || (smoothing == 2 && (vsmooth || !v_shift))) return 1;
+  if (v_bias_correction && smoothing != 2) return 1;
   const int64_t NB = ceil_div(N, 64), N64 = NB * 64, NB128 = ceil_div(N, 128);
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -183,26 +223,40 @@ int orc_quantize(int B, int Nsrc, int N, int H, int D, const uint16_t* q, const 
         return bf16_float(x[((static_cast<int64_t>(b) * Nsrc + src) * H + h) * D + d]);
       };
 
-      // Q and K: per 64-token block of the layout.
+      // Q and K: per 64-token block of the layout (K shifted by its sequence mean when
+      // smoothing is on).
       for (int t = 0; t < 2; t++) {
         const uint16_t* x = t == 0 ? q : k;
         const int32_t* perm = t == 0 ? perm_q : perm_kv;
         const bool per_head = t == 0 ? false : (perm_kv_per_head != 0);
         uint8_t* codes = t == 0 ? q8 : k8;
         float* scales = t == 0 ? q_scale : k_scale;
+        std::vector<float> shift(D, 0.0f);
+        if (t == 1 && smoothing >= 1) {
+          std::vector<float> kl(static_cast<size_t>(N) * D, 0.0f);
+          std::vector<char> kvalid(N, 0);
+          for (int64_t i = 0; i < N; i++) {
+            const int64_t s = src_index(perm, per_head, i);
+            if (s < 0) continue;
+            kvalid[i] = 1;
+            for (int d = 0; d < D; d++) kl[i * D + d] = elem(x, s, d);
+          }
+          for (int d = 0; d < D; d++) shift[d] = seq_mean(kl.data() + d, D, kvalid, N);
+        }
+        auto value = [&](int64_t s, int d) -> float { return elem(x, s, d) - shift[d]; };  // FP32
         for (int64_t blk = 0; blk < NB; blk++) {
           float amax = 0.0f;
           for (int64_t i = blk * 64; i < std::min<int64_t>(N, blk * 64 + 64); i++) {
             const int64_t s = src_index(perm, per_head, i);
             if (s < 0) continue;
-            for (int d = 0; d < D; d++) amax = std::max(amax, std::fabs(elem(x, s, d)));
+            for (int d = 0; d < D; d++) amax = std::max(amax, std::fabs(value(s, d)));
           }
           const BlockScale sc = block_scale(amax);
           scales[bh * NB + blk] = sc.scale;
           for (int64_t i = blk * 64; i < blk * 64 + 64; i++) {
             uint8_t* row = codes + (bh * N64 + i) * D;
             const int64_t s = i < N ? src_index(perm, per_head, i) : -1;
-            for (int d = 0; d < D; d++) row[d] = s < 0 ? 0 : quant_code(elem(x, s, d), sc);
+            for (int d = 0; d < D; d++) row[d] = s < 0 ? 0 : quant_code(value(s, d), sc);
           }
         }
       }
@@ -234,6 +288,14 @@ int orc_quantize(int B, int Nsrc, int N, int H, int D, const uint16_t* q, const 
           }
         }
       }
+      std::vector<float> vmean(D, 0.0f);
+      if (smoothing == 2) {
+        for (int d = 0; d < D; d++) {
+          vmean[d] = seq_mean(vl.data() + d, D, valid, N);
+          for (int64_t i = 0; i < N; i++)
+            if (valid[i]) vl[i * D + d] = vl[i * D + d] - vmean[d];  // FP32 subtraction
+        }
+      }
       for (int d = 0; d < D; d++) {
         float amax = 0.0f;
         for (int64_t i = 0; i < N; i++)
@@ -243,6 +305,19 @@ int orc_quantize(int B, int Nsrc, int N, int H, int D, const uint16_t* q, const 
         uint8_t* row = v8t + (bh * D + d) * N64;
         for (int64_t i = 0; i < N64; i++)
           row[i] = (i < N && valid[i]) ? quant_code(vl[i * D + d], sc) : 0;
+        if (v_shift) {
+          float c = vmean[d];
+          if (v_bias_correction) {
+            std::vector<float> err(N, 0.0f);
+            for (int64_t i = 0; i < N; i++)
+              if (valid[i]) {
+                const float deq = static_cast<float>(e4m3_value(row[i])) * sc.scale;  // FP32 product
+                err[i] = deq - vl[i * D + d];                                          // FP32
+              }
+            c = c - seq_mean(err.data(), 1, valid, N);
+          }
+          v_shift[bh * D + d] = c;
+        }
       }
     }
   }
@@ -285,7 +360,8 @@ int orc_quantize(int B, int Nsrc, int N, int H, int D, const uint16_t* q, const 
 // rows: the layout query indices to compute (same for every (b, h)), n_rows of them.
 // Outputs: out f64 [B, H, n_rows, D]; out_bf16 [B, H, n_rows, D] or null; underflow
 // [B, H, n_rows] or null (keys with p > 0 whose P code is 0); row_valid [B, H, n_rows] or null;
-// amb_bound [B, H, n_rows, D] or null (modes 2-3).
+// amb_bound [B, H, n_rows, D] or null (modes 2-3); v_shift [B, H, D] or null (mode 3: the
+// vector sequence-mean smoothing adds to every output row, see orc_quantize).
 //
 // Ambiguous P codes. The pages fix P8 = E4M3(S p) but not how p is evaluated; an FP32
 // evaluation (the kernel's precision) can land on either side of a rounding boundary when S p
@@ -311,7 +387,7 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
                   int expcast, int tile_tokens, int n_tiles, const int32_t* tile_len,
                   const int32_t* row_ptr, const int32_t* col_idx, const int32_t* rows,
                   int64_t n_rows, double* out, uint16_t* out_bf16, int64_t* underflow,
-                  uint8_t* row_valid, double* amb_bound) {
+                  uint8_t* row_valid, double* amb_bound, const float* v_shift) {
   if (mode < 0 || mode > 3 || B < 1 || N < 1 || H < 1 || D < 1 || n_rows < 0) return 1;
   if (mode < 3 && (!qd || !kd || !vd)) return 1;
   if (mode == 3 && (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale)) return 1;
@@ -570,6 +646,10 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
             for (int d = 0; d < D; d++)
               amb_bound[o_idx * D + d] = (amb_v[d] + amb_l * std::fabs(o[d]) + amb_pv[d]) / (S * l) +
                                          2.0 * std::fabs(o[d]) * amb_lx / l;
+          // sequence-mean smoothing ([TF] MiniMax-H3 section): each softmax row sums to 1, so
+          // the attention of the shifted V plus mean_T(V) is the attention of V
+          if (mode == 3 && v_shift)
+            for (int d = 0; d < D; d++) o[d] += static_cast<double>(v_shift[bh * D + d]);
         }
         if (out_bf16)
           for (int d = 0; d < D; d++) out_bf16[o_idx * D + d] = bf16_bits(static_cast<float>(o[d]));
