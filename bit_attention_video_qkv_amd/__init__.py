@@ -40,7 +40,8 @@ class _QuantArgs(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("N_src", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("D", ctypes.c_int32), ("perm_q", ctypes.c_void_p),
                 ("perm_kv", ctypes.c_void_p), ("perm_kv_per_head", ctypes.c_int32),
-                ("vsmooth", ctypes.c_int32)]
+                ("vsmooth", ctypes.c_int32), ("smoothing", ctypes.c_int32),
+                ("v_bias_correction", ctypes.c_int32), ("v_shift", ctypes.c_void_p)]
 
 
 class _Sparse(ctypes.Structure):
@@ -53,7 +54,8 @@ class _FwdOpts(ctypes.Structure):
     _fields_ = [("softmax_scale", ctypes.c_float), ("p_scale", ctypes.c_float),
                 ("kv_order", ctypes.c_int), ("pcast", ctypes.c_int),
                 ("sparse", ctypes.POINTER(_Sparse)), ("out_rows", ctypes.c_void_p),
-                ("n_out", ctypes.c_int32), ("underflow", ctypes.c_void_p)]
+                ("n_out", ctypes.c_int32), ("underflow", ctypes.c_void_p),
+                ("v_shift", ctypes.c_void_p)]
 
 
 _lib = None
@@ -121,9 +123,10 @@ class Quantized:
     B: int
     N: int
     H: int
+    v_shift: torch.Tensor | None = None  # FP32 [B, H, 128] from sequence-mean smoothing (V)
 
 
-def alloc_quantized(B, N, H, vsmooth, device):
+def alloc_quantized(B, N, H, vsmooth, device, smoothing=0):
     NB = (N + 63) // 64
     N64 = NB * 64
     NB128 = (N + 127) // 128
@@ -134,7 +137,8 @@ def alloc_quantized(B, N, H, vsmooth, device):
         v8t=torch.empty((B, H, HEAD_DIM, N64), **u8), q_scale=torch.empty((B, H, NB), **f32),
         k_scale=torch.empty((B, H, NB), **f32), v_scale=torch.empty((B, H, HEAD_DIM), **f32),
         v_mean=torch.empty((B, H, NB128, HEAD_DIM), dtype=torch.int16, device=device) if vsmooth else None,
-        B=B, N=N, H=H)
+        B=B, N=N, H=H,
+        v_shift=torch.empty((B, H, HEAD_DIM), **f32) if smoothing == 2 else None)
 
 
 def quantize_workspace(B, N, H, vsmooth, device):
@@ -143,9 +147,11 @@ def quantize_workspace(B, N, H, vsmooth, device):
 
 
 def quantize_qkv(q, k, v, perm_q=None, perm_kv=None, vsmooth=False, n_layout=None, out=None,
-                 workspace=None):
+                 workspace=None, smoothing=0, v_bias_correction=False):
     """q, k, v: bf16 device tensors [B, N_src, H, 128]. perm_q: int32 device [N] or None;
-    perm_kv: int32 device [N] (shared by heads) or [B, H, N] or None. Returns Quantized."""
+    perm_kv: int32 device [N] (shared by heads) or [B, H, N] or None. smoothing: 0 none, 1 K,
+    2 K and V sequence-mean smoothing (then Quantized.v_shift is set; v_bias_correction adds the
+    rounding-bias compensation). Returns Quantized."""
     B, Nsrc, H, D = q.shape
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.shape != q.shape:
@@ -157,9 +163,11 @@ def quantize_qkv(q, k, v, perm_q=None, perm_kv=None, vsmooth=False, n_layout=Non
         n_layout = perm_q.shape[0] if perm_q is not None else (
             perm_kv.shape[-1] if perm_kv is not None else Nsrc)
     N = int(n_layout)
-    qz = out if out is not None else alloc_quantized(B, N, H, vsmooth, q.device)
+    qz = out if out is not None else alloc_quantized(B, N, H, vsmooth, q.device, smoothing)
     ws = workspace if workspace is not None else quantize_workspace(B, N, H, vsmooth, q.device)
-    args = _QuantArgs(B, Nsrc, N, H, D, _ptr(perm_q), _ptr(perm_kv), per_head, 1 if vsmooth else 0)
+    args = _QuantArgs(B, Nsrc, N, H, D, _ptr(perm_q), _ptr(perm_kv), per_head, 1 if vsmooth else 0,
+                      int(smoothing), 1 if v_bias_correction else 0,
+                      _ptr(qz.v_shift) if smoothing == 2 else None)
     st = lib().fp8attn_quantize_qkv(
         ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(qz.q8), _ptr(qz.k8), _ptr(qz.v8t),
         _ptr(qz.q_scale), _ptr(qz.k_scale), _ptr(qz.v_scale), _ptr(qz.v_mean) if vsmooth else None,
@@ -245,7 +253,7 @@ def forward(qz: Quantized, softmax_scale=1.0 / math.sqrt(HEAD_DIM), p_scale=256.
     sp = sparse._c() if sparse is not None else None
     opts = _FwdOpts(float(softmax_scale), float(p_scale), int(kv_order), int(pcast),
                     ctypes.pointer(sp) if sp is not None else None, _ptr(out_rows), int(n_out),
-                    _ptr(underflow))
+                    _ptr(underflow), _ptr(qz.v_shift))
     st = lib().fp8attn_forward(
         B, N, H, HEAD_DIM, _ptr(qz.q8), _ptr(qz.k8), _ptr(qz.v8t), _ptr(qz.q_scale),
         _ptr(qz.k_scale), _ptr(qz.v_scale), _ptr(qz.v_mean), ctypes.byref(opts), _ptr(out),

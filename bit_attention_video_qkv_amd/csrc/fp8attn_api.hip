@@ -59,7 +59,11 @@ size_t fp8attn_quantize_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t
   (void)vsmooth;
   if (B < 1 || N < 1 || H < 1 || D != kHeadDim) return 0;
   const size_t bh = static_cast<size_t>(B) * H;
-  return round_up(bh * cdiv(N, 128) * kHeadDim * sizeof(float)) + round_up(bh * kHeadDim * sizeof(float));
+  // channel amax partials and inverse scales, then the smoothing sums, counts and means (the
+  // size covers every option, so one workspace serves all calls of a shape)
+  return round_up(bh * cdiv(N, 128) * kHeadDim * sizeof(float)) + round_up(bh * kHeadDim * sizeof(float)) +
+         round_up(2 * bh * cdiv(N, 64) * kHeadDim * sizeof(float)) + round_up(bh * cdiv(N, 64) * sizeof(int32_t)) +
+         round_up(2 * bh * kHeadDim * sizeof(float));
 }
 
 fp8attn_status fp8attn_quantize_qkv(const fp8attn_quant_args* a, const void* q, const void* k,
@@ -75,6 +79,10 @@ fp8attn_status fp8attn_quantize_qkv(const fp8attn_quant_args* a, const void* q, 
   if (!a->perm_kv && a->N != a->N_src) return FP8ATTN_EINVAL;
   if (a->perm_kv_per_head != 0 && a->perm_kv_per_head != 1) return FP8ATTN_EINVAL;
   if (a->vsmooth != 0 && a->vsmooth != 1) return FP8ATTN_EINVAL;
+  if (a->smoothing < 0 || a->smoothing > 2 || (a->smoothing == 2 && a->vsmooth)) return FP8ATTN_EINVAL;
+  if (a->v_bias_correction != 0 && a->v_bias_correction != 1) return FP8ATTN_EINVAL;
+  if (a->v_bias_correction && a->smoothing != 2) return FP8ATTN_EINVAL;
+  if (a->smoothing == 2 && (!a->v_shift || !aligned(a->v_shift, 16))) return FP8ATTN_EINVAL;
   const void* p16[] = {q, k, v, q8, k8, v8t, v_scale, workspace};
   for (const void* ptr : p16)
     if (!ptr || !aligned(ptr, 16)) return FP8ATTN_EINVAL;
@@ -108,10 +116,20 @@ fp8attn_status fp8attn_quantize_qkv(const fp8attn_quant_args* a, const void* q, 
   p.NB128 = cdiv(a->N, 128);
   p.perm_kv_per_head = a->perm_kv_per_head;
   p.vsmooth = a->vsmooth;
+  p.smoothing = a->smoothing;
+  p.v_bias_correction = a->v_bias_correction;
+  p.v_shift = a->smoothing == 2 ? a->v_shift : nullptr;
   const size_t bh = static_cast<size_t>(a->B) * a->H;
-  p.ws_partial = static_cast<float*>(workspace);
-  p.ws_inv = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      round_up(bh * p.NB128 * kHeadDim * sizeof(float)));
+  char* ws = static_cast<char*>(workspace);
+  p.ws_partial = reinterpret_cast<float*>(ws);
+  ws += round_up(bh * p.NB128 * kHeadDim * sizeof(float));
+  p.ws_inv = reinterpret_cast<float*>(ws);
+  ws += round_up(bh * kHeadDim * sizeof(float));
+  p.ws_bsum = reinterpret_cast<float*>(ws);
+  ws += round_up(2 * bh * p.NB * kHeadDim * sizeof(float));
+  p.ws_cnt = reinterpret_cast<int32_t*>(ws);
+  ws += round_up(bh * p.NB * sizeof(int32_t));
+  p.ws_mean = reinterpret_cast<float*>(ws);
   return from_hip(fp8attn::launch_quantize(p, stream));
 }
 
@@ -142,6 +160,7 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
   const bool sparse = o->sparse != nullptr;
   if (vsmooth && (sparse || !aligned(v_mean, 16))) return FP8ATTN_EINVAL;
   if (o->underflow && (o->pcast != FP8ATTN_PCAST_RNE || !aligned(o->underflow, 8))) return FP8ATTN_EINVAL;
+  if (o->v_shift && (vsmooth || !aligned(o->v_shift, 16))) return FP8ATTN_EINVAL;
   if (o->out_rows ? (o->n_out < 1 || !aligned(o->out_rows, 4)) : (o->n_out != N)) return FP8ATTN_EINVAL;
   if (sparse) {
     const fp8attn_sparse* s = o->sparse;
@@ -167,6 +186,7 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
   p.out = static_cast<uint16_t*>(out);
   p.out_rows = o->out_rows;
   p.underflow = o->underflow;
+  p.v_shift = o->v_shift;
   p.N = N;
   p.NB = cdiv(N, 64);
   p.N64 = p.NB * 64;

@@ -631,11 +631,22 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
           for (int e = 0; e < 4; e++) gs[e] = gs[e] > 0.0f ? gs[e] : 1.0f;
         }
+        // sequence-mean smoothing: every softmax row sums to one, so the V shift comes back
+        // as a constant vector
+        float c[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.v_shift) {
+          const float4 cv = *reinterpret_cast<const float4*>(p.v_shift + bh * kHeadDim + d0);
+          c[0] = cv.x;
+          c[1] = cv.y;
+          c[2] = cv.z;
+          c[3] = cv.w;
+        }
+        float ov[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) ov[e] = oacc[dt][4 * g + e] * gs[e] * inv_l + c[e];
         uint2 o;
-        o.x = static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * g + 0] * gs[0] * inv_l)) |
-              (static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * g + 1] * gs[1] * inv_l)) << 16);
-        o.y = static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * g + 2] * gs[2] * inv_l)) |
-              (static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * g + 3] * gs[3] * inv_l)) << 16);
+        o.x = static_cast<uint32_t>(f32_to_bf16_rne(ov[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(ov[1])) << 16);
+        o.y = static_cast<uint32_t>(f32_to_bf16_rne(ov[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(ov[3])) << 16);
         *reinterpret_cast<uint2*>(orow + d0) = o;
       }
   }

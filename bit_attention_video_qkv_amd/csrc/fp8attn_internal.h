@@ -21,9 +21,17 @@ struct QuantParams {
   uint16_t* v_mean;
   float* ws_partial;  // [B*H, NB128, 128] per-block channel amax
   float* ws_inv;      // [B*H, 128] 448 / channel amax
+  // sequence-mean smoothing (0: off, 1: K, 2: K and V) and the V bias correction
+  float* v_shift;     // [B*H, 128] output vector added to O, or null
+  float* ws_bsum;     // [2, B*H, NB, 128] FP32 block sums (K, V; the V half is reused for the
+                      // block sums of the V rounding error)
+  int32_t* ws_cnt;    // [B*H, NB] valid rows per 64-row block
+  float* ws_mean;     // [2, B*H, 128] sequence means of K and V
   int64_t B, H, Nsrc, N, N64, NB, NB128;
   int perm_kv_per_head;
   int vsmooth;
+  int smoothing;
+  int v_bias_correction;
 };
 
 struct AttnParams {
@@ -34,6 +42,7 @@ struct AttnParams {
   const float* k_scale;
   const float* v_scale;
   const uint16_t* v_mean;   // V-Smooth block means (bf16) or null
+  const float* v_shift;     // [B*H, 128] added to every output row before BF16, or null
   float* mu_f;              // V-Smooth: [B*H, NB128, 128] mean * (1 / s_r) workspace
   uint16_t* out;            // bf16 [B, n_out, H, 128]
   const int32_t* out_rows;  // [N] or null

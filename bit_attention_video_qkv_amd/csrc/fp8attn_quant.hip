@@ -5,16 +5,27 @@
 // s = max|X_block| / 448; one scale per (batch, head, channel) for V over all tokens; V is
 // written token-contiguous so the PV contraction reads keys contiguously. VC-Attention article
 // section 二: V-Smooth subtracts the mean of each 128-row block of the (cluster-permuted) V and
-// quantises the residual; the mean is kept as one 16-bit vector per block.
+// quantises the residual; the mean is kept as one 16-bit vector per block. TeleFuser blog,
+// MiniMax-H3 section: sequence-mean smoothing subtracts the per-head FP32 token mean from K
+// (and V), and the attention adds the V mean back (optionally minus the mean rounding error of
+// the quantised V, the bias compensation).
 //
 // Launch plan on the caller's stream (all row loads are 256-byte rows of the source layout
 // [B, N_src, H, 128], so every gather stays coalesced):
+//   0. (smoothing)   seq_block_sums grid (NB, B*H, 1 or 2): FP32 column sums of each 64-row
+//                    block of K (and V), rows in ascending order; seq_tree_mean grid (B*H, 1|2):
+//                    pairwise tree over the block sums -> the means (and v_shift).
 //   1. quant_qk      grid (NB, B*H, 2): amax of a 64-row Q or K block -> scale -> codes.
 //   2. v_block_stats grid (NB128, B*H): per 128-row block, per channel: amax of V, or (V-Smooth)
 //                    the block mean (exact FP64 column sums) and the residual amax.
 //   3. v_finalize    grid (B*H): channel amax over blocks -> v_scale and its inverse.
 //   4. v_encode      grid (NB, B*H): codes of a 64-row block, transposed through LDS into
-//                    [B, H, 128, N64].
+//                    [B, H, 128, N64]; with the bias correction also the FP32 column sums of
+//                    the rounding error of the block's valid rows.
+//   5. (bias correction) seq_tree_mean over the error sums -> v_shift = mean_V - mean error.
+//
+// Every sum of the smoothing path follows one fixed order (in-block ascending, then the tree),
+// with explicitly rounded FP32 operations, so the means and v_shift are reproducible bit for bit.
 #include "fp8attn_common.h"
 #include "fp8attn_internal.h"
 
@@ -64,6 +75,69 @@ __device__ __forceinline__ float block_max_256(float v, float* red) {
   return r;
 }
 
+// 0a. FP32 column sums of one 64-row block of K (z = 0) or V (z = 1), valid rows in ascending
+// order; thread d owns channel d. The valid-row count is written by the K pass.
+__global__ __launch_bounds__(kHeadDim) void seq_block_sums(QuantParams p) {
+  const int64_t blk = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int z = blockIdx.z;
+  const int64_t b = bh / p.H, h = bh % p.H;
+  const uint16_t* src = z == 0 ? p.k : p.v;
+  const int d = threadIdx.x;
+  float acc = 0.0f;
+  int cnt = 0;
+#pragma unroll 16
+  for (int r = 0; r < kBlock; r++) {
+    const int64_t s = gather_src(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, blk * kBlock + r);
+    if (s >= 0) {
+      acc = __fadd_rn(acc, bf16_to_f32(src_row(src, b, s, h, p.Nsrc, p.H)[d]));
+      cnt++;
+    }
+  }
+  p.ws_bsum[((z * p.B * p.H + bh) * p.NB + blk) * kHeadDim + d] = acc;
+  if (z == 0 && d == 0) p.ws_cnt[bh * p.NB + blk] = cnt;
+}
+
+// 0b / 5. Pairwise tree over the NB block sums of one (b, h) and channel, in place: level L
+// adds element k*2^(L+1) + 2^L into element k*2^(L+1) when it exists (an element without a
+// partner is carried up unchanged), which is the level-by-level halving s[i] = s[2i] + s[2i+1]
+// on the strided positions. mean = total / valid rows (0 when there are none).
+//   pass 0: blockIdx.y = 0 K, 1 V -> ws_mean; the V pass also writes v_shift = mean_V unless
+//           the bias correction follows.
+//   pass 1: the V half holds the error sums -> v_shift = mean_V - mean error.
+__global__ __launch_bounds__(256) void seq_tree_mean(QuantParams p, int pass) {
+  __shared__ int cnt_s[4];
+  const int64_t bh = blockIdx.x;
+  const int z = pass ? 1 : static_cast<int>(blockIdx.y);
+  float* x = p.ws_bsum + (z * p.B * p.H + bh) * p.NB * kHeadDim;
+  const int tid = threadIdx.x;
+  for (int64_t stride = 1; stride < p.NB; stride *= 2) {
+    const int64_t pairs = (p.NB + 2 * stride - 1) / (2 * stride);
+    for (int64_t w = tid; w < pairs * kHeadDim; w += 256) {
+      const int64_t i = (w / kHeadDim) * 2 * stride;
+      const int d = static_cast<int>(w % kHeadDim);
+      if (i + stride < p.NB) x[i * kHeadDim + d] = __fadd_rn(x[i * kHeadDim + d], x[(i + stride) * kHeadDim + d]);
+    }
+    __threadfence();
+    __syncthreads();
+  }
+  int c = 0;
+  for (int64_t j = tid; j < p.NB; j += 256) c += p.ws_cnt[bh * p.NB + j];
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+  if ((tid & 63) == 0) cnt_s[tid >> 6] = c;
+  __syncthreads();
+  const int count = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
+  if (tid < kHeadDim) {
+    const float m = count > 0 ? __fdiv_rn(x[tid], static_cast<float>(count)) : 0.0f;
+    if (pass == 0) {
+      p.ws_mean[(z * p.B * p.H + bh) * kHeadDim + tid] = m;
+      if (z == 1 && !p.v_bias_correction) p.v_shift[bh * kHeadDim + tid] = m;
+    } else {
+      p.v_shift[bh * kHeadDim + tid] = __fsub_rn(p.ws_mean[(p.B * p.H + bh) * kHeadDim + tid], m);
+    }
+  }
+}
+
 // 1. Q / K block quantisation. Thread t handles channels 8*(t%16) .. +7 of rows t/16 + 16*p.
 __global__ __launch_bounds__(256) void quant_qk(QuantParams p) {
   __shared__ float red[4];
@@ -79,6 +153,11 @@ __global__ __launch_bounds__(256) void quant_qk(QuantParams p) {
 
   const int chunk = threadIdx.x & 15;
   const int row0 = threadIdx.x >> 4;
+  // K' = fl32(K - mean_K) on valid rows when smoothing is on (padding rows stay zero)
+  const bool shift = which == 1 && p.smoothing >= 1;
+  float mk[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) mk[j] = shift ? p.ws_mean[bh * kHeadDim + chunk * 8 + j] : 0.0f;
   Bf16x8 x[4];
   float amax = 0.0f;
 #pragma unroll
@@ -87,6 +166,9 @@ __global__ __launch_bounds__(256) void quant_qk(QuantParams p) {
     const int64_t s = gather_src(perm, per_head, bh, p.N, p.Nsrc, i);
     if (s >= 0) {
       x[pass] = load8(src_row(src, b, s, h, p.Nsrc, p.H) + chunk * 8);
+      if (shift)
+#pragma unroll
+        for (int j = 0; j < 8; j++) x[pass].v[j] = __fsub_rn(x[pass].v[j], mk[j]);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; j++) x[pass].v[j] = 0.0f;
@@ -123,6 +205,11 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
   const int rg = threadIdx.x >> 4;
   if (threadIdx.x == 0) n_valid_s = 0;
   __syncthreads();
+  // V' = fl32(V - mean_V) on valid rows under smoothing 2 (never together with V-Smooth)
+  const bool shift = p.smoothing == 2;
+  float mv[8];
+#pragma unroll
+  for (int q = 0; q < 8; q++) mv[q] = shift ? p.ws_mean[(p.B * p.H + bh) * kHeadDim + chunk * 8 + q] : 0.0f;
 
   Bf16x8 x[8];
   bool valid[8];
@@ -135,6 +222,9 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
     my_valid += (chunk == 0 && valid[pass]) ? 1 : 0;
     if (valid[pass]) {
       x[pass] = load8(src_row(p.v, b, s, h, p.Nsrc, p.H) + chunk * 8);
+      if (shift)
+#pragma unroll
+        for (int q = 0; q < 8; q++) x[pass].v[q] = __fsub_rn(x[pass].v[q], mv[q]);
     } else {
 #pragma unroll
       for (int q = 0; q < 8; q++) x[pass].v[q] = 0.0f;
@@ -198,7 +288,26 @@ __global__ __launch_bounds__(128) void v_finalize(QuantParams p) {
   p.ws_inv[bh * kHeadDim + d] = m > 0.0f ? __fdiv_rn(448.0f, m) : 0.0f;
 }
 
-// 4. V codes of a 64-row block, transposed to token-contiguous rows of v8t.
+// fl32(a * b) that is never fused into a following add: hipcc contracts a*b - c into an FMA
+// (its __fmul_rn is a plain operator and the fp-contract pragma is not honoured), and the
+// rounding error of V' is defined with a separately rounded product.
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+  float p = a * b;
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
+// Exact value of an OCP E4M3 byte (finite codes; the encoder saturates, so 0x7F/0xFF never occur).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e == 0 ? static_cast<float>(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// 4. V codes of a 64-row block, transposed to token-contiguous rows of v8t. BIAS: also the FP32
+// column sums (valid rows, ascending) of err = fl32(fl32(decode(code) * s_v) - V') into the V half
+// of ws_bsum, for the bias-corrected v_shift.
+template <bool BIAS>
 __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim][kBlock + 16];  // [channel][token]
   const int64_t blk = blockIdx.x;
@@ -206,12 +315,16 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
   const int64_t b = bh / p.H, h = bh % p.H;
   const int chunk = threadIdx.x & 15;
   const int row0 = threadIdx.x >> 4;
-  float inv[8], mhat[8];
+  const bool shift = p.smoothing == 2;
+  float inv[8], mhat[8], sv[8];
 #pragma unroll
   for (int q = 0; q < 8; q++) {
     inv[q] = p.ws_inv[bh * kHeadDim + chunk * 8 + q];
-    mhat[q] = 0.0f;
+    mhat[q] = shift ? p.ws_mean[(p.B * p.H + bh) * kHeadDim + chunk * 8 + q] : 0.0f;
+    sv[q] = BIAS ? p.v_scale[bh * kHeadDim + chunk * 8 + q] : 0.0f;
   }
+  __shared__ float err_s[BIAS ? kBlock : 1][BIAS ? kHeadDim : 1];
+  __shared__ int valid_s[BIAS ? kBlock : 1];
 #pragma unroll
   for (int pass = 0; pass < 4; pass++) {
     const int t = row0 + 16 * pass;
@@ -225,11 +338,24 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
 #pragma unroll
         for (int q = 0; q < 8; q++) mhat[q] = bf16_to_f32(mrow[q]);
       }
-      float y[8];
+      float r[8], y[8];
 #pragma unroll
-      for (int q = 0; q < 8; q++) y[q] = (x.v[q] - mhat[q]) * inv[q];
+      for (int q = 0; q < 8; q++) {
+        r[q] = __fsub_rn(x.v[q], mhat[q]);
+        y[q] = r[q] * inv[q];
+      }
       lo = e4m3x4(y[0], y[1], y[2], y[3]);
       hi = e4m3x4(y[4], y[5], y[6], y[7]);
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+          const uint32_t code = ((q < 4 ? lo : hi) >> (8 * (q & 3))) & 0xFFu;
+          err_s[t][chunk * 8 + q] = __fsub_rn(mul_rounded(e4m3_decode(code), sv[q]), r[q]);
+        }
+      }
+    }
+    if constexpr (BIAS) {
+      if (chunk == 0) valid_s[t] = s >= 0;
     }
 #pragma unroll
     for (int q = 0; q < 4; q++) {
@@ -245,14 +371,33 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
   uint4* dst = reinterpret_cast<uint4*>(p.v8t + (bh * kHeadDim + d) * p.N64 + blk * kBlock + 32 * half);
   dst[0] = srcp[0];
   dst[1] = srcp[1];
+  if constexpr (BIAS) {
+    if (threadIdx.x < kHeadDim) {
+      float acc = 0.0f;
+      for (int t = 0; t < kBlock; t++)
+        if (valid_s[t]) acc = __fadd_rn(acc, err_s[t][threadIdx.x]);
+      p.ws_bsum[((p.B * p.H + bh) * p.NB + blk) * kHeadDim + threadIdx.x] = acc;
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
+  const unsigned bh = static_cast<unsigned>(p.B * p.H);
+  hipError_t e;
+  if (p.smoothing >= 1) {
+    hipLaunchKernelGGL(seq_block_sums, dim3(static_cast<unsigned>(p.NB), bh, static_cast<unsigned>(p.smoothing)),
+                       dim3(kHeadDim), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(seq_tree_mean, dim3(bh, static_cast<unsigned>(p.smoothing)), dim3(256), 0, stream, p, 0);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 g_qk(static_cast<unsigned>(p.NB), static_cast<unsigned>(p.B * p.H), 2);
   hipLaunchKernelGGL(quant_qk, g_qk, dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(v_block_stats, dim3(static_cast<unsigned>(p.NB128), static_cast<unsigned>(p.B * p.H)),
                      dim3(256), 0, stream, p);
@@ -261,8 +406,15 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(v_finalize, dim3(static_cast<unsigned>(p.B * p.H)), dim3(kHeadDim), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(v_encode, dim3(static_cast<unsigned>(p.NB), static_cast<unsigned>(p.B * p.H)),
-                     dim3(256), 0, stream, p);
+  const dim3 g_enc(static_cast<unsigned>(p.NB), bh);
+  if (!p.v_bias_correction) {
+    hipLaunchKernelGGL(v_encode<false>, g_enc, dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(v_encode<true>, g_enc, dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(seq_tree_mean, dim3(bh, 1), dim3(256), 0, stream, p, 1);
   return hipGetLastError();
 }
 

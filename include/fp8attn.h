@@ -66,20 +66,32 @@ typedef enum fp8attn_pcast {
  * V-Smooth (vsmooth = 1): per 128-row block j of the permuted V', mu_j = mean of the valid
  *   rows (FP64 sum / count, rounded to FP32 then BF16 = v_mean), R = fl32(V' - mu_hat_j), and
  *   R is quantised per channel in place of V (v_scale then holds the residual scales).
+ * Sequence-mean smoothing (TeleFuser blog "FP8 Sol-Attn", MiniMax-H3 section: subtract the
+ *   per-head token mean of K and V in FP32 before quantisation, add the V mean back to the
+ *   output): smoothing = 1 shifts K, 2 shifts K and V. mean = FP32 sum of each 64-row block's
+ *   valid rows in ascending order, the block sums combined by a pairwise tree (level by level
+ *   s[i] = s[2i] + s[2i+1], an odd last one carried), divided by the valid-row count (0 if none);
+ *   K' = fl32(K - mean_K), V' = fl32(V - mean_V) are then quantised as above. smoothing = 2
+ *   writes v_shift = mean_V, or with v_bias_correction = 1 (the section's compensation of the
+ *   mean bias that rounding V' to E4M3 leaves) fl32(mean_V - e), e = the same mean taken over
+ *   fl32(fl32(decode(code) * v_scale) - V'). Pass v_shift to fp8attn_forward.
  *
  * Arguments (device pointers unless noted):
  *   args      host pointer; B, N_src, N, H, D (= 128), perm_q [N] or NULL (identity; then
  *             N == N_src), perm_kv [N] (perm_kv_per_head = 0) or [B*H*N] (= 1) or NULL,
- *             vsmooth 0/1.
+ *             vsmooth 0/1, smoothing 0/1/2 (2 excludes vsmooth), v_bias_correction 0/1
+ *             (needs smoothing 2), v_shift FP32 [B, H, D] output, 16-byte aligned, required
+ *             when smoothing = 2 (ignored otherwise).
  *   q, k, v   bf16 [B, N_src, H, D] (row-major, 16-byte aligned).
  *   q8, k8    E4M3 [B, H, N64, D]; rows >= N are written as code 0.
  *   v8t       E4M3 [B, H, D, N64]; columns >= N and padding positions are code 0.
  *   q_scale, k_scale   FP32 [B, H, NB].      v_scale   FP32 [B, H, D].
  *   v_mean    bf16 [B, H, NB128, D] when vsmooth, else ignored (may be NULL).
  *   workspace device scratch of at least fp8attn_quantize_workspace_bytes(...) bytes,
- *             16-byte aligned; its contents are overwritten.
+ *             16-byte aligned; its contents are overwritten. The size covers every option.
  * Errors: EINVAL on null/misaligned pointers, non-positive sizes, N != N_src without
- *   perm_q, too-small workspace; EUNSUPPORTED on D != 128 or a device other than gfx950.
+ *   perm_q, too-small workspace, smoothing outside 0..2, smoothing 2 with vsmooth, bias
+ *   correction without smoothing 2; EUNSUPPORTED on D != 128 or a device other than gfx950.
  * ------------------------------------------------------------------------------------------ */
 typedef struct fp8attn_quant_args {
   int32_t B, N_src, N, H, D;
@@ -87,6 +99,9 @@ typedef struct fp8attn_quant_args {
   const int32_t* perm_kv;
   int32_t perm_kv_per_head;
   int32_t vsmooth;
+  int32_t smoothing;
+  int32_t v_bias_correction;
+  float* v_shift;
 } fp8attn_quant_args;
 
 size_t fp8attn_quantize_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D,
@@ -162,6 +177,7 @@ fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, i
  * sparse padding) have p = 0. End: O = acc * v_scale / (S l), rounded to BF16.
  * V-Smooth (v_mean != NULL): the block's row sum r restores the mean, O = ((s_r / S) acc +
  * sum r mu_hat_j) / l, j the 128-row V block of each key block.
+ * Sequence-mean smoothing (opts->v_shift != NULL): O = acc * v_scale / (S l) + v_shift.
  *
  * Arguments (device pointers unless noted):
  *   q8, k8, v8t, q_scale, k_scale, v_scale, v_mean   as written by fp8attn_quantize_qkv
@@ -175,7 +191,9 @@ fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, i
  *                    or NULL (identity); lets a gathered layout write O in source order;
  *     n_out          number of rows of `out` (N when out_rows is NULL);
  *     underflow      device uint64 [B*H] or NULL; when non-NULL the counts of keys whose
- *                    p > 0 but whose P code is 0 are ADDED to it (RNE mode only; slower).
+ *                    p > 0 but whose P code is 0 are ADDED to it (RNE mode only; slower);
+ *     v_shift        device FP32 [B*H, D] (16-byte aligned) from sequence-mean smoothing, or
+ *                    NULL; when given O += v_shift before the BF16 rounding. Not with V-Smooth.
  *   out       bf16 [B, n_out, H, D]; rows a query does not own are left untouched.
  *   workspace device scratch of fp8attn_forward_workspace_bytes(...) bytes (may be 0 / NULL
  *             when that is 0).
@@ -192,6 +210,7 @@ typedef struct fp8attn_fwd_opts {
   const int32_t* out_rows;
   int32_t n_out;
   unsigned long long* underflow;
+  const float* v_shift;
 } fp8attn_fwd_opts;
 
 size_t fp8attn_forward_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D,

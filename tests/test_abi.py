@@ -62,14 +62,22 @@ def test_quantize_rejects_bad_arguments(m):
                                   _fake(), ctypes.c_size_t(16), None) == 1   # workspace too small
     assert call(A(1, 64, 64, 2, 128, None, None, 0, 1), ptrs[:9] + [None]) == 1  # vsmooth, no mean
     assert L.fp8attn_quantize_qkv(None, *ptrs, _fake(), ws, None) == 1
+    # sequence-mean smoothing options
+    assert call(A(1, 64, 64, 2, 128, None, None, 0, 0, 3, 0, _fake())) == 1   # smoothing 3
+    assert call(A(1, 64, 64, 2, 128, None, None, 0, 0, -1, 0, _fake())) == 1  # smoothing -1
+    assert call(A(1, 64, 64, 2, 128, None, None, 0, 1, 2, 0, _fake())) == 1   # + V-Smooth
+    assert call(A(1, 64, 64, 2, 128, None, None, 0, 0, 1, 1, _fake())) == 1   # bias, smoothing 1
+    assert call(A(1, 64, 64, 2, 128, None, None, 0, 0, 2, 2, _fake())) == 1   # bias flag 2
+    assert call(A(1, 64, 64, 2, 128, None, None, 0, 0, 2, 0, None)) == 1      # no v_shift
+    assert call(A(1, 64, 64, 2, 128, None, None, 0, 0, 2, 1, _fake(0x10004))) == 1  # misaligned
 
 
 def _opts(m, **kw):
     o = dict(softmax_scale=0.088, p_scale=256.0, kv_order=1, pcast=0, sparse=None, out_rows=None,
-             n_out=256, underflow=None)
+             n_out=256, underflow=None, v_shift=None)
     o.update(kw)
     return m._FwdOpts(o["softmax_scale"], o["p_scale"], o["kv_order"], o["pcast"], o["sparse"],
-                      o["out_rows"], o["n_out"], o["underflow"])
+                      o["out_rows"], o["n_out"], o["underflow"], o["v_shift"])
 
 
 def test_forward_rejects_bad_arguments(m):
@@ -97,6 +105,8 @@ def test_forward_rejects_bad_arguments(m):
     sp = m._Sparse(128, 2, _fake(), _fake(), _fake())
     assert call(_opts(m, sparse=ctypes.pointer(sp)), v_mean=_fake()) == 1   # sparse + V-Smooth
     assert call(_opts(m), v_mean=_fake(), ws=0) == 1                    # V-Smooth needs workspace
+    assert call(_opts(m, v_shift=_fake()), v_mean=_fake(), ws=1 << 24) == 1  # V shift + V-Smooth
+    assert call(_opts(m, v_shift=_fake(0x10008))) == 1                  # misaligned v_shift
 
 
 @pytest.mark.parametrize("grid", [(21, 45, 80, 6, 8, 8, 1, 1, 1), (5, 7, 9, 2, 4, 8, 1, 1, 0),
@@ -123,7 +133,8 @@ def test_sta_build_capacity_error(m):
 
 def test_workspace_sizes(m):
     L = m.lib()
-    assert L.fp8attn_quantize_workspace_bytes(1, 75600, 40, 128, 0) >= 40 * 591 * 128 * 4
+    assert L.fp8attn_quantize_workspace_bytes(1, 75600, 40, 128, 0) >= 40 * 591 * 128 * 4 + \
+        2 * 40 * 1182 * 128 * 4   # + the smoothing block sums of K and V
     assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0) == 0
     assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1) == 24 * 384 * 128 * 4
     assert L.fp8attn_quantize_workspace_bytes(1, 100, 2, 64, 0) == 0

@@ -45,11 +45,13 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
-def _gpu_quantize(m, q, k, v, perm_q=None, perm_kv=None, vsmooth=False, n_layout=None):
+def _gpu_quantize(m, q, k, v, perm_q=None, perm_kv=None, vsmooth=False, n_layout=None,
+                  smoothing=0, bias=False):
     qd, kd, vd = (x.to(DEV) for x in (q, k, v))
     pq = None if perm_q is None else torch.from_numpy(np.ascontiguousarray(perm_q)).to(DEV)
     pkv = None if perm_kv is None else torch.from_numpy(np.ascontiguousarray(perm_kv)).to(DEV)
-    qz = m.quantize_qkv(qd, kd, vd, perm_q=pq, perm_kv=pkv, vsmooth=vsmooth, n_layout=n_layout)
+    qz = m.quantize_qkv(qd, kd, vd, perm_q=pq, perm_kv=pkv, vsmooth=vsmooth, n_layout=n_layout,
+                        smoothing=smoothing, v_bias_correction=bias)
     torch.cuda.synchronize()
     return qz
 
@@ -62,6 +64,10 @@ def _compare_quant(qz, ref):
         assert np.array_equal(_np(getattr(qz, key)).view(np.uint32), ref[key].view(np.uint32)), key
     if ref.get("v_mean") is not None:
         assert np.array_equal(_np(qz.v_mean).view(np.uint16), ref["v_mean"]), "v_mean"
+    if ref.get("v_shift") is not None:
+        assert np.array_equal(_np(qz.v_shift).view(np.uint32), ref["v_shift"].view(np.uint32)), "v_shift"
+    else:
+        assert qz.v_shift is None
 
 
 def _compare_out(gpu_rows, ref_rows, what, amb=None):
@@ -235,17 +241,19 @@ def test_vsmooth_constant_value_exact(m, orc):
         assert torch.equal(out.view(torch.int16), want.view(torch.int16))
 
 
-def _sparse_case(m, orc, grid, H, seed, reverse, expcast=False):
+def _sparse_case(m, orc, grid, H, seed, reverse, expcast=False, smoothing=0, bias=False):
     T, Hg, W, tt, th, tw, rt, rh, rw = grid
     lay = orc.sta_layout(*grid)
     perm = lay["perm"]
     n_src = T * Hg * W
-    q, k, v = workloads.make_qkv(1, n_src, H, seed=seed)
+    q, k, v = workloads.make_qkv(1, n_src, H, seed=seed,
+                                 kind="channel_offset" if smoothing else "normal")
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
-    ref_q = orc.quantize(qb, kb, vb, perm_q=perm, perm_kv=perm)
+    ref_q = orc.quantize(qb, kb, vb, perm_q=perm, perm_kv=perm, smoothing=smoothing,
+                         v_bias_correction=bias)
     ref, _, _, rv, amb = orc.attention_fp8(ref_q, kv_reverse=reverse, expcast=expcast, sparse=lay,
                                            return_amb=True)
-    qz = _gpu_quantize(m, q, k, v, perm_q=perm, perm_kv=perm)
+    qz = _gpu_quantize(m, q, k, v, perm_q=perm, perm_kv=perm, smoothing=smoothing, bias=bias)
     _compare_quant(qz, ref_q)
     sp = m.sparse_to_device(m.sta_build(*grid), DEV)
     out_rows = torch.from_numpy(perm).to(DEV)
@@ -268,6 +276,89 @@ def test_attention_sparse_expcast_and_odd_tiles(m, orc):
     _sparse_case(m, orc, (10, 20, 20, 6, 8, 8, 1, 1, 1), H=1, seed=42, reverse=True, expcast=True)
     _sparse_case(m, orc, (5, 7, 9, 2, 4, 8, 1, 1, 0), H=2, seed=43, reverse=False)
     _sparse_case(m, orc, (9, 10, 11, 3, 8, 8, 1, 0, 1), H=1, seed=44, reverse=True)
+
+
+# ------------------------------------------------------------------------------------------
+# Sequence-mean smoothing (K, K+V, K+V with the V bias correction)
+# ------------------------------------------------------------------------------------------
+SMOOTH_MODES = [(1, False), (2, False), (2, True)]
+
+
+@pytest.mark.parametrize("smoothing,bias", SMOOTH_MODES)
+@pytest.mark.parametrize("B,N,H,seed", [(1, 1000, 3, 51), (2, 37, 1, 52), (1, 8256, 2, 53)])
+def test_quantize_smoothing_bit_exact(m, orc, smoothing, bias, B, N, H, seed):
+    """Codes, scales and v_shift bit-exact: the means use one fixed FP32 summation order on
+    both sides (N = 8256 gives 129 64-row blocks, an odd tree level)."""
+    say("quantize smoothing", smoothing, bias, B, N, H)
+    q, k, v = workloads.make_qkv(B, N, H, seed, kind="channel_offset")
+    ref = orc.quantize(_bits(q), _bits(k), _bits(v), smoothing=smoothing, v_bias_correction=bias)
+    qz = _gpu_quantize(m, q, k, v, smoothing=smoothing, bias=bias)
+    _compare_quant(qz, ref)
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_quantize_smoothing_gather_bit_exact(m, orc, per_head):
+    """Padding positions (-1) are left out of every mean and stay code 0."""
+    say("quantize smoothing gather, per_head", per_head)
+    rng = np.random.default_rng(54)
+    Nsrc, N, H = 700, 900, 2
+    q, k, v = workloads.make_qkv(1, Nsrc, H, 55, kind="channel_offset")
+    perm_q = np.where(np.arange(N) < Nsrc, np.arange(N), -1).astype(np.int32)
+    if per_head:
+        pkv = np.stack([rng.permutation(N) for _ in range(H)])[None]
+    else:
+        pkv = rng.permutation(N)
+    pkv = np.where(pkv >= Nsrc, -1, pkv).astype(np.int32)
+    for smoothing, bias in SMOOTH_MODES:
+        ref = orc.quantize(_bits(q), _bits(k), _bits(v), perm_q=perm_q, perm_kv=pkv,
+                           smoothing=smoothing, v_bias_correction=bias)
+        qz = _gpu_quantize(m, q, k, v, perm_q=perm_q, perm_kv=pkv, n_layout=N,
+                           smoothing=smoothing, bias=bias)
+        _compare_quant(qz, ref)
+
+
+def test_quantize_smoothing_all_padding_head(m, orc):
+    """A layout whose K/V positions are all padding: means 0, scales 0, codes 0, v_shift 0."""
+    say("quantize smoothing, all padding")
+    q, k, v = workloads.make_qkv(1, 64, 1, 56, kind="channel_offset")
+    pkv = np.full(128, -1, np.int32)
+    pq = np.arange(128, dtype=np.int32) % 64
+    ref = orc.quantize(_bits(q), _bits(k), _bits(v), perm_q=pq, perm_kv=pkv, smoothing=2,
+                       v_bias_correction=True)
+    assert np.all(ref["v_shift"] == 0)
+    qz = _gpu_quantize(m, q, k, v, perm_q=pq, perm_kv=pkv, n_layout=128, smoothing=2, bias=True)
+    _compare_quant(qz, ref)
+
+
+@pytest.mark.parametrize("N,smoothing,bias,reverse,expcast", [
+    (1000, 2, True, True, False), (777, 1, False, False, False), (512, 2, False, True, True),
+    (2500, 2, True, False, False)])
+def test_attention_smoothing_small(m, orc, N, smoothing, bias, reverse, expcast):
+    say("attention smoothing", N, smoothing, bias, reverse, expcast)
+    H = 2
+    q, k, v = workloads.make_qkv(1, N, H, seed=60 + N, kind="channel_offset")
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb, smoothing=smoothing, v_bias_correction=bias)
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=reverse, expcast=expcast,
+                                          return_amb=True)
+    qz = _gpu_quantize(m, q, k, v, smoothing=smoothing, bias=bias)
+    _compare_quant(qz, ref_q)
+    out = _run_attn(m, qz, kv_order=int(reverse),
+                    pcast=m.FP8ATTN_PCAST_EXPCAST if expcast else m.FP8ATTN_PCAST_RNE)
+    got = _gpu_rows(out, np.arange(N))
+    _compare_out(got, ref, f"smoothing {smoothing} bias {bias}", amb)
+    tr = lambda a: np.ascontiguousarray(orc.bf16_decode(a).transpose(0, 2, 1, 3))
+    ex, _, _ = orc.attention_ref(orc.MODE_EXACT, tr(qb), tr(kb), tr(vb))
+    c = _cos(got, ex)
+    say(f"cosine vs FP64 exact {c:.6f}")
+    assert c >= COS_MIN
+
+
+def test_attention_smoothing_sparse(m, orc):
+    say("sparse + smoothing")
+    _sparse_case(m, orc, (10, 20, 20, 6, 8, 8, 1, 1, 1), H=2, seed=61, reverse=True, smoothing=2,
+                 bias=True)
+    _sparse_case(m, orc, (5, 7, 9, 2, 4, 8, 1, 1, 0), H=1, seed=62, reverse=False, smoothing=1)
 
 
 @pytest.mark.parametrize("delta,S,reverse", [(7, 1.0, False), (7, 256.0, True), (9, 256.0, False)])

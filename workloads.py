@@ -19,6 +19,10 @@ Recipe (fixed; every config draws FP32 ``randn`` [1, N, H, 128] for Q, then K, t
   same tensors out in (6,8,8) tiles on the grid padded to 24x48x80 (N' = 92160).
 * ``vsmooth``    B=1, H=24, N=49152, seed 5. Q, K N(0,1). V N(0,1) with 5% of the tokens per
   head (2458) multiplied by 20 on 8 distinct random channels each (token outliers).
+
+Kind ``channel_offset`` (test inputs for sequence-mean smoothing): Q, K, V N(0,1), then K and V
+each get a per-(head, channel) offset drawn after V as 4 * randn [H, 128] (K's first), the
+shared token bias that the TeleFuser MiniMax-H3 section removes before quantising.
 """
 from __future__ import annotations
 
@@ -74,6 +78,9 @@ def make_qkv(B, N, H, seed, kind="normal", delta=None, head_dim=D, sink_keys=4,
             sub = v[0, toks, h, :]
             sub.scatter_(1, ch, sub.gather(1, ch) * 20.0)
             v[0, toks, h, :] = sub
+    elif kind == "channel_offset":
+        for t in (k, v):
+            t += 4.0 * torch.randn((H, head_dim), generator=g, dtype=torch.float32)
     else:
         raise ValueError(kind)
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
