@@ -71,6 +71,10 @@ def main():
     ap.add_argument("--workload", default="wan14b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    ap.add_argument("--smoothing", type=int, default=0, choices=(0, 1, 2),
+                    help="sequence-mean smoothing in the quantisation: 0 none, 1 K, 2 K and V")
+    ap.add_argument("--bias-correction", action="store_true",
+                    help="with --smoothing 2: the V rounding-bias correction")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -91,6 +95,15 @@ def main():
         return
 
     cfg_name, sparse, vs, desc = WORKLOADS[args.workload]
+    if args.smoothing == 2 and vs:
+        print("--smoothing 2 shifts V and cannot be combined with V-Smooth", file=sys.stderr)
+        sys.exit(2)
+    if args.bias_correction and args.smoothing != 2:
+        print("--bias-correction needs --smoothing 2", file=sys.stderr)
+        sys.exit(2)
+    if args.smoothing:
+        desc += (f"; sequence-mean smoothing of {'K' if args.smoothing == 1 else 'K and V'}"
+                 + (" with the V bias correction" if args.bias_correction else ""))
     dev = torch.device("cuda:0")
     t0 = time.time()
     q, k, v = workloads.workload(cfg_name)
@@ -122,7 +135,7 @@ def main():
         cluster_ms = c0.elapsed_time(c1)
         assert torch.equal(perm_kv, m_perm)
         log(f"V-Smooth clustering (16 clusters, 8 channels, 10 rounds): {cluster_ms:.3f} ms, once")
-    qz = fa.alloc_quantized(B, n_layout, H, vs, dev)
+    qz = fa.alloc_quantized(B, n_layout, H, vs, dev, smoothing=args.smoothing)
     ws_q = fa.quantize_workspace(B, n_layout, H, vs, dev)
     ws_f = fa.forward_workspace(B, n_layout, H, vs, dev)
     out = torch.zeros((B, n_out, H, D), dtype=torch.bfloat16, device=dev)
@@ -130,7 +143,8 @@ def main():
 
     def step(ev=None):
         fa.quantize_qkv(qd, kd, vd, perm_q=perm_q, perm_kv=perm_kv, vsmooth=vs, n_layout=n_layout,
-                        out=qz, workspace=ws_q)
+                        out=qz, workspace=ws_q, smoothing=args.smoothing,
+                        v_bias_correction=args.bias_correction)
         if ev is not None:
             ev[0].record()
         fa.forward(qz, p_scale=256.0, kv_order=fa.FP8ATTN_KV_REVERSE, pcast=pcast, sparse=sp,
@@ -183,7 +197,8 @@ def main():
         "dtype": "e4m3",
         "data": "synthetic",
         "config": {"workload": desc, "global_batch": B, "seq_len": N, "heads": H, "head_dim": D,
-                   "parallelism": "none (one GPU)", "name": args.workload},
+                   "parallelism": "none (one GPU)", "name": args.workload,
+                   "smoothing": args.smoothing, "v_bias_correction": args.bias_correction},
         "quantize_ms": round(ms_step - ms_attn, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
@@ -226,11 +241,13 @@ def cpu_baseline(args, cfg_name, sparse, vs):
     t0 = time.time()
     if sparse:
         lay = oracle.sta_layout(21, 45, 80, 6, 8, 8, 1, 1, 1)
-        qz = oracle.quantize(bq, bk, bv, perm_q=lay["perm"], perm_kv=lay["perm"])
+        qz = oracle.quantize(bq, bk, bv, perm_q=lay["perm"], perm_kv=lay["perm"],
+                             smoothing=args.smoothing, v_bias_correction=args.bias_correction)
     else:
         lay = None
         perm_kv = oracle.vsmooth_perm(bv) if vs else None  # the head's cluster order
-        qz = oracle.quantize(bq, bk, bv, vsmooth=vs, perm_kv=perm_kv)
+        qz = oracle.quantize(bq, bk, bv, vsmooth=vs, perm_kv=perm_kv, smoothing=args.smoothing,
+                             v_bias_correction=args.bias_correction)
     t_quant = time.time() - t0
     Nl = qz["N"]
     rng = np.random.default_rng(0)

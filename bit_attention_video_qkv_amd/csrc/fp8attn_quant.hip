@@ -13,8 +13,9 @@
 // Launch plan on the caller's stream (all row loads are 256-byte rows of the source layout
 // [B, N_src, H, 128], so every gather stays coalesced):
 //   0. (smoothing)   seq_block_sums grid (NB, B*H, 1 or 2): FP32 column sums of each 64-row
-//                    block of K (and V), rows in ascending order; seq_tree_mean grid (B*H, 1|2):
-//                    pairwise tree over the block sums -> the means (and v_shift).
+//                    block of K (and V), rows in ascending order; seq_tree_pass (LDS passes of
+//                    the pairwise tree over the block sums) and seq_mean_final -> the means
+//                    (and v_shift).
 //   1. quant_qk      grid (NB, B*H, 2): amax of a 64-row Q or K block -> scale -> codes.
 //   2. v_block_stats grid (NB128, B*H): per 128-row block, per channel: amax of V, or (V-Smooth)
 //                    the block mean (exact FP64 column sums) and the residual amax.
@@ -22,7 +23,7 @@
 //   4. v_encode      grid (NB, B*H): codes of a 64-row block, transposed through LDS into
 //                    [B, H, 128, N64]; with the bias correction also the FP32 column sums of
 //                    the rounding error of the block's valid rows.
-//   5. (bias correction) seq_tree_mean over the error sums -> v_shift = mean_V - mean error.
+//   5. (bias correction) the same tree over the error sums -> v_shift = mean_V - mean error.
 //
 // Every sum of the smoothing path follows one fixed order (in-block ascending, then the tree),
 // with explicitly rounded FP32 operations, so the means and v_shift are reproducible bit for bit.
@@ -76,65 +77,103 @@ __device__ __forceinline__ float block_max_256(float v, float* red) {
 }
 
 // 0a. FP32 column sums of one 64-row block of K (z = 0) or V (z = 1), valid rows in ascending
-// order; thread d owns channel d. The valid-row count is written by the K pass.
-__global__ __launch_bounds__(kHeadDim) void seq_block_sums(QuantParams p) {
+// order. The block is staged through LDS as bf16 with coalesced 16-byte row loads (thread t:
+// channels 8*(t%16)..+7 of rows t/16 + 16*p); thread d < 128 then sums channel d down the rows.
+// The valid-row count is written by the K pass.
+__global__ __launch_bounds__(256) void seq_block_sums(QuantParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kBlock][kHeadDim + 8];
+  __shared__ uint32_t valid_bits[2];  // bit r: row r of the block is valid
+  if (threadIdx.x < 2) valid_bits[threadIdx.x] = 0u;
+  __syncthreads();
   const int64_t blk = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int z = blockIdx.z;
   const int64_t b = bh / p.H, h = bh % p.H;
   const uint16_t* src = z == 0 ? p.k : p.v;
-  const int d = threadIdx.x;
-  float acc = 0.0f;
-  int cnt = 0;
-#pragma unroll 16
-  for (int r = 0; r < kBlock; r++) {
+  const int chunk = threadIdx.x & 15;
+  const int row0 = threadIdx.x >> 4;
+#pragma unroll
+  for (int pass = 0; pass < 4; pass++) {
+    const int r = row0 + 16 * pass;
     const int64_t s = gather_src(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, blk * kBlock + r);
-    if (s >= 0) {
-      acc = __fadd_rn(acc, bf16_to_f32(src_row(src, b, s, h, p.Nsrc, p.H)[d]));
-      cnt++;
-    }
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+    if (s >= 0) raw = *reinterpret_cast<const uint4*>(src_row(src, b, s, h, p.Nsrc, p.H) + chunk * 8);
+    *reinterpret_cast<uint4*>(&tile[r][chunk * 8]) = raw;
+    if (chunk == 0 && s >= 0) atomicOr(&valid_bits[r >> 5], 1u << (r & 31));
   }
-  p.ws_bsum[((z * p.B * p.H + bh) * p.NB + blk) * kHeadDim + d] = acc;
-  if (z == 0 && d == 0) p.ws_cnt[bh * p.NB + blk] = cnt;
+  __syncthreads();
+  const int d = threadIdx.x;
+  if (d < kHeadDim) {
+    const uint64_t vm = static_cast<uint64_t>(valid_bits[0]) | (static_cast<uint64_t>(valid_bits[1]) << 32);
+    float acc = 0.0f;
+#pragma unroll 16
+    for (int r = 0; r < kBlock; r++) {
+      const float sum = __fadd_rn(acc, bf16_to_f32(tile[r][d]));
+      acc = ((vm >> r) & 1u) ? sum : acc;
+    }
+    const int cnt = __popcll(vm);
+    p.ws_bsum[((z * p.B * p.H + bh) * p.NB + blk) * kHeadDim + d] = acc;
+    if (z == 0 && d == 0) p.ws_cnt[bh * p.NB + blk] = cnt;
+  }
 }
 
-// 0b / 5. Pairwise tree over the NB block sums of one (b, h) and channel, in place: level L
-// adds element k*2^(L+1) + 2^L into element k*2^(L+1) when it exists (an element without a
-// partner is carried up unchanged), which is the level-by-level halving s[i] = s[2i] + s[2i+1]
-// on the strided positions. mean = total / valid rows (0 when there are none).
-//   pass 0: blockIdx.y = 0 K, 1 V -> ws_mean; the V pass also writes v_shift = mean_V unless
-//           the bias correction follows.
-//   pass 1: the V half holds the error sums -> v_shift = mean_V - mean error.
-__global__ __launch_bounds__(256) void seq_tree_mean(QuantParams p, int pass) {
-  __shared__ int cnt_s[4];
-  const int64_t bh = blockIdx.x;
-  const int z = pass ? 1 : static_cast<int>(blockIdx.y);
-  float* x = p.ws_bsum + (z * p.B * p.H + bh) * p.NB * kHeadDim;
-  const int tid = threadIdx.x;
-  for (int64_t stride = 1; stride < p.NB; stride *= 2) {
-    const int64_t pairs = (p.NB + 2 * stride - 1) / (2 * stride);
-    for (int64_t w = tid; w < pairs * kHeadDim; w += 256) {
-      const int64_t i = (w / kHeadDim) * 2 * stride;
-      const int d = static_cast<int>(w % kHeadDim);
-      if (i + stride < p.NB) x[i * kHeadDim + d] = __fadd_rn(x[i * kHeadDim + d], x[(i + stride) * kHeadDim + d]);
+// 0b / 5. Pairwise tree over the NB block sums of one (b, h) and channel. The tree is the
+// level-by-level halving s[i] = s[2i] + s[2i+1] with an odd last element carried up; on block
+// positions it reads: at level l, position k*2^(l+1) adds position k*2^(l+1) + 2^l when that is
+// < NB. A node depends only on the blocks below it, so the tree is evaluated in passes: each
+// pass reduces aligned groups of kTreeSpan consecutive nodes (spacing `stride` blocks) in LDS,
+// in place, until one node is left; seq_mean_final then divides by the valid-row count.
+constexpr int kTreeSpan = 256;
+constexpr int kTreeCh = 32;
+
+// grid (ceil(nodes / kTreeSpan), B*H*nz, 128 / kTreeCh); tensor z = z_first + y / (B*H).
+__global__ __launch_bounds__(256) void seq_tree_pass(QuantParams p, int z_first, int64_t stride,
+                                                      int64_t nodes) {
+  __shared__ float s[kTreeSpan][kTreeCh + 1];
+  const int64_t BH = p.B * p.H;
+  const int64_t bh = blockIdx.y % BH;
+  const int z = z_first + static_cast<int>(blockIdx.y / BH);
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kTreeSpan;
+  const int c0 = blockIdx.z * kTreeCh;
+  float* x = p.ws_bsum + (z * BH + bh) * p.NB * kHeadDim + c0;
+  const int n_here = static_cast<int>(min<int64_t>(kTreeSpan, nodes - g0));
+  for (int w = threadIdx.x; w < n_here * kTreeCh; w += 256) {
+    const int i = w / kTreeCh, c = w % kTreeCh;
+    s[i][c] = x[(g0 + i) * stride * kHeadDim + c];
+  }
+  __syncthreads();
+  for (int st = 1; st < n_here; st *= 2) {
+    for (int w = threadIdx.x; w < (kTreeSpan / (2 * st)) * kTreeCh; w += 256) {
+      const int i = (w / kTreeCh) * 2 * st, c = w % kTreeCh;
+      if (g0 + i + st < nodes) s[i][c] = __fadd_rn(s[i][c], s[i + st][c]);
     }
-    __threadfence();
     __syncthreads();
   }
+  if (threadIdx.x < kTreeCh) x[g0 * stride * kHeadDim + threadIdx.x] = s[0][threadIdx.x];
+}
+
+// mean = root / valid rows (0 when there are none). grid (B*H, nz), 128 threads.
+//   pass 0: tensor y (0 K, 1 V) -> ws_mean; the V pass also writes v_shift = mean_V unless the
+//           bias correction follows.
+//   pass 1: the V half holds the error sums -> v_shift = mean_V - mean error.
+__global__ __launch_bounds__(kHeadDim) void seq_mean_final(QuantParams p, int pass) {
+  __shared__ int cnt_s[2];
+  const int64_t bh = blockIdx.x;
+  const int z = pass ? 1 : static_cast<int>(blockIdx.y);
+  const int d = threadIdx.x;
   int c = 0;
-  for (int64_t j = tid; j < p.NB; j += 256) c += p.ws_cnt[bh * p.NB + j];
+  for (int64_t j = d; j < p.NB; j += kHeadDim) c += p.ws_cnt[bh * p.NB + j];
   for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
-  if ((tid & 63) == 0) cnt_s[tid >> 6] = c;
+  if ((d & 63) == 0) cnt_s[d >> 6] = c;
   __syncthreads();
-  const int count = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
-  if (tid < kHeadDim) {
-    const float m = count > 0 ? __fdiv_rn(x[tid], static_cast<float>(count)) : 0.0f;
-    if (pass == 0) {
-      p.ws_mean[(z * p.B * p.H + bh) * kHeadDim + tid] = m;
-      if (z == 1 && !p.v_bias_correction) p.v_shift[bh * kHeadDim + tid] = m;
-    } else {
-      p.v_shift[bh * kHeadDim + tid] = __fsub_rn(p.ws_mean[(p.B * p.H + bh) * kHeadDim + tid], m);
-    }
+  const int count = cnt_s[0] + cnt_s[1];
+  const float root = p.ws_bsum[(z * p.B * p.H + bh) * p.NB * kHeadDim + d];
+  const float m = count > 0 ? __fdiv_rn(root, static_cast<float>(count)) : 0.0f;
+  if (pass == 0) {
+    p.ws_mean[(z * p.B * p.H + bh) * kHeadDim + d] = m;
+    if (z == 1 && !p.v_bias_correction) p.v_shift[bh * kHeadDim + d] = m;
+  } else {
+    p.v_shift[bh * kHeadDim + d] = __fsub_rn(p.ws_mean[(p.B * p.H + bh) * kHeadDim + d], m);
   }
 }
 
@@ -306,7 +345,8 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 
 // 4. V codes of a 64-row block, transposed to token-contiguous rows of v8t. BIAS: also the FP32
 // column sums (valid rows, ascending) of err = fl32(fl32(decode(code) * s_v) - V') into the V half
-// of ws_bsum, for the bias-corrected v_shift.
+// of ws_bsum, for the bias-corrected v_shift; the input rows are kept in LDS as bf16 and the codes
+// are read back from the transpose tile.
 template <bool BIAS>
 __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim][kBlock + 16];  // [channel][token]
@@ -316,15 +356,18 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
   const int chunk = threadIdx.x & 15;
   const int row0 = threadIdx.x >> 4;
   const bool shift = p.smoothing == 2;
-  float inv[8], mhat[8], sv[8];
+  float inv[8], mhat[8];
 #pragma unroll
   for (int q = 0; q < 8; q++) {
     inv[q] = p.ws_inv[bh * kHeadDim + chunk * 8 + q];
     mhat[q] = shift ? p.ws_mean[(p.B * p.H + bh) * kHeadDim + chunk * 8 + q] : 0.0f;
-    sv[q] = BIAS ? p.v_scale[bh * kHeadDim + chunk * 8 + q] : 0.0f;
   }
-  __shared__ float err_s[BIAS ? kBlock : 1][BIAS ? kHeadDim : 1];
-  __shared__ int valid_s[BIAS ? kBlock : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t vin_s[BIAS ? kBlock : 1][BIAS ? kHeadDim + 8 : 8];
+  __shared__ uint32_t valid_bits[2];  // BIAS: bit t = row t of the block is valid
+  if constexpr (BIAS) {
+    if (threadIdx.x < 2) valid_bits[threadIdx.x] = 0u;
+    __syncthreads();
+  }
 #pragma unroll
   for (int pass = 0; pass < 4; pass++) {
     const int t = row0 + 16 * pass;
@@ -332,7 +375,9 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
     const int64_t s = gather_src(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, i);
     uint32_t lo = 0, hi = 0;
     if (s >= 0) {
-      const Bf16x8 x = load8(src_row(p.v, b, s, h, p.Nsrc, p.H) + chunk * 8);
+      const uint16_t* row = src_row(p.v, b, s, h, p.Nsrc, p.H) + chunk * 8;
+      const Bf16x8 x = load8(row);
+      if constexpr (BIAS) *reinterpret_cast<uint4*>(&vin_s[t][chunk * 8]) = *reinterpret_cast<const uint4*>(row);
       if (p.vsmooth) {
         const uint16_t* mrow = p.v_mean + (bh * p.NB128 + i / kVBlock) * kHeadDim + chunk * 8;
 #pragma unroll
@@ -346,16 +391,9 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
       }
       lo = e4m3x4(y[0], y[1], y[2], y[3]);
       hi = e4m3x4(y[4], y[5], y[6], y[7]);
-      if constexpr (BIAS) {
-#pragma unroll
-        for (int q = 0; q < 8; q++) {
-          const uint32_t code = ((q < 4 ? lo : hi) >> (8 * (q & 3))) & 0xFFu;
-          err_s[t][chunk * 8 + q] = __fsub_rn(mul_rounded(e4m3_decode(code), sv[q]), r[q]);
-        }
-      }
     }
     if constexpr (BIAS) {
-      if (chunk == 0) valid_s[t] = s >= 0;
+      if (chunk == 0 && s >= 0) atomicOr(&valid_bits[t >> 5], 1u << (t & 31));
     }
 #pragma unroll
     for (int q = 0; q < 4; q++) {
@@ -372,27 +410,55 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
   dst[0] = srcp[0];
   dst[1] = srcp[1];
   if constexpr (BIAS) {
+    // The rounding error of channel c, rows in ascending order (the bias correction exists only
+    // with V smoothing, so V' = fl32(V - mean_V)): err = fl32(fl32(decode(code) * s_v) - V').
     if (threadIdx.x < kHeadDim) {
+      const int c = threadIdx.x;
+      const float mv = p.ws_mean[(p.B * p.H + bh) * kHeadDim + c];
+      const float svc = p.v_scale[bh * kHeadDim + c];
+      const uint64_t vm = static_cast<uint64_t>(valid_bits[0]) | (static_cast<uint64_t>(valid_bits[1]) << 32);
       float acc = 0.0f;
-      for (int t = 0; t < kBlock; t++)
-        if (valid_s[t]) acc = __fadd_rn(acc, err_s[t][threadIdx.x]);
-      p.ws_bsum[((p.B * p.H + bh) * p.NB + blk) * kHeadDim + threadIdx.x] = acc;
+#pragma unroll 2
+      for (int t4 = 0; t4 < kBlock; t4 += 4) {
+        const uint32_t codes = *reinterpret_cast<const uint32_t*>(&tile[c][t4]);
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const float r = __fsub_rn(bf16_to_f32(vin_s[t4 + u][c]), mv);
+          const float e = __fsub_rn(mul_rounded(e4m3_decode((codes >> (8 * u)) & 0xFFu), svc), r);
+          const float sum = __fadd_rn(acc, e);
+          acc = ((vm >> (t4 + u)) & 1u) ? sum : acc;
+        }
+      }
+      p.ws_bsum[((p.B * p.H + bh) * p.NB + blk) * kHeadDim + c] = acc;
     }
   }
 }
 
 }  // namespace
 
+// Tree passes and the final division for tensors z_first .. z_first + nz - 1.
+static hipError_t launch_seq_means(const QuantParams& p, int z_first, int nz, int pass, hipStream_t stream) {
+  const unsigned bhz = static_cast<unsigned>(p.B * p.H * nz);
+  for (int64_t stride = 1, nodes = p.NB; nodes > 1; stride *= kTreeSpan, nodes = (nodes + kTreeSpan - 1) / kTreeSpan) {
+    const dim3 grid(static_cast<unsigned>((nodes + kTreeSpan - 1) / kTreeSpan), bhz, kHeadDim / kTreeCh);
+    hipLaunchKernelGGL(seq_tree_pass, grid, dim3(256), 0, stream, p, z_first, stride, nodes);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(seq_mean_final, dim3(static_cast<unsigned>(p.B * p.H), static_cast<unsigned>(nz)),
+                     dim3(kHeadDim), 0, stream, p, pass);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
   const unsigned bh = static_cast<unsigned>(p.B * p.H);
   hipError_t e;
   if (p.smoothing >= 1) {
     hipLaunchKernelGGL(seq_block_sums, dim3(static_cast<unsigned>(p.NB), bh, static_cast<unsigned>(p.smoothing)),
-                       dim3(kHeadDim), 0, stream, p);
+                       dim3(256), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(seq_tree_mean, dim3(bh, static_cast<unsigned>(p.smoothing)), dim3(256), 0, stream, p, 0);
-    e = hipGetLastError();
+    e = launch_seq_means(p, 0, p.smoothing, 0, stream);
     if (e != hipSuccess) return e;
   }
   const dim3 g_qk(static_cast<unsigned>(p.NB), static_cast<unsigned>(p.B * p.H), 2);
@@ -414,8 +480,7 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(v_encode<true>, g_enc, dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(seq_tree_mean, dim3(bh, 1), dim3(256), 0, stream, p, 1);
-  return hipGetLastError();
+  return launch_seq_means(p, 1, 1, 1, stream);
 }
 
 }  // namespace fp8attn

@@ -285,10 +285,12 @@ SMOOTH_MODES = [(1, False), (2, False), (2, True)]
 
 
 @pytest.mark.parametrize("smoothing,bias", SMOOTH_MODES)
-@pytest.mark.parametrize("B,N,H,seed", [(1, 1000, 3, 51), (2, 37, 1, 52), (1, 8256, 2, 53)])
+@pytest.mark.parametrize("B,N,H,seed", [(1, 1000, 3, 51), (2, 37, 1, 52), (1, 8256, 2, 53),
+                                         (1, 16448, 1, 57)])
 def test_quantize_smoothing_bit_exact(m, orc, smoothing, bias, B, N, H, seed):
     """Codes, scales and v_shift bit-exact: the means use one fixed FP32 summation order on
-    both sides (N = 8256 gives 129 64-row blocks, an odd tree level)."""
+    both sides (N = 8256 gives 129 64-row blocks, an odd tree level; N = 16448 gives 257
+    blocks, more than one 256-node group of the device's tree passes)."""
     say("quantize smoothing", smoothing, bias, B, N, H)
     q, k, v = workloads.make_qkv(B, N, H, seed, kind="channel_offset")
     ref = orc.quantize(_bits(q), _bits(k), _bits(v), smoothing=smoothing, v_bias_correction=bias)
@@ -422,9 +424,11 @@ def _slice_heads(t, heads):
     return t[:, :, heads, :].contiguous()
 
 
-@pytest.mark.parametrize("name", ["wan13b", "wan14b", "vsmooth"])
+@pytest.mark.parametrize("name", ["wan13b", "wan14b", "vsmooth", "wan14b+smoothing"])
 def test_full_size_sampled(m, orc, name):
     say("full size", name)
+    smooth = name.endswith("+smoothing")      # K and V smoothing with the bias correction
+    name = name.split("+")[0]
     q, k, v = workloads.workload(name)
     B, N, H, _ = q.shape
     heads = [0, H - 1]
@@ -435,13 +439,16 @@ def test_full_size_sampled(m, orc, name):
         perm = np.zeros((1, H, N), np.int32)
         perm[:] = np.arange(N, dtype=np.int32)
         perm[0, heads] = perm_s[0]
-    qz = _gpu_quantize(m, q, k, v, perm_kv=perm, vsmooth=vs)
+    sm = 2 if smooth else 0
+    qz = _gpu_quantize(m, q, k, v, perm_kv=perm, vsmooth=vs, smoothing=sm, bias=smooth)
     out = _run_attn(m, qz, kv_order=1, pcast=m.FP8ATTN_PCAST_EXPCAST if vs else m.FP8ATTN_PCAST_RNE)
     qs, ks, vsl = (_bits(_slice_heads(t, heads)) for t in (q, k, v))
-    ref_q = orc.quantize(qs, ks, vsl, perm_kv=None if perm is None else perm[:, heads], vsmooth=vs)
+    ref_q = orc.quantize(qs, ks, vsl, perm_kv=None if perm is None else perm[:, heads], vsmooth=vs,
+                         smoothing=sm, v_bias_correction=smooth)
     for key in ("q8", "k8", "v8t"):
         assert np.array_equal(_np(getattr(qz, key)[:, heads]), ref_q[key]), key
-    for key in ("q_scale", "k_scale", "v_scale"):
+    keys = ("q_scale", "k_scale", "v_scale") + (("v_shift",) if smooth else ())
+    for key in keys:
         assert np.array_equal(_np(getattr(qz, key)[:, heads]), ref_q[key]), key
     rows = workloads.sample_rows(N, 48, seed=7)
     ref, _, _, _, amb = orc.attention_fp8(ref_q, rows=rows, kv_reverse=True, expcast=vs,
