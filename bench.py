@@ -56,6 +56,9 @@ WORKLOADS = {
     "vsmooth": ("vsmooth", False, True,
                 "V-Smooth + ExpCast, B=1 H=24 N=49152 D=128, 5% token outliers x20 in V, "
                 "16-cluster k-means permutation (reused, not timed), S=256, reverse KV order"),
+    "sink4096": ("sink4096", False, False,
+                 "sink stress, B=1 H=8 N=4096 D=128, 4 sink keys with logit offset 9, S=256, "
+                 "reverse KV order (256 query tiles: below the machine's width)"),
 }
 
 
@@ -75,6 +78,11 @@ def main():
                     help="sequence-mean smoothing in the quantisation: 0 none, 1 K, 2 K and V")
     ap.add_argument("--bias-correction", action="store_true",
                     help="with --smoothing 2: the V rounding-bias correction")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="run only this many heads of the workload (one GPU's share of a head-"
+                         "sharded run); 0 = all")
+    ap.add_argument("--kv-splits", default="1",
+                    help="split-KV pieces: 1 (none), 2..16, or auto (dense workloads)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -95,6 +103,10 @@ def main():
         return
 
     cfg_name, sparse, vs, desc = WORKLOADS[args.workload]
+    kv_splits = fa.FP8ATTN_KV_SPLITS_AUTO if args.kv_splits == "auto" else int(args.kv_splits)
+    if sparse and kv_splits > 1:
+        print("split-KV is for dense workloads", file=sys.stderr)
+        sys.exit(2)
     if args.smoothing == 2 and vs:
         print("--smoothing 2 shifts V and cannot be combined with V-Smooth", file=sys.stderr)
         sys.exit(2)
@@ -106,7 +118,10 @@ def main():
                  + (" with the V bias correction" if args.bias_correction else ""))
     dev = torch.device("cuda:0")
     t0 = time.time()
-    q, k, v = workloads.workload(cfg_name)
+    q, k, v = workloads.workload(cfg_name, delta=9 if cfg_name == "sink4096" else None,
+                                 heads=args.heads or None)
+    if args.heads:
+        desc += f"; {args.heads} of its heads (one GPU's share)"
     B, N, H, D = q.shape
     log(f"inputs {args.workload} B={B} N={N} H={H} D={D} generated in {time.time() - t0:.1f}s")
 
@@ -137,7 +152,7 @@ def main():
         log(f"V-Smooth clustering (16 clusters, 8 channels, 10 rounds): {cluster_ms:.3f} ms, once")
     qz = fa.alloc_quantized(B, n_layout, H, vs, dev, smoothing=args.smoothing)
     ws_q = fa.quantize_workspace(B, n_layout, H, vs, dev)
-    ws_f = fa.forward_workspace(B, n_layout, H, vs, dev)
+    ws_f = fa.forward_workspace(B, n_layout, H, vs, dev, 1 if sparse else kv_splits)
     out = torch.zeros((B, n_out, H, D), dtype=torch.bfloat16, device=dev)
     pcast = fa.FP8ATTN_PCAST_EXPCAST if vs else fa.FP8ATTN_PCAST_RNE
 
@@ -148,7 +163,8 @@ def main():
         if ev is not None:
             ev[0].record()
         fa.forward(qz, p_scale=256.0, kv_order=fa.FP8ATTN_KV_REVERSE, pcast=pcast, sparse=sp,
-                   out_rows=out_rows, n_out=n_out, out=out, workspace=ws_f)
+                   out_rows=out_rows, n_out=n_out, out=out, workspace=ws_f,
+                   kv_splits=1 if sparse else kv_splits)
         if ev is not None:
             ev[1].record()
 
@@ -198,7 +214,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "global_batch": B, "seq_len": N, "heads": H, "head_dim": D,
                    "parallelism": "none (one GPU)", "name": args.workload,
-                   "smoothing": args.smoothing, "v_bias_correction": args.bias_correction},
+                   "smoothing": args.smoothing, "v_bias_correction": args.bias_correction,
+                   "kv_splits": args.kv_splits},
         "quantize_ms": round(ms_step - ms_attn, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
@@ -234,7 +251,7 @@ def cpu_baseline(args, cfg_name, sparse, vs):
     import workloads
 
     oracle._load()
-    q, k, v = workloads.workload(cfg_name, heads=1)
+    q, k, v = workloads.workload(cfg_name, heads=1, delta=9 if cfg_name == "sink4096" else None)
     B, N, H, D = q.shape
     bq, bk, bv = workloads.bits(q), workloads.bits(k), workloads.bits(v)
     rows_n = args.cpu_rows or 16384

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8attn.so")
 
 FP8ATTN_KV_FORWARD, FP8ATTN_KV_REVERSE = 0, 1
 FP8ATTN_PCAST_RNE, FP8ATTN_PCAST_EXPCAST = 0, 1
+FP8ATTN_KV_SPLITS_AUTO, FP8ATTN_KV_SPLITS_MAX = -1, 16
 HEAD_DIM = 128
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or device", 3: "HIP runtime error"}
@@ -55,7 +56,7 @@ class _FwdOpts(ctypes.Structure):
                 ("kv_order", ctypes.c_int), ("pcast", ctypes.c_int),
                 ("sparse", ctypes.POINTER(_Sparse)), ("out_rows", ctypes.c_void_p),
                 ("n_out", ctypes.c_int32), ("underflow", ctypes.c_void_p),
-                ("v_shift", ctypes.c_void_p)]
+                ("v_shift", ctypes.c_void_p), ("kv_splits", ctypes.c_int32)]
 
 
 _lib = None
@@ -82,7 +83,7 @@ def lib():
             ctypes.POINTER(_FwdOpts), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
             ctypes.c_void_p]
         L.fp8attn_forward_workspace_bytes.restype = ctypes.c_size_t
-        L.fp8attn_forward_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+        L.fp8attn_forward_workspace_bytes.argtypes = [ctypes.c_int32] * 6
         L.fp8attn_sta_build.restype = ctypes.c_int
         L.fp8attn_sta_build.argtypes = [ctypes.c_int32] * 9 + [ctypes.c_void_p] * 4 + [
             ctypes.c_int32, ctypes.c_void_p]
@@ -232,16 +233,17 @@ def sparse_to_device(layout, device):
                   to(layout["row_ptr"]), to(layout["col_idx"]))
 
 
-def forward_workspace(B, N, H, vsmooth, device):
-    n = int(lib().fp8attn_forward_workspace_bytes(B, N, H, HEAD_DIM, 1 if vsmooth else 0))
+def forward_workspace(B, N, H, vsmooth, device, kv_splits=1):
+    n = int(lib().fp8attn_forward_workspace_bytes(B, N, H, HEAD_DIM, 1 if vsmooth else 0, int(kv_splits)))
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def forward(qz: Quantized, softmax_scale=1.0 / math.sqrt(HEAD_DIM), p_scale=256.0,
             kv_order=FP8ATTN_KV_REVERSE, pcast=FP8ATTN_PCAST_RNE, sparse: Sparse | None = None,
-            out_rows=None, n_out=None, underflow=None, out=None, workspace=None):
+            out_rows=None, n_out=None, underflow=None, out=None, workspace=None, kv_splits=1):
     """Attention forward on quantised operands. Returns bf16 [B, n_out, H, 128] (``out`` when
-    given; rows the call does not own keep their previous contents)."""
+    given; rows the call does not own keep their previous contents). kv_splits: 1 (no split),
+    2..16 or FP8ATTN_KV_SPLITS_AUTO (split-KV, dense only)."""
     B, N, H = qz.B, qz.N, qz.H
     dev = qz.q8.device
     if n_out is None:
@@ -249,11 +251,12 @@ def forward(qz: Quantized, softmax_scale=1.0 / math.sqrt(HEAD_DIM), p_scale=256.
     if out is None:
         out = torch.zeros((B, n_out, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
     vs = qz.v_mean is not None
-    ws = workspace if workspace is not None else forward_workspace(B, N, H, vs, dev)
+    ks = 1 if sparse is not None else int(kv_splits)
+    ws = workspace if workspace is not None else forward_workspace(B, N, H, vs, dev, ks)
     sp = sparse._c() if sparse is not None else None
     opts = _FwdOpts(float(softmax_scale), float(p_scale), int(kv_order), int(pcast),
                     ctypes.pointer(sp) if sp is not None else None, _ptr(out_rows), int(n_out),
-                    _ptr(underflow), _ptr(qz.v_shift))
+                    _ptr(underflow), _ptr(qz.v_shift), int(kv_splits))
     st = lib().fp8attn_forward(
         B, N, H, HEAD_DIM, _ptr(qz.q8), _ptr(qz.k8), _ptr(qz.v8t), _ptr(qz.q_scale),
         _ptr(qz.k_scale), _ptr(qz.v_scale), _ptr(qz.v_mean), ctypes.byref(opts), _ptr(out),

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 
@@ -40,6 +41,54 @@ fp8attn_status check_device() {
 }
 
 fp8attn_status from_hip(hipError_t e) { return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_EHIP; }
+
+bool valid_splits_arg(int32_t kv_splits) {
+  return kv_splits == FP8ATTN_KV_SPLITS_AUTO || (kv_splits >= 0 && kv_splits <= FP8ATTN_KV_SPLITS_MAX);
+}
+
+// Compute units of the current device (cached per device; 256 when it cannot be queried).
+std::atomic<int> g_cus[64];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = g_cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 256;
+    g_cus[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+// Split-KV pieces for a dense forward: the key blocks are cut at multiples of
+// L = 2 * ceil(NB / (2 * want)) blocks (whole 128-row V blocks); returns ceil(NB / L) and L, or 1
+// and NB without a split. Auto (measured on MI355X; only sequences of at least 16384 tokens, as
+// shorter ones lose more to each piece's prologue and the merge than they gain), with
+// rounds = query tiles / (2 workgroups per CU x CUs):
+//   rounds < 1                                   -> ceil(1 / rounds) pieces (at most 8);
+//   1 <= rounds < 4, last round at most 35% full -> 3 pieces;
+//   otherwise                                    -> 1.
+int resolve_splits(int32_t B, int32_t N, int32_t H, int32_t kv_splits, int64_t* split_blocks) {
+  const int64_t NB = cdiv(N, 64);
+  int64_t want = kv_splits;
+  if (kv_splits == FP8ATTN_KV_SPLITS_AUTO) {
+    const int64_t base = static_cast<int64_t>(B) * H * cdiv(N, 128);
+    const int64_t slots = 2 * static_cast<int64_t>(device_cus());
+    const int64_t last = base % slots;  // workgroups of the last, partial round
+    want = 1;
+    if (NB >= 256) {
+      if (base < slots) want = std::min<int64_t>(8, cdiv(slots, base));
+      else if (base < 4 * slots && last > 0 && 20 * last <= 7 * slots) want = 3;
+    }
+  }
+  if (want <= 1) {
+    *split_blocks = NB;
+    return 1;
+  }
+  const int64_t L = 2 * cdiv(NB, 2 * want);
+  *split_blocks = L;
+  return static_cast<int>(cdiv(NB, L));
+}
 
 }  // namespace
 
@@ -133,9 +182,16 @@ fp8attn_status fp8attn_quantize_qkv(const fp8attn_quant_args* a, const void* q, 
   return from_hip(fp8attn::launch_quantize(p, stream));
 }
 
-size_t fp8attn_forward_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D, int32_t vsmooth) {
-  if (B < 1 || N < 1 || H < 1 || D != kHeadDim || !vsmooth) return 0;
-  return round_up(static_cast<size_t>(B) * H * cdiv(N, 128) * kHeadDim * sizeof(float));
+size_t fp8attn_forward_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D, int32_t vsmooth,
+                                       int32_t kv_splits) {
+  if (B < 1 || N < 1 || H < 1 || D != kHeadDim || !valid_splits_arg(kv_splits)) return 0;
+  const size_t bh = static_cast<size_t>(B) * H;
+  size_t n = vsmooth ? round_up(bh * cdiv(N, 128) * kHeadDim * sizeof(float)) : 0;
+  int64_t split_blocks = 0;
+  const int splits = resolve_splits(B, N, H, kv_splits, &split_blocks);
+  if (splits > 1)
+    n += round_up(splits * bh * N * kHeadDim * sizeof(float)) + round_up(splits * bh * N * sizeof(float));
+  return n;
 }
 
 fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const uint8_t* q8,
@@ -168,7 +224,12 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
     if (static_cast<int64_t>(s->tile_tokens) * s->n_tiles != N) return FP8ATTN_EINVAL;
     if (!s->tile_len || !s->row_ptr || !s->col_idx) return FP8ATTN_EINVAL;
   }
-  const size_t need = fp8attn_forward_workspace_bytes(B, N, H, D, vsmooth ? 1 : 0);
+  if (!valid_splits_arg(o->kv_splits)) return FP8ATTN_EINVAL;
+  if (sparse && o->kv_splits > 1) return FP8ATTN_EINVAL;
+  int64_t split_blocks = 0;
+  const int splits = sparse ? 1 : resolve_splits(B, N, H, o->kv_splits, &split_blocks);
+  if (total_bh * cdiv(N, 64) * splits > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
+  const size_t need = fp8attn_forward_workspace_bytes(B, N, H, D, vsmooth ? 1 : 0, sparse ? 1 : o->kv_splits);
   if (need && (!workspace || !aligned(workspace, 16) || workspace_bytes < need)) return FP8ATTN_EINVAL;
   const fp8attn_status dev = check_device();
   if (dev != FP8ATTN_OK) return dev;
@@ -183,6 +244,14 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
   p.v_scale = v_scale;
   p.v_mean = v_mean;
   p.mu_f = vsmooth ? static_cast<float*>(workspace) : nullptr;
+  p.splits = splits;
+  p.split_blocks = splits > 1 ? split_blocks : cdiv(N, 64);
+  if (splits > 1) {
+    const size_t bh = static_cast<size_t>(total_bh);
+    char* ws = static_cast<char*>(workspace) + (vsmooth ? round_up(bh * cdiv(N, 128) * kHeadDim * sizeof(float)) : 0);
+    p.o_part = reinterpret_cast<float*>(ws);
+    p.lse = reinterpret_cast<float*>(ws + round_up(splits * bh * N * kHeadDim * sizeof(float)));
+  }
   p.out = static_cast<uint16_t*>(out);
   p.out_rows = o->out_rows;
   p.underflow = o->underflow;

@@ -185,10 +185,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   auto slot = [&](int i) -> uint8_t* { return lds + i * kSlotBytes; };
 
   // ---- work item (XCD-major: dispatch round-robins workgroups over the 8 XCDs) ----
+  // (work order: query tile fastest, then KV piece, then (b, h), so that the workgroups of one
+  // XCD share the K/V tiles of one piece)
   const int per_xcd = (p.total_work + 7) / 8;
   const int work = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (work >= p.total_work) return;
-  const int64_t bh = work / p.n_qtiles;
+  const int64_t bh = work / (p.n_qtiles * p.splits);
+  const int split = (work / p.n_qtiles) % p.splits;
   const int64_t q0 = static_cast<int64_t>(work % p.n_qtiles) * kRowsPerWg;
   const int64_t b = bh / p.H, h = bh % p.H;
 
@@ -210,17 +213,24 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   const int per_tile = p.tile_tokens / kBlock;
   auto nblk_of_len = [&](int len) -> int { return min((len + kBlock - 1) / kBlock, per_tile); };
 
-  // ---- key-block sequence ----
+  // ---- key-block sequence (dense: the piece [kb_lo, kb_hi) of the key blocks, visited in KV
+  // order; e0 is its first position in the visiting order) ----
   int n_iter = 0;
+  int64_t e0 = 0;
+  bool has_last_block = true;  // the piece holds key block NB-1 (the only partial one)
   if constexpr (SPARSE) {
     for (int e = e_begin; e < e_end; e++) n_iter += nblk_of_len(p.tile_len[p.col_idx[e]]);
   } else {
-    n_iter = static_cast<int>(p.NB);
+    const int64_t kb_lo = static_cast<int64_t>(split) * p.split_blocks;
+    const int64_t kb_hi = min(p.NB, kb_lo + p.split_blocks);
+    n_iter = static_cast<int>(kb_hi - kb_lo);
+    e0 = p.reverse ? p.NB - kb_hi : kb_lo;
+    has_last_block = kb_hi == p.NB;
   }
-  if (n_iter == 0) return;  // a query tile without key blocks has no defined output
+  if (n_iter <= 0) return;  // a query tile without key blocks has no defined output
 
   KvCursor lc;  // the copy engine's cursor: the next K block to stage
-  lc.e = 0;
+  lc.e = static_cast<int>(e0);
   lc.bt = 0;
   lc.v = 0;
   lc.len = 0;
@@ -266,8 +276,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // Dense V-Smooth: key block j closes its 128-row V block when the next block lies elsewhere.
   auto closes_vblock = [&](int j) -> bool {
     if (j + 1 >= n_iter) return true;
-    const int64_t kb = p.reverse ? (p.NB - 1 - j) : j;
-    const int64_t kn = p.reverse ? (p.NB - 2 - j) : j + 1;
+    const int64_t e = e0 + j;
+    const int64_t kb = p.reverse ? (p.NB - 1 - e) : e;
+    const int64_t kn = p.reverse ? (p.NB - 2 - e) : e + 1;
     return (kb >> 1) != (kn >> 1);
   };
 
@@ -589,7 +600,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   using kNoMask = std::integral_constant<bool, false>;
   using kMasked = std::integral_constant<bool, true>;
   using kLoopMask = std::integral_constant<bool, SPARSE>;
-  const bool partial_tail = !SPARSE && (p.N % kBlock) != 0;
+  const bool partial_tail = !SPARSE && (p.N % kBlock) != 0 && has_last_block;
   int j_begin = 0, j_end = n_iter, sidx = 1;  // sidx: slot of pair j+1
   if (partial_tail && p.reverse) {
     iteration(kMasked{}, 0, slot(1));
@@ -614,6 +625,36 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   bool ok = qrow < p.N;
   if constexpr (SPARSE) ok = ok && static_cast<int>(qrow % p.tile_tokens) < q_valid_len;
   const float l_tot = xsum(l_part);
+  if constexpr (!SPARSE) {
+    if (p.splits > 1) {
+      // split-KV: this piece's normalised O (FP32) and log2 of its weight, m + log2(l)
+      if (ok) {
+        const float inv_l = 1.0f / l_tot;
+        const int64_t prow = (static_cast<int64_t>(split) * p.B * p.H + bh) * p.N + qrow;
+        float* orow = p.o_part + prow * kHeadDim;
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+          for (int g = 0; g < 4; g++) {
+            const int d0 = 32 * dt + 8 * g + 4 * lh;
+            const float4 sv = *reinterpret_cast<const float4*>(p.v_scale + bh * kHeadDim + d0);
+            float gs[4] = {sv.x, sv.y, sv.z, sv.w};
+            if constexpr (VSMOOTH) {
+#pragma unroll
+              for (int e = 0; e < 4; e++) gs[e] = gs[e] > 0.0f ? gs[e] : 1.0f;
+            }
+            float4 o;
+            o.x = oacc[dt][4 * g + 0] * gs[0] * inv_l;
+            o.y = oacc[dt][4 * g + 1] * gs[1] * inv_l;
+            o.z = oacc[dt][4 * g + 2] * gs[2] * inv_l;
+            o.w = oacc[dt][4 * g + 3] * gs[3] * inv_l;
+            *reinterpret_cast<float4*>(orow + d0) = o;
+          }
+        if (lh == 0) p.lse[prow] = m_run + __log2f(l_tot);
+      }
+      return;
+    }
+  }
   int64_t dst = qrow;
   if (ok && p.out_rows) dst = p.out_rows[qrow];
   ok = ok && dst >= 0 && dst < p.n_out;
@@ -663,13 +704,61 @@ __global__ __launch_bounds__(128) void vsmooth_mean_factors(AttnParams p) {
   p.mu_f[idx] = bf16_to_f32(p.v_mean[idx]) * f;
 }
 
+// Split-KV merge ([TF] long-sequence split-KV, log-sum-exp reduction): per row,
+// O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s, then the sequence-mean
+// V shift, BF16 and the row scatter. 32 threads per row (4 channels each), 8 rows per workgroup.
+__global__ __launch_bounds__(256) void split_merge(AttnParams p) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int64_t bh = blockIdx.y;
+  const int c = (threadIdx.x & 31) * 4;
+  if (row >= p.N) return;
+  int64_t dst = row;
+  if (p.out_rows) dst = p.out_rows[row];
+  if (dst < 0 || dst >= p.n_out) return;
+  const int64_t BH = static_cast<int64_t>(p.B) * p.H;
+  float M = -INFINITY;
+  for (int s = 0; s < p.splits; s++) M = fmaxf(M, p.lse[(s * BH + bh) * p.N + row]);
+  float wsum = 0.0f;
+  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < p.splits; s++) {
+    const int64_t prow = (s * BH + bh) * p.N + row;
+    const float w = __builtin_amdgcn_exp2f(p.lse[prow] - M);
+    const float4 o = *reinterpret_cast<const float4*>(p.o_part + prow * kHeadDim + c);
+    wsum += w;
+    a[0] = __builtin_fmaf(w, o.x, a[0]);
+    a[1] = __builtin_fmaf(w, o.y, a[1]);
+    a[2] = __builtin_fmaf(w, o.z, a[2]);
+    a[3] = __builtin_fmaf(w, o.w, a[3]);
+  }
+  const float inv = 1.0f / wsum;
+  float sh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (p.v_shift) {
+    const float4 cv = *reinterpret_cast<const float4*>(p.v_shift + bh * kHeadDim + c);
+    sh[0] = cv.x;
+    sh[1] = cv.y;
+    sh[2] = cv.z;
+    sh[3] = cv.w;
+  }
+  const int64_t b = bh / p.H, h = bh % p.H;
+  uint2 o;
+  o.x = static_cast<uint32_t>(f32_to_bf16_rne(a[0] * inv + sh[0])) |
+        (static_cast<uint32_t>(f32_to_bf16_rne(a[1] * inv + sh[1])) << 16);
+  o.y = static_cast<uint32_t>(f32_to_bf16_rne(a[2] * inv + sh[2])) |
+        (static_cast<uint32_t>(f32_to_bf16_rne(a[3] * inv + sh[3])) << 16);
+  *reinterpret_cast<uint2*>(p.out + ((b * p.n_out + dst) * p.H + h) * kHeadDim + c) = o;
+}
+
 template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS>
 hipError_t launch_variant(AttnParams& p, hipStream_t stream) {
   const int rows = WAVES * 32;
   p.n_qtiles = static_cast<int>((p.N + rows - 1) / rows);
-  p.total_work = p.B * p.H * p.n_qtiles;
+  p.total_work = p.B * p.H * p.n_qtiles * p.splits;
   const unsigned grid = static_cast<unsigned>(((p.total_work + 7) / 8) * 8);
   hipLaunchKernelGGL((attn_fwd<WAVES, SPARSE, EXPCAST, VSMOOTH, STATS>), dim3(grid), dim3(WAVES * 64), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL(split_merge, dim3(static_cast<unsigned>((p.N + 7) / 8), static_cast<unsigned>(p.B * p.H)),
+                     dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -58,6 +58,12 @@ struct AttnParams {
   float logit_scale;  // softmax_scale * log2(e)
   float log2S;
   int reverse;
+  // split-KV (dense): splits pieces of split_blocks key blocks; each piece writes its normalised
+  // output and log2-sum-exp, which split_merge combines. splits = 1: no split, o_part null.
+  int splits;
+  int64_t split_blocks;
+  float* o_part;  // [splits, B*H, N, 128]
+  float* lse;     // [splits, B*H, N]
 };
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t stream);

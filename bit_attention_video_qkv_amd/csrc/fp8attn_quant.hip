@@ -19,7 +19,7 @@
 //   1. quant_qk      grid (NB, B*H, 2): amax of a 64-row Q or K block -> scale -> codes.
 //   2. v_block_stats grid (NB128, B*H): per 128-row block, per channel: amax of V, or (V-Smooth)
 //                    the block mean (exact FP64 column sums) and the residual amax.
-//   3. v_finalize    grid (B*H): channel amax over blocks -> v_scale and its inverse.
+//   3. v_finalize    grid (B*H, 4): channel amax over blocks -> v_scale and its inverse.
 //   4. v_encode      grid (NB, B*H): codes of a 64-row block, transposed through LDS into
 //                    [B, H, 128, N64]; with the bias correction also the FP32 column sums of
 //                    the rounding error of the block's valid rows.
@@ -318,13 +318,23 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
 }
 
 // 3. Channel amax over the 128-row blocks -> v_scale and the inverse scale used to encode.
-__global__ __launch_bounds__(128) void v_finalize(QuantParams p) {
+// grid (B*H, 4): 32 channels per workgroup, 32 threads per channel take every 32nd block (the
+// maximum is exact in any order), then one thread per channel combines them.
+__global__ __launch_bounds__(1024) void v_finalize(QuantParams p) {
+  __shared__ float red[32][33];
   const int64_t bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int c = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const int d = blockIdx.y * 32 + c;
   float m = 0.0f;
-  for (int64_t j = 0; j < p.NB128; j++) m = fmaxf(m, p.ws_partial[(bh * p.NB128 + j) * kHeadDim + d]);
-  p.v_scale[bh * kHeadDim + d] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 0.0f;
-  p.ws_inv[bh * kHeadDim + d] = m > 0.0f ? __fdiv_rn(448.0f, m) : 0.0f;
+#pragma unroll 4
+  for (int64_t j = g; j < p.NB128; j += 32) m = fmaxf(m, p.ws_partial[(bh * p.NB128 + j) * kHeadDim + d]);
+  red[g][c] = m;
+  __syncthreads();
+  if (g == 0) {
+    for (int k = 1; k < 32; k++) m = fmaxf(m, red[k][c]);
+    p.v_scale[bh * kHeadDim + d] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 0.0f;
+    p.ws_inv[bh * kHeadDim + d] = m > 0.0f ? __fdiv_rn(448.0f, m) : 0.0f;
+  }
 }
 
 // fl32(a * b) that is never fused into a following add: hipcc contracts a*b - c into an FMA
@@ -469,7 +479,7 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
                      dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(v_finalize, dim3(static_cast<unsigned>(p.B * p.H)), dim3(kHeadDim), 0, stream, p);
+  hipLaunchKernelGGL(v_finalize, dim3(static_cast<unsigned>(p.B * p.H), kHeadDim / 32), dim3(1024), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g_enc(static_cast<unsigned>(p.NB), bh);

@@ -48,6 +48,11 @@ typedef enum fp8attn_kv_order {
   FP8ATTN_KV_REVERSE = 1   /* key blocks visited NB-1 .. 0 (sink block last) */
 } fp8attn_kv_order;
 
+/* Split-KV piece count for fp8attn_fwd_opts.kv_splits: 0 or 1 = one piece, 2..MAX = requested
+ * count, AUTO = chosen from the shape and the device's compute-unit count. */
+#define FP8ATTN_KV_SPLITS_AUTO (-1)
+#define FP8ATTN_KV_SPLITS_MAX 16
+
 typedef enum fp8attn_pcast {
   FP8ATTN_PCAST_RNE = 0,     /* P8 = E4M3_RNE(S * exp(x - m)) */
   FP8ATTN_PCAST_EXPCAST = 1  /* P8 byte = clamp(rint(8 z + 56 - 0.35), 0, 126), z = log2(S p) */
@@ -178,6 +183,14 @@ fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, i
  * V-Smooth (v_mean != NULL): the block's row sum r restores the mean, O = ((s_r / S) acc +
  * sum r mu_hat_j) / l, j the 128-row V block of each key block.
  * Sequence-mean smoothing (opts->v_shift != NULL): O = acc * v_scale / (S l) + v_shift.
+ * Split-KV (TeleFuser blog "FP8 Sol-Attn", long-sequence split-KV: pieces of the KV sequence run
+ *   their own online softmax and are merged by log-sum-exp), dense only: with P pieces requested
+ *   the key blocks are cut at absolute multiples of L = 2 * ceil(NB / (2 P)) blocks (whole
+ *   128-row V blocks), giving ceil(NB / L) pieces; each piece runs the loop above in kv_order
+ *   from its own m = -inf and yields o_s (the end formula) and lse_s = log2 of its weight; then
+ *   O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max lse_s, + v_shift, BF16.
+ *   The result differs from the one-piece result by P-code rounding only (each piece has its
+ *   own running max).
  *
  * Arguments (device pointers unless noted):
  *   q8, k8, v8t, q_scale, k_scale, v_scale, v_mean   as written by fp8attn_quantize_qkv
@@ -193,13 +206,21 @@ fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, i
  *     underflow      device uint64 [B*H] or NULL; when non-NULL the counts of keys whose
  *                    p > 0 but whose P code is 0 are ADDED to it (RNE mode only; slower);
  *     v_shift        device FP32 [B*H, D] (16-byte aligned) from sequence-mean smoothing, or
- *                    NULL; when given O += v_shift before the BF16 rounding. Not with V-Smooth.
+ *                    NULL; when given O += v_shift before the BF16 rounding. Not with V-Smooth;
+ *     kv_splits      0/1 (no split), 2..FP8ATTN_KV_SPLITS_MAX, or FP8ATTN_KV_SPLITS_AUTO:
+ *                    for N >= 16384, with rounds = B*H*ceil(N/128) / (2 * compute units):
+ *                    rounds < 1 gives min(8, ceil(1 / rounds)) pieces; 1 <= rounds < 4 with
+ *                    the last round at most 35% full gives 3; anything else one piece.
+ *                    Dense only (sparse: 0, 1 or AUTO, which then means 1). The pieces'
+ *                    partial outputs live in the workspace.
  *   out       bf16 [B, n_out, H, D]; rows a query does not own are left untouched.
- *   workspace device scratch of fp8attn_forward_workspace_bytes(...) bytes (may be 0 / NULL
- *             when that is 0).
+ *   workspace device scratch of fp8attn_forward_workspace_bytes(B, N, H, D, vsmooth,
+ *             kv_splits) bytes, 16-byte aligned (may be NULL when that is 0). With more than one
+ *             piece it holds FP32 [pieces, B*H, N, D] partial outputs and [pieces, B*H, N] lse.
  * Errors: EINVAL on bad pointers/sizes, S outside (0, 448], sparse with V-Smooth, sparse
  *   N != n_tiles * tile_tokens or tile_tokens not a multiple of 64, ExpCast with underflow
- *   counting; EUNSUPPORTED on D != 128 or a device other than gfx950.
+ *   counting, kv_splits out of range or > 1 with sparse; EUNSUPPORTED on D != 128 or a device
+ *   other than gfx950.
  * ------------------------------------------------------------------------------------------ */
 typedef struct fp8attn_fwd_opts {
   float softmax_scale;
@@ -211,10 +232,13 @@ typedef struct fp8attn_fwd_opts {
   int32_t n_out;
   unsigned long long* underflow;
   const float* v_shift;
+  int32_t kv_splits;
 } fp8attn_fwd_opts;
 
+/* Workspace of fp8attn_forward for the shape, V-Smooth (0/1) and kv_splits (as in the options;
+ * pass 1 for a sparse call); 0 when none is needed or an argument is invalid. */
 size_t fp8attn_forward_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D,
-                                       int32_t vsmooth);
+                                       int32_t vsmooth, int32_t kv_splits);
 
 fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const uint8_t* q8,
                                const uint8_t* k8, const uint8_t* v8t, const float* q_scale,

@@ -162,14 +162,16 @@ def _sparse_args(sparse):
 
 
 def attention_fp8(qz, rows=None, softmax_scale=1.0 / math.sqrt(128.0), p_scale=256.0,
-                  kv_reverse=False, expcast=False, sparse=None, return_amb=False):
+                  kv_reverse=False, expcast=False, sparse=None, return_amb=False, kv_splits=1):
     """Full FP8 path (TeleFuser "SM90 CuTe Mainloop" + the P-cast paper's order/scale +
     VC-Attention's V-Smooth restore and ExpCast codes) on the output of ``quantize``.
     Returns (out f64 [B,H,R,D], out_bf16 uint16 [B,H,R,D], underflow int64 [B,H,R],
     row_valid uint8 [B,H,R]) and, with return_amb, amb_bound f64 [B,H,R,D]: per output element,
     the largest change that P codes lying within the evaluation error of a rounding boundary
     (FP32 and the E4M3 matrix-core contraction) and the contraction's own truncation can
-    explain."""
+    explain. kv_splits > 1: split-KV (TeleFuser long-sequence split-KV), dense rows only: the
+    key blocks are cut at multiples of 2*ceil(NB/(2*kv_splits)) blocks, each piece runs its own
+    online softmax and the pieces are merged by log-sum-exp."""
     B, H, N64, D = qz["q8"].shape
     N = qz["N"]
     rows = np.arange(N, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
@@ -186,14 +188,14 @@ def attention_fp8(qz, rows=None, softmax_scale=1.0 / math.sqrt(128.0), p_scale=2
         _p(qz["v_mean"]) if qz.get("vsmooth") else None, ctypes.c_double(softmax_scale),
         ctypes.c_double(p_scale), 1 if kv_reverse else 0, 1 if expcast else 0, tt, nt, _p(tl),
         _p(rp), _p(ci), _p(rows), ctypes.c_int64(R), _p(out), _p(ob), _p(uf), _p(rv), _p(amb),
-        _p(qz.get("v_shift")))
+        _p(qz.get("v_shift")), int(kv_splits))
     if rc != 0:
         raise ValueError("oracle attention: invalid arguments")
     return (out, ob, uf, rv, amb) if return_amb else (out, ob, uf, rv)
 
 
 def attention_ref(mode, q, k, v, rows=None, softmax_scale=1.0 / math.sqrt(128.0),
-                  p_scale=256.0, kv_reverse=False, expcast=False, sparse=None):
+                  p_scale=256.0, kv_reverse=False, expcast=False, sparse=None, kv_splits=1):
     """Unquantised modes on float64 [B, H, N, D] layout-order inputs: MODE_EXACT (two-pass
     FP64 softmax), MODE_NOQUANT (streaming loop, no casts), MODE_PCAST (only P cast to
     E4M3, the P-cast paper's kernel-faithful simulation). Returns (out, underflow, row_valid)."""
@@ -211,7 +213,7 @@ def attention_ref(mode, q, k, v, rows=None, softmax_scale=1.0 / math.sqrt(128.0)
         int(mode), B, N, H, D, _p(q), _p(k), _p(v), None, None, None, None, None, None, None,
         ctypes.c_double(softmax_scale), ctypes.c_double(p_scale), 1 if kv_reverse else 0,
         1 if expcast else 0, tt, nt, _p(tl), _p(rp), _p(ci), _p(rows), ctypes.c_int64(R),
-        _p(out), None, _p(uf), _p(rv), None, None)
+        _p(out), None, _p(uf), _p(rv), None, None, int(kv_splits))
     if rc != 0:
         raise ValueError("oracle attention_ref: invalid arguments")
     return out, uf, rv

@@ -361,7 +361,8 @@ int orc_quantize(int B, int Nsrc, int N, int H, int D, const uint16_t* q, const 
 // Outputs: out f64 [B, H, n_rows, D]; out_bf16 [B, H, n_rows, D] or null; underflow
 // [B, H, n_rows] or null (keys with p > 0 whose P code is 0); row_valid [B, H, n_rows] or null;
 // amb_bound [B, H, n_rows, D] or null (modes 2-3); v_shift [B, H, D] or null (mode 3: the
-// vector sequence-mean smoothing adds to every output row, see orc_quantize).
+// vector sequence-mean smoothing adds to every output row, see orc_quantize); kv_splits: 1 (or
+// 0) streams each row in one piece, > 1 is split-KV (dense rows, modes 1-3, see below).
 //
 // Ambiguous P codes. The pages fix P8 = E4M3(S p) but not how p is evaluated; an FP32
 // evaluation (the kernel's precision) can land on either side of a rounding boundary when S p
@@ -387,7 +388,7 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
                   int expcast, int tile_tokens, int n_tiles, const int32_t* tile_len,
                   const int32_t* row_ptr, const int32_t* col_idx, const int32_t* rows,
                   int64_t n_rows, double* out, uint16_t* out_bf16, int64_t* underflow,
-                  uint8_t* row_valid, double* amb_bound, const float* v_shift) {
+                  uint8_t* row_valid, double* amb_bound, const float* v_shift, int kv_splits) {
   if (mode < 0 || mode > 3 || B < 1 || N < 1 || H < 1 || D < 1 || n_rows < 0) return 1;
   if (mode < 3 && (!qd || !kd || !vd)) return 1;
   if (mode == 3 && (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale)) return 1;
@@ -489,6 +490,14 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
             for (int64_t kb = 0; kb < NB; kb++) blocks.push_back(kb);
           }
           if (kv_reverse) std::reverse(blocks.begin(), blocks.end());
+          // One streaming pass over a sequence of key blocks: the row's normalised output, its
+          // running max and row sum, and the ambiguity bound of that output.
+          struct Pass {
+            std::vector<double> o, amb;
+            double m = 0.0, l = 0.0, lx = 0.0;
+            int64_t n_under = 0;
+          };
+          auto stream = [&](const std::vector<int64_t>& seq) -> Pass {
 
           double m = -std::numeric_limits<double>::infinity(), l = 0.0;
           std::vector<double> acc(D, 0.0), accM(D, 0.0);
@@ -525,7 +534,7 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
           double x[64], pv[64], dx[64];
           bool kv_ok[64];
           double dm_run = 0.0;     // error bound of the running max
-          for (const int64_t kb : blocks) {
+          for (const int64_t kb : seq) {
             double mblk = -std::numeric_limits<double>::infinity();
             for (int t = 0; t < 64; t++) {
               const int64_t kk = kb * 64 + t;
@@ -633,19 +642,77 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
             }
             m = m_new;
           }
+          Pass ps;
+          ps.o.assign(D, 0.0);
+          ps.amb.assign(D, 0.0);
           for (int d = 0; d < D; d++) {
             if (mode == 3) {
               const double sv = static_cast<double>(v_scale[bh * D + d]);
-              o[d] = vsmooth ? ((sv / S) * acc[d] + accM[d]) / l : acc[d] * sv / (S * l);
+              ps.o[d] = vsmooth ? ((sv / S) * acc[d] + accM[d]) / l : acc[d] * sv / (S * l);
             } else {
-              o[d] = acc[d] / l;  // mode 2 already divided P by S
+              ps.o[d] = acc[d] / l;  // mode 2 already divided P by S
             }
           }
-          if (underflow) underflow[o_idx] = n_under;
           if (amb_bound)
             for (int d = 0; d < D; d++)
-              amb_bound[o_idx * D + d] = (amb_v[d] + amb_l * std::fabs(o[d]) + amb_pv[d]) / (S * l) +
-                                         2.0 * std::fabs(o[d]) * amb_lx / l;
+              ps.amb[d] = (amb_v[d] + amb_l * std::fabs(ps.o[d]) + amb_pv[d]) / (S * l) +
+                          2.0 * std::fabs(ps.o[d]) * amb_lx / l;
+          ps.m = m;
+          ps.l = l;
+          ps.lx = amb_lx / l;
+          ps.n_under = n_under;
+          return ps;
+        };
+
+        // Split-KV ([TF] long-sequence split-KV: the KV sequence is cut into pieces that run
+        // their own online softmax, merged by log-sum-exp). Reading: dense rows only; the cuts
+        // sit at absolute multiples of L = 2 * ceil(NB / (2 * kv_splits)) blocks (whole 128-row
+        // V blocks); each piece keeps the row's KV order; piece s gives o_s, m_s, l_s and
+        // O = sum_s w_s o_s / sum_s w_s with w_s = l_s * exp(m_s - max m).
+        std::vector<Pass> parts;
+        if (kv_splits <= 1 || sparse) {
+          parts.push_back(stream(blocks));
+        } else {
+          const int64_t L = 2 * ceil_div(NB, 2 * static_cast<int64_t>(kv_splits));
+          for (int64_t lo = 0; lo < NB; lo += L) {
+            std::vector<int64_t> piece;
+            for (const int64_t kb : blocks)
+              if (kb >= lo && kb < lo + L) piece.push_back(kb);
+            parts.push_back(stream(piece));
+          }
+        }
+        if (parts.size() == 1) {
+          for (int d = 0; d < D; d++) o[d] = parts[0].o[d];
+          if (amb_bound)
+            for (int d = 0; d < D; d++) amb_bound[o_idx * D + d] = parts[0].amb[d];
+          if (underflow) underflow[o_idx] = parts[0].n_under;
+        } else {
+          double mmax = -std::numeric_limits<double>::infinity();
+          for (const Pass& ps : parts) mmax = std::max(mmax, ps.m);
+          std::vector<double> w(parts.size());
+          double wsum = 0.0;
+          int64_t n_under = 0;
+          for (size_t sidx = 0; sidx < parts.size(); sidx++) {
+            w[sidx] = parts[sidx].l * std::exp(parts[sidx].m - mmax);
+            wsum += w[sidx];
+            n_under += parts[sidx].n_under;
+          }
+          for (int d = 0; d < D; d++) {
+            double acc_o = 0.0;
+            for (size_t sidx = 0; sidx < parts.size(); sidx++) acc_o += w[sidx] * parts[sidx].o[d];
+            o[d] = acc_o / wsum;
+          }
+          // each piece's bound, plus the change of its weight that its row-sum bound allows
+          if (amb_bound)
+            for (int d = 0; d < D; d++) {
+              double a = 0.0;
+              for (size_t sidx = 0; sidx < parts.size(); sidx++)
+                a += w[sidx] / wsum *
+                     (parts[sidx].amb[d] + 2.0 * parts[sidx].lx * (std::fabs(parts[sidx].o[d]) + std::fabs(o[d])));
+              amb_bound[o_idx * D + d] = a;
+            }
+          if (underflow) underflow[o_idx] = n_under;
+        }
           // sequence-mean smoothing ([TF] MiniMax-H3 section): each softmax row sums to 1, so
           // the attention of the shifted V plus mean_T(V) is the attention of V
           if (mode == 3 && v_shift)

@@ -74,10 +74,10 @@ def test_quantize_rejects_bad_arguments(m):
 
 def _opts(m, **kw):
     o = dict(softmax_scale=0.088, p_scale=256.0, kv_order=1, pcast=0, sparse=None, out_rows=None,
-             n_out=256, underflow=None, v_shift=None)
+             n_out=256, underflow=None, v_shift=None, kv_splits=1)
     o.update(kw)
     return m._FwdOpts(o["softmax_scale"], o["p_scale"], o["kv_order"], o["pcast"], o["sparse"],
-                      o["out_rows"], o["n_out"], o["underflow"], o["v_shift"])
+                      o["out_rows"], o["n_out"], o["underflow"], o["v_shift"], o["kv_splits"])
 
 
 def test_forward_rejects_bad_arguments(m):
@@ -107,6 +107,11 @@ def test_forward_rejects_bad_arguments(m):
     assert call(_opts(m), v_mean=_fake(), ws=0) == 1                    # V-Smooth needs workspace
     assert call(_opts(m, v_shift=_fake()), v_mean=_fake(), ws=1 << 24) == 1  # V shift + V-Smooth
     assert call(_opts(m, v_shift=_fake(0x10008))) == 1                  # misaligned v_shift
+    assert call(_opts(m, kv_splits=17)) == 1                             # > FP8ATTN_KV_SPLITS_MAX
+    assert call(_opts(m, kv_splits=-2)) == 1
+    sp = m._Sparse(128, 2, _fake(), _fake(), _fake())
+    assert call(_opts(m, sparse=ctypes.pointer(sp), kv_splits=2)) == 1   # split-KV is dense only
+    assert call(_opts(m, kv_splits=2), ws=0) == 1                         # pieces need workspace
 
 
 @pytest.mark.parametrize("grid", [(21, 45, 80, 6, 8, 8, 1, 1, 1), (5, 7, 9, 2, 4, 8, 1, 1, 0),
@@ -135,8 +140,22 @@ def test_workspace_sizes(m):
     L = m.lib()
     assert L.fp8attn_quantize_workspace_bytes(1, 75600, 40, 128, 0) >= 40 * 591 * 128 * 4 + \
         2 * 40 * 1182 * 128 * 4   # + the smoothing block sums of K and V
-    assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0) == 0
-    assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1) == 24 * 384 * 128 * 4
+    assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0, 1) == 0
+    assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1, 0) == 24 * 384 * 128 * 4
+    # split-KV: 4096 tokens = 64 key blocks, 2 pieces of 32 blocks; 3 requested -> L = 22, 3 pieces
+    assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 2) == 2 * 8 * 4096 * 129 * 4
+    assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 3) == 3 * 8 * 4096 * 129 * 4
+    # 5 blocks, 16 requested: L = 2, 3 pieces
+    assert L.fp8attn_forward_workspace_bytes(1, 300, 1, 128, 0, 16) == \
+        -(-3 * 300 * 128 * 4 // 256) * 256 + -(-3 * 300 * 4 // 256) * 256
+    assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 17) == 0
+    # auto (no device here: 256 compute units assumed): one piece for the large shapes and for
+    # short sequences; H=1, N=75600 (591 query tiles, 1.15 rounds) -> ceil(3 * 512 / 591) = 3
+    auto = m.FP8ATTN_KV_SPLITS_AUTO
+    assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0, auto) == 0
+    assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, auto) == 0
+    assert L.fp8attn_forward_workspace_bytes(1, 75600, 1, 128, 0, auto) == \
+        L.fp8attn_forward_workspace_bytes(1, 75600, 1, 128, 0, 3) > 0
     assert L.fp8attn_quantize_workspace_bytes(1, 100, 2, 64, 0) == 0
 
 

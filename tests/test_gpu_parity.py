@@ -363,6 +363,103 @@ def test_attention_smoothing_sparse(m, orc):
     _sparse_case(m, orc, (5, 7, 9, 2, 4, 8, 1, 1, 0), H=1, seed=62, reverse=False, smoothing=1)
 
 
+# ------------------------------------------------------------------------------------------
+# Split-KV (pieces of the key sequence merged by log-sum-exp)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("N,H,splits,reverse,expcast", [
+    (1000, 2, 2, True, False), (2500, 2, 3, False, False), (300, 1, 2, True, False),
+    (4096, 8, 4, True, False), (777, 2, 16, False, True), (64, 1, 2, True, False)])
+def test_attention_split_kv_small(m, orc, N, H, splits, reverse, expcast):
+    say("split-KV", N, H, splits, reverse, expcast)
+    q, k, v = workloads.make_qkv(1, N, H, seed=70 + N + splits)
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb)
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=reverse, expcast=expcast,
+                                          return_amb=True, kv_splits=splits)
+    qz = _gpu_quantize(m, q, k, v)
+    out = _run_attn(m, qz, kv_order=int(reverse), kv_splits=splits,
+                    pcast=m.FP8ATTN_PCAST_EXPCAST if expcast else m.FP8ATTN_PCAST_RNE)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, f"split-KV {splits}", amb)
+
+
+def test_attention_split_kv_vsmooth_and_smoothing(m, orc):
+    """V-Smooth: every piece holds whole 128-row V blocks (odd block counts included); sequence
+    mean smoothing: v_shift is added after the merge."""
+    say("split-KV + V-Smooth, + smoothing")
+    N, H = 1000, 2
+    q, k, v = workloads.make_qkv(1, N, H, seed=81, kind="token_outliers")
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    perm = orc.vsmooth_perm(vb)
+    ref_q = orc.quantize(qb, kb, vb, perm_kv=perm, vsmooth=True)
+    for splits, rev in ((3, True), (2, False)):
+        ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=rev, expcast=True, return_amb=True,
+                                              kv_splits=splits)
+        qz = _gpu_quantize(m, q, k, v, perm_kv=perm, vsmooth=True)
+        out = _run_attn(m, qz, kv_order=int(rev), kv_splits=splits, pcast=m.FP8ATTN_PCAST_EXPCAST)
+        _compare_out(_gpu_rows(out, np.arange(N)), ref, f"split-KV {splits} vsmooth", amb)
+    q, k, v = workloads.make_qkv(1, N, H, seed=82, kind="channel_offset")
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb, smoothing=2, v_bias_correction=True)
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=True, return_amb=True, kv_splits=2)
+    qz = _gpu_quantize(m, q, k, v, smoothing=2, bias=True)
+    out = _run_attn(m, qz, kv_order=1, kv_splits=2)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, "split-KV 2 smoothing", amb)
+
+
+def _auto_splits(m, B, N, H):
+    """The documented AUTO policy, evaluated here from the device's compute-unit count."""
+    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    base = B * H * -(-N // 128)
+    last = base % slots
+    if -(-N // 64) >= 256:
+        if base < slots:
+            return min(8, -(-slots // base))
+        if base < 4 * slots and 0 < last and 20 * last <= 7 * slots:
+            return 3
+    return 1
+
+
+def test_attention_split_kv_auto(m, orc):
+    """A long sequence with few heads (H=2, N=20000) fills under one round of the machine, so
+    AUTO splits it; sampled rows against the oracle with the same piece count. The sink-stress
+    shape (N=4096) stays whole."""
+    assert _auto_splits(m, 1, 4096, 8) == 1
+    N, H = 20000, 2
+    splits = _auto_splits(m, 1, N, H)
+    say("split-KV auto on H=2 N=20000:", splits, "pieces")
+    assert splits > 1
+    q, k, v = workloads.make_qkv(1, N, H, seed=83, kind="channel_outliers")
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb)
+    rows = workloads.sample_rows(N, 200, seed=9)
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, rows=rows, kv_reverse=True, return_amb=True,
+                                          kv_splits=splits)
+    qz = _gpu_quantize(m, q, k, v)
+    out = _run_attn(m, qz, kv_order=1, kv_splits=m.FP8ATTN_KV_SPLITS_AUTO)
+    _compare_out(_gpu_rows(out, rows), ref, "auto split", amb)
+
+
+@pytest.mark.parametrize("delta,S,reverse", [(9, 256.0, False), (7, 1.0, True)])
+def test_attention_split_kv_sink_underflow(m, orc, delta, S, reverse):
+    """Sink stress (H=8, N=4096) in 4 pieces: outputs and underflow counts against the oracle."""
+    q, k, v = workloads.workload("sink4096", delta=delta)
+    B, N, H, _ = q.shape
+    splits = 4
+    say("split-KV on sink4096:", splits, "pieces")
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb)
+    ref, _, uf, _, amb = orc.attention_fp8(ref_q, p_scale=S, kv_reverse=reverse, return_amb=True,
+                                           kv_splits=splits)
+    qz = _gpu_quantize(m, q, k, v)
+    cnt = torch.zeros(H, dtype=torch.int64, device=DEV)
+    out = _run_attn(m, qz, p_scale=S, kv_order=int(reverse), underflow=cnt, kv_splits=splits)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, "sink split", amb)
+    g = _np(cnt).astype(np.float64)
+    o = uf.sum(axis=2)[0].astype(np.float64)
+    say("underflow gpu", g, "oracle", o)
+    assert np.all(np.abs(g - o) <= 1e-4 * N * N + 1e-3 * o)
+
+
 @pytest.mark.parametrize("delta,S,reverse", [(7, 1.0, False), (7, 256.0, True), (9, 256.0, False)])
 def test_underflow_counter(m, orc, delta, S, reverse):
     say("underflow", delta, S, reverse)
@@ -424,10 +521,11 @@ def _slice_heads(t, heads):
     return t[:, :, heads, :].contiguous()
 
 
-@pytest.mark.parametrize("name", ["wan13b", "wan14b", "vsmooth", "wan14b+smoothing"])
+@pytest.mark.parametrize("name", ["wan13b", "wan14b", "vsmooth", "wan14b+smoothing", "wan13b+split3"])
 def test_full_size_sampled(m, orc, name):
     say("full size", name)
     smooth = name.endswith("+smoothing")      # K and V smoothing with the bias correction
+    splits = int(name.split("+split")[1]) if "+split" in name else 1
     name = name.split("+")[0]
     q, k, v = workloads.workload(name)
     B, N, H, _ = q.shape
@@ -441,7 +539,8 @@ def test_full_size_sampled(m, orc, name):
         perm[0, heads] = perm_s[0]
     sm = 2 if smooth else 0
     qz = _gpu_quantize(m, q, k, v, perm_kv=perm, vsmooth=vs, smoothing=sm, bias=smooth)
-    out = _run_attn(m, qz, kv_order=1, pcast=m.FP8ATTN_PCAST_EXPCAST if vs else m.FP8ATTN_PCAST_RNE)
+    out = _run_attn(m, qz, kv_order=1, pcast=m.FP8ATTN_PCAST_EXPCAST if vs else m.FP8ATTN_PCAST_RNE,
+                    kv_splits=splits)
     qs, ks, vsl = (_bits(_slice_heads(t, heads)) for t in (q, k, v))
     ref_q = orc.quantize(qs, ks, vsl, perm_kv=None if perm is None else perm[:, heads], vsmooth=vs,
                          smoothing=sm, v_bias_correction=smooth)
@@ -452,7 +551,7 @@ def test_full_size_sampled(m, orc, name):
         assert np.array_equal(_np(getattr(qz, key)[:, heads]), ref_q[key]), key
     rows = workloads.sample_rows(N, 48, seed=7)
     ref, _, _, _, amb = orc.attention_fp8(ref_q, rows=rows, kv_reverse=True, expcast=vs,
-                                          return_amb=True)
+                                          return_amb=True, kv_splits=splits)
     got = _gpu_rows(out[:, :, heads], rows)
     _compare_out(got, ref, name, amb)
 
