@@ -161,8 +161,47 @@ def _sparse_args(sparse):
     return int(sparse["tile_tokens"]), int(tl.shape[0]), tl, rp, ci, (tl, rp, ci)
 
 
+class _OrcSol(ctypes.Structure):
+    _fields_ = [("mask", ctypes.c_void_p), ("kq8", ctypes.c_void_p), ("kq_scale", ctypes.c_void_p),
+                ("vsum", ctypes.c_void_p)]
+
+
+def sol_prepare(qz, tau=1.0, estimator=0, sink_blocks=1, softmax_scale=1.0 / math.sqrt(128.0)):
+    """Sol routing (TeleFuser "Sol Routing"): K/V block summaries, quantised K summaries, the
+    per-Q-block threshold theta = mu + tau * sigma (estimator 0 diag, 1 exact) and the
+    exact-block bitmask, on the output of ``quantize`` (layout order, no V-Smooth). Returns a dict:
+    ksum f32 [B,H,NB,D], vsum uint16 bf16 [B,H,NB,D], kq8 uint8 [B,H,64*NBg,D], kq_scale f32
+    [B,H,NBg], theta f64 [B,H,NB], mask and amb_mask uint64 [B,H,NB,W] (bit j%64 of word j//64:
+    KV block j is exact for Q block u; amb_mask flags decisions within the device's evaluation
+    error of theta, where either bit is correct)."""
+    B, H, N64, D = qz["q8"].shape
+    N = qz["N"]
+    NB = -(-N // 64)
+    NBg = W = -(-NB // 64)
+    out = dict(ksum=np.zeros((B, H, NB, D), np.float32), vsum=np.zeros((B, H, NB, D), np.uint16),
+               kq8=np.zeros((B, H, 64 * NBg, D), np.uint8), kq_scale=np.zeros((B, H, NBg), np.float32),
+               theta=np.zeros((B, H, NB), np.float64), mask=np.zeros((B, H, NB, W), np.uint64),
+               amb_mask=np.zeros((B, H, NB, W), np.uint64))
+    rc = _load().orc_sol_prepare(
+        B, N, H, D, _p(qz["q8"]), _p(qz["k8"]), _p(qz["v8t"]), _p(qz["q_scale"]), _p(qz["k_scale"]),
+        _p(qz["v_scale"]), ctypes.c_double(tau), int(estimator), int(sink_blocks),
+        ctypes.c_double(softmax_scale), _p(out["ksum"]), _p(out["vsum"]), _p(out["kq8"]),
+        _p(out["kq_scale"]), _p(out["theta"]), _p(out["mask"]), _p(out["amb_mask"]))
+    if rc != 0:
+        raise ValueError("oracle sol_prepare: invalid arguments")
+    return out
+
+
+def mask_bits(mask, NB):
+    """uint64 words [..., W] -> bool [..., NB]."""
+    w = np.ascontiguousarray(mask, np.uint64)
+    bits = ((w[..., :, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).astype(bool)
+    return bits.reshape(*w.shape[:-1], -1)[..., :NB]
+
+
 def attention_fp8(qz, rows=None, softmax_scale=1.0 / math.sqrt(128.0), p_scale=256.0,
-                  kv_reverse=False, expcast=False, sparse=None, return_amb=False, kv_splits=1):
+                  kv_reverse=False, expcast=False, sparse=None, return_amb=False, kv_splits=1,
+                  sol=None):
     """Full FP8 path (TeleFuser "SM90 CuTe Mainloop" + the P-cast paper's order/scale +
     VC-Attention's V-Smooth restore and ExpCast codes) on the output of ``quantize``.
     Returns (out f64 [B,H,R,D], out_bf16 uint16 [B,H,R,D], underflow int64 [B,H,R],
@@ -171,7 +210,9 @@ def attention_fp8(qz, rows=None, softmax_scale=1.0 / math.sqrt(128.0), p_scale=2
     (FP32 and the E4M3 matrix-core contraction) and the contraction's own truncation can
     explain. kv_splits > 1: split-KV (TeleFuser long-sequence split-KV), dense rows only: the
     key blocks are cut at multiples of 2*ceil(NB/(2*kv_splits)) blocks, each piece runs its own
-    online softmax and the pieces are merged by log-sum-exp."""
+    online softmax and the pieces are merged by log-sum-exp. sol: the dict of ``sol_prepare``
+    (its ``mask`` may be replaced by another valid mask): Sol routing, the exact route over the
+    masked blocks and the summary route over the others, merged by log-sum-exp."""
     B, H, N64, D = qz["q8"].shape
     N = qz["N"]
     rows = np.arange(N, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
@@ -182,13 +223,17 @@ def attention_fp8(qz, rows=None, softmax_scale=1.0 / math.sqrt(128.0), p_scale=2
     rv = np.zeros((B, H, R), np.uint8)
     amb = np.zeros((B, H, R, D), np.float64) if return_amb else None
     tt, nt, tl, rp, ci, _keep = _sparse_args(sparse)
+    sol_c = None
+    if sol is not None:
+        sol_keep = [np.ascontiguousarray(sol[k_]) for k_ in ("mask", "kq8", "kq_scale", "vsum")]
+        sol_c = _OrcSol(*(a_.ctypes.data for a_ in sol_keep))
     rc = _load().orc_attention(
         MODE_FP8, B, N, H, D, None, None, None, _p(qz["q8"]), _p(qz["k8"]), _p(qz["v8t"]),
         _p(qz["q_scale"]), _p(qz["k_scale"]), _p(qz["v_scale"]),
         _p(qz["v_mean"]) if qz.get("vsmooth") else None, ctypes.c_double(softmax_scale),
         ctypes.c_double(p_scale), 1 if kv_reverse else 0, 1 if expcast else 0, tt, nt, _p(tl),
         _p(rp), _p(ci), _p(rows), ctypes.c_int64(R), _p(out), _p(ob), _p(uf), _p(rv), _p(amb),
-        _p(qz.get("v_shift")), int(kv_splits))
+        _p(qz.get("v_shift")), int(kv_splits), ctypes.byref(sol_c) if sol_c is not None else None)
     if rc != 0:
         raise ValueError("oracle attention: invalid arguments")
     return (out, ob, uf, rv, amb) if return_amb else (out, ob, uf, rv)
@@ -213,7 +258,7 @@ def attention_ref(mode, q, k, v, rows=None, softmax_scale=1.0 / math.sqrt(128.0)
         int(mode), B, N, H, D, _p(q), _p(k), _p(v), None, None, None, None, None, None, None,
         ctypes.c_double(softmax_scale), ctypes.c_double(p_scale), 1 if kv_reverse else 0,
         1 if expcast else 0, tt, nt, _p(tl), _p(rp), _p(ci), _p(rows), ctypes.c_int64(R),
-        _p(out), None, _p(uf), _p(rv), None, None, int(kv_splits))
+        _p(out), None, _p(uf), _p(rv), None, None, int(kv_splits), None)
     if rc != 0:
         raise ValueError("oracle attention_ref: invalid arguments")
     return out, uf, rv

@@ -122,6 +122,14 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 extern "C" {
 
+// Sol routing inputs of orc_attention (see orc_sol_prepare for the layouts).
+struct OrcSol {
+  const uint64_t* mask;     // exact-block bitmask [B, H, NB, W]
+  const uint8_t* kq8;       // quantised K summaries [B, H, 64 * NBg, D]
+  const float* kq_scale;    // [B, H, NBg]
+  const uint16_t* vsum;     // V summaries, bf16 [B, H, NB, D]
+};
+
 // ---------------------------------------------------------------------------------------
 // Codec entry points (used by the format pins).
 // ---------------------------------------------------------------------------------------
@@ -325,6 +333,176 @@ int orc_quantize(int B, int Nsrc, int N, int H, int D, const uint16_t* q, const 
 }
 
 // ---------------------------------------------------------------------------------------
+// Sol routing ([TF] "Sol Routing" and "SM90 CuTe Mainloop": 64-token Q/KV blocks, K and V
+// summaries per KV block, a threshold theta = mu + tau * sigma per Q block from a diag or exact
+// estimator, a route QK of the block-quantised Q with the quantised K summaries, an exact-block
+// bitmask, sinks always exact). Readings (where the page is silent):
+//  * summaries come from the dequantised E4M3 K and V of the block's n_j valid keys:
+//      sK = sum_t decode(K8[t, d])   (exact in FP32: multiples of 2^-9 below 2^15 in magnitude)
+//      kbar[j, d] = fl32(fl32(sK * s_k[j]) / n_j);   vbar likewise with s_v[d], stored as BF16;
+//  * the K summaries are quantised like K: groups of 64 summaries, scale = fl32(amax / 448),
+//    codes E4M3(fl32(kbar * fl32(448 / amax)));
+//  * mu and sigma are the mean and standard deviation of the block's route scores over all
+//    pairs (valid query i of the block, KV block j), from second moments: with q_i the
+//    dequantised queries, qbar their mean, Mq = mean_i q_i q_i^T, and over the summaries
+//    m = mean_j kbar_j, Mk = mean_j kbar_j kbar_j^T (FP64, every summary weighted equally):
+//      mu = ss * qbar . m,   E2 = ss^2 * sum_{d,e} Mq[d, e] Mk[d, e]   (estimator 1, "exact": the
+//      full second moments, which give the exact mean square over the pairs) or
+//      E2 = ss^2 * sum_d Mq[d, d] Mk[d, d]   (estimator 0, "diag": per-channel moments only),
+//      sigma = sqrt(max(E2 - mu^2, 0)),   theta_u = mu + tau * sigma   (ss = softmax_scale);
+//  * route score r_ij = (q8_i . kq8_j) * s_q[u] * kq_scale[j / 64] * softmax_scale; KV block j is
+//    exact for Q block u when j < sink_blocks or some valid query i of u has r_ij >= theta_u.
+// A device evaluates r_ij on the matrix cores (R17: each group of 8 products truncated, error
+// below 2^-11 of the group maxima) and theta in floating point, so a decision within
+// b_ij = 2^-11 * sum_g max |q k| * scales + 2^-20 * |r_ij| + 2^-14 * (|mu| + |tau| sqrt(E2))
+// of the threshold can go either way: such bits are flagged in amb_mask (the mask holds the exact
+// decision).
+// Shapes: q8, k8 [B, H, N64, D], v8t [B, H, D, N64]; ksum f32 [B, H, NB, D]; vsum bf16 [B, H, NB,
+// D]; kq8 [B, H, 64 * NBg, D] (NBg = ceil(NB / 64)); kq_scale [B, H, NBg]; theta f64 [B, H, NB];
+// mask, amb_mask uint64 [B, H, NB, W] (W = ceil(NB / 64); bit j % 64 of word j / 64).
+// ---------------------------------------------------------------------------------------
+int orc_sol_prepare(int B, int N, int H, int D, const uint8_t* q8, const uint8_t* k8,
+                    const uint8_t* v8t, const float* q_scale, const float* k_scale,
+                    const float* v_scale, double tau, int estimator, int sink_blocks,
+                    double softmax_scale, float* ksum, uint16_t* vsum, uint8_t* kq8,
+                    float* kq_scale, double* theta, uint64_t* mask, uint64_t* amb_mask) {
+  if (B < 1 || N < 1 || H < 1 || D < 1 || estimator < 0 || estimator > 1 || sink_blocks < 0) return 1;
+  const int64_t NB = ceil_div(N, 64), N64 = NB * 64, NBg = ceil_div(NB, 64), W = ceil_div(NB, 64);
+  std::vector<double> code_value(256);
+  for (int c = 0; c < 256; c++) code_value[c] = e4m3_value(static_cast<uint8_t>(c));
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int b = 0; b < B; b++) {
+    for (int h = 0; h < H; h++) {
+      const int64_t bh = static_cast<int64_t>(b) * H + h;
+      // summaries
+      for (int64_t j = 0; j < NB; j++) {
+        const int64_t n = std::min<int64_t>(64, N - 64 * j);
+        for (int d = 0; d < D; d++) {
+          float sk = 0.0f, sv = 0.0f;
+          for (int64_t t = 64 * j; t < 64 * j + n; t++) {
+            sk += static_cast<float>(code_value[k8[(bh * N64 + t) * D + d]]);
+            sv += static_cast<float>(code_value[v8t[(bh * D + d) * N64 + t]]);
+          }
+          const float kb = (sk * k_scale[bh * NB + j]) / static_cast<float>(n);
+          const float vb = (sv * v_scale[bh * D + d]) / static_cast<float>(n);
+          ksum[(bh * NB + j) * D + d] = kb;
+          vsum[(bh * NB + j) * D + d] = bf16_bits(vb);
+        }
+      }
+      // quantised K summaries (groups of 64 summaries; padding summaries code 0)
+      for (int64_t g = 0; g < NBg; g++) {
+        float amax = 0.0f;
+        for (int64_t j = 64 * g; j < std::min(NB, 64 * g + 64); j++)
+          for (int d = 0; d < D; d++) amax = std::max(amax, std::fabs(ksum[(bh * NB + j) * D + d]));
+        const BlockScale sc = block_scale(amax);
+        kq_scale[bh * NBg + g] = sc.scale;
+        for (int64_t j = 64 * g; j < 64 * g + 64; j++)
+          for (int d = 0; d < D; d++)
+            kq8[(bh * NBg * 64 + j) * D + d] = j < NB ? quant_code(ksum[(bh * NB + j) * D + d], sc) : 0;
+      }
+      // moments of the summaries
+      std::vector<double> mk(D, 0.0), Mk(static_cast<size_t>(D) * D, 0.0);
+      for (int d = 0; d < D; d++) {
+        for (int64_t j = 0; j < NB; j++) mk[d] += static_cast<double>(ksum[(bh * NB + j) * D + d]);
+        mk[d] /= static_cast<double>(NB);
+      }
+      for (int d = 0; d < D; d++)
+        for (int e = 0; e < D; e++) {
+          if (estimator == 0 && e != d) continue;
+          double acc = 0.0;
+          for (int64_t j = 0; j < NB; j++)
+            acc += static_cast<double>(ksum[(bh * NB + j) * D + d]) * static_cast<double>(ksum[(bh * NB + j) * D + e]);
+          Mk[static_cast<size_t>(d) * D + e] = acc / static_cast<double>(NB);
+        }
+      // thresholds and the route
+      for (int64_t u = 0; u < NB; u++) {
+        const int64_t nq = std::min<int64_t>(64, N - 64 * u);
+        const double sq = q_scale[bh * NB + u];
+        std::vector<double> qbar(D, 0.0), Mq(static_cast<size_t>(D) * D, 0.0);
+        for (int64_t i = 64 * u; i < 64 * u + nq; i++) {
+          const uint8_t* qr = q8 + (bh * N64 + i) * D;
+          for (int d = 0; d < D; d++) {
+            const double qd = code_value[qr[d]] * sq;
+            qbar[d] += qd;
+            for (int e = 0; e < D; e++) {
+              if (estimator == 0 && e != d) continue;
+              Mq[static_cast<size_t>(d) * D + e] += qd * code_value[qr[e]] * sq;
+            }
+          }
+        }
+        double mu = 0.0, e2 = 0.0;
+        for (int d = 0; d < D; d++) {
+          qbar[d] /= static_cast<double>(nq);
+          mu += qbar[d] * mk[d];
+          for (int e = 0; e < D; e++) e2 += Mq[static_cast<size_t>(d) * D + e] / static_cast<double>(nq) *
+                                            Mk[static_cast<size_t>(d) * D + e];
+        }
+        mu *= softmax_scale;
+        e2 *= softmax_scale * softmax_scale;
+        const double th = mu + tau * std::sqrt(std::max(e2 - mu * mu, 0.0));
+        const double th_err = std::ldexp(1.0, -14) * (std::fabs(mu) + std::fabs(tau) * std::sqrt(e2));
+        theta[bh * NB + u] = th;
+        uint64_t* mrow = mask + (bh * NB + u) * W;
+        uint64_t* arow = amb_mask + (bh * NB + u) * W;
+        for (int64_t w = 0; w < W; w++) mrow[w] = arow[w] = 0;
+        for (int64_t j = 0; j < NB; j++) {
+          const uint64_t bit = 1ull << (j % 64);
+          if (j < sink_blocks) {
+            mrow[j / 64] |= bit;
+            continue;
+          }
+          const double sc = sq * static_cast<double>(kq_scale[bh * NBg + j / 64]) * softmax_scale;
+          bool any_ge = false, any_amb = false;
+          for (int64_t i = 64 * u; i < 64 * u + nq; i++) {
+            const uint8_t* qr = q8 + (bh * N64 + i) * D;
+            const uint8_t* kr = kq8 + (bh * NBg * 64 + j) * D;
+            double dot = 0.0, gsum = 0.0;
+            for (int g = 0; g < D; g += 8) {
+              double gm = 0.0;
+              for (int d = g; d < std::min(D, g + 8); d++) {
+                const double pr = code_value[qr[d]] * code_value[kr[d]];
+                dot += pr;
+                gm = std::max(gm, std::fabs(pr));
+              }
+              gsum += gm;
+            }
+            const double r = dot * sc;
+            const double bnd = std::ldexp(gsum, -11) * sc + std::ldexp(1.0, -20) * std::fabs(r) + th_err;
+            if (r >= th) any_ge = true;
+            if (std::fabs(r - th) <= bnd) any_amb = true;
+          }
+          if (any_ge) mrow[j / 64] |= bit;
+          // ambiguous unless some query is clearly above, or every query clearly below
+          bool clearly_above = false;
+          if (any_amb) {
+            for (int64_t i = 64 * u; i < 64 * u + nq && !clearly_above; i++) {
+              const uint8_t* qr = q8 + (bh * N64 + i) * D;
+              const uint8_t* kr = kq8 + (bh * NBg * 64 + j) * D;
+              double dot = 0.0, gsum = 0.0;
+              for (int g = 0; g < D; g += 8) {
+                double gm = 0.0;
+                for (int d = g; d < std::min(D, g + 8); d++) {
+                  const double pr = code_value[qr[d]] * code_value[kr[d]];
+                  dot += pr;
+                  gm = std::max(gm, std::fabs(pr));
+                }
+                gsum += gm;
+              }
+              const double r = dot * sc;
+              const double bnd = std::ldexp(gsum, -11) * sc + std::ldexp(1.0, -20) * std::fabs(r) + th_err;
+              if (r - th > bnd) clearly_above = true;
+            }
+            if (!clearly_above) arow[j / 64] |= bit;
+          }
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------------------
 // Attention forward. One routine serves every mode; each output row is independent.
 //
 // mode 0 EXACT    softmax(QK^T * scale) V in FP64, two passes, no quantisation.
@@ -388,12 +566,16 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
                   int expcast, int tile_tokens, int n_tiles, const int32_t* tile_len,
                   const int32_t* row_ptr, const int32_t* col_idx, const int32_t* rows,
                   int64_t n_rows, double* out, uint16_t* out_bf16, int64_t* underflow,
-                  uint8_t* row_valid, double* amb_bound, const float* v_shift, int kv_splits) {
+                  uint8_t* row_valid, double* amb_bound, const float* v_shift, int kv_splits,
+                  const OrcSol* sol) {
   if (mode < 0 || mode > 3 || B < 1 || N < 1 || H < 1 || D < 1 || n_rows < 0) return 1;
   if (mode < 3 && (!qd || !kd || !vd)) return 1;
   if (mode == 3 && (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale)) return 1;
   if (!(p_scale > 0.0)) return 1;
   const bool sparse = tile_len != nullptr;
+  if (sol && (mode != 3 || sparse || v_mean || kv_splits > 1 || !sol->mask || !sol->kq8 ||
+              !sol->kq_scale || !sol->vsum))
+    return 1;
   if (sparse && (tile_tokens <= 0 || tile_tokens % 64 != 0 ||
                  static_cast<int64_t>(tile_tokens) * n_tiles != N || !row_ptr || !col_idx))
     return 1;
@@ -670,7 +852,73 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
         // V blocks); each piece keeps the row's KV order; piece s gives o_s, m_s, l_s and
         // O = sum_s w_s o_s / sum_s w_s with w_s = l_s * exp(m_s - max m).
         std::vector<Pass> parts;
-        if (kv_splits <= 1 || sparse) {
+        if (sol) {
+          // Sol routing: the exact route streams the row's exact blocks (in KV order); the
+          // summary route treats each other block as n_j copies of (kbar_j, vbar_j), scored with
+          // the route score; the two are merged like split-KV pieces (an empty route has no
+          // weight).
+          const int64_t u = i / 64, W = ceil_div(NB, 64), NBg = ceil_div(NB, 64);
+          const uint64_t* mrow = sol->mask + (bh * NB + u) * W;
+          auto is_exact = [&](int64_t j) { return ((mrow[j / 64] >> (j % 64)) & 1ull) != 0; };
+          std::vector<int64_t> ex;
+          for (const int64_t kb : blocks)
+            if (is_exact(kb)) ex.push_back(kb);
+          if (!ex.empty()) parts.push_back(stream(ex));
+          std::vector<double> xs(NB, 0.0), bs(NB, 0.0);
+          double mS = -std::numeric_limits<double>::infinity();
+          for (int64_t j = 0; j < NB; j++) {
+            if (is_exact(j)) continue;
+            const uint8_t* qr = q8 + (bh * N64 + i) * D;
+            const uint8_t* kr = sol->kq8 + (bh * NBg * 64 + j) * D;
+            double dot = 0.0, gsum = 0.0;
+            for (int g = 0; g < D; g += 8) {
+              double gm = 0.0;
+              for (int d = g; d < std::min(D, g + 8); d++) {
+                const double pr = code_value[qr[d]] * code_value[kr[d]];
+                dot += pr;
+                gm = std::max(gm, std::fabs(pr));
+              }
+              gsum += gm;
+            }
+            const double sc = static_cast<double>(q_scale[bh * NB + u]) *
+                              static_cast<double>(sol->kq_scale[bh * NBg + j / 64]) * softmax_scale;
+            xs[j] = dot * sc;
+            bs[j] = std::ldexp(gsum, -11) * sc;
+            mS = std::max(mS, xs[j]);
+          }
+          if (mS > -std::numeric_limits<double>::infinity()) {
+            Pass ps;
+            ps.o.assign(D, 0.0);
+            ps.amb.assign(D, 0.0);
+            double lS = 0.0, dl = 0.0;
+            std::vector<double> wj(NB, 0.0);
+            for (int64_t j = 0; j < NB; j++) {
+              if (is_exact(j)) continue;
+              wj[j] = static_cast<double>(std::min<int64_t>(64, N - 64 * j)) * std::exp(xs[j] - mS);
+              lS += wj[j];
+            }
+            for (int64_t j = 0; j < NB; j++) {
+              if (wj[j] == 0.0) continue;
+              for (int d = 0; d < D; d++)
+                ps.o[d] += wj[j] * bf16_value(sol->vsum[(bh * NB + j) * D + d]);
+              // a device evaluates the score on the matrix cores and the weight in BF16
+              dl += wj[j] * (bs[j] + std::ldexp(1.0, -9));
+            }
+            for (int d = 0; d < D; d++) ps.o[d] /= lS;
+            if (amb_bound)
+              for (int64_t j = 0; j < NB; j++) {
+                if (wj[j] == 0.0) continue;
+                const double e = wj[j] / lS * (2.0 * bs[j] + std::ldexp(1.0, -8));
+                for (int d = 0; d < D; d++)
+                  ps.amb[d] += e * (std::fabs(bf16_value(sol->vsum[(bh * NB + j) * D + d])) + std::fabs(ps.o[d]));
+              }
+            ps.m = mS;
+            ps.l = lS;
+            ps.lx = dl / lS;
+            ps.n_under = 0;
+            parts.push_back(ps);
+          }
+        } else if (kv_splits <= 1 || sparse) {
           parts.push_back(stream(blocks));
         } else {
           const int64_t L = 2 * ceil_div(NB, 2 * static_cast<int64_t>(kv_splits));
