@@ -7,6 +7,8 @@ mirror the C ABI in ``include/fp8attn.h``:
 * ``quantize_qkv``  -> ``fp8attn_quantize_qkv``
 * ``forward``       -> ``fp8attn_forward``
 * ``sta_build``     -> ``fp8attn_sta_build`` (host helper)
+* ``vsmooth_cluster`` -> ``fp8attn_vsmooth_cluster``
+* ``sol_forward``   -> ``fp8attn_sol_forward``
 
 There is no fallback: if the library is missing or the device is not gfx950 these calls raise.
 """
@@ -51,6 +53,13 @@ class _Sparse(ctypes.Structure):
                 ("col_idx", ctypes.c_void_p)]
 
 
+class _SolOpts(ctypes.Structure):
+    _fields_ = [("softmax_scale", ctypes.c_float), ("p_scale", ctypes.c_float),
+                ("kv_order", ctypes.c_int), ("pcast", ctypes.c_int), ("tau", ctypes.c_float),
+                ("estimator", ctypes.c_int32), ("sink_blocks", ctypes.c_int32),
+                ("v_shift", ctypes.c_void_p)]
+
+
 class _FwdOpts(ctypes.Structure):
     _fields_ = [("softmax_scale", ctypes.c_float), ("p_scale", ctypes.c_float),
                 ("kv_order", ctypes.c_int), ("pcast", ctypes.c_int),
@@ -63,7 +72,8 @@ _lib = None
 
 EXPORTED = ("fp8attn_quantize_qkv", "fp8attn_quantize_workspace_bytes", "fp8attn_forward",
             "fp8attn_forward_workspace_bytes", "fp8attn_sta_build", "fp8attn_status_string",
-            "fp8attn_vsmooth_cluster", "fp8attn_vsmooth_cluster_workspace_bytes")
+            "fp8attn_vsmooth_cluster", "fp8attn_vsmooth_cluster_workspace_bytes",
+            "fp8attn_sol_forward", "fp8attn_sol_workspace_bytes")
 
 
 def lib():
@@ -94,6 +104,12 @@ def lib():
         L.fp8attn_vsmooth_cluster.restype = ctypes.c_int
         L.fp8attn_vsmooth_cluster.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] + [ctypes.c_int32] * 3 + [
             ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
+        L.fp8attn_sol_workspace_bytes.restype = ctypes.c_size_t
+        L.fp8attn_sol_workspace_bytes.argtypes = [ctypes.c_int32] * 4
+        L.fp8attn_sol_forward.restype = ctypes.c_int
+        L.fp8attn_sol_forward.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 6 + [
+            ctypes.POINTER(_SolOpts), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_size_t, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -263,3 +279,35 @@ def forward(qz: Quantized, softmax_scale=1.0 / math.sqrt(HEAD_DIM), p_scale=256.
         _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel()), _stream(dev))
     _check("fp8attn_forward", st)
     return out
+
+
+def sol_workspace(B, N, H, device):
+    n = int(lib().fp8attn_sol_workspace_bytes(B, N, H, HEAD_DIM))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def sol_forward(qz: Quantized, tau=3.0, estimator=0, sink_blocks=1,
+                softmax_scale=1.0 / math.sqrt(HEAD_DIM), p_scale=256.0,
+                kv_order=FP8ATTN_KV_REVERSE, pcast=FP8ATTN_PCAST_RNE, out=None, workspace=None,
+                return_mask=False):
+    """fp8attn_sol_forward: Sol routing attention on quantised operands (layout order, no
+    V-Smooth). Returns bf16 [B, N, H, 128], and with return_mask the exact-block mask, uint64
+    words [B, H, NB, ceil(NB / 64)] (bit j % 64 of word j // 64: KV block j exact)."""
+    if qz.v_mean is not None:
+        raise ValueError("Sol routing takes operands quantised without V-Smooth")
+    B, N, H = qz.B, qz.N, qz.H
+    dev = qz.q8.device
+    NB = (N + 63) // 64
+    W = (NB + 63) // 64
+    if out is None:
+        out = torch.empty((B, N, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    ws = workspace if workspace is not None else sol_workspace(B, N, H, dev)
+    mask = torch.empty((B, H, NB, W), dtype=torch.int64, device=dev) if return_mask else None
+    opts = _SolOpts(float(softmax_scale), float(p_scale), int(kv_order), int(pcast), float(tau),
+                    int(estimator), int(sink_blocks), _ptr(qz.v_shift))
+    st = lib().fp8attn_sol_forward(
+        B, N, H, HEAD_DIM, _ptr(qz.q8), _ptr(qz.k8), _ptr(qz.v8t), _ptr(qz.q_scale),
+        _ptr(qz.k_scale), _ptr(qz.v_scale), ctypes.byref(opts), _ptr(out), _ptr(mask), _ptr(ws),
+        ctypes.c_size_t(ws.numel()), _stream(dev))
+    _check("fp8attn_sol_forward", st)
+    return (out, mask) if return_mask else out

@@ -280,6 +280,143 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
   return from_hip(fp8attn::launch_attention(p, variant, stream));
 }
 
+namespace {
+
+struct SolLayout {
+  int64_t NB, NBg, NBp, W;
+  size_t ksum, vsumT, kq8, kq_scale, mk, Mk, theta, mask, o_part, lse, total;
+};
+
+SolLayout sol_layout(int32_t B, int32_t N, int32_t H) {
+  SolLayout L;
+  const size_t bh = static_cast<size_t>(B) * H;
+  L.NB = cdiv(N, 64);
+  L.NBg = cdiv(L.NB, 64);
+  L.NBp = 64 * L.NBg;
+  L.W = L.NBg;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += round_up(bytes);
+    return o;
+  };
+  L.ksum = take(bh * L.NB * kHeadDim * sizeof(float));
+  L.vsumT = take(bh * kHeadDim * L.NBp * sizeof(uint16_t));
+  L.kq8 = take(bh * L.NBp * kHeadDim);
+  L.kq_scale = take(bh * L.NBg * sizeof(float));
+  L.mk = take(bh * kHeadDim * sizeof(double));
+  L.Mk = take(bh * kHeadDim * kHeadDim * sizeof(double));
+  L.theta = take(bh * L.NB * sizeof(float));
+  L.mask = take(bh * L.NB * L.W * sizeof(uint64_t));
+  L.o_part = take(2 * bh * N * kHeadDim * sizeof(float));
+  L.lse = take(2 * bh * N * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+size_t fp8attn_sol_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D) {
+  if (B < 1 || N < 1 || H < 1 || D != kHeadDim) return 0;
+  return sol_layout(B, N, H).total;
+}
+
+fp8attn_status fp8attn_sol_forward(int32_t B, int32_t N, int32_t H, int32_t D, const uint8_t* q8,
+                                   const uint8_t* k8, const uint8_t* v8t, const float* q_scale,
+                                   const float* k_scale, const float* v_scale,
+                                   const fp8attn_sol_opts* o, void* out, uint64_t* route_mask,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!o || B < 1 || N < 1 || H < 1 || D < 1) return FP8ATTN_EINVAL;
+  if (D != kHeadDim) return FP8ATTN_EUNSUPPORTED;
+  const int64_t total_bh = static_cast<int64_t>(B) * H;
+  if (total_bh > 65535 || total_bh * cdiv(N, 64) > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
+  const void* p16[] = {q8, k8, v8t, v_scale, out, workspace};
+  for (const void* ptr : p16)
+    if (!ptr || !aligned(ptr, 16)) return FP8ATTN_EINVAL;
+  if (!q_scale || !k_scale || !aligned(q_scale, 4) || !aligned(k_scale, 4)) return FP8ATTN_EINVAL;
+  if (route_mask && !aligned(route_mask, 8)) return FP8ATTN_EINVAL;
+  if (!(o->softmax_scale > 0.0f) || !isfinite(o->softmax_scale)) return FP8ATTN_EINVAL;
+  if (!(o->p_scale > 0.0f) || !(o->p_scale <= 448.0f)) return FP8ATTN_EINVAL;
+  if (o->kv_order != FP8ATTN_KV_FORWARD && o->kv_order != FP8ATTN_KV_REVERSE) return FP8ATTN_EINVAL;
+  if (o->pcast != FP8ATTN_PCAST_RNE && o->pcast != FP8ATTN_PCAST_EXPCAST) return FP8ATTN_EINVAL;
+  if (!isfinite(o->tau) || o->estimator < 0 || o->estimator > 1 || o->sink_blocks < 0) return FP8ATTN_EINVAL;
+  if (o->v_shift && !aligned(o->v_shift, 16)) return FP8ATTN_EINVAL;
+  const SolLayout L = sol_layout(B, N, H);
+  if (workspace_bytes < L.total) return FP8ATTN_EINVAL;
+  const fp8attn_status dev = check_device();
+  if (dev != FP8ATTN_OK) return dev;
+
+  char* ws = static_cast<char*>(workspace);
+  uint64_t* mask = route_mask ? route_mask : reinterpret_cast<uint64_t*>(ws + L.mask);
+  float* o_part = reinterpret_cast<float*>(ws + L.o_part);
+  float* lse = reinterpret_cast<float*>(ws + L.lse);
+  const double log2S = log2(static_cast<double>(o->p_scale));
+
+  fp8attn::SolParams sp;
+  std::memset(&sp, 0, sizeof(sp));
+  sp.q8 = q8;
+  sp.k8 = k8;
+  sp.v8t = v8t;
+  sp.q_scale = q_scale;
+  sp.k_scale = k_scale;
+  sp.v_scale = v_scale;
+  sp.ksum = reinterpret_cast<float*>(ws + L.ksum);
+  sp.vsumT = reinterpret_cast<uint16_t*>(ws + L.vsumT);
+  sp.kq8 = reinterpret_cast<uint8_t*>(ws + L.kq8);
+  sp.kq_scale = reinterpret_cast<float*>(ws + L.kq_scale);
+  sp.mk = reinterpret_cast<double*>(ws + L.mk);
+  sp.Mk = reinterpret_cast<double*>(ws + L.Mk);
+  sp.theta = reinterpret_cast<float*>(ws + L.theta);
+  sp.mask = mask;
+  sp.o_part = o_part + total_bh * N * kHeadDim;  // piece 1: the summary route
+  sp.lse = lse + total_bh * N;
+  sp.N = N;
+  sp.NB = L.NB;
+  sp.N64 = L.NB * 64;
+  sp.NBg = L.NBg;
+  sp.NBp = L.NBp;
+  sp.W = L.W;
+  sp.B = B;
+  sp.H = H;
+  sp.softmax_scale = o->softmax_scale;
+  sp.log2S = static_cast<float>(log2S);
+  sp.tau = o->tau;
+  sp.estimator = o->estimator;
+  sp.sink_blocks = o->sink_blocks;
+  hipError_t e = fp8attn::launch_sol(sp, stream);
+  if (e != hipSuccess) return FP8ATTN_EHIP;
+
+  fp8attn::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q8 = q8;
+  p.k8 = k8;
+  p.v8t = v8t;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.out = static_cast<uint16_t*>(out);
+  p.v_shift = o->v_shift;
+  p.N = N;
+  p.NB = L.NB;
+  p.N64 = L.NB * 64;
+  p.NB128 = cdiv(N, 128);
+  p.n_out = N;
+  p.B = B;
+  p.H = H;
+  p.logit_scale = static_cast<float>(static_cast<double>(o->softmax_scale) * 1.4426950408889634);
+  p.log2S = static_cast<float>(log2S);
+  p.reverse = o->kv_order == FP8ATTN_KV_REVERSE ? 1 : 0;
+  p.splits = 1;
+  p.split_blocks = L.NB;
+  p.o_part = o_part;
+  p.lse = lse;
+  p.sol_mask = mask;
+  p.sol_words = L.W;
+  int variant = fp8attn::kVarSol;
+  if (o->pcast == FP8ATTN_PCAST_EXPCAST) variant |= fp8attn::kVarExpCast;
+  return from_hip(fp8attn::launch_attention(p, variant, stream));
+}
+
 // Host-side tile layout. Each token's tile follows from its raster coordinates; tokens are
 // bucketed per tile in raster order (valid first), then padded with -1; the neighbour list of a
 // tile is every tile whose tile coordinates are within the per-axis Chebyshev radius.

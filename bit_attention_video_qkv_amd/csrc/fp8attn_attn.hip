@@ -171,7 +171,7 @@ struct KvCursor {
 // QK(j+1) writes its result into the registers the softmax of block j has just consumed, so a
 // wave needs one S tile of registers; two workgroups share each CU, so every SIMD runs two such
 // waves whose barriers and dependency stalls cover each other.
-template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS>
+template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS, bool SOL>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd(AttnParams p) {
   constexpr int kThreads = WAVES * 64;
   constexpr int kRowsPerWg = WAVES * 32;
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // ---- sparse row of this query tile ----
   int e_begin = 0, e_end = 0, q_valid_len = 0;
-  if constexpr (SPARSE) {
+  if constexpr (SPARSE && !SOL) {
     const int u = static_cast<int>(q0 / p.tile_tokens);
     e_begin = p.row_ptr[u];
     e_end = p.row_ptr[u + 1];
@@ -218,7 +218,26 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   int n_iter = 0;
   int64_t e0 = 0;
   bool has_last_block = true;  // the piece holds key block NB-1 (the only partial one)
-  if constexpr (SPARSE) {
+  // Sol: the exact blocks of this 64-row Q block are the set bits of its mask row, visited in
+  // KV order (uniform scans of the mask words)
+  const uint64_t* sol_row = SOL ? p.sol_mask + (bh * p.NB + q0 / kBlock) * p.sol_words : nullptr;
+  auto sol_next = [&](int64_t pos) -> int64_t {  // first exact block at or after pos, or -1
+    if (pos >= p.NB) return -1;
+    int64_t w = pos >> 6;
+    uint64_t m = sol_row[w] & (~0ull << (pos & 63));
+    while (m == 0ull && ++w < p.sol_words) m = sol_row[w];
+    return m ? (w << 6) + __builtin_ctzll(m) : -1;
+  };
+  auto sol_prev = [&](int64_t pos) -> int64_t {  // last exact block at or before pos, or -1
+    if (pos < 0) return -1;
+    int64_t w = pos >> 6;
+    uint64_t m = sol_row[w] & ((pos & 63) == 63 ? ~0ull : ((1ull << ((pos & 63) + 1)) - 1ull));
+    while (m == 0ull && --w >= 0) m = sol_row[w];
+    return m ? (w << 6) + 63 - __builtin_clzll(m) : -1;
+  };
+  if constexpr (SOL) {
+    for (int64_t w = 0; w < p.sol_words; w++) n_iter += __builtin_popcountll(sol_row[w]);
+  } else if constexpr (SPARSE) {
     for (int e = e_begin; e < e_end; e++) n_iter += nblk_of_len(p.tile_len[p.col_idx[e]]);
   } else {
     const int64_t kb_lo = static_cast<int64_t>(split) * p.split_blocks;
@@ -227,21 +246,38 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     e0 = p.reverse ? p.NB - kb_hi : kb_lo;
     has_last_block = kb_hi == p.NB;
   }
-  if (n_iter <= 0) return;  // a query tile without key blocks has no defined output
+  if (n_iter <= 0) {
+    if constexpr (SOL) {
+      // no exact block: the exact route has no weight
+      for (int r = threadIdx.x; r < kRowsPerWg * (kHeadDim / 4); r += kThreads) {
+        const int64_t row = q0 + r / (kHeadDim / 4);
+        if (row >= p.N) continue;
+        reinterpret_cast<float4*>(p.o_part + (bh * p.N + row) * kHeadDim)[r % (kHeadDim / 4)] =
+            make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (r % (kHeadDim / 4) == 0) p.lse[bh * p.N + row] = -INFINITY;
+      }
+    }
+    return;  // (otherwise: a query tile without key blocks has no defined output)
+  }
 
   KvCursor lc;  // the copy engine's cursor: the next K block to stage
   lc.e = static_cast<int>(e0);
   lc.bt = 0;
   lc.v = 0;
   lc.len = 0;
-  if constexpr (SPARSE) {
+  if constexpr (SOL) {
+    lc.v = static_cast<int>(p.reverse ? sol_prev(p.NB - 1) : sol_next(0));
+  } else if constexpr (SPARSE) {
     lc.e = p.reverse ? e_end - 1 : e_begin;
     lc.v = p.col_idx[lc.e];
     lc.len = p.tile_len[lc.v];
     lc.bt = p.reverse ? nblk_of_len(lc.len) - 1 : 0;
   }
   auto block_of = [&](const KvCursor& c, int& limit) -> int64_t {
-    if constexpr (SPARSE) {
+    if constexpr (SOL) {
+      limit = static_cast<int>(min<int64_t>(kBlock, p.N - static_cast<int64_t>(c.v) * kBlock));
+      return c.v;
+    } else if constexpr (SPARSE) {
       limit = min(kBlock, c.len - c.bt * kBlock);
       return static_cast<int64_t>(c.v) * per_tile + c.bt;
     } else {
@@ -251,7 +287,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     }
   };
   auto advance = [&](KvCursor& c) {
-    if constexpr (SPARSE) {
+    if constexpr (SOL) {
+      c.v = static_cast<int>(p.reverse ? sol_prev(c.v - 1) : sol_next(c.v + 1));
+    } else if constexpr (SPARSE) {
       if (!p.reverse) {
         if (++c.bt >= nblk_of_len(c.len)) {
           c.e++;
@@ -599,8 +637,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // end of tiles anywhere in the sequence, so every block checks its valid-key count. ----
   using kNoMask = std::integral_constant<bool, false>;
   using kMasked = std::integral_constant<bool, true>;
-  using kLoopMask = std::integral_constant<bool, SPARSE>;
-  const bool partial_tail = !SPARSE && (p.N % kBlock) != 0 && has_last_block;
+  using kLoopMask = std::integral_constant<bool, SPARSE || SOL>;
+  const bool partial_tail = !SPARSE && !SOL && (p.N % kBlock) != 0 && has_last_block;
   int j_begin = 0, j_end = n_iter, sidx = 1;  // sidx: slot of pair j+1
   if (partial_tail && p.reverse) {
     iteration(kMasked{}, 0, slot(1));
@@ -623,11 +661,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // ---- epilogue: O = acc * g_d / l', BF16, scattered to the destination rows ----
   bool ok = qrow < p.N;
-  if constexpr (SPARSE) ok = ok && static_cast<int>(qrow % p.tile_tokens) < q_valid_len;
+  if constexpr (SPARSE && !SOL) ok = ok && static_cast<int>(qrow % p.tile_tokens) < q_valid_len;
   const float l_tot = xsum(l_part);
-  if constexpr (!SPARSE) {
-    if (p.splits > 1) {
-      // split-KV: this piece's normalised O (FP32) and log2 of its weight, m + log2(l)
+  if constexpr (!SPARSE || SOL) {
+    if (p.o_part) {
+      // split-KV piece or Sol exact route: this piece's normalised O (FP32) and log2 of its
+      // weight, m + log2(l)
       if (ok) {
         const float inv_l = 1.0f / l_tot;
         const int64_t prow = (static_cast<int64_t>(split) * p.B * p.H + bh) * p.N + qrow;
@@ -748,15 +787,28 @@ __global__ __launch_bounds__(256) void split_merge(AttnParams p) {
   *reinterpret_cast<uint2*>(p.out + ((b * p.n_out + dst) * p.H + h) * kHeadDim + c) = o;
 }
 
-template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS>
+template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS, bool SOL = false>
 hipError_t launch_variant(AttnParams& p, hipStream_t stream) {
   const int rows = WAVES * 32;
   p.n_qtiles = static_cast<int>((p.N + rows - 1) / rows);
   p.total_work = p.B * p.H * p.n_qtiles * p.splits;
   const unsigned grid = static_cast<unsigned>(((p.total_work + 7) / 8) * 8);
-  hipLaunchKernelGGL((attn_fwd<WAVES, SPARSE, EXPCAST, VSMOOTH, STATS>), dim3(grid), dim3(WAVES * 64), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd<WAVES, SPARSE, EXPCAST, VSMOOTH, STATS, SOL>), dim3(grid), dim3(WAVES * 64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL(split_merge, dim3(static_cast<unsigned>((p.N + 7) / 8), static_cast<unsigned>(p.B * p.H)),
+                     dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Sol: the exact route (two waves per 64-row Q block, the mask's blocks) writes piece 0; the
+// summary route has written piece 1; then the two are merged.
+template <bool EXPCAST>
+hipError_t launch_sol_exact(AttnParams p, hipStream_t stream) {
+  p.splits = 1;
+  hipError_t e = launch_variant<2, true, EXPCAST, false, false, true>(p, stream);
+  if (e != hipSuccess) return e;
+  p.splits = 2;
   hipLaunchKernelGGL(split_merge, dim3(static_cast<unsigned>((p.N + 7) / 8), static_cast<unsigned>(p.B * p.H)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -767,6 +819,7 @@ hipError_t launch_variant(AttnParams& p, hipStream_t stream) {
 hipError_t launch_attention(AttnParams p, int variant, hipStream_t stream) {
   const bool ec = variant & kVarExpCast, vs = variant & kVarVSmooth, sp = variant & kVarSparse,
              st = variant & kVarStats;
+  if (variant & kVarSol) return ec ? launch_sol_exact<true>(p, stream) : launch_sol_exact<false>(p, stream);
   if (vs) {
     hipLaunchKernelGGL(vsmooth_mean_factors, dim3(static_cast<unsigned>(p.NB128), static_cast<unsigned>(p.B * p.H)),
                        dim3(kHeadDim), 0, stream, p);

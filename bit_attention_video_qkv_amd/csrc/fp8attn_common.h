@@ -34,6 +34,13 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
+// Exact value of an OCP E4M3 byte (finite codes; the encoders saturate, so 0x7F/0xFF never occur).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e == 0 ? static_cast<float>(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;

@@ -64,7 +64,41 @@ struct AttnParams {
   int64_t split_blocks;
   float* o_part;  // [splits, B*H, N, 128]
   float* lse;     // [splits, B*H, N]
+  // Sol routing: exact-block mask [B*H, NB, sol_words] of the exact route (the attention then
+  // writes its partial output as piece 0), or null
+  const uint64_t* sol_mask;
+  int64_t sol_words;
 };
+
+// Sol routing preparation and summary route (fp8attn_sol.hip).
+struct SolParams {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8t;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  float* ksum;       // [B*H, NB, 128] K summaries (FP32)
+  uint16_t* vsumT;   // [B*H, 128, NBp] V summaries (bf16), summary-contiguous, zero padded
+  uint8_t* kq8;      // [B*H, NBp, 128] quantised K summaries
+  float* kq_scale;   // [B*H, NBg]
+  double* mk;        // [B*H, 128] mean of the summaries
+  double* Mk;        // [B*H, 128, 128] second moment of the summaries
+  float* theta;      // [B*H, NB]
+  uint64_t* mask;    // [B*H, NB, W]
+  float* o_part;     // piece 1 of the merge buffers: [B*H, N, 128]
+  float* lse;        // [B*H, N]
+  int64_t N, N64, NB, NBg, NBp, W;
+  int B, H;
+  float softmax_scale;
+  float log2S;
+  double tau;
+  int estimator;
+  int sink_blocks;
+};
+
+// Summaries, quantised K summaries, moments, thresholds, then the route (mask + summary route).
+hipError_t launch_sol(const SolParams& p, hipStream_t stream);
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t stream);
 
@@ -89,6 +123,7 @@ enum AttnVariant : int {
   kVarVSmooth = 2,
   kVarSparse = 4,
   kVarStats = 8,
+  kVarSol = 16,
 };
 
 // Launches the attention forward for the variant bits; p.n_qtiles / p.total_work are filled in.

@@ -346,13 +346,6 @@ __device__ __forceinline__ float mul_rounded(float a, float b) {
   return p;
 }
 
-// Exact value of an OCP E4M3 byte (finite codes; the encoder saturates, so 0x7F/0xFF never occur).
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float mag = e == 0 ? static_cast<float>(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (c & 0x80u) ? -mag : mag;
-}
-
 // 4. V codes of a 64-row block, transposed to token-contiguous rows of v8t. BIAS: also the FP32
 // column sums (valid rows, ascending) of err = fl32(fl32(decode(code) * s_v) - V') into the V half
 // of ws_bsum, for the bias-corrected v_shift; the input rows are kept in LDS as bf16 and the codes

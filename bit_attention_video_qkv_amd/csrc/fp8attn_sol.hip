@@ -1,0 +1,387 @@
+// Sol routing (TeleFuser blog "FP8 Sol-Attn: H100 视频 DiT 的量化稀疏注意力", sections "Sol Routing"
+// and "SM90 CuTe Mainloop"): the sequence is cut into 64-token Q and KV blocks; every KV block
+// gets a K summary and a V summary; a threshold theta = mu + tau * sigma per Q block (diag or
+// exact estimator) decides, from a route QK of the block-quantised Q with the quantised K
+// summaries, which KV blocks take the exact route (full E4M3 QK, online softmax, E4M3 PV) and
+// which the summary route (the block as n_j copies of its summary key and value). Sink blocks are
+// always exact.
+//
+// Readings (the page leaves these open):
+//  * summaries are block means of the dequantised E4M3 K and V:
+//      kbar = fl32(fl32(sum_t decode(K8) * s_k) / n_j)   (the code sum is exact in FP32),
+//      vbar likewise with the channel scale, stored as BF16;
+//  * the K summaries are quantised like K, per group of 64 summaries (scale = amax / 448);
+//  * mu and sigma are the mean and standard deviation of the Q block's route scores over all
+//    pairs (valid query, KV block), from second moments: mu = ss * qbar . m,
+//    E2 = ss^2 * sum_{d,e} Mq[d,e] Mk[d,e] ("exact") or ss^2 * sum_d Mq[d,d] Mk[d,d] ("diag"),
+//    m and Mk the mean and second moment of the summaries, Mq the block's query second moment;
+//  * a KV block is exact for Q block u when some valid query of u has a route score >= theta_u;
+//  * the exact route runs the ordinary kernel over the exact blocks; this file computes the
+//    summary route: weights n_j * exp(r_ij - m) with r_ij the route score, applied to the V
+//    summaries; the two routes are merged by log-sum-exp like split-KV pieces.
+//
+// Kernels (launch order):
+//   sol_summaries  grid (NBp, B*H)         K and V summaries
+//   sol_kquant     grid (NBg, B*H)         quantised K summaries
+//   sol_kmoments   grid (B*H, 16)          mean and second moment of the summaries (FP64)
+//   sol_theta      grid (NB, B*H)          threshold per Q block
+//   sol_route      grid (NB, B*H), 2 waves route QK (E4M3 MFMA), mask, summary route (BF16 MFMA)
+#include "fp8attn_common.h"
+#include "fp8attn_internal.h"
+
+namespace fp8attn {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16f mfma_bf16(const bf16x8& a, const bf16x8& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 1. Summaries of KV block j (grid over the padded count NBp: padding summaries get a zero V
+// summary, which the summary PV multiplies by p = 0). Threads 0..127: K channel d; 128..255: V
+// channel d. Rows and positions past N hold code 0 (the quantisation contract), so all 64 are
+// summed.
+__global__ __launch_bounds__(256) void sol_summaries(SolParams p) {
+  const int64_t j = blockIdx.x, bh = blockIdx.y;
+  if (j >= p.NB) {
+    if (threadIdx.x >= kHeadDim) p.vsumT[(bh * kHeadDim + threadIdx.x - kHeadDim) * p.NBp + j] = 0;
+    return;
+  }
+  const int n = static_cast<int>(min<int64_t>(64, p.N - 64 * j));
+  if (threadIdx.x < kHeadDim) {
+    const int d = threadIdx.x;
+    const uint8_t* kp = p.k8 + (bh * p.N64 + 64 * j) * kHeadDim + d;
+    float s = 0.0f;
+#pragma unroll 16
+    for (int r = 0; r < 64; r++) s += e4m3_decode(kp[r * kHeadDim]);
+    const float prod = s * p.k_scale[bh * p.NB + j];
+    p.ksum[(bh * p.NB + j) * kHeadDim + d] = __fdiv_rn(prod, static_cast<float>(n));
+  } else {
+    const int d = threadIdx.x - kHeadDim;
+    const uint4* vp = reinterpret_cast<const uint4*>(p.v8t + (bh * kHeadDim + d) * p.N64 + 64 * j);
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const uint4 w = vp[c];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+#pragma unroll
+        for (int b = 0; b < 4; b++) s += e4m3_decode((ws[q] >> (8 * b)) & 0xFFu);
+    }
+    const float prod = s * p.v_scale[bh * kHeadDim + d];
+    p.vsumT[(bh * kHeadDim + d) * p.NBp + j] = f32_to_bf16_rne(__fdiv_rn(prod, static_cast<float>(n)));
+  }
+}
+
+// 2. Quantised K summaries: group g = summaries 64g .. 64g+63 (rows >= NB are zero). Thread t:
+// channels 8*(t%16)..+7 of rows t/16 + 16*pass.
+__global__ __launch_bounds__(256) void sol_kquant(SolParams p) {
+  __shared__ float red[4];
+  const int64_t g = blockIdx.x, bh = blockIdx.y;
+  const int chunk = threadIdx.x & 15, row0 = threadIdx.x >> 4;
+  float x[4][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int pass = 0; pass < 4; pass++) {
+    const int64_t j = 64 * g + row0 + 16 * pass;
+    if (j < p.NB) {
+      const float4* src = reinterpret_cast<const float4*>(p.ksum + (bh * p.NB + j) * kHeadDim + chunk * 8);
+      const float4 a = src[0], b = src[1];
+      x[pass][0] = a.x; x[pass][1] = a.y; x[pass][2] = a.z; x[pass][3] = a.w;
+      x[pass][4] = b.x; x[pass][5] = b.y; x[pass][6] = b.z; x[pass][7] = b.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; q++) x[pass][q] = 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; q++) amax = fmaxf(amax, fabsf(x[pass][q]));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = amax > 0.0f ? __fdiv_rn(448.0f, amax) : 0.0f;
+  if (threadIdx.x == 0) p.kq_scale[bh * p.NBg + g] = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 0.0f;
+#pragma unroll
+  for (int pass = 0; pass < 4; pass++) {
+    const int64_t j = 64 * g + row0 + 16 * pass;
+    float y[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) y[q] = x[pass][q] * inv;
+    uint2 out;
+    out.x = e4m3x4(y[0], y[1], y[2], y[3]);
+    out.y = e4m3x4(y[4], y[5], y[6], y[7]);
+    *reinterpret_cast<uint2*>(p.kq8 + (bh * p.NBp + j) * kHeadDim + chunk * 8) = out;
+  }
+}
+
+// 3. Mean and second moment of the summaries (FP64, ascending j). grid (B*H, 16): workgroup y
+// computes rows 8y..8y+7 of Mk (thread t: row 8y + t/32, columns 4*(t%32)..+3); y = 0 also the
+// mean.
+__global__ __launch_bounds__(256) void sol_kmoments(SolParams p) {
+  const int64_t bh = blockIdx.x;
+  const int d = blockIdx.y * 8 + (threadIdx.x >> 5);
+  const int e0 = (threadIdx.x & 31) * 4;
+  const float* ks = p.ksum + bh * p.NB * kHeadDim;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int64_t j = 0; j < p.NB; j++) {
+    const double a = static_cast<double>(ks[j * kHeadDim + d]);
+    const float4 b = *reinterpret_cast<const float4*>(ks + j * kHeadDim + e0);
+    acc[0] += a * static_cast<double>(b.x);
+    acc[1] += a * static_cast<double>(b.y);
+    acc[2] += a * static_cast<double>(b.z);
+    acc[3] += a * static_cast<double>(b.w);
+  }
+  const double inv_nb = 1.0 / static_cast<double>(p.NB);
+#pragma unroll
+  for (int q = 0; q < 4; q++) p.Mk[(bh * kHeadDim + d) * kHeadDim + e0 + q] = acc[q] * inv_nb;
+  if (blockIdx.y == 0 && threadIdx.x < kHeadDim) {
+    double m = 0.0;
+    for (int64_t j = 0; j < p.NB; j++) m += static_cast<double>(ks[j * kHeadDim + threadIdx.x]);
+    p.mk[bh * kHeadDim + threadIdx.x] = m * inv_nb;
+  }
+}
+
+__device__ __forceinline__ double block_sum_128(double v, double* red) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const double r = red[0] + red[1];
+  __syncthreads();
+  return r;
+}
+
+// 4. Threshold of Q block u. Thread e: channel e. The decoded query codes c_i (exact in FP32)
+// sit in LDS; q_i = s_q * c_i.
+__global__ __launch_bounds__(128) void sol_theta(SolParams p) {
+  __shared__ float c[64][kHeadDim + 1];
+  __shared__ double red[2];
+  const int64_t u = blockIdx.x, bh = blockIdx.y;
+  const int e = threadIdx.x;
+  const int nq = static_cast<int>(min<int64_t>(64, p.N - 64 * u));
+  const uint8_t* qb = p.q8 + (bh * p.N64 + 64 * u) * kHeadDim;
+  for (int i = 0; i < 64; i++) c[i][e] = i < nq ? e4m3_decode(qb[i * kHeadDim + e]) : 0.0f;
+  __syncthreads();
+  const double sq = p.q_scale[bh * p.NB + u];
+  double csum = 0.0, csq = 0.0;
+  for (int i = 0; i < nq; i++) {
+    csum += c[i][e];
+    csq += static_cast<double>(c[i][e]) * c[i][e];
+  }
+  // mu = ss * sq * mean_i c_i . m
+  const double mu = block_sum_128(csum / nq * p.mk[bh * kHeadDim + e], red) * sq * p.softmax_scale;
+  double part;
+  if (p.estimator == 0) {
+    part = csq / nq * p.Mk[(bh * kHeadDim + e) * kHeadDim + e];
+  } else {
+    // sum_i c_i[e] (Mk c_i)[e] / nq, with (Mk c_i)[e] = sum_d Mk[d][e] c_i[d] (Mk symmetric)
+    float y[64];
+#pragma unroll
+    for (int i = 0; i < 64; i++) y[i] = 0.0f;
+    const double* mrow = p.Mk + bh * kHeadDim * kHeadDim + e;
+    for (int d = 0; d < kHeadDim; d++) {
+      const float m = static_cast<float>(mrow[d * kHeadDim]);
+#pragma unroll
+      for (int i = 0; i < 64; i++) y[i] = __builtin_fmaf(m, c[i][d], y[i]);
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < 64; i++) acc += static_cast<double>(c[i][e]) * y[i];
+    part = acc / nq;
+  }
+  const double e2 = block_sum_128(part, red) * sq * sq * p.softmax_scale * p.softmax_scale;
+  if (e == 0) {
+    const double var = e2 - mu * mu;
+    p.theta[bh * p.NB + u] = static_cast<float>(mu + p.tau * sqrt(var > 0.0 ? var : 0.0));
+  }
+}
+
+// 5. Route of Q block u (64 queries, two waves of 32): per group of 64 summaries, route scores by
+// E4M3 MFMA (S^T = Kq Q^T: lane (query l32, half h) register r of tile t holds summary
+// 32t + 8(r/4) + 4h + r%4), the group's mask word (OR over the block's queries, plus sinks), then
+// the summary route's online softmax over the non-exact summaries and its PV by BF16 MFMA
+// (O^T = Vbar^T P^T; k-step (t, s) covers summaries 32t + 16s + {4h + b, 8 + 4h + b}).
+__global__ __launch_bounds__(128) void sol_route(SolParams p) {
+  __shared__ uint32_t word_s[2][2];
+  const int64_t u = blockIdx.x, bh = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, lh = lane >> 5, l32 = lane & 31;
+  const int64_t qrow = 64 * u + 32 * wave + l32;
+  const bool qvalid = qrow < p.N;
+  const float theta = p.theta[bh * p.NB + u];
+  const float sq = p.q_scale[bh * p.NB + u];
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  v8i qop[2];
+#pragma unroll
+  for (int c = 0; c < 2; c++) {
+    const uint4* g = reinterpret_cast<const uint4*>(p.q8 + (bh * p.N64 + qrow) * kHeadDim + 64 * c + 32 * lh);
+    const uint4 a = g[0], b = g[1];  // rows past N are code 0 (row < N64)
+    qop[c][0] = a.x; qop[c][1] = a.y; qop[c][2] = a.z; qop[c][3] = a.w;
+    qop[c][4] = b.x; qop[c][5] = b.y; qop[c][6] = b.z; qop[c][7] = b.w;
+  }
+  v16f oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) oacc[dt][r] = 0.0f;
+  float m_run = -INFINITY;  // log2 units
+  float l_part = 0.0f;
+
+  for (int64_t g = 0; g < p.NBg; g++) {
+    const float cs = sq * p.kq_scale[bh * p.NBg + g] * p.softmax_scale;
+    float x[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      v8i kop[2];
+      const int64_t krow = 64 * g + 32 * t + l32;
+#pragma unroll
+      for (int c = 0; c < 2; c++) {
+        const uint4* gk = reinterpret_cast<const uint4*>(p.kq8 + (bh * p.NBp + krow) * kHeadDim + 64 * c + 32 * lh);
+        const uint4 a = gk[0], b = gk[1];
+        kop[c][0] = a.x; kop[c][1] = a.y; kop[c][2] = a.z; kop[c][3] = a.w;
+        kop[c][4] = b.x; kop[c][5] = b.y; kop[c][6] = b.z; kop[c][7] = b.w;
+      }
+      v16f z;
+#pragma unroll
+      for (int r = 0; r < 16; r++) z[r] = 0.0f;
+      v16f acc = mfma_f8(kop[0], qop[0], z);
+      acc = mfma_f8(kop[1], qop[1], acc);
+#pragma unroll
+      for (int r = 0; r < 16; r++) x[t][r] = acc[r] * cs;
+    }
+    // mask bits of this lane's query: bit (summary - 64g)
+    uint32_t lo_bits = 0, hi_bits = 0;
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int js = 32 * t + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const bool hit = qvalid && 64 * g + js < p.NB && x[t][r] >= theta;
+        if (js < 32) lo_bits |= hit ? (1u << js) : 0u;
+        else hi_bits |= hit ? (1u << (js - 32)) : 0u;
+      }
+    for (int off = 32; off >= 1; off >>= 1) {
+      lo_bits |= __shfl_xor(lo_bits, off, 64);
+      hi_bits |= __shfl_xor(hi_bits, off, 64);
+    }
+    if (lane == 0) {
+      word_s[wave][0] = lo_bits;
+      word_s[wave][1] = hi_bits;
+    }
+    __syncthreads();
+    uint64_t word = (static_cast<uint64_t>(word_s[0][1] | word_s[1][1]) << 32) | (word_s[0][0] | word_s[1][0]);
+    __syncthreads();
+    const int64_t sink_end = min<int64_t>(static_cast<int64_t>(p.sink_blocks), p.NB) - 64 * g;
+    if (sink_end > 0) word |= sink_end >= 64 ? ~0ull : ((1ull << sink_end) - 1ull);
+    if (threadIdx.x == 0) p.mask[(bh * p.NB + u) * p.W + g] = word;
+
+    // summary route over the non-exact summaries of the group
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int js = 32 * t + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int64_t j = 64 * g + js;
+        const bool summ = j < p.NB && ((word >> js) & 1ull) == 0ull;
+        const float n = static_cast<float>(min<int64_t>(64, p.N - 64 * j));
+        x[t][r] = summ ? __builtin_fmaf(x[t][r], kLog2e, __log2f(n)) : -INFINITY;
+        mloc = fmaxf(mloc, x[t][r]);
+      }
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+      mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float m_new = fmaxf(m_run, mloc);
+    if (m_new == -INFINITY) continue;  // nothing to add yet (uniform per query row)
+    const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.0f;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float pv = __builtin_amdgcn_exp2f(x[t][r] - m_new);
+        psum += pv;
+        pb[t][r >> 3][r & 7] = static_cast<__bf16>(pv);
+      }
+    l_part = alpha * l_part + psum;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int s = 0; s < 2; s++)
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+          const uint16_t* vrow = p.vsumT + (bh * kHeadDim + 32 * dt + l32) * p.NBp + 64 * g + 32 * t + 16 * s + 4 * lh;
+          const uint2 a0 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + 8);
+          const uint32_t w4[4] = {a0.x, a0.y, a1.x, a1.y};
+          bf16x8 av;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            av[2 * q] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w4[q] & 0xFFFFu));
+            av[2 * q + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w4[q] >> 16));
+          }
+          oacc[dt] = mfma_bf16(av, pb[t][s], oacc[dt]);
+        }
+  }
+
+  // epilogue: the summary route's normalised output (piece 1) and log2 of its weight, in the
+  // units of the exact route (S-scaled row sums)
+  if (!qvalid) return;
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+  const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  float* orow = p.o_part + (bh * p.N + qrow) * kHeadDim;
+  const bool any = m_run > -INFINITY;
+  const float inv_l = any ? 1.0f / l_tot : 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; g4++) {
+      const int d0 = 32 * dt + 8 * g4 + 4 * lh;
+      float4 o;
+      o.x = oacc[dt][4 * g4 + 0] * inv_l;
+      o.y = oacc[dt][4 * g4 + 1] * inv_l;
+      o.z = oacc[dt][4 * g4 + 2] * inv_l;
+      o.w = oacc[dt][4 * g4 + 3] * inv_l;
+      *reinterpret_cast<float4*>(orow + d0) = o;
+    }
+  if (lh == 0) p.lse[bh * p.N + qrow] = any ? m_run + __log2f(l_tot) + p.log2S : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_sol(const SolParams& p, hipStream_t stream) {
+  const unsigned bh = static_cast<unsigned>(p.B * p.H);
+  hipLaunchKernelGGL(sol_summaries, dim3(static_cast<unsigned>(p.NBp), bh), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sol_kquant, dim3(static_cast<unsigned>(p.NBg), bh), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sol_kmoments, dim3(bh, kHeadDim / 8), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sol_theta, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sol_route, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace fp8attn

@@ -247,6 +247,56 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
                                void* out, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * fp8attn_sol_forward — Sol routing attention (TeleFuser blog "FP8 Sol-Attn", sections "Sol
+ * Routing" and "SM90 CuTe Mainloop") on the output of fp8attn_quantize_qkv (layout order, no
+ * V-Smooth, no gathers needed). 64-token Q and KV blocks (NB = ceil(N / 64)):
+ *   summaries   kbar_j = fl32(fl32(sum_t decode(K8) * s_k,j) / n_j), vbar_j likewise with the
+ *               V channel scales, rounded to BF16 (n_j valid keys of block j);
+ *   route keys  the K summaries quantised like K per group of 64 summaries (amax / 448);
+ *   threshold   per Q block u: theta_u = mu + tau * sigma, the mean and standard deviation of
+ *               the block's route scores over all (valid query, KV block) pairs from second
+ *               moments: mu = ss qbar . m, E2 = ss^2 sum_de Mq[d,e] Mk[d,e] (estimator 1, exact)
+ *               or ss^2 sum_d Mq[d,d] Mk[d,d] (estimator 0, diag), sigma^2 = E2 - mu^2; m, Mk:
+ *               mean and second moment of the K summaries, Mq: the block's query second moment;
+ *   route       r_ij = (q8_i . kq8_j) s_q s_kq softmax_scale on the matrix cores; KV block j is
+ *               exact for Q block u if j < sink_blocks or some valid query of u has r_ij >=
+ *               theta_u; decisions within the matrix cores' rounding of theta may go either way;
+ *   exact route the fp8attn_forward loop over the exact blocks in kv_order (own running max);
+ *   summary     the other blocks as n_j copies of (kbar_j, vbar_j), scored by r_ij, weights in
+ *               BF16 on the matrix cores;
+ *   output      the two routes merged by log-sum-exp, + v_shift, BF16.
+ * Arguments (device pointers unless noted):
+ *   q8 .. v_scale  as written by fp8attn_quantize_qkv (vsmooth = 0).
+ *   opts       host pointer: softmax_scale > 0, p_scale in (0, 448], kv_order, pcast, tau
+ *              (finite), estimator 0/1, sink_blocks >= 0, v_shift (FP32 [B*H, D], 16-byte
+ *              aligned) or NULL.
+ *   out        bf16 [B, N, H, D].
+ *   route_mask uint64 [B*H, NB, W] (W = ceil(NB / 64); bit j % 64 of word j / 64 = KV block j
+ *              exact for Q block u) or NULL.
+ *   workspace  fp8attn_sol_workspace_bytes(B, N, H, D) bytes, 16-byte aligned.
+ * Errors: EINVAL on bad pointers/sizes/options; EUNSUPPORTED on D != 128 or a device other
+ *   than gfx950.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct fp8attn_sol_opts {
+  float softmax_scale;
+  float p_scale;
+  fp8attn_kv_order kv_order;
+  fp8attn_pcast pcast;
+  float tau;
+  int32_t estimator;
+  int32_t sink_blocks;
+  const float* v_shift;
+} fp8attn_sol_opts;
+
+size_t fp8attn_sol_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D);
+
+fp8attn_status fp8attn_sol_forward(int32_t B, int32_t N, int32_t H, int32_t D, const uint8_t* q8,
+                                   const uint8_t* k8, const uint8_t* v8t, const float* q_scale,
+                                   const float* k_scale, const float* v_scale,
+                                   const fp8attn_sol_opts* opts, void* out, uint64_t* route_mask,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fp8attn_status_string(fp8attn_status s);
 

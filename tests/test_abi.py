@@ -183,3 +183,34 @@ def test_cluster_rejects_bad_arguments(m):
     assert call(v=None) == EINVAL and call(v=_fake(0x10008)) == EINVAL
     assert call(perm=None) == EINVAL and call(lab=_fake(0x10002)) == EINVAL
     assert call(ws=None) == EINVAL and call(wsb=need - 1) == EINVAL
+
+
+def test_sol_rejects_bad_arguments(m):
+    L = m.lib()
+    need = L.fp8attn_sol_workspace_bytes(1, 1000, 2, 128)
+    assert need > 2 * 2 * 1000 * 128 * 4
+    assert L.fp8attn_sol_workspace_bytes(1, 1000, 2, 64) == 0
+    P = [_fake()] * 6
+
+    def call(D=128, ws=need, mask=None, **kw):
+        o = dict(softmax_scale=0.088, p_scale=256.0, kv_order=1, pcast=0, tau=3.0, estimator=0,
+                 sink_blocks=1, v_shift=None)
+        o.update(kw)
+        opts = m._SolOpts(o["softmax_scale"], o["p_scale"], o["kv_order"], o["pcast"], o["tau"],
+                          o["estimator"], o["sink_blocks"], o["v_shift"])
+        return L.fp8attn_sol_forward(1, 1000, 2, D, *P, ctypes.byref(opts), _fake(), mask,
+                                     _fake(), ctypes.c_size_t(ws), None)
+
+    assert call(D=64) == 2
+    assert call(ws=need - 1) == 1
+    assert call(estimator=2) == 1
+    assert call(sink_blocks=-1) == 1
+    assert call(tau=float("nan")) == 1
+    assert call(tau=float("inf")) == 1
+    assert call(p_scale=449.0) == 1
+    assert call(softmax_scale=0.0) == 1
+    assert call(kv_order=2) == 1
+    assert call(mask=_fake(0x10004)) == 1
+    assert call(v_shift=_fake(0x10004)) == 1
+    assert L.fp8attn_sol_forward(1, 1000, 2, 128, *P, None, _fake(), None, _fake(),
+                                 ctypes.c_size_t(need), None) == 1

@@ -460,6 +460,64 @@ def test_attention_split_kv_sink_underflow(m, orc, delta, S, reverse):
     assert np.all(np.abs(g - o) <= 1e-4 * N * N + 1e-3 * o)
 
 
+# ------------------------------------------------------------------------------------------
+# Sol routing (exact / summary routes chosen per 64-token Q block)
+# ------------------------------------------------------------------------------------------
+def _check_route_mask(orc, gpu_words, ref, NB):
+    """Every bit the oracle decides beyond the device's evaluation error must match; flagged
+    (ambiguous) bits may go either way. Returns the device mask as the oracle's uint64 words."""
+    words = np.ascontiguousarray(gpu_words).view(np.uint64)
+    g = orc.mask_bits(words, NB)
+    r = orc.mask_bits(ref["mask"], NB)
+    a = orc.mask_bits(ref["amb_mask"], NB)
+    bad = (g != r) & ~a
+    say(f"route: {g.mean():.3f} of blocks exact, {int(a.sum())} ambiguous, "
+        f"{int(((g != r) & a).sum())} decided the other way, {int(bad.sum())} wrong")
+    assert not bad.any()
+    return words
+
+
+@pytest.mark.parametrize("N,H,tau,est,sinks,reverse,expcast", [
+    (1000, 2, 2.0, 0, 1, True, False), (2500, 2, 3.0, 1, 2, False, False),
+    (300, 1, 1.0, 1, 0, True, False), (777, 2, 2.5, 0, 1, True, True),
+    (4160, 2, 3.0, 0, 1, True, False), (1000, 2, -50.0, 0, 0, True, False),
+    (1000, 2, 50.0, 0, 0, False, False)])
+def test_sol_small(m, orc, N, H, tau, est, sinks, reverse, expcast):
+    say("sol", N, H, tau, est, sinks, reverse, expcast)
+    q, k, v = workloads.make_qkv(1, N, H, seed=90 + N, kind="channel_outliers")
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb)
+    ref_sol = orc.sol_prepare(ref_q, tau=tau, estimator=est, sink_blocks=sinks)
+    qz = _gpu_quantize(m, q, k, v)
+    out, mask = m.sol_forward(qz, tau=tau, estimator=est, sink_blocks=sinks, kv_order=int(reverse),
+                              pcast=m.FP8ATTN_PCAST_EXPCAST if expcast else m.FP8ATTN_PCAST_RNE,
+                              return_mask=True)
+    torch.cuda.synchronize()
+    NB = -(-N // 64)
+    sol = dict(ref_sol)
+    sol["mask"] = _check_route_mask(orc, _np(mask), ref_sol, NB)
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=reverse, expcast=expcast,
+                                          return_amb=True, sol=sol)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, f"sol tau={tau}", amb)
+
+
+def test_sol_with_smoothing(m, orc):
+    """Sequence-mean smoothing under Sol: K shifted before the summaries, V shift restored."""
+    say("sol + smoothing")
+    N, H = 1500, 2
+    q, k, v = workloads.make_qkv(1, N, H, seed=97, kind="channel_offset")
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb, smoothing=2, v_bias_correction=True)
+    ref_sol = orc.sol_prepare(ref_q, tau=2.5, estimator=1, sink_blocks=1)
+    qz = _gpu_quantize(m, q, k, v, smoothing=2, bias=True)
+    out, mask = m.sol_forward(qz, tau=2.5, estimator=1, sink_blocks=1, return_mask=True)
+    torch.cuda.synchronize()
+    sol = dict(ref_sol)
+    sol["mask"] = _check_route_mask(orc, _np(mask), ref_sol, -(-N // 64))
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=True, return_amb=True, sol=sol)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, "sol smoothing", amb)
+
+
 @pytest.mark.parametrize("delta,S,reverse", [(7, 1.0, False), (7, 256.0, True), (9, 256.0, False)])
 def test_underflow_counter(m, orc, delta, S, reverse):
     say("underflow", delta, S, reverse)
