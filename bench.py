@@ -83,6 +83,11 @@ def main():
                          "sharded run); 0 = all")
     ap.add_argument("--kv-splits", default="1",
                     help="split-KV pieces: 1 (none), 2..16, or auto (dense workloads)")
+    ap.add_argument("--sol-tau", type=float, default=None,
+                    help="Sol routing with this threshold multiplier (dense workloads)")
+    ap.add_argument("--sol-estimator", type=int, default=0, choices=(0, 1),
+                    help="Sol threshold estimator: 0 diag, 1 exact")
+    ap.add_argument("--sol-sinks", type=int, default=1, help="Sol: leading KV blocks always exact")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -107,6 +112,13 @@ def main():
     if sparse and kv_splits > 1:
         print("split-KV is for dense workloads", file=sys.stderr)
         sys.exit(2)
+    sol = args.sol_tau is not None
+    if sol and (sparse or vs or kv_splits != 1):
+        print("Sol routing runs on dense workloads without V-Smooth or split-KV", file=sys.stderr)
+        sys.exit(2)
+    if sol:
+        desc += (f"; Sol routing (tau {args.sol_tau}, {'exact' if args.sol_estimator else 'diag'} "
+                 f"estimator, {args.sol_sinks} sink blocks)")
     if args.smoothing == 2 and vs:
         print("--smoothing 2 shifts V and cannot be combined with V-Smooth", file=sys.stderr)
         sys.exit(2)
@@ -156,15 +168,22 @@ def main():
     out = torch.zeros((B, n_out, H, D), dtype=torch.bfloat16, device=dev)
     pcast = fa.FP8ATTN_PCAST_EXPCAST if vs else fa.FP8ATTN_PCAST_RNE
 
+    ws_sol = fa.sol_workspace(B, n_layout, H, dev) if sol else None
+
     def step(ev=None):
         fa.quantize_qkv(qd, kd, vd, perm_q=perm_q, perm_kv=perm_kv, vsmooth=vs, n_layout=n_layout,
                         out=qz, workspace=ws_q, smoothing=args.smoothing,
                         v_bias_correction=args.bias_correction)
         if ev is not None:
             ev[0].record()
-        fa.forward(qz, p_scale=256.0, kv_order=fa.FP8ATTN_KV_REVERSE, pcast=pcast, sparse=sp,
-                   out_rows=out_rows, n_out=n_out, out=out, workspace=ws_f,
-                   kv_splits=1 if sparse else kv_splits)
+        if sol:
+            fa.sol_forward(qz, tau=args.sol_tau, estimator=args.sol_estimator,
+                           sink_blocks=args.sol_sinks, p_scale=256.0, kv_order=fa.FP8ATTN_KV_REVERSE,
+                           pcast=pcast, out=out, workspace=ws_sol)
+        else:
+            fa.forward(qz, p_scale=256.0, kv_order=fa.FP8ATTN_KV_REVERSE, pcast=pcast, sparse=sp,
+                       out_rows=out_rows, n_out=n_out, out=out, workspace=ws_f,
+                       kv_splits=1 if sparse else kv_splits)
         if ev is not None:
             ev[1].record()
 
@@ -192,12 +211,31 @@ def main():
         rp, ci = lay["row_ptr"], lay["col_idx"]
         pairs = sum(int(tl[u]) * int(tl[ci[rp[u]:rp[u + 1]]].sum()) for u in range(len(tl)))
         attn_flops = 4.0 * pairs * D * H * B   # algorithmic work of the sparse kernel
+    elif sol:
+        # algorithmic work of Sol: exact-route pairs (4D each), the route QK of every query with
+        # every summary (2D) and the summary PV over the non-exact summaries (2D)
+        _, mask = fa.sol_forward(qz, tau=args.sol_tau, estimator=args.sol_estimator,
+                                 sink_blocks=args.sol_sinks, p_scale=256.0, kv_order=fa.FP8ATTN_KV_REVERSE,
+                                 pcast=pcast, out=out, workspace=ws_sol, return_mask=True)
+        words = mask.cpu().numpy().view(np.uint64)
+        NBk = -(-N // 64)
+        bits = ((words[..., :, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).astype(bool)
+        bits = bits.reshape(*words.shape[:-1], -1)[..., :NBk]          # [B, H, NB(q), NB(k)]
+        rows_q = np.minimum(64, N - 64 * np.arange(NBk))
+        keys_k = np.minimum(64, N - 64 * np.arange(NBk))
+        exact_pairs = float(np.einsum("bhuj,u,j->", bits.astype(np.float64), rows_q, keys_k))
+        summ_rows = float(np.einsum("bhuj,u->", (~bits).astype(np.float64), rows_q))
+        attn_flops = 4.0 * exact_pairs * D + 2.0 * N * NBk * D * B * H + 2.0 * summ_rows * D
+        sol_exact_frac = float(bits.mean())
+        log(f"Sol: {100 * sol_exact_frac:.2f}% of (Q block, KV block) pairs exact")
     else:
         attn_flops = dense_flops
     achieved = attn_flops / (ms_attn * 1e-3) / 1e12
     log(f"step {ms_step:.3f} ms, attention kernel {ms_attn:.3f} ms, quantize {ms_step - ms_attn:.3f} ms")
 
-    traffic = MEASURED_TRAFFIC.get((code_sha(ATTN_SRC), args.workload))
+    # the counters were taken on the workload's default configuration only
+    default_cfg = not (args.heads or sol or args.smoothing or args.kv_splits != "1")
+    traffic = MEASURED_TRAFFIC.get((code_sha(ATTN_SRC), args.workload)) if default_cfg else None
 
     result = {
         "metric": METRIC,
@@ -215,7 +253,9 @@ def main():
         "config": {"workload": desc, "global_batch": B, "seq_len": N, "heads": H, "head_dim": D,
                    "parallelism": "none (one GPU)", "name": args.workload,
                    "smoothing": args.smoothing, "v_bias_correction": args.bias_correction,
-                   "kv_splits": args.kv_splits},
+                   "kv_splits": args.kv_splits,
+                   "sol": None if not sol else {"tau": args.sol_tau, "estimator": args.sol_estimator,
+                                                 "sink_blocks": args.sol_sinks}},
         "quantize_ms": round(ms_step - ms_attn, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
@@ -225,6 +265,10 @@ def main():
 
     if cluster_ms is not None:
         result["vsmooth_cluster_ms_once"] = round(cluster_ms, 3)
+    if sol:
+        result["sol_exact_fraction"] = round(sol_exact_frac, 5)
+        result["roofline"]["kernel"] = "fp8attn_sol_forward (all kernels)"
+        result["roofline"]["traffic"] = None
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, cfg_name, sparse, vs)
     print(json.dumps(result), flush=True)

@@ -79,7 +79,7 @@ struct SolParams {
   const float* k_scale;
   const float* v_scale;
   float* ksum;       // [B*H, NB, 128] K summaries (FP32)
-  uint16_t* vsumT;   // [B*H, 128, NBp] V summaries (bf16), summary-contiguous, zero padded
+  uint16_t* vsumT;   // V summaries (bf16, B*H*NBp*128 values) in the summary PV's operand order
   uint8_t* kq8;      // [B*H, NBp, 128] quantised K summaries
   float* kq_scale;   // [B*H, NBg]
   double* mk;        // [B*H, 128] mean of the summaries

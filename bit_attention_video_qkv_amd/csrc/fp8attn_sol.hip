@@ -9,7 +9,7 @@
 // Readings (the page leaves these open):
 //  * summaries are block means of the dequantised E4M3 K and V:
 //      kbar = fl32(fl32(sum_t decode(K8) * s_k) / n_j)   (the code sum is exact in FP32),
-//      vbar likewise with the channel scale, stored as BF16;
+//      vbar likewise with the channel scale, stored as BF16 (in the summary PV's operand order);
 //  * the K summaries are quantised like K, per group of 64 summaries (scale = amax / 448);
 //  * mu and sigma are the mean and standard deviation of the Q block's route scores over all
 //    pairs (valid query, KV block), from second moments: mu = ss * qbar . m,
@@ -25,7 +25,8 @@
 //   sol_kquant     grid (NBg, B*H)         quantised K summaries
 //   sol_kmoments   grid (B*H, 16)          mean and second moment of the summaries (FP64)
 //   sol_theta      grid (NB, B*H)          threshold per Q block
-//   sol_route      grid (NB, B*H), 2 waves route QK (E4M3 MFMA), mask, summary route (BF16 MFMA)
+//   sol_mask       grid (NB, B*H), 2 waves route QK (E4M3 MFMA) -> exact-block mask
+//   sol_summary    grid (ceil(N/128), B*H) route QK again, summary route (BF16 MFMA)
 #include "fp8attn_common.h"
 #include "fp8attn_internal.h"
 
@@ -45,23 +46,43 @@ __device__ __forceinline__ v16f mfma_bf16(const bf16x8& a, const bf16x8& b, cons
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// V summaries are stored in the order the summary PV reads them: for (b*h, group g, tile t,
+// k-step s, channel tile dt), 64 lanes x 8 BF16 values, lane 32h + l32 holding channel
+// 32dt + l32 and summaries 32t + 16s + {4h + 0..3, 8 + 4h + 0..3} (element e: summary
+// 32t + 16s + 8(e/4) + 4h + e%4), so each operand is one 16-byte load per lane.
+__device__ __forceinline__ int64_t vsum_index(const SolParams& p, int64_t bh, int64_t j, int d) {
+  const int64_t g = j >> 6;
+  const int js = static_cast<int>(j & 63), t = js >> 5, s = (js >> 4) & 1, rem = js & 15;
+  const int h = (rem >> 2) & 1, e = 4 * (rem >> 3) + (rem & 3);
+  const int dt = d >> 5, lane = 32 * h + (d & 31);
+  return ((((bh * p.NBg + g) * 2 + t) * 2 + s) * 4 + dt) * 512 + lane * 8 + e;
+}
+
 // 1. Summaries of KV block j (grid over the padded count NBp: padding summaries get a zero V
 // summary, which the summary PV multiplies by p = 0). Threads 0..127: K channel d; 128..255: V
 // channel d. Rows and positions past N hold code 0 (the quantisation contract), so all 64 are
 // summed.
 __global__ __launch_bounds__(256) void sol_summaries(SolParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t kt[64][kHeadDim + 16];
   const int64_t j = blockIdx.x, bh = blockIdx.y;
   if (j >= p.NB) {
-    if (threadIdx.x >= kHeadDim) p.vsumT[(bh * kHeadDim + threadIdx.x - kHeadDim) * p.NBp + j] = 0;
+    if (threadIdx.x >= kHeadDim) p.vsumT[vsum_index(p, bh, j, threadIdx.x - kHeadDim)] = 0;
     return;
   }
+  // the K tile (64 rows x 128 bytes) through LDS with 16-byte loads
+  const uint4* ksrc = reinterpret_cast<const uint4*>(p.k8 + (bh * p.N64 + 64 * j) * kHeadDim);
+#pragma unroll
+  for (int c = 0; c < 2; c++) {
+    const int L = c * 256 + threadIdx.x;  // 512 chunks of 16 bytes
+    *reinterpret_cast<uint4*>(&kt[L >> 3][(L & 7) * 16]) = ksrc[L];
+  }
+  __syncthreads();
   const int n = static_cast<int>(min<int64_t>(64, p.N - 64 * j));
   if (threadIdx.x < kHeadDim) {
     const int d = threadIdx.x;
-    const uint8_t* kp = p.k8 + (bh * p.N64 + 64 * j) * kHeadDim + d;
     float s = 0.0f;
 #pragma unroll 16
-    for (int r = 0; r < 64; r++) s += e4m3_decode(kp[r * kHeadDim]);
+    for (int r = 0; r < 64; r++) s += e4m3_decode(kt[r][d]);
     const float prod = s * p.k_scale[bh * p.NB + j];
     p.ksum[(bh * p.NB + j) * kHeadDim + d] = __fdiv_rn(prod, static_cast<float>(n));
   } else {
@@ -78,7 +99,7 @@ __global__ __launch_bounds__(256) void sol_summaries(SolParams p) {
         for (int b = 0; b < 4; b++) s += e4m3_decode((ws[q] >> (8 * b)) & 0xFFu);
     }
     const float prod = s * p.v_scale[bh * kHeadDim + d];
-    p.vsumT[(bh * kHeadDim + d) * p.NBp + j] = f32_to_bf16_rne(__fdiv_rn(prod, static_cast<float>(n)));
+    p.vsumT[vsum_index(p, bh, j, d)] = f32_to_bf16_rne(__fdiv_rn(prod, static_cast<float>(n)));
   }
 }
 
@@ -168,8 +189,17 @@ __global__ __launch_bounds__(128) void sol_theta(SolParams p) {
   const int64_t u = blockIdx.x, bh = blockIdx.y;
   const int e = threadIdx.x;
   const int nq = static_cast<int>(min<int64_t>(64, p.N - 64 * u));
-  const uint8_t* qb = p.q8 + (bh * p.N64 + 64 * u) * kHeadDim;
-  for (int i = 0; i < 64; i++) c[i][e] = i < nq ? e4m3_decode(qb[i * kHeadDim + e]) : 0.0f;
+  const uint4* qb = reinterpret_cast<const uint4*>(p.q8 + (bh * p.N64 + 64 * u) * kHeadDim);
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int L = k * 128 + e;  // 512 chunks of 16 bytes: row L / 8, bytes 16 * (L % 8) ..
+    const int i = L >> 3, d0 = (L & 7) * 16;
+    const uint4 w = qb[L];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 16; q++)
+      c[i][d0 + q] = i < nq ? e4m3_decode((ws[q >> 2] >> (8 * (q & 3))) & 0xFFu) : 0.0f;
+  }
   __syncthreads();
   const double sq = p.q_scale[bh * p.NB + u];
   double csum = 0.0, csq = 0.0;
@@ -205,12 +235,44 @@ __global__ __launch_bounds__(128) void sol_theta(SolParams p) {
   }
 }
 
-// 5. Route of Q block u (64 queries, two waves of 32): per group of 64 summaries, route scores by
-// E4M3 MFMA (S^T = Kq Q^T: lane (query l32, half h) register r of tile t holds summary
-// 32t + 8(r/4) + 4h + r%4), the group's mask word (OR over the block's queries, plus sinks), then
-// the summary route's online softmax over the non-exact summaries and its PV by BF16 MFMA
-// (O^T = Vbar^T P^T; k-step (t, s) covers summaries 32t + 16s + {4h + b, 8 + 4h + b}).
-__global__ __launch_bounds__(128) void sol_route(SolParams p) {
+// Route scores of 32 queries (this wave) against the 64 quantised summaries of group g:
+// S^T = Kq Q^T; lane (query l32, half h) register r of tile t holds summary 32t + 8(r/4) + 4h + r%4.
+__device__ __forceinline__ void route_scores(const SolParams& p, int64_t bh, int64_t g, const v8i (&qop)[2],
+                                             int lh, int l32, float cs, float (&x)[2][16]) {
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    v8i kop[2];
+    const int64_t krow = 64 * g + 32 * t + l32;
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      const uint4* gk = reinterpret_cast<const uint4*>(p.kq8 + (bh * p.NBp + krow) * kHeadDim + 64 * c + 32 * lh);
+      const uint4 a = gk[0], b = gk[1];
+      kop[c][0] = a.x; kop[c][1] = a.y; kop[c][2] = a.z; kop[c][3] = a.w;
+      kop[c][4] = b.x; kop[c][5] = b.y; kop[c][6] = b.z; kop[c][7] = b.w;
+    }
+    v16f z;
+#pragma unroll
+    for (int r = 0; r < 16; r++) z[r] = 0.0f;
+    v16f acc = mfma_f8(kop[0], qop[0], z);
+    acc = mfma_f8(kop[1], qop[1], acc);
+#pragma unroll
+    for (int r = 0; r < 16; r++) x[t][r] = acc[r] * cs;
+  }
+}
+
+__device__ __forceinline__ void load_q_operand(const SolParams& p, int64_t bh, int64_t qrow, int lh, v8i (&qop)[2]) {
+#pragma unroll
+  for (int c = 0; c < 2; c++) {
+    const uint4* g = reinterpret_cast<const uint4*>(p.q8 + (bh * p.N64 + qrow) * kHeadDim + 64 * c + 32 * lh);
+    const uint4 a = g[0], b = g[1];  // rows past N are code 0 (row < N64)
+    qop[c][0] = a.x; qop[c][1] = a.y; qop[c][2] = a.z; qop[c][3] = a.w;
+    qop[c][4] = b.x; qop[c][5] = b.y; qop[c][6] = b.z; qop[c][7] = b.w;
+  }
+}
+
+// 5. Exact-block mask of Q block u (64 queries, two waves of 32): per group of 64 summaries, the
+// route scores against theta_u, ORed over the block's valid queries, plus the sinks.
+__global__ __launch_bounds__(128) void sol_mask(SolParams p) {
   __shared__ uint32_t word_s[2][2];
   const int64_t u = blockIdx.x, bh = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -219,47 +281,11 @@ __global__ __launch_bounds__(128) void sol_route(SolParams p) {
   const bool qvalid = qrow < p.N;
   const float theta = p.theta[bh * p.NB + u];
   const float sq = p.q_scale[bh * p.NB + u];
-  constexpr float kLog2e = 1.4426950408889634f;
-
   v8i qop[2];
-#pragma unroll
-  for (int c = 0; c < 2; c++) {
-    const uint4* g = reinterpret_cast<const uint4*>(p.q8 + (bh * p.N64 + qrow) * kHeadDim + 64 * c + 32 * lh);
-    const uint4 a = g[0], b = g[1];  // rows past N are code 0 (row < N64)
-    qop[c][0] = a.x; qop[c][1] = a.y; qop[c][2] = a.z; qop[c][3] = a.w;
-    qop[c][4] = b.x; qop[c][5] = b.y; qop[c][6] = b.z; qop[c][7] = b.w;
-  }
-  v16f oacc[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) oacc[dt][r] = 0.0f;
-  float m_run = -INFINITY;  // log2 units
-  float l_part = 0.0f;
-
+  load_q_operand(p, bh, qrow, lh, qop);
   for (int64_t g = 0; g < p.NBg; g++) {
-    const float cs = sq * p.kq_scale[bh * p.NBg + g] * p.softmax_scale;
     float x[2][16];
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-      v8i kop[2];
-      const int64_t krow = 64 * g + 32 * t + l32;
-#pragma unroll
-      for (int c = 0; c < 2; c++) {
-        const uint4* gk = reinterpret_cast<const uint4*>(p.kq8 + (bh * p.NBp + krow) * kHeadDim + 64 * c + 32 * lh);
-        const uint4 a = gk[0], b = gk[1];
-        kop[c][0] = a.x; kop[c][1] = a.y; kop[c][2] = a.z; kop[c][3] = a.w;
-        kop[c][4] = b.x; kop[c][5] = b.y; kop[c][6] = b.z; kop[c][7] = b.w;
-      }
-      v16f z;
-#pragma unroll
-      for (int r = 0; r < 16; r++) z[r] = 0.0f;
-      v16f acc = mfma_f8(kop[0], qop[0], z);
-      acc = mfma_f8(kop[1], qop[1], acc);
-#pragma unroll
-      for (int r = 0; r < 16; r++) x[t][r] = acc[r] * cs;
-    }
-    // mask bits of this lane's query: bit (summary - 64g)
+    route_scores(p, bh, g, qop, lh, l32, sq * p.kq_scale[bh * p.NBg + g] * p.softmax_scale, x);
     uint32_t lo_bits = 0, hi_bits = 0;
 #pragma unroll
     for (int t = 0; t < 2; t++)
@@ -279,13 +305,49 @@ __global__ __launch_bounds__(128) void sol_route(SolParams p) {
       word_s[wave][1] = hi_bits;
     }
     __syncthreads();
-    uint64_t word = (static_cast<uint64_t>(word_s[0][1] | word_s[1][1]) << 32) | (word_s[0][0] | word_s[1][0]);
+    if (threadIdx.x == 0) {
+      uint64_t word = (static_cast<uint64_t>(word_s[0][1] | word_s[1][1]) << 32) | (word_s[0][0] | word_s[1][0]);
+      const int64_t sink_end = min<int64_t>(static_cast<int64_t>(p.sink_blocks), p.NB) - 64 * g;
+      if (sink_end > 0) word |= sink_end >= 64 ? ~0ull : ((1ull << sink_end) - 1ull);
+      p.mask[(bh * p.NB + u) * p.W + g] = word;
+    }
     __syncthreads();
-    const int64_t sink_end = min<int64_t>(static_cast<int64_t>(p.sink_blocks), p.NB) - 64 * g;
-    if (sink_end > 0) word |= sink_end >= 64 ? ~0ull : ((1ull << sink_end) - 1ull);
-    if (threadIdx.x == 0) p.mask[(bh * p.NB + u) * p.W + g] = word;
+  }
+}
 
-    // summary route over the non-exact summaries of the group
+// 6. Summary route: per query, online softmax over the non-exact summaries (scored by the route
+// score, weighted by the block length) and its PV by BF16 MFMA (O^T = Vbar^T P^T; k-step (t, s)
+// covers summaries 32t + 16s + {4h + b, 8 + 4h + b}). Every wave works alone (32 queries of Q
+// block qrow / 64; four waves per workgroup).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sol_summary(SolParams p) {
+  const int64_t bh = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, lh = lane >> 5, l32 = lane & 31;
+  const int64_t q32 = static_cast<int64_t>(blockIdx.x) * 4 + wave;  // 32-query slice
+  if (q32 * 32 >= p.N) return;
+  const int64_t u = q32 >> 1;
+  const int64_t qrow = 32 * q32 + l32;
+  const bool qvalid = qrow < p.N;
+  const float sq = p.q_scale[bh * p.NB + u];
+  const uint64_t* mrow = p.mask + (bh * p.NB + u) * p.W;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  v8i qop[2];
+  load_q_operand(p, bh, qrow, lh, qop);
+  v16f oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) oacc[dt][r] = 0.0f;
+  float m_run = -INFINITY;  // log2 units
+  float l_part = 0.0f;
+
+  for (int64_t g = 0; g < p.NBg; g++) {
+    const uint64_t word = mrow[g];
+    const int64_t nsum = min<int64_t>(64, p.NB - 64 * g) - __builtin_popcountll(word);
+    if (nsum <= 0) continue;  // every summary of the group is exact (uniform)
+    float x[2][16];
+    route_scores(p, bh, g, qop, lh, l32, sq * p.kq_scale[bh * p.NBg + g] * p.softmax_scale, x);
     float mloc = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; t++)
@@ -294,8 +356,9 @@ __global__ __launch_bounds__(128) void sol_route(SolParams p) {
         const int js = 32 * t + 8 * (r >> 2) + 4 * lh + (r & 3);
         const int64_t j = 64 * g + js;
         const bool summ = j < p.NB && ((word >> js) & 1ull) == 0ull;
-        const float n = static_cast<float>(min<int64_t>(64, p.N - 64 * j));
-        x[t][r] = summ ? __builtin_fmaf(x[t][r], kLog2e, __log2f(n)) : -INFINITY;
+        // log2 of the block length: 6 for full blocks
+        const float lgn = j == p.NB - 1 ? __log2f(static_cast<float>(p.N - 64 * j)) : 6.0f;
+        x[t][r] = summ ? __builtin_fmaf(x[t][r], kLog2e, lgn) : -INFINITY;
         mloc = fmaxf(mloc, x[t][r]);
       }
     {
@@ -303,7 +366,6 @@ __global__ __launch_bounds__(128) void sol_route(SolParams p) {
       mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
     const float m_new = fmaxf(m_run, mloc);
-    if (m_new == -INFINITY) continue;  // nothing to add yet (uniform per query row)
     const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.0f;
@@ -317,26 +379,20 @@ __global__ __launch_bounds__(128) void sol_route(SolParams p) {
         pb[t][r >> 3][r & 7] = static_cast<__bf16>(pv);
       }
     l_part = alpha * l_part + psum;
+    if (alpha != 1.0f) {
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++)
+      for (int dt = 0; dt < 4; dt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
+        for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
+    }
 #pragma unroll
     for (int t = 0; t < 2; t++)
 #pragma unroll
       for (int s = 0; s < 2; s++)
 #pragma unroll
         for (int dt = 0; dt < 4; dt++) {
-          const uint16_t* vrow = p.vsumT + (bh * kHeadDim + 32 * dt + l32) * p.NBp + 64 * g + 32 * t + 16 * s + 4 * lh;
-          const uint2 a0 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + 8);
-          const uint32_t w4[4] = {a0.x, a0.y, a1.x, a1.y};
-          bf16x8 av;
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            av[2 * q] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w4[q] & 0xFFFFu));
-            av[2 * q + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(w4[q] >> 16));
-          }
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(
+              p.vsumT + ((((bh * p.NBg + g) * 2 + t) * 2 + s) * 4 + dt) * 512 + lane * 8);
           oacc[dt] = mfma_bf16(av, pb[t][s], oacc[dt]);
         }
   }
@@ -380,7 +436,11 @@ hipError_t launch_sol(const SolParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(sol_theta, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sol_route, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(sol_mask, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned slices = static_cast<unsigned>((p.N + 127) / 128);  // four 32-query waves each
+  hipLaunchKernelGGL(sol_summary, dim3(slices, bh), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
