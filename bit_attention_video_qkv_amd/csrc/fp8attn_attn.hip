@@ -81,40 +81,6 @@ __device__ __forceinline__ v8i load_op_lds(const uint8_t* base, int off0, int of
   return r;
 }
 
-// Waits until at most N vector-memory operations of this wave are outstanding (they complete
-// in issue order, so every older global->LDS copy has landed).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// Workgroup barrier without the release/acquire fence of __syncthreads(): that fence makes the
-// compiler wait for every outstanding global->LDS copy, including those meant to stay in flight
-// across the barrier. Callers order their own LDS traffic with explicit waits; the "memory"
-// clobber keeps the compiler from moving memory operations across the barrier.
-__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
-
-// Direct global->LDS copies (each lane: 16 or 4 bytes from gbase + voff to LDS lds_addr + 16 *
-// lane or + 4 * lane). Issued as opaque instructions: the compiler would otherwise treat every
-// later LDS read as possibly overlapping a copy still in flight and drain all of them first,
-// which would cost the copies' prefetch distance. The kernel orders them itself (explicit
-// vmcnt waits and barriers).
-__device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)p));
-}
-// A wave-uniform pointer as an SGPR pair (the copies take their base from scalar registers).
-__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
-  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-__device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(gbase)),
-               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory", "m0");
-}
 __device__ __forceinline__ void copy4_to_lds(const void* gbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(gbase)),
                "s"(__builtin_amdgcn_readfirstlane(lds_addr))

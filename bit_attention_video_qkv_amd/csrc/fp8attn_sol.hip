@@ -25,8 +25,8 @@
 //   sol_kquant     grid (NBg, B*H)         quantised K summaries
 //   sol_kmoments   grid (B*H, 16)          mean and second moment of the summaries (FP64)
 //   sol_theta      grid (NB, B*H)          threshold per Q block
-//   sol_mask       grid (NB, B*H), 2 waves route QK (E4M3 MFMA) -> exact-block mask
-//   sol_summary    grid (ceil(N/128), B*H) route QK again, summary route (BF16 MFMA)
+//   sol_route      grid (ceil(NB/2), B*H), 4 waves: per group of 64 summaries staged in LDS, the
+//                  route QK (E4M3 MFMA), the exact-block mask, the summary route (BF16 MFMA)
 #include "fp8attn_common.h"
 #include "fp8attn_internal.h"
 
@@ -235,31 +235,6 @@ __global__ __launch_bounds__(128) void sol_theta(SolParams p) {
   }
 }
 
-// Route scores of 32 queries (this wave) against the 64 quantised summaries of group g:
-// S^T = Kq Q^T; lane (query l32, half h) register r of tile t holds summary 32t + 8(r/4) + 4h + r%4.
-__device__ __forceinline__ void route_scores(const SolParams& p, int64_t bh, int64_t g, const v8i (&qop)[2],
-                                             int lh, int l32, float cs, float (&x)[2][16]) {
-#pragma unroll
-  for (int t = 0; t < 2; t++) {
-    v8i kop[2];
-    const int64_t krow = 64 * g + 32 * t + l32;
-#pragma unroll
-    for (int c = 0; c < 2; c++) {
-      const uint4* gk = reinterpret_cast<const uint4*>(p.kq8 + (bh * p.NBp + krow) * kHeadDim + 64 * c + 32 * lh);
-      const uint4 a = gk[0], b = gk[1];
-      kop[c][0] = a.x; kop[c][1] = a.y; kop[c][2] = a.z; kop[c][3] = a.w;
-      kop[c][4] = b.x; kop[c][5] = b.y; kop[c][6] = b.z; kop[c][7] = b.w;
-    }
-    v16f z;
-#pragma unroll
-    for (int r = 0; r < 16; r++) z[r] = 0.0f;
-    v16f acc = mfma_f8(kop[0], qop[0], z);
-    acc = mfma_f8(kop[1], qop[1], acc);
-#pragma unroll
-    for (int r = 0; r < 16; r++) x[t][r] = acc[r] * cs;
-  }
-}
-
 __device__ __forceinline__ void load_q_operand(const SolParams& p, int64_t bh, int64_t qrow, int lh, v8i (&qop)[2]) {
 #pragma unroll
   for (int c = 0; c < 2; c++) {
@@ -270,22 +245,103 @@ __device__ __forceinline__ void load_q_operand(const SolParams& p, int64_t bh, i
   }
 }
 
-// 5. Exact-block mask of Q block u (64 queries, two waves of 32): per group of 64 summaries, the
-// route scores against theta_u, ORed over the block's valid queries, plus the sinks.
-__global__ __launch_bounds__(128) void sol_mask(SolParams p) {
-  __shared__ uint32_t word_s[2][2];
-  const int64_t u = blockIdx.x, bh = blockIdx.y;
+// LDS slot of one group of 64 summaries: the quantised K summaries (64 rows of 128 bytes, the
+// 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 7), so that 16 lanes reading 16 rows
+// touch every bank once) and the V summaries in operand order (16 blocks of 64 lanes x 16 bytes).
+constexpr int kSlotK = 64 * kHeadDim;          // 8 KB
+constexpr int kSlotBytes = kSlotK + 64 * kHeadDim * 2;  // + 16 KB
+constexpr int kCopiesPerThread = kSlotBytes / 16 / 256;  // 6
+
+__device__ __forceinline__ int kq_swz(int row) { return (row >> 1) & 7; }
+
+// 5. Route of two Q blocks (workgroup of four waves; waves 2b and 2b+1 hold the 64 queries of Q
+// block 2x + b). Per group of 64 summaries, staged in LDS (double-buffered direct copies):
+//   route scores S^T = Kq Q^T on the E4M3 matrix cores (lane (query l32, half h) register r of
+//   tile t holds summary 32t + 8(r/4) + 4h + r%4); the group's mask word = OR over the Q block's
+//   valid queries of (score >= theta), plus the sinks;
+//   the summary route over the non-exact summaries: online softmax of (score * log2 e +
+//   log2 n_j) and PV with the V summaries on the BF16 matrix cores (O^T = Vbar^T P^T; a lane's
+//   P values of tile t, registers 8s..8s+7, are the B operand of k-step (t, s)).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sol_route(SolParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSlotBytes];
+  __shared__ uint32_t word_s[4][2];
+  const int64_t bh = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, lh = lane >> 5, l32 = lane & 31;
-  const int64_t qrow = 64 * u + 32 * wave + l32;
-  const bool qvalid = qrow < p.N;
-  const float theta = p.theta[bh * p.NB + u];
-  const float sq = p.q_scale[bh * p.NB + u];
+  const int64_t u = 2 * static_cast<int64_t>(blockIdx.x) + (wave >> 1);  // this wave's Q block
+  const bool ublock = u < p.NB;                                          // (uniform per wave)
+  const int64_t qrow = 64 * u + 32 * (wave & 1) + l32;
+  const bool qvalid = ublock && qrow < p.N;
+  const float theta = ublock ? p.theta[bh * p.NB + u] : 0.0f;
+  const float sq = ublock ? p.q_scale[bh * p.NB + u] : 0.0f;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  // copies of group g into slot g & 1: thread t issues chunks L = r * 256 + t (r < 6); the first
+  // 512 chunks are the K summary tile (swizzled), the next 1024 the V summary tile (contiguous)
+  const uint8_t* kq_base = p.kq8 + bh * p.NBp * kHeadDim;
+  const uint8_t* vs_base = reinterpret_cast<const uint8_t*>(p.vsumT) + bh * p.NBg * (64 * kHeadDim * 2);
+  auto stage = [&](int64_t g) {
+    const uint32_t l0 = lds_addr_of(lds + (g & 1) * kSlotBytes);
+#pragma unroll
+    for (int r = 0; r < kCopiesPerThread; r++) {
+      const int L = r * 256 + static_cast<int>(threadIdx.x);
+      const uint32_t ldst = l0 + (r * 256 + wave * 64) * 16;
+      if (r < 2) {
+        const int row = L >> 3, pc = L & 7, c = pc ^ kq_swz(row);
+        copy16_to_lds(kq_base + g * 64 * kHeadDim, static_cast<uint32_t>(row * kHeadDim + c * 16), ldst);
+      } else {
+        copy16_to_lds(vs_base + g * (64 * kHeadDim * 2), static_cast<uint32_t>((L - 512) * 16), ldst);
+      }
+    }
+  };
+
   v8i qop[2];
-  load_q_operand(p, bh, qrow, lh, qop);
+  load_q_operand(p, bh, ublock ? qrow : 0, lh, qop);
+  v16f oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) oacc[dt][r] = 0.0f;
+  float m_run = -INFINITY;  // log2 units
+  float l_part = 0.0f;
+
+  stage(0);
   for (int64_t g = 0; g < p.NBg; g++) {
+    if (g + 1 < p.NBg) {
+      stage(g + 1);
+      wait_vmcnt<kCopiesPerThread>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_nofence();  // group g has landed in every wave's view
+    const uint8_t* ks = lds + (g & 1) * kSlotBytes;
+    const uint8_t* vsl = ks + kSlotK;
+
+    // route scores
+    const float cs = sq * p.kq_scale[bh * p.NBg + g] * p.softmax_scale;
     float x[2][16];
-    route_scores(p, bh, g, qop, lh, l32, sq * p.kq_scale[bh * p.NBg + g] * p.softmax_scale, x);
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const int row = 32 * t + l32;
+      const int sw = kq_swz(row);
+      v8i kop[2];
+#pragma unroll
+      for (int c = 0; c < 2; c++) {
+        const int c0 = 4 * c + 2 * lh;
+        const uint4 a = *reinterpret_cast<const uint4*>(ks + row * kHeadDim + ((c0 ^ sw) * 16));
+        const uint4 b = *reinterpret_cast<const uint4*>(ks + row * kHeadDim + (((c0 + 1) ^ sw) * 16));
+        kop[c][0] = a.x; kop[c][1] = a.y; kop[c][2] = a.z; kop[c][3] = a.w;
+        kop[c][4] = b.x; kop[c][5] = b.y; kop[c][6] = b.z; kop[c][7] = b.w;
+      }
+      v16f z;
+#pragma unroll
+      for (int r = 0; r < 16; r++) z[r] = 0.0f;
+      v16f acc = mfma_f8(kop[0], qop[0], z);
+      acc = mfma_f8(kop[1], qop[1], acc);
+#pragma unroll
+      for (int r = 0; r < 16; r++) x[t][r] = acc[r] * cs;
+    }
+    // mask word of the Q block
     uint32_t lo_bits = 0, hi_bits = 0;
 #pragma unroll
     for (int t = 0; t < 2; t++)
@@ -304,97 +360,65 @@ __global__ __launch_bounds__(128) void sol_mask(SolParams p) {
       word_s[wave][0] = lo_bits;
       word_s[wave][1] = hi_bits;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint64_t word = (static_cast<uint64_t>(word_s[0][1] | word_s[1][1]) << 32) | (word_s[0][0] | word_s[1][0]);
-      const int64_t sink_end = min<int64_t>(static_cast<int64_t>(p.sink_blocks), p.NB) - 64 * g;
-      if (sink_end > 0) word |= sink_end >= 64 ? ~0ull : ((1ull << sink_end) - 1ull);
-      p.mask[(bh * p.NB + u) * p.W + g] = word;
-    }
-    __syncthreads();
-  }
-}
+    barrier_nofence();
+    const int pw = wave & 2;  // first wave of this Q block's pair
+    uint64_t word = (static_cast<uint64_t>(word_s[pw][1] | word_s[pw + 1][1]) << 32) |
+                    (word_s[pw][0] | word_s[pw + 1][0]);
+    const int64_t sink_end = min<int64_t>(static_cast<int64_t>(p.sink_blocks), p.NB) - 64 * g;
+    if (sink_end > 0) word |= sink_end >= 64 ? ~0ull : ((1ull << sink_end) - 1ull);
+    if (ublock && (wave & 1) == 0 && lane == 0) p.mask[(bh * p.NB + u) * p.W + g] = word;
 
-// 6. Summary route: per query, online softmax over the non-exact summaries (scored by the route
-// score, weighted by the block length) and its PV by BF16 MFMA (O^T = Vbar^T P^T; k-step (t, s)
-// covers summaries 32t + 16s + {4h + b, 8 + 4h + b}). Every wave works alone (32 queries of Q
-// block qrow / 64; four waves per workgroup).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sol_summary(SolParams p) {
-  const int64_t bh = blockIdx.y;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, lh = lane >> 5, l32 = lane & 31;
-  const int64_t q32 = static_cast<int64_t>(blockIdx.x) * 4 + wave;  // 32-query slice
-  if (q32 * 32 >= p.N) return;
-  const int64_t u = q32 >> 1;
-  const int64_t qrow = 32 * q32 + l32;
-  const bool qvalid = qrow < p.N;
-  const float sq = p.q_scale[bh * p.NB + u];
-  const uint64_t* mrow = p.mask + (bh * p.NB + u) * p.W;
-  constexpr float kLog2e = 1.4426950408889634f;
-
-  v8i qop[2];
-  load_q_operand(p, bh, qrow, lh, qop);
-  v16f oacc[4];
+    // summary route
+    const int64_t nsum = min<int64_t>(64, p.NB - 64 * g) - __builtin_popcountll(word & (~0ull >> (64 - min<int64_t>(64, p.NB - 64 * g))));
+    if (ublock && nsum > 0) {
+      float mloc = -INFINITY;
 #pragma unroll
-  for (int dt = 0; dt < 4; dt++)
+      for (int t = 0; t < 2; t++)
 #pragma unroll
-    for (int r = 0; r < 16; r++) oacc[dt][r] = 0.0f;
-  float m_run = -INFINITY;  // log2 units
-  float l_part = 0.0f;
-
-  for (int64_t g = 0; g < p.NBg; g++) {
-    const uint64_t word = mrow[g];
-    const int64_t nsum = min<int64_t>(64, p.NB - 64 * g) - __builtin_popcountll(word);
-    if (nsum <= 0) continue;  // every summary of the group is exact (uniform)
-    float x[2][16];
-    route_scores(p, bh, g, qop, lh, l32, sq * p.kq_scale[bh * p.NBg + g] * p.softmax_scale, x);
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; t++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int js = 32 * t + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const int64_t j = 64 * g + js;
-        const bool summ = j < p.NB && ((word >> js) & 1ull) == 0ull;
-        // log2 of the block length: 6 for full blocks
-        const float lgn = j == p.NB - 1 ? __log2f(static_cast<float>(p.N - 64 * j)) : 6.0f;
-        x[t][r] = summ ? __builtin_fmaf(x[t][r], kLog2e, lgn) : -INFINITY;
-        mloc = fmaxf(mloc, x[t][r]);
-      }
-    {
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
-      mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.0f;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; t++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const float pv = __builtin_amdgcn_exp2f(x[t][r] - m_new);
-        psum += pv;
-        pb[t][r >> 3][r & 7] = static_cast<__bf16>(pv);
-      }
-    l_part = alpha * l_part + psum;
-    if (alpha != 1.0f) {
-#pragma unroll
-      for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
-    }
-#pragma unroll
-    for (int t = 0; t < 2; t++)
-#pragma unroll
-      for (int s = 0; s < 2; s++)
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(
-              p.vsumT + ((((bh * p.NBg + g) * 2 + t) * 2 + s) * 4 + dt) * 512 + lane * 8);
-          oacc[dt] = mfma_bf16(av, pb[t][s], oacc[dt]);
+        for (int r = 0; r < 16; r++) {
+          const int js = 32 * t + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int64_t j = 64 * g + js;
+          const bool summ = j < p.NB && ((word >> js) & 1ull) == 0ull;
+          const float lgn = j == p.NB - 1 ? __log2f(static_cast<float>(p.N - 64 * j)) : 6.0f;
+          x[t][r] = summ ? __builtin_fmaf(x[t][r], kLog2e, lgn) : -INFINITY;
+          mloc = fmaxf(mloc, x[t][r]);
         }
+      {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+        mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.0f;
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const float pv = __builtin_amdgcn_exp2f(x[t][r] - m_new);
+          psum += pv;
+          pb[t][r >> 3][r & 7] = static_cast<__bf16>(pv);
+        }
+      l_part = alpha * l_part + psum;
+      if (alpha != 1.0f) {
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++)
+#pragma unroll
+          for (int dt = 0; dt < 4; dt++) {
+            const bf16x8 av = *reinterpret_cast<const bf16x8*>(vsl + ((((t * 2 + s2) * 4 + dt) * 64 + lane) * 16));
+            oacc[dt] = mfma_bf16(av, pb[t][s2], oacc[dt]);
+          }
+    }
+    wait_lgkm0();
+    barrier_nofence();  // every read of this slot is done before the next group refills it
   }
 
   // epilogue: the summary route's normalised output (piece 1) and log2 of its weight, in the
@@ -436,11 +460,7 @@ hipError_t launch_sol(const SolParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(sol_theta, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sol_mask, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const unsigned slices = static_cast<unsigned>((p.N + 127) / 128);  // four 32-query waves each
-  hipLaunchKernelGGL(sol_summary, dim3(slices, bh), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(sol_route, dim3(static_cast<unsigned>((p.NB + 1) / 2), bh), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
