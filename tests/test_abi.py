@@ -51,6 +51,7 @@ def test_quantize_rejects_bad_arguments(m):
     call = lambda a, p=ptrs: L.fp8attn_quantize_qkv(ctypes.byref(a), *p, _fake(), ws, None)
     assert call(A(1, 64, 64, 2, 64, None, None, 0, 0)) == 2            # D != 128
     assert call(A(0, 64, 64, 2, 128, None, None, 0, 0)) == 1           # B < 1
+    assert call(A(2, 64, 64, 32768, 128, None, None, 0, 0)) == 2       # B * H > 65535
     assert call(A(1, 64, 65, 2, 128, None, None, 0, 0)) == 1           # N != N_src, no perm
     bad = list(ptrs)
     bad[0] = None
@@ -90,6 +91,8 @@ def test_forward_rejects_bad_arguments(m):
                                  ctypes.c_size_t(ws), None)
 
     assert call(_opts(m), D=64) == 2
+    assert L.fp8attn_forward(2, 256, 32768, 128, *P, ctypes.byref(_opts(m)), _fake(), None,
+                             ctypes.c_size_t(0), None) == 2            # B * H > 65535
     assert call(_opts(m, p_scale=500.0)) == 1
     assert call(_opts(m, p_scale=0.0)) == 1
     assert call(_opts(m, p_scale=float("nan"))) == 1

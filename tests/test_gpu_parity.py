@@ -575,6 +575,29 @@ def test_vsmooth_cluster_matches_oracle(m, orc, N, H, K, F, iters):
 # ------------------------------------------------------------------------------------------
 # Full-size workloads (benchmark launch configuration), sampled heads and rows
 # ------------------------------------------------------------------------------------------
+def test_maximum_batch_heads(m, orc):
+    """B * H = 65535 (the largest count the library takes) with a ragged two-block sequence:
+    codes, scales and outputs of sampled (b, h) against the oracle. Inputs are drawn on the
+    device from a seeded generator; the oracle receives the same bf16 bytes of those heads."""
+    B, H, N = 3, 21845, 101
+    say("maximum batch*heads", B, H, N)
+    g = torch.Generator(device=DEV).manual_seed(123)
+    q, k, v = (torch.randn((B, N, H, 128), generator=g, device=DEV).to(torch.bfloat16) for _ in range(3))
+    qz = m.quantize_qkv(q, k, v)
+    out = m.forward(qz, kv_order=1)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 12345), (2, H - 1)):
+        sl = lambda t: _bits(t[b:b + 1, :, h:h + 1].contiguous().cpu())
+        ref_q = orc.quantize(sl(q), sl(k), sl(v))
+        for key in ("q8", "k8", "v8t", "q_scale", "k_scale", "v_scale"):
+            assert np.array_equal(_np(getattr(qz, key)[b:b + 1, h:h + 1]), ref_q[key]), (key, b, h)
+        ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=True, return_amb=True)
+        got = out[b:b + 1, :, h:h + 1].float().cpu().numpy().transpose(0, 2, 1, 3).astype(np.float64)
+        _compare_out(got, ref, f"max heads ({b}, {h})", amb)
+    del q, k, v, qz, out
+    torch.cuda.empty_cache()
+
+
 def _slice_heads(t, heads):
     return t[:, :, heads, :].contiguous()
 
