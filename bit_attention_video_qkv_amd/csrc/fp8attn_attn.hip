@@ -554,17 +554,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       if (closes_vblock(j)) {
         // rank-one mean restore of the V block that block j closes (its factors travel in pair
         // j+1); O holds blocks up to j-1 in the units of the running max of block j, like r
+        // as FP32 MFMAs on the matrix cores (O^T += mu r^T with K = 2, the second k slot zero:
+        // lanes of half 0 bring mu[32dt + l32] and their query's r), which keeps the VALU free
         const float* mu = reinterpret_cast<const float*>(sl + kMeanOff);
+        const float rb = lh == 0 ? r_cur : 0.0f;
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-          for (int g = 0; g < 4; g++) {
-            const float4 m4 = *reinterpret_cast<const float4*>(mu + 32 * dt + 8 * g + 4 * lh);
-            oacc[dt][4 * g + 0] = __builtin_fmaf(r_cur, m4.x, oacc[dt][4 * g + 0]);
-            oacc[dt][4 * g + 1] = __builtin_fmaf(r_cur, m4.y, oacc[dt][4 * g + 1]);
-            oacc[dt][4 * g + 2] = __builtin_fmaf(r_cur, m4.z, oacc[dt][4 * g + 2]);
-            oacc[dt][4 * g + 3] = __builtin_fmaf(r_cur, m4.w, oacc[dt][4 * g + 3]);
-          }
+        for (int dt = 0; dt < 4; dt++) {
+          const float ma = lh == 0 ? mu[32 * dt + l32] : 0.0f;
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ma, rb, oacc[dt], 0, 0, 0);
+        }
         r_cur = 0.0f;
       }
     }
