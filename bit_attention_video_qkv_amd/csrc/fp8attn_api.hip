@@ -458,11 +458,39 @@ fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, i
 }
 
 
+namespace {
+
+struct ClusterLayout {
+  size_t feat, labels, part1, part2, featsel, cent, csum, ccount, total;
+};
+
+ClusterLayout cluster_layout(int32_t B, int32_t N, int32_t H, int32_t n_feat) {
+  ClusterLayout L;
+  const size_t bh = static_cast<size_t>(B) * H;
+  const size_t nc = static_cast<size_t>(fp8attn::cluster_chunks(N));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += round_up(bytes);
+    return o;
+  };
+  L.feat = take(bh * N * n_feat * sizeof(float));
+  L.labels = take(bh * N * sizeof(int32_t));
+  L.part1 = take(bh * nc * kHeadDim * sizeof(double));
+  L.part2 = take(bh * nc * kHeadDim * sizeof(double));
+  L.featsel = take(bh * fp8attn::kMaxFeatures * sizeof(int32_t));
+  L.cent = take(bh * fp8attn::kMaxClusters * fp8attn::kMaxFeatures * sizeof(double));
+  L.csum = take(bh * nc * fp8attn::kMaxClusters * (fp8attn::kMaxFeatures + 1) * sizeof(double));
+  L.ccount = take(bh * nc * fp8attn::kMaxClusters * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
 size_t fp8attn_vsmooth_cluster_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D, int32_t n_feat) {
   if (B < 1 || N < 1 || H < 1 || D != 128 || n_feat < 1 || n_feat > fp8attn::kMaxFeatures) return 0;
-  const int64_t bhn = static_cast<int64_t>(B) * H * N;
-  const size_t feat = static_cast<size_t>(bhn) * n_feat * sizeof(float);
-  return ((feat + 255) / 256) * 256 + static_cast<size_t>(bhn) * sizeof(int32_t);
+  return cluster_layout(B, N, H, n_feat).total;
 }
 
 fp8attn_status fp8attn_vsmooth_cluster(int32_t B, int32_t N, int32_t H, int32_t D, const void* v,
@@ -486,10 +514,17 @@ fp8attn_status fp8attn_vsmooth_cluster(int32_t B, int32_t N, int32_t H, int32_t 
   p.v = static_cast<const uint16_t*>(v);
   p.perm = perm;
   p.labels = labels;
-  const int64_t bhn = static_cast<int64_t>(B) * H * N;
-  const size_t feat = static_cast<size_t>(bhn) * n_feat * sizeof(float);
-  p.ws_feat = static_cast<float*>(workspace);
-  p.ws_labels = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + ((feat + 255) / 256) * 256);
+  const ClusterLayout L = cluster_layout(B, N, H, n_feat);
+  char* ws = static_cast<char*>(workspace);
+  p.ws_feat = reinterpret_cast<float*>(ws + L.feat);
+  p.ws_labels = reinterpret_cast<int32_t*>(ws + L.labels);
+  p.ws_part1 = reinterpret_cast<double*>(ws + L.part1);
+  p.ws_part2 = reinterpret_cast<double*>(ws + L.part2);
+  p.ws_featsel = reinterpret_cast<int32_t*>(ws + L.featsel);
+  p.ws_cent = reinterpret_cast<double*>(ws + L.cent);
+  p.ws_csum = reinterpret_cast<double*>(ws + L.csum);
+  p.ws_ccount = reinterpret_cast<int32_t*>(ws + L.ccount);
+  p.n_chunks = fp8attn::cluster_chunks(N);
   p.N = N;
   p.B = B;
   p.H = H;

@@ -11,8 +11,18 @@
 //     in FP64, ties to the lower cluster id; an empty cluster keeps its centroid;
 //   * perm = the head's tokens stably sorted by cluster id.
 //
-// One 1024-thread workgroup per (b, h). Every reduction runs in a fixed order, so the result is
-// deterministic; sums are FP64 (the features are bf16 values, exact in FP32).
+// Work is split into chunks of kChunk tokens (many workgroups per head); partial results are
+// combined in ascending chunk order, so every result is deterministic. The features are bf16
+// values: sums of them in FP64 are exact for any realistic value range (fewer than 2^21 tokens
+// of 8-bit mantissas spanning under 24 binades), which makes the means and centroids independent
+// of the summation order. Distances are formed with separately rounded products (never fused).
+//
+// Kernels per head (b, h), grids (chunks, B*H) unless noted:
+//   vc_colsum   channel sums per chunk                     vc_sqdev  centred sums of squares
+//   vc_select   (B*H): variances, feature choice, initial centroids
+//   vc_gather   the selected features of every token (FP32)
+//   vc_step     assignment (+ per-chunk cluster sums, or the final per-chunk counts)
+//   vc_update   (B*H): centroids from the chunk sums          vc_scatter  stable scatter
 #include "fp8attn_common.h"
 #include "fp8attn_internal.h"
 
@@ -20,192 +30,257 @@ namespace fp8attn {
 
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kChunk = 2048;  // tokens per chunk
+constexpr int kTpt = kChunk / 256;  // tokens per thread in vc_step / vc_scatter (contiguous)
 
-// Fixed-order tree sum of one double per thread over the workgroup; every thread gets the total.
-__device__ double block_sum(double v, double* red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const double r = red[0];
-  __syncthreads();
-  return r;
+__device__ __forceinline__ double dmul_rounded(double a, double b) {
+  double p = a * b;
+  asm volatile("" : "+v"(p));
+  return p;
 }
 
-__global__ __launch_bounds__(kThreads) void vsmooth_cluster(ClusterParams p) {
-  __shared__ double red[kThreads];
-  __shared__ double stat[kHeadDim];
-  __shared__ double cent[kMaxClusters * kMaxFeatures];
-  __shared__ int feat[kMaxFeatures];
-  __shared__ int counts[kMaxClusters][kThreads / 8 + 1];  // per cluster, per 8-thread group
-
-  const int tid = threadIdx.x;
-  const int64_t bh = blockIdx.x;
+__device__ __forceinline__ float vval(const ClusterParams& p, int64_t bh, int64_t t, int d) {
   const int64_t b = bh / p.H, h = bh % p.H;
-  const int64_t N = p.N;
-  const int K = p.n_clusters, F = p.n_feat;
-  auto vval = [&](int64_t t, int d) -> float {
-    return bf16_to_f32(p.v[((b * N + t) * p.H + h) * kHeadDim + d]);
-  };
+  return bf16_to_f32(p.v[((b * p.N + t) * p.H + h) * kHeadDim + d]);
+}
 
-  // ---- channel variance: mean, then the centred sum of squares (8 token groups x 128 ch) ----
-  const int g = tid / kHeadDim, d = tid % kHeadDim;
-  for (int pass = 0; pass < 2; pass++) {
-    double acc = 0.0;
-    const double mean = pass ? stat[d] : 0.0;
-    for (int64_t t = g; t < N; t += kThreads / kHeadDim) {
-      const double x = static_cast<double>(vval(t, d));
-      acc += pass ? (x - mean) * (x - mean) : x;
-    }
-    red[tid] = acc;
-    __syncthreads();
-    if (tid < kHeadDim) {
-      double s = 0.0;
-      for (int gg = 0; gg < kThreads / kHeadDim; gg++) s += red[gg * kHeadDim + tid];
-      stat[tid] = s / static_cast<double>(N);  // mean, then variance
-    }
-    __syncthreads();
+// 1. channel sums of the chunk (FP64, exact): two token halves of 128 channel threads.
+__global__ __launch_bounds__(256) void vc_colsum(ClusterParams p) {
+  __shared__ double red[kHeadDim];
+  const int64_t c = blockIdx.x, bh = blockIdx.y;
+  const int d = threadIdx.x & 127, half = threadIdx.x >> 7;
+  const int64_t t0 = c * kChunk, t1 = min<int64_t>(p.N, t0 + kChunk);
+  double acc = 0.0;
+#pragma unroll 8
+  for (int64_t t = t0 + half; t < t1; t += 2) acc += static_cast<double>(vval(p, bh, t, d));
+  if (half == 1) red[d] = acc;
+  __syncthreads();
+  if (half == 0) p.ws_part1[(bh * p.n_chunks + c) * kHeadDim + d] = acc + red[d];
+}
+
+// 2. centred sums of squares of the chunk around the head's channel mean.
+__global__ __launch_bounds__(256) void vc_sqdev(ClusterParams p) {
+  __shared__ double red[kHeadDim];
+  const int64_t c = blockIdx.x, bh = blockIdx.y;
+  const int d = threadIdx.x & 127, half = threadIdx.x >> 7;
+  double s = 0.0;
+  for (int64_t k = 0; k < p.n_chunks; k++) s += p.ws_part1[(bh * p.n_chunks + k) * kHeadDim + d];
+  const double mean = s / static_cast<double>(p.N);
+  const int64_t t0 = c * kChunk, t1 = min<int64_t>(p.N, t0 + kChunk);
+  double acc = 0.0;
+#pragma unroll 8
+  for (int64_t t = t0 + half; t < t1; t += 2) {
+    const double x = static_cast<double>(vval(p, bh, t, d)) - mean;
+    acc += dmul_rounded(x, x);
   }
-  // ---- feature choice: the F largest variances (first channel on ties), ascending order ----
-  if (tid == 0) {
+  if (half == 1) red[d] = acc;
+  __syncthreads();
+  if (half == 0) p.ws_part2[(bh * p.n_chunks + c) * kHeadDim + d] = acc + red[d];
+}
+
+// 3. variances -> the n_feat largest (first channel on ties), ascending; initial centroids.
+__global__ __launch_bounds__(kHeadDim) void vc_select(ClusterParams p) {
+  __shared__ double var[kHeadDim];
+  __shared__ int feat[kMaxFeatures];
+  const int64_t bh = blockIdx.x;
+  const int d = threadIdx.x;
+  double s = 0.0;
+  for (int64_t k = 0; k < p.n_chunks; k++) s += p.ws_part2[(bh * p.n_chunks + k) * kHeadDim + d];
+  var[d] = s / static_cast<double>(p.N);
+  __syncthreads();
+  if (d == 0) {
     bool taken[kHeadDim];
     for (int c = 0; c < kHeadDim; c++) taken[c] = false;
-    for (int f = 0; f < F; f++) {
+    for (int f = 0; f < p.n_feat; f++) {
       int best = -1;
       for (int c = 0; c < kHeadDim; c++)
-        if (!taken[c] && (best < 0 || stat[c] > stat[best])) best = c;
+        if (!taken[c] && (best < 0 || var[c] > var[best])) best = c;
       taken[best] = true;
       feat[f] = best;
     }
-    for (int i = 1; i < F; i++)  // insertion sort, ascending
+    for (int i = 1; i < p.n_feat; i++)  // insertion sort, ascending
       for (int j = i; j > 0 && feat[j - 1] > feat[j]; j--) {
         const int tmp = feat[j];
         feat[j] = feat[j - 1];
         feat[j - 1] = tmp;
       }
+    for (int f = 0; f < p.n_feat; f++) p.ws_featsel[bh * kMaxFeatures + f] = feat[f];
   }
   __syncthreads();
-
-  // ---- gather the features of every token (FP32, exact) ----
-  float* fv = p.ws_feat + bh * N * F;
-  for (int64_t t = tid; t < N; t += kThreads)
-    for (int f = 0; f < F; f++) fv[t * F + f] = vval(t, feat[f]);
-  int32_t* lab = p.ws_labels + bh * N;
-  __syncthreads();  // the gathered features are read by other threads of the workgroup below
-
-  if (tid < K * F) {
-    const int c = tid / F, f = tid % F;
-    const int64_t t0 = (static_cast<int64_t>(2 * c + 1) * N) / (2 * K);
-    cent[tid] = static_cast<double>(fv[t0 * F + f]);
+  for (int i = d; i < p.n_clusters * p.n_feat; i += kHeadDim) {
+    const int c = i / p.n_feat, f = i % p.n_feat;
+    const int64_t t0 = (static_cast<int64_t>(2 * c + 1) * p.N) / (2 * p.n_clusters);
+    p.ws_cent[(bh * kMaxClusters + c) * kMaxFeatures + f] = static_cast<double>(vval(p, bh, t0, feat[f]));
   }
+}
+
+// 4. the selected features of the chunk's tokens, FP32 [N, n_feat] per head.
+__global__ __launch_bounds__(256) void vc_gather(ClusterParams p) {
+  const int64_t c = blockIdx.x, bh = blockIdx.y;
+  const int64_t t0 = c * kChunk, t1 = min<int64_t>(p.N, t0 + kChunk);
+  const int F = p.n_feat;
+  for (int64_t i = t0 * F + threadIdx.x; i < t1 * F; i += 256) {
+    const int64_t t = i / F;
+    const int f = static_cast<int>(i % F);
+    p.ws_feat[bh * p.N * F + i] = vval(p, bh, t, p.ws_featsel[bh * kMaxFeatures + f]);
+  }
+}
+
+// 5. assignment of the chunk's tokens (thread i: tokens t0 + kTpt*i .. +kTpt-1). With sums: per
+// cluster, the chunk's feature sums and count (wave butterflies, then the 4 waves in order).
+// Final step (sums = 0): the chunk's count per cluster.
+__global__ __launch_bounds__(256) void vc_step(ClusterParams p, int sums) {
+  __shared__ double cent[kMaxClusters * kMaxFeatures];
+  __shared__ double wred[4][kMaxFeatures + 1];
+  __shared__ int cnt_s[kMaxClusters];
+  const int64_t c = blockIdx.x, bh = blockIdx.y;
+  const int K = p.n_clusters, F = p.n_feat;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < K * kMaxFeatures; i += 256) cent[i] = p.ws_cent[bh * kMaxClusters * kMaxFeatures + i];
+  if (tid < kMaxClusters) cnt_s[tid] = 0;
   __syncthreads();
-
-  // each thread owns one contiguous chunk of tokens (this also makes the final scatter stable)
-  const int64_t chunk = (N + kThreads - 1) / kThreads;
-  const int64_t t_begin = min(N, tid * chunk), t_end = min(N, t_begin + chunk);
-
-  auto assign = [&]() {
-    for (int64_t t = t_begin; t < t_end; t++) {
-      int best = 0;
-      double bd = INFINITY;
-      for (int c = 0; c < K; c++) {
-        double dist = 0.0;
-        for (int f = 0; f < F; f++) {
-          const double diff = static_cast<double>(fv[t * F + f]) - cent[c * F + f];
-          dist += diff * diff;
-        }
-        if (dist < bd) {
-          bd = dist;
-          best = c;
-        }
-      }
-      lab[t] = best;
-    }
-  };
-
-  for (int it = 0; it < p.iters; it++) {
-    assign();
-    __syncthreads();
-    for (int c = 0; c < K; c++) {
-      double cnt = 0.0;
-      for (int64_t t = t_begin; t < t_end; t++) cnt += lab[t] == c ? 1.0 : 0.0;
-      const double total = block_sum(cnt, red);
+  const int64_t tb = c * kChunk + static_cast<int64_t>(tid) * kTpt;
+  const float* fv = p.ws_feat + bh * p.N * F;
+  int lab[kTpt];
+#pragma unroll
+  for (int k = 0; k < kTpt; k++) {
+    const int64_t t = tb + k;
+    lab[k] = -1;
+    if (t >= p.N) continue;
+    int best = 0;
+    double bd = INFINITY;
+    for (int cl = 0; cl < K; cl++) {
+      double dist = 0.0;
       for (int f = 0; f < F; f++) {
-        double s = 0.0;
-        for (int64_t t = t_begin; t < t_end; t++)
-          if (lab[t] == c) s += static_cast<double>(fv[t * F + f]);
-        const double sum = block_sum(s, red);
-        if (tid == 0 && total > 0.0) cent[c * F + f] = sum / total;
+        const double diff = static_cast<double>(fv[t * F + f]) - cent[cl * kMaxFeatures + f];
+        dist += dmul_rounded(diff, diff);
+      }
+      if (dist < bd) {
+        bd = dist;
+        best = cl;
+      }
+    }
+    lab[k] = best;
+    p.ws_labels[bh * p.N + t] = best;
+  }
+  if (!sums) {
+#pragma unroll
+    for (int k = 0; k < kTpt; k++)
+      if (lab[k] >= 0) atomicAdd(&cnt_s[lab[k]], 1);  // integer counts: order-free
+    __syncthreads();
+    if (tid < K) p.ws_ccount[(bh * p.n_chunks + c) * kMaxClusters + tid] = cnt_s[tid];
+    return;
+  }
+  for (int cl = 0; cl < K; cl++) {
+    double part[kMaxFeatures + 1];
+#pragma unroll
+    for (int f = 0; f <= kMaxFeatures; f++) part[f] = 0.0;
+#pragma unroll
+    for (int k = 0; k < kTpt; k++) {
+      if (lab[k] != cl) continue;
+#pragma unroll
+      for (int f = 0; f < kMaxFeatures; f++)
+        if (f < F) part[f] += static_cast<double>(fv[(tb + k) * F + f]);
+      part[kMaxFeatures] += 1.0;
+    }
+#pragma unroll
+    for (int f = 0; f <= kMaxFeatures; f++) {
+      if (f < F || f == kMaxFeatures) {
+        double x = part[f];
+        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+        if (lane == 0) wred[wave][f == kMaxFeatures ? F : f] = x;
       }
     }
     __syncthreads();
+    if (tid <= F) {
+      const double tot = ((wred[0][tid] + wred[1][tid]) + wred[2][tid]) + wred[3][tid];
+      p.ws_csum[((bh * p.n_chunks + c) * kMaxClusters + cl) * (kMaxFeatures + 1) + tid] = tot;
+    }
+    __syncthreads();
   }
-  assign();
-  __syncthreads();
+}
 
-  // ---- stable counting sort by cluster id. Counts per 8-thread group keep the LDS small; the
-  // eight threads of a group then place their chunks in thread order. ----
-  const int grp = tid / 8, lane8 = tid % 8;
-  int my_cnt[kMaxClusters];
-  for (int c = 0; c < K; c++) my_cnt[c] = 0;
-  for (int64_t t = t_begin; t < t_end; t++) my_cnt[lab[t]]++;
-  // group totals (lane 0 of each group sums its group in thread order)
-  for (int c = 0; c < K; c++) {
-    red[tid] = static_cast<double>(my_cnt[c]);
-    __syncthreads();
-    if (lane8 == 0) {
-      int s = 0;
-      for (int l = 0; l < 8; l++) s += static_cast<int>(red[tid + l]);
-      counts[c][grp] = s;
-    }
-    __syncthreads();
+// 6. centroids: chunk sums in ascending chunk order; an empty cluster keeps its centroid.
+__global__ __launch_bounds__(512) void vc_update(ClusterParams p) {
+  const int64_t bh = blockIdx.x;
+  const int i = threadIdx.x;
+  const int F = p.n_feat;
+  if (i >= p.n_clusters * F) return;
+  const int cl = i / F, f = i % F;
+  double s = 0.0, n = 0.0;
+  for (int64_t k = 0; k < p.n_chunks; k++) {
+    const double* row = p.ws_csum + ((bh * p.n_chunks + k) * kMaxClusters + cl) * (kMaxFeatures + 1);
+    s += row[f];
+    n += row[F];
   }
-  // exclusive prefix over (cluster, group) in that order: one thread per cluster scans its row,
-  // then the cluster bases are chained
+  if (n > 0.0) p.ws_cent[(bh * kMaxClusters + cl) * kMaxFeatures + f] = s / n;
+}
+
+// 7. stable scatter: positions ordered by (cluster, token). Base of (cluster, chunk) = tokens of
+// lower clusters + tokens of this cluster in earlier chunks; inside the chunk, thread i's
+// contiguous tokens come after those of threads < i.
+__global__ __launch_bounds__(256) void vc_scatter(ClusterParams p) {
+  __shared__ int base[kMaxClusters];
+  __shared__ int scan[kMaxClusters][257];
+  const int64_t c = blockIdx.x, bh = blockIdx.y;
+  const int K = p.n_clusters, tid = threadIdx.x;
   if (tid < K) {
-    int run = 0;
-    for (int gg = 0; gg < kThreads / 8; gg++) {
-      const int v = counts[tid][gg];
-      counts[tid][gg] = run;
-      run += v;
-    }
-    counts[tid][kThreads / 8] = run;  // cluster total
+    int before = 0;
+    for (int cl = 0; cl < tid; cl++)
+      for (int64_t k = 0; k < p.n_chunks; k++) before += p.ws_ccount[(bh * p.n_chunks + k) * kMaxClusters + cl];
+    for (int64_t k = 0; k < c; k++) before += p.ws_ccount[(bh * p.n_chunks + k) * kMaxClusters + tid];
+    base[tid] = before;
   }
+  const int64_t tb = c * kChunk + static_cast<int64_t>(tid) * kTpt;
+  int lab[kTpt];
+  int my[kMaxClusters];
+  for (int cl = 0; cl < K; cl++) my[cl] = 0;
+#pragma unroll
+  for (int k = 0; k < kTpt; k++) {
+    const int64_t t = tb + k;
+    lab[k] = t < p.N ? p.ws_labels[bh * p.N + t] : -1;
+    for (int cl = 0; cl < K; cl++) my[cl] += lab[k] == cl ? 1 : 0;
+  }
+  for (int cl = 0; cl < K; cl++) scan[cl][tid] = my[cl];
   __syncthreads();
-  if (tid == 0) {
-    int base = 0;
-    for (int c = 0; c < K; c++) {
-      const int tot = counts[c][kThreads / 8];
-      counts[c][kThreads / 8] = base;
-      base += tot;
+  if (tid < K) {  // exclusive prefix over the threads, per cluster
+    int run = 0;
+    for (int i = 0; i < 256; i++) {
+      const int v = scan[tid][i];
+      scan[tid][i] = run;
+      run += v;
     }
   }
   __syncthreads();
   int pos[kMaxClusters];
-  for (int c = 0; c < K; c++) {
-    // offset of this thread inside its group: counts of the earlier lanes of the group
-    red[tid] = static_cast<double>(my_cnt[c]);
-    __syncthreads();
-    int before = 0;
-    for (int l = 0; l < lane8; l++) before += static_cast<int>(red[grp * 8 + l]);
-    pos[c] = counts[c][kThreads / 8] + counts[c][grp] + before;
-    __syncthreads();
+  for (int cl = 0; cl < K; cl++) pos[cl] = base[cl] + scan[cl][tid];
+  int32_t* out = p.perm + bh * p.N;
+#pragma unroll
+  for (int k = 0; k < kTpt; k++) {
+    if (lab[k] < 0) continue;
+    out[pos[lab[k]]++] = static_cast<int32_t>(tb + k);
+    if (p.labels) p.labels[bh * p.N + tb + k] = lab[k];
   }
-  int32_t* out = p.perm + bh * N;
-  for (int64_t t = t_begin; t < t_end; t++) out[pos[lab[t]]++] = static_cast<int32_t>(t);
-  if (p.labels)
-    for (int64_t t = t_begin; t < t_end; t++) p.labels[bh * N + t] = lab[t];
 }
 
 }  // namespace
 
 hipError_t launch_cluster(const ClusterParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(vsmooth_cluster, dim3(static_cast<unsigned>(p.B * p.H)), dim3(kThreads), 0, stream, p);
+  const unsigned bh = static_cast<unsigned>(p.B * p.H), nc = static_cast<unsigned>(p.n_chunks);
+  const dim3 g(nc, bh);
+  hipLaunchKernelGGL(vc_colsum, g, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(vc_sqdev, g, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(vc_select, dim3(bh), dim3(kHeadDim), 0, stream, p);
+  hipLaunchKernelGGL(vc_gather, g, dim3(256), 0, stream, p);
+  for (int it = 0; it < p.iters; it++) {
+    hipLaunchKernelGGL(vc_step, g, dim3(256), 0, stream, p, 1);
+    hipLaunchKernelGGL(vc_update, dim3(bh), dim3(512), 0, stream, p);
+  }
+  hipLaunchKernelGGL(vc_step, g, dim3(256), 0, stream, p, 0);
+  hipLaunchKernelGGL(vc_scatter, g, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
+
+int64_t cluster_chunks(int64_t N) { return (N + kChunk - 1) / kChunk; }
 
 }  // namespace fp8attn

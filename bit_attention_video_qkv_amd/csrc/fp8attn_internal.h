@@ -111,11 +111,18 @@ struct ClusterParams {
   int32_t* labels;     // [B, H, N] or null
   float* ws_feat;      // [B*H, N, n_feat]
   int32_t* ws_labels;  // [B*H, N]
-  int64_t N;
+  double* ws_part1;    // [B*H, n_chunks, 128] channel sums per chunk
+  double* ws_part2;    // [B*H, n_chunks, 128] centred sums of squares per chunk
+  int32_t* ws_featsel; // [B*H, kMaxFeatures]
+  double* ws_cent;     // [B*H, kMaxClusters, kMaxFeatures]
+  double* ws_csum;     // [B*H, n_chunks, kMaxClusters, kMaxFeatures + 1] (sums, count)
+  int32_t* ws_ccount;  // [B*H, n_chunks, kMaxClusters]
+  int64_t N, n_chunks;
   int B, H;
   int n_clusters, n_feat, iters;
 };
 
+int64_t cluster_chunks(int64_t N);  // token chunks of the clustering kernels
 hipError_t launch_cluster(const ClusterParams& p, hipStream_t stream);
 
 enum AttnVariant : int {
