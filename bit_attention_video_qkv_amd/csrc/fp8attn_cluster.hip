@@ -82,15 +82,15 @@ __global__ __launch_bounds__(256) void vc_sqdev(ClusterParams p) {
 __global__ __launch_bounds__(kHeadDim) void vc_select(ClusterParams p) {
   __shared__ double var[kHeadDim];
   __shared__ int feat[kMaxFeatures];
+  __shared__ bool taken[kHeadDim];
   const int64_t bh = blockIdx.x;
   const int d = threadIdx.x;
   double s = 0.0;
   for (int64_t k = 0; k < p.n_chunks; k++) s += p.ws_part2[(bh * p.n_chunks + k) * kHeadDim + d];
   var[d] = s / static_cast<double>(p.N);
+  taken[d] = false;
   __syncthreads();
   if (d == 0) {
-    bool taken[kHeadDim];
-    for (int c = 0; c < kHeadDim; c++) taken[c] = false;
     for (int f = 0; f < p.n_feat; f++) {
       int best = -1;
       for (int c = 0; c < kHeadDim; c++)
@@ -141,6 +141,12 @@ __global__ __launch_bounds__(256) void vc_step(ClusterParams p, int sums) {
   __syncthreads();
   const int64_t tb = c * kChunk + static_cast<int64_t>(tid) * kTpt;
   const float* fv = p.ws_feat + bh * p.N * F;
+  // the thread's tokens' features, loaded once (zero beyond n_feat and past N)
+  float fx[kTpt][kMaxFeatures];
+#pragma unroll
+  for (int k = 0; k < kTpt; k++)
+#pragma unroll
+    for (int f = 0; f < kMaxFeatures; f++) fx[k][f] = (tb + k < p.N && f < F) ? fv[(tb + k) * F + f] : 0.0f;
   int lab[kTpt];
 #pragma unroll
   for (int k = 0; k < kTpt; k++) {
@@ -151,9 +157,12 @@ __global__ __launch_bounds__(256) void vc_step(ClusterParams p, int sums) {
     double bd = INFINITY;
     for (int cl = 0; cl < K; cl++) {
       double dist = 0.0;
-      for (int f = 0; f < F; f++) {
-        const double diff = static_cast<double>(fv[t * F + f]) - cent[cl * kMaxFeatures + f];
-        dist += dmul_rounded(diff, diff);
+#pragma unroll
+      for (int f = 0; f < kMaxFeatures; f++) {
+        if (f < F) {
+          const double diff = static_cast<double>(fx[k][f]) - cent[cl * kMaxFeatures + f];
+          dist += dmul_rounded(diff, diff);
+        }
       }
       if (dist < bd) {
         bd = dist;
@@ -179,8 +188,7 @@ __global__ __launch_bounds__(256) void vc_step(ClusterParams p, int sums) {
     for (int k = 0; k < kTpt; k++) {
       if (lab[k] != cl) continue;
 #pragma unroll
-      for (int f = 0; f < kMaxFeatures; f++)
-        if (f < F) part[f] += static_cast<double>(fv[(tb + k) * F + f]);
+      for (int f = 0; f < kMaxFeatures; f++) part[f] += static_cast<double>(fx[k][f]);
       part[kMaxFeatures] += 1.0;
     }
 #pragma unroll
