@@ -56,6 +56,10 @@ WORKLOADS = {
     "vsmooth": ("vsmooth", False, True,
                 "V-Smooth + ExpCast, B=1 H=24 N=49152 D=128, 5% token outliers x20 in V, "
                 "16-cluster k-means permutation (reused, not timed), S=256, reverse KV order"),
+    "wan14b_local": ("wan14b_local", False, False,
+                     "Wan-14B-720p-shaped dense FP8 attention on video-like inputs (logits falling "
+                     "off with 3D distance on the 21x45x80 grid), B=1 H=40 N=75600 D=128, S=256, "
+                     "reverse KV order"),
     "sink4096": ("sink4096", False, False,
                  "sink stress, B=1 H=8 N=4096 D=128, 4 sink keys with logit offset 9, S=256, "
                  "reverse KV order (256 query tiles: below the machine's width)"),

@@ -184,25 +184,32 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   int n_iter = 0;
   int64_t e0 = 0;
   bool has_last_block = true;  // the piece holds key block NB-1 (the only partial one)
-  // Sol: the exact blocks of this 64-row Q block are the set bits of its mask row, visited in
-  // KV order (uniform scans of the mask words)
-  const uint64_t* sol_row = SOL ? p.sol_mask + (bh * p.NB + q0 / kBlock) * p.sol_words : nullptr;
-  auto sol_next = [&](int64_t pos) -> int64_t {  // first exact block at or after pos, or -1
+  // Sol: the staged key blocks are the set bits of the workgroup's Q-block mask (four waves: the
+  // union of its two Q blocks' masks, and each wave pair masks out the blocks that are not exact
+  // for its own Q block), visited in KV order by uniform scans of the mask words
+  constexpr bool kSolPair = SOL && WAVES == 4;  // two Q blocks per workgroup (else one)
+  const int64_t sol_ua = q0 / kBlock;
+  const bool sol_has_b = kSolPair && sol_ua + 1 < p.NB;
+  const uint64_t* sol_row_a = SOL ? p.sol_mask + (bh * p.NB + sol_ua) * p.sol_words : nullptr;
+  const uint64_t* sol_row_b = SOL && sol_has_b ? sol_row_a + p.sol_words : nullptr;
+  const uint64_t* sol_row_mine = (SOL && wave >= 2) ? sol_row_b : sol_row_a;  // null: no Q block
+  auto sol_word = [&](int64_t w) -> uint64_t { return sol_row_a[w] | (sol_has_b ? sol_row_b[w] : 0ull); };
+  auto sol_next = [&](int64_t pos) -> int64_t {  // first staged block at or after pos, or -1
     if (pos >= p.NB) return -1;
     int64_t w = pos >> 6;
-    uint64_t m = sol_row[w] & (~0ull << (pos & 63));
-    while (m == 0ull && ++w < p.sol_words) m = sol_row[w];
+    uint64_t m = sol_word(w) & (~0ull << (pos & 63));
+    while (m == 0ull && ++w < p.sol_words) m = sol_word(w);
     return m ? (w << 6) + __builtin_ctzll(m) : -1;
   };
-  auto sol_prev = [&](int64_t pos) -> int64_t {  // last exact block at or before pos, or -1
+  auto sol_prev = [&](int64_t pos) -> int64_t {  // last staged block at or before pos, or -1
     if (pos < 0) return -1;
     int64_t w = pos >> 6;
-    uint64_t m = sol_row[w] & ((pos & 63) == 63 ? ~0ull : ((1ull << ((pos & 63) + 1)) - 1ull));
-    while (m == 0ull && --w >= 0) m = sol_row[w];
+    uint64_t m = sol_word(w) & ((pos & 63) == 63 ? ~0ull : ((1ull << ((pos & 63) + 1)) - 1ull));
+    while (m == 0ull && --w >= 0) m = sol_word(w);
     return m ? (w << 6) + 63 - __builtin_clzll(m) : -1;
   };
   if constexpr (SOL) {
-    for (int64_t w = 0; w < p.sol_words; w++) n_iter += __builtin_popcountll(sol_row[w]);
+    for (int64_t w = 0; w < p.sol_words; w++) n_iter += __builtin_popcountll(sol_word(w));
   } else if constexpr (SPARSE) {
     for (int e = e_begin; e < e_end; e++) n_iter += nblk_of_len(p.tile_len[p.col_idx[e]]);
   } else {
@@ -326,6 +333,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     if (wave == 0 && lane == 0) {
       copy4_to_lds(p.k_scale + bh * p.NB + kb, 0u, l0 + kMetaOff);
       *reinterpret_cast<int*>(sl + kMetaOff + 4) = limit;
+      if constexpr (kSolPair) *reinterpret_cast<int*>(sl + kMetaOff + 8) = static_cast<int>(kb);
     }
     kb_prev = kb;
   };
@@ -369,6 +377,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   v8i kop[2][2], vop[4];
   float sk_cur = 0.0f, sk_next = 0.0f;
   int lim_cur = kBlock, lim_next = kBlock;
+  int kb_next = 0;                      // Sol: key block of the next K tile
+  bool ex_cur = false, ex_next = false;  // Sol: that block is not exact for this wave's Q block
 
   // Per-lane byte offsets of the 16-byte operand chunks inside a slot (K rows in the permuted
   // order, swizzled chunks).
@@ -404,6 +414,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   auto read_meta = [&](const uint8_t* base) {
     sk_next = *reinterpret_cast<const float*>(base + kMetaOff);
     lim_next = *reinterpret_cast<const int*>(base + kMetaOff + 4);
+    if constexpr (kSolPair) {
+      // looked up one block ahead, so the mask word's load has a whole block to land
+      kb_next = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(base + kMetaOff + 8));
+      ex_next = sol_row_mine == nullptr || ((sol_row_mine[kb_next >> 6] >> (kb_next & 63)) & 1ull) == 0ull;
+    }
   };
   auto qk_half = [&](int t) {
     v16f z;
@@ -442,9 +457,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       for (int r = 0; r < 16; r++) x[16 * t + r] = sacc[t][r];
     if constexpr (kMask) {
       // only blocks with padding keys pay for the selects; the empty asm keeps the compiler from
-      // hoisting the per-key compares out of the (uniform) branch
-      if (__builtin_amdgcn_readfirstlane(lim_cur) < kBlock) {
-        int nv = lim_cur - 32 * lh;  // valid keys among this lane's 32
+      // hoisting the per-key compares out of the (uniform) branch. Sol: a block outside this
+      // wave's own Q-block mask counts as fully masked.
+      bool excluded = false;
+      if constexpr (kSolPair) excluded = ex_cur;
+      if (__builtin_amdgcn_readfirstlane(lim_cur) < kBlock || excluded) {
+        int nv = excluded ? 0 : lim_cur - 32 * lh;  // valid keys among this lane's 32
         asm volatile("" : "+v"(nv));
 #pragma unroll
         for (int q = 0; q < 32; q++) x[q] = q < nv ? x[q] : -INFINITY;
@@ -573,6 +591,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     barrier_nofence();
     sk_cur = sk_next;
     lim_cur = lim_next;
+    ex_cur = ex_next;
     if (j + 4 <= n_iter) stage(j + 4, sl);
   };
 
@@ -594,6 +613,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   barrier_nofence();
   sk_cur = sk_next;
   lim_cur = lim_next;
+  ex_cur = ex_next;
   if (n_iter >= 3) stage(3, slot(0));
 
   // ---- mainloop. Dense: the one block with fewer than 64 valid keys (the last key block, first
@@ -632,7 +652,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       // split-KV piece or Sol exact route: this piece's normalised O (FP32) and log2 of its
       // weight, m + log2(l)
       if (ok) {
-        const float inv_l = 1.0f / l_tot;
+        // (Sol: a wave none of whose staged blocks was exact for its Q block has no weight)
+        const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         const int64_t prow = (static_cast<int64_t>(split) * p.B * p.H + bh) * p.N + qrow;
         float* orow = p.o_part + prow * kHeadDim;
 #pragma unroll
@@ -653,7 +674,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
             o.w = oacc[dt][4 * g + 3] * gs[3] * inv_l;
             *reinterpret_cast<float4*>(orow + d0) = o;
           }
-        if (lh == 0) p.lse[prow] = m_run + __log2f(l_tot);
+        if (lh == 0) p.lse[prow] = l_tot > 0.0f ? m_run + __log2f(l_tot) : -INFINITY;
       }
       return;
     }
@@ -765,8 +786,10 @@ hipError_t launch_variant(AttnParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Sol: the exact route (two waves per 64-row Q block, the mask's blocks) writes piece 0; the
-// summary route has written piece 1; then the two are merged.
+// Sol: the exact route (two waves per 64-row Q block over its mask's blocks; the kernel also has
+// a four-wave form over the union of two Q blocks' masks, which only pays when neighbouring Q
+// blocks share most exact blocks) writes piece 0; the summary route has written piece 1; then the
+// two are merged.
 template <bool EXPCAST>
 hipError_t launch_sol_exact(AttnParams p, hipStream_t stream) {
   p.splits = 1;

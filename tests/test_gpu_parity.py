@@ -501,6 +501,25 @@ def test_sol_small(m, orc, N, H, tau, est, sinks, reverse, expcast):
     _compare_out(_gpu_rows(out, np.arange(N)), ref, f"sol tau={tau}", amb)
 
 
+@pytest.mark.parametrize("grid,tau,reverse", [((5, 12, 16), 3.0, True), ((4, 9, 20), 2.0, False)])
+def test_sol_video_local(m, orc, grid, tau, reverse):
+    """Video-like inputs (logits falling off with 3D distance): exact blocks cluster around the
+    query; same checks as above."""
+    N, H = grid[0] * grid[1] * grid[2], 2
+    say("sol video-local", grid, tau)
+    q, k, v = workloads.make_qkv(1, N, H, seed=98, kind="video_local", grid=grid)
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb)
+    ref_sol = orc.sol_prepare(ref_q, tau=tau, estimator=0, sink_blocks=1)
+    qz = _gpu_quantize(m, q, k, v)
+    out, mask = m.sol_forward(qz, tau=tau, kv_order=int(reverse), return_mask=True)
+    torch.cuda.synchronize()
+    sol = dict(ref_sol)
+    sol["mask"] = _check_route_mask(orc, _np(mask), ref_sol, -(-N // 64))
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=reverse, return_amb=True, sol=sol)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, f"sol video-local tau={tau}", amb)
+
+
 def test_sol_with_smoothing(m, orc):
     """Sequence-mean smoothing under Sol: K shifted before the summaries, V shift restored."""
     say("sol + smoothing")

@@ -19,6 +19,15 @@ Recipe (fixed; every config draws FP32 ``randn`` [1, N, H, 128] for Q, then K, t
   same tensors out in (6,8,8) tiles on the grid padded to 24x48x80 (N' = 92160).
 * ``vsmooth``    B=1, H=24, N=49152, seed 5. Q, K N(0,1). V N(0,1) with 5% of the tokens per
   head (2458) multiplied by 20 on 8 distinct random channels each (token outliers).
+* ``wan14b_local`` B=1, H=40, N=75600 (21x45x80), seed 6, kind ``video_local`` (below).
+
+Kind ``video_local`` (test and bench inputs for Sol routing; needs ``grid``): attention that
+falls off with the distance of the tokens on the (T, Hg, W) latent grid, as in video DiTs. Q, K
+and V are first drawn N(0,1) as above; then, drawing in this order from the same generator,
+F = randn [3, 128] / sigma (sigma = 1.5 grid steps) and b = 2 pi rand [128] give the random
+Fourier features phi(x) = sqrt(2 / 128) cos(x F + b) of each token's grid position x (raster
+order t, h, w), and Q = 16 phi + 0.5 Q, K = 16 phi + 0.5 K (so q . k / sqrt(128) peaks near
+22 * exp(-|x - y|^2 / (2 sigma^2)) for nearby tokens); V stays N(0,1).
 
 Kind ``channel_offset`` (test inputs for sequence-mean smoothing): Q, K, V N(0,1), then K and V
 each get a per-(head, channel) offset drawn after V as 4 * randn [H, 128] (K's first), the
@@ -39,6 +48,7 @@ CONFIGS = {
     "wan13b": dict(B=1, H=12, N=32760, seed=3, grid=(21, 30, 52)),
     "wan14b": dict(B=1, H=40, N=75600, seed=4, grid=(21, 45, 80)),
     "vsmooth": dict(B=1, H=24, N=49152, seed=5),
+    "wan14b_local": dict(B=1, H=40, N=75600, seed=6, grid=(21, 45, 80)),
 }
 
 
@@ -48,7 +58,7 @@ def _bits(x: torch.Tensor) -> np.ndarray:
 
 
 def make_qkv(B, N, H, seed, kind="normal", delta=None, head_dim=D, sink_keys=4,
-             outlier_tokens_frac=0.05, n_outlier_channels=4):
+             outlier_tokens_frac=0.05, n_outlier_channels=4, grid=None):
     """Returns bf16 torch tensors (q, k, v), each [B, N, H, head_dim], on the CPU."""
     g = torch.Generator("cpu").manual_seed(int(seed))
     shape = (B, N, H, head_dim)
@@ -78,6 +88,17 @@ def make_qkv(B, N, H, seed, kind="normal", delta=None, head_dim=D, sink_keys=4,
             sub = v[0, toks, h, :]
             sub.scatter_(1, ch, sub.gather(1, ch) * 20.0)
             v[0, toks, h, :] = sub
+    elif kind == "video_local":
+        T, Hg, W = grid
+        assert T * Hg * W == N
+        sigma = 1.5
+        Fm = torch.randn((3, head_dim), generator=g, dtype=torch.float64) / sigma
+        bph = 2.0 * math.pi * torch.rand((head_dim,), generator=g, dtype=torch.float64)
+        t, h, w = torch.meshgrid(torch.arange(T), torch.arange(Hg), torch.arange(W), indexing="ij")
+        x = torch.stack([t.reshape(-1), h.reshape(-1), w.reshape(-1)], dim=1).to(torch.float64)
+        phi = (math.sqrt(2.0 / head_dim) * torch.cos(x @ Fm + bph)).to(torch.float32)   # [N, D]
+        q = 16.0 * phi[None, :, None, :] + 0.5 * q
+        k = 16.0 * phi[None, :, None, :] + 0.5 * k
     elif kind == "channel_offset":
         for t in (k, v):
             t += 4.0 * torch.randn((H, head_dim), generator=g, dtype=torch.float32)
@@ -96,10 +117,10 @@ def workload(name, delta=None, heads=None, tokens=None):
     if tokens is not None:
         N = int(tokens)
     kind = {"dense512": "normal", "sink4096": "sink", "wan13b": "channel_outliers",
-            "wan14b": "normal", "vsmooth": "token_outliers"}[name]
+            "wan14b": "normal", "vsmooth": "token_outliers", "wan14b_local": "video_local"}[name]
     if name == "sink4096":
         seed = 20 + int(delta)
-    return make_qkv(B, N, H, seed, kind=kind, delta=delta)
+    return make_qkv(B, N, H, seed, kind=kind, delta=delta, grid=c.get("grid"))
 
 
 def bits(x: torch.Tensor) -> np.ndarray:
