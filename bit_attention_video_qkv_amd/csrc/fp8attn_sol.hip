@@ -262,9 +262,25 @@ __device__ __forceinline__ int kq_swz(int row) { return (row >> 1) & 7; }
 //   the summary route over the non-exact summaries: online softmax of (score * log2 e +
 //   log2 n_j) and PV with the V summaries on the BF16 matrix cores (O^T = Vbar^T P^T; a lane's
 //   P values of tile t, registers 8s..8s+7, are the B operand of k-step (t, s)).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void sol_route(SolParams p) {
+// The per-summary bookkeeping (mask bits, selection) stays in vector registers: the scalar unit
+// issues for a SIMD only every fourth cycle, so per-summary scalar work would bound the kernel.
+typedef const __attribute__((address_space(4))) float ConstF32;
+
+// OR over the 64 lanes: DPP within each row of 16 lanes, then across row pairs and halves.
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  v |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  v |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x124, 0xF, 0xF, false));  // rotate 4
+  v |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, false));  // rotate 8
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = a[0] | a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return b[0] | b[1];
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void sol_route(SolParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSlotBytes];
-  __shared__ uint32_t word_s[4][2];
+  __shared__ uint64_t word_s[4];
   const int64_t bh = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, lh = lane >> 5, l32 = lane & 31;
@@ -272,9 +288,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool ublock = u < p.NB;                                          // (uniform per wave)
   const int64_t qrow = 64 * u + 32 * (wave & 1) + l32;
   const bool qvalid = ublock && qrow < p.N;
-  const float theta = ublock ? p.theta[bh * p.NB + u] : 0.0f;
+  const float theta_u = ublock ? p.theta[bh * p.NB + u] : 0.0f;
+  const float theta = qvalid ? theta_u : INFINITY;  // rows past N never make a block exact
   const float sq = ublock ? p.q_scale[bh * p.NB + u] : 0.0f;
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kLn2 = 0.6931471805599453f;
+  constexpr float kLazy = 8.0f;
+  // every KV block holds 64 tokens except the last one
+  const float lg_last = __log2f(static_cast<float>(p.N - 64 * (p.NB - 1)));
+  // the group scales are read-only here: scalar loads, which leave the copies' counter alone
+  ConstF32* kqs = (ConstF32*)(p.kq_scale + bh * p.NBg);
 
   // copies of group g into slot g & 1: thread t issues chunks L = r * 256 + t (r < 6); the first
   // 512 chunks are the K summary tile (swizzled), the next 1024 the V summary tile (contiguous)
@@ -307,18 +330,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   stage(0);
   for (int64_t g = 0; g < p.NBg; g++) {
-    if (g + 1 < p.NBg) {
-      stage(g + 1);
-      wait_vmcnt<kCopiesPerThread>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    barrier_nofence();  // group g has landed in every wave's view
+    wait_vmcnt<0>();
+    // group g has landed in every wave's view, and every wave is done with the other slot
+    barrier_nofence();
+    if (g + 1 < p.NBg) stage(g + 1);
     const uint8_t* ks = lds + (g & 1) * kSlotBytes;
     const uint8_t* vsl = ks + kSlotK;
+    const int64_t left = p.NB - 64 * g;  // summaries from this group on
+    const uint64_t valid = left >= 64 ? ~0ull : (1ull << left) - 1ull;
 
     // route scores
-    const float cs = sq * p.kq_scale[bh * p.NBg + g] * p.softmax_scale;
+    const float cs = sq * kqs[g] * p.softmax_scale;
     float x[2][16];
 #pragma unroll
     for (int t = 0; t < 2; t++) {
@@ -341,72 +363,88 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; r++) x[t][r] = acc[r] * cs;
     }
-    // mask word of the Q block
-    uint32_t lo_bits = 0, hi_bits = 0;
+    // mask word of this wave's 32 queries: each lane packs its hits at the summaries' bit
+    // positions, then an OR over the wave (the two half-waves hold different summaries)
+    uint32_t wt[2];
 #pragma unroll
-    for (int t = 0; t < 2; t++)
+    for (int t = 0; t < 2; t++) {
+      uint32_t b = 0u;
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int js = 32 * t + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const bool hit = qvalid && 64 * g + js < p.NB && x[t][r] >= theta;
-        if (js < 32) lo_bits |= hit ? (1u << js) : 0u;
-        else hi_bits |= hit ? (1u << (js - 32)) : 0u;
-      }
-    for (int off = 32; off >= 1; off >>= 1) {
-      lo_bits |= __shfl_xor(lo_bits, off, 64);
-      hi_bits |= __shfl_xor(hi_bits, off, 64);
+      for (int r = 0; r < 16; r++) b |= x[t][r] >= theta ? 1u << (8 * (r >> 2) + (r & 3)) : 0u;
+      wt[t] = wave_or(b << (4 * lh));
     }
-    if (lane == 0) {
-      word_s[wave][0] = lo_bits;
-      word_s[wave][1] = hi_bits;
-    }
+    // (readfirstlane returns a signed int: widen through uint32_t, not by sign extension)
+    uint64_t word = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wt[1]))) << 32) |
+                    static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wt[0]));
+    if (lane == 0) word_s[wave] = word;
+    wait_lgkm0();
     barrier_nofence();
     const int pw = wave & 2;  // first wave of this Q block's pair
-    uint64_t word = (static_cast<uint64_t>(word_s[pw][1] | word_s[pw + 1][1]) << 32) |
-                    (word_s[pw][0] | word_s[pw + 1][0]);
+    word = (word_s[pw] | word_s[pw + 1]) & valid;
     const int64_t sink_end = min<int64_t>(static_cast<int64_t>(p.sink_blocks), p.NB) - 64 * g;
     if (sink_end > 0) word |= sink_end >= 64 ? ~0ull : ((1ull << sink_end) - 1ull);
     if (ublock && (wave & 1) == 0 && lane == 0) p.mask[(bh * p.NB + u) * p.W + g] = word;
 
-    // summary route
-    const int64_t nsum = min<int64_t>(64, p.NB - 64 * g) - __builtin_popcountll(word & (~0ull >> (64 - min<int64_t>(64, p.NB - 64 * g))));
-    if (ublock && nsum > 0) {
+    // summary route over the group's non-exact summaries
+    const uint64_t sbits = valid & ~word;
+    if (ublock && sbits != 0ull) {
+      if (sbits != ~0ull) {  // exact and padding summaries drop out
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          const uint32_t sv = static_cast<uint32_t>(sbits >> (32 * t)) >> (4 * lh);  // this lane's bits
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int pos = 8 * (r >> 2) + (r & 3);
+            const uint32_t keep = static_cast<uint32_t>(static_cast<int32_t>(sv << (31 - pos)) >> 31);
+            x[t][r] = __uint_as_float((__float_as_uint(x[t][r]) & keep) | (0xFF800000u & ~keep));
+          }
+        }
+      }
+      if (left <= 64) {  // the last KV block weighs its token count instead of 64
+        const int jl = static_cast<int>(left) - 1;
+        const float dx = (lg_last - 6.0f) * kLn2;
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+#pragma unroll
+          for (int r = 0; r < 16; r++)
+            if (32 * t + 8 * (r >> 2) + 4 * lh + (r & 3) == jl) x[t][r] += dx;
+      }
       float mloc = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; t++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int js = 32 * t + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const int64_t j = 64 * g + js;
-          const bool summ = j < p.NB && ((word >> js) & 1ull) == 0ull;
-          const float lgn = j == p.NB - 1 ? __log2f(static_cast<float>(p.N - 64 * j)) : 6.0f;
-          x[t][r] = summ ? __builtin_fmaf(x[t][r], kLog2e, lgn) : -INFINITY;
-          mloc = fmaxf(mloc, x[t][r]);
-        }
+        for (int r = 0; r < 16; r++) mloc = fmaxf(mloc, x[t][r]);
       {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
         mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      // weight exponents score * log2 e + 6 (mloc is finite: the group has a summary-routed
+      // block). The reference point m_run moves only when some row's maximum passes it by more
+      // than kLazy, so the accumulators are rescaled a few times per row, not every group;
+      // weights stay below 2^kLazy.
+      const float ml2 = __builtin_fmaf(mloc, kLog2e, 6.0f);
+      if (__builtin_amdgcn_ballot_w64(ml2 > m_run + kLazy) != 0ull) {
+        const float m_new = fmaxf(m_run, ml2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on a row's first group
+        m_run = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
+      }
+      const float c6 = 6.0f - m_run;
       float psum = 0.0f;
       bf16x8 pb[2][2];
 #pragma unroll
       for (int t = 0; t < 2; t++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-          const float pv = __builtin_amdgcn_exp2f(x[t][r] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(x[t][r], kLog2e, c6));
           psum += pv;
           pb[t][r >> 3][r & 7] = static_cast<__bf16>(pv);
         }
-      l_part = alpha * l_part + psum;
-      if (alpha != 1.0f) {
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
-      }
+      l_part += psum;
 #pragma unroll
       for (int t = 0; t < 2; t++)
 #pragma unroll
@@ -417,8 +455,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             oacc[dt] = mfma_bf16(av, pb[t][s2], oacc[dt]);
           }
     }
-    wait_lgkm0();
-    barrier_nofence();  // every read of this slot is done before the next group refills it
+    wait_lgkm0();  // every read of this slot has returned before the next barrier frees it
   }
 
   // epilogue: the summary route's normalised output (piece 1) and log2 of its weight, in the
