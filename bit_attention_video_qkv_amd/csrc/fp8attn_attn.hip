@@ -35,6 +35,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kTileBytes = kBlock * kHeadDim;  // 8 KB: one 64-key K tile or V tile
 
@@ -56,6 +57,25 @@ __device__ __forceinline__ int k_row_of(int t, int i) {
 
 __device__ __forceinline__ v16f mfma_f8(const v8i& a, const v8i& b, const v16f& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// ExpCast row sums on the matrix cores: C += A B with B = the wave's E4M3 P bytes (the PV B
+// operand: lane l holds query l % 32, keys [32 (l / 32), +32)) read as the B operand of a
+// 16x16x128 MFMA, and A a 0/1 selector. Lane group g = l / 16 of either operand carries the
+// same quarter of the 128-deep contraction, so output column n sums, over the groups g that row
+// m selects, the bytes of lane 16 g + n: query n's keys in groups 0 and 2, query n + 16's in
+// groups 1 and 3. Output lane L holds column L % 16 in rows 4 (L / 16) .. +3; selecting groups
+// of L's parity, (L / 16) % 2 = (L / 4 of the row) % 2, gives every lane the sum over all 64 keys
+// of the query it owns in the PV layout (L % 32), in all four registers.
+__device__ __forceinline__ v8i rowsum_selector(int lane) {
+  const int sel = ((lane >> 4) & 1) == ((lane >> 2) & 1) ? 0x38383838 : 0;  // E4M3 1.0 or 0
+  v8i a;
+#pragma unroll
+  for (int w = 0; w < 8; w++) a[w] = sel;
+  return a;
+}
+__device__ __forceinline__ v4f mfma_rowsum(const v8i& sel, const v8i& p8, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, p8, c, 0, 0, 0, 0, 0, 0);
 }
 
 // IEEE maximum (v_maximum3_f32 on gfx950): unlike fmaxf it needs no NaN canonicalisation of
@@ -371,8 +391,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
   for (int w = 0; w < 8; w++) pop[w] = 0;
   float m_run = -INFINITY;  // running max, log2 units
-  float l_part = 0.0f;      // this lane's 32-key share of the S-scaled row sum
-  float r_cur = 0.0f;       // V-Smooth: S-scaled row sum of the open V block
+  // Standard cast: this lane's 32-key share of the S-scaled row sum. ExpCast: the whole row's
+  // S-scaled sum over the closed V blocks (V-Smooth), else unused.
+  float l_part = 0.0f;
+  float r_cur = 0.0f;       // V-Smooth, standard cast: S-scaled row sum of the open V block
+  // ExpCast: S-scaled row sums of the P codes accumulated on the matrix cores (lacc[0] in every
+  // lane: the lane's whole query row), rescaled with O; with V-Smooth only since the last mean
+  // restore. The restore of a V block closed at block j waits for block j's sum, one block later
+  // (mu_pend: that V block's mean factors, rs_pend: a restore is pending).
+  const v8i rs_sel = rowsum_selector(lane);
+  v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float mu_pend[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  bool rs_pend = false;
   unsigned long long n_under = 0;
   v8i kop[2][2], vop[4];
   float sk_cur = 0.0f, sk_next = 0.0f;
@@ -434,6 +464,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   auto pv = [&]() {
 #pragma unroll
     for (int dt = 0; dt < 4; dt++) oacc[dt] = mfma_f8(vop[dt], pop, oacc[dt]);
+    if constexpr (EXPCAST) lacc = mfma_rowsum(rs_sel, pop, lacc);
   };
 
   // Orders the QK MFMAs of key sub-tile t of the next block after the P bytes of sub-tile t of
@@ -478,30 +509,29 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     const float mloc = fmax_ieee(mlo, mhi);
     // every visited block holds a valid key, so the max is finite after the first block; the
     // guard only keeps a fully masked first block from producing NaN
-    const float m_cand = fmax_ieee(m_run, xmax(mloc) * cs);
+    const float xrow = xmax(mloc);
+    const float m_cand = fmax_ieee(m_run, xrow * cs);
     const float m_new = m_cand == -INFINITY ? 0.0f : m_cand;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_cand;
-    float lsum;
+    float lsum = 0.0f;
     if constexpr (EXPCAST) {
+      // code = clamp(rint(8 z + 56 - 0.35), 0, 126) with z = log2(S p~): one FMA per key, then
+      // v_cvt_pk_u8_f32, which rounds to nearest even, saturates to [0, 255] (NaN and -inf to
+      // 0) and inserts the byte into the P word. The largest code of the block is that of the
+      // row maximum, 8 log2 S + 55.65 <= 126.11 for S <= 448, so the upper clamp is inactive;
+      // b8 is lowered only if the rounding of b8 at huge logits would carry the row maximum to
+      // 0x7F (E4M3 NaN). The row sums come from the matrix cores (pv).
       const float c8 = 8.0f * cs;
-      const float b8 = 8.0f * (p.log2S - m_new) + 55.65f;
-      float l4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float b8 = 8.0f * (p.log2S - m_new) + 55.65f;
+      b8 -= fmaxf(__builtin_fmaf(xrow, c8, b8) - 126.25f, 0.0f);
 #pragma unroll
       for (int w = 0; w < 8; w++) {
-        uint32_t word = 0;
+        uint32_t word = static_cast<uint32_t>(pop[w]);  // every byte is overwritten
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const float tq = __builtin_fmaf(x[4 * w + q], c8, b8);
-          const float code = fminf(fmaxf(__builtin_rintf(tq), 0.0f), 126.0f);
-          word |= static_cast<uint32_t>(code) << (8 * q);
-        }
+        for (int q = 0; q < 4; q++) word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(x[4 * w + q], c8, b8), q, word);
         pop[w] = static_cast<int>(word);
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(word), false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(word), true);
-        l4[w & 3] += (lo[0] + lo[1]) + (hi[0] + hi[1]);
       }
-      lsum = (l4[0] + l4[1]) + (l4[2] + l4[3]);
       tie_k(0, lsum);
       tie_k(1, lsum);
       interleave_region1();
@@ -546,9 +576,29 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         issue_qk_half(t);
       }
     }
-    l_part = alpha * l_part + lsum;
-    if constexpr (VSMOOTH) r_cur = alpha * r_cur + xsum(lsum);
+    if constexpr (!EXPCAST) {
+      l_part = alpha * l_part + lsum;
+      if constexpr (VSMOOTH) r_cur = alpha * r_cur + xsum(lsum);
+    }
     return alpha;
+  };
+
+  // V-Smooth with ExpCast: rank-one mean restore O^T += mu r^T of a closed V block from its
+  // factors kept in registers and its row sum on the matrix cores (lacc), which then restarts.
+  auto keep_mean_factors = [&](const uint8_t* sl) {
+    const float* mu = reinterpret_cast<const float*>(sl + kMeanOff);
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) mu_pend[dt] = lh == 0 ? mu[32 * dt + l32] : 0.0f;
+    rs_pend = true;
+  };
+  auto restore_pending = [&]() {
+    const float r = lacc[0];
+    const float rb = lh == 0 ? r : 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(mu_pend[dt], rb, oacc[dt], 0, 0, 0);
+    l_part += r;
+    lacc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    rs_pend = false;
   };
 
   // One key block j; `sl` is the slot of pair j+1 (read here, then refilled with pair j+4).
@@ -567,8 +617,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       for (int dt = 0; dt < 4; dt++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[dt][r] *= alpha;
+      if constexpr (EXPCAST) {
+        lacc[0] *= alpha;  // the only register of the sum that is read
+        if constexpr (VSMOOTH) l_part *= alpha;
+      }
     }
-    if constexpr (VSMOOTH) {
+    if constexpr (VSMOOTH && EXPCAST) {
+      // ExpCast: the row sum of a V block's last key block is on the matrix cores one block
+      // later, so the restore of the V block closed at block j-1 happens here (O and lacc both
+      // in the units of the running max of block j), and block j's closing is recorded
+      if (rs_pend) restore_pending();
+      if (closes_vblock(j)) keep_mean_factors(sl);
+    } else if constexpr (VSMOOTH) {
       if (closes_vblock(j)) {
         // rank-one mean restore of the V block that block j closes (its factors travel in pair
         // j+1); O holds blocks up to j-1 in the units of the running max of block j, like r
@@ -636,6 +696,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   }
   if (partial_tail && !p.reverse) iteration(kMasked{}, n_iter - 1, slot(sidx));
   pv();  // PV of the last block (vop = V(n_iter - 1))
+  if constexpr (VSMOOTH && EXPCAST) {
+    if (rs_pend) restore_pending();  // the last block closes its V block
+  }
 
   if constexpr (STATS) {
     unsigned long long tot = n_under;
@@ -646,7 +709,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // ---- epilogue: O = acc * g_d / l', BF16, scattered to the destination rows ----
   bool ok = qrow < p.N;
   if constexpr (SPARSE && !SOL) ok = ok && static_cast<int>(qrow % p.tile_tokens) < q_valid_len;
-  const float l_tot = xsum(l_part);
+  // the S-scaled row sum: standard cast, the two lane halves' shares; ExpCast, the matrix-core
+  // sum, whole in every lane (with V-Smooth, collected per V block in l_part)
+  float l_tot;
+  if constexpr (EXPCAST) l_tot = VSMOOTH ? l_part : lacc[0];
+  else l_tot = xsum(l_part);
   if constexpr (!SPARSE || SOL) {
     if (p.o_part) {
       // split-KV piece or Sol exact route: this piece's normalised O (FP32) and log2 of its
