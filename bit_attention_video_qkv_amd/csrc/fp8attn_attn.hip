@@ -357,6 +357,40 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     }
     kb_prev = kb;
   };
+  // Dense steady state (a K block and a V block to stage, pair index >= 1): the same pair with
+  // less bookkeeping. Wave 0 copies s_k first, so that after its K/V copies every wave has the
+  // same number of copies of this pair in flight; the valid-key count is not staged (dense
+  // blocks are full except NB-1, whose count is lim_tail).
+  // The source pointers move by one tile per pair in the KV order: st_k / st_s at the next K
+  // block kb and its s_k, st_v at the V tile of block kb_prev (set by stage_dense_init).
+  const int64_t kv_dir = p.reverse ? -1 : 1;
+  const uint8_t* st_k = kbase;
+  const uint8_t* st_v = vbase;
+  const float* st_s = p.k_scale;
+  auto stage_dense_init = [&]() {
+    const int64_t kb = p.reverse ? (p.NB - 1 - lc.e) : lc.e;
+    st_k = kbase + kb * kTileBytes;
+    st_v = vbase + kb_prev * kBlock;
+    st_s = p.k_scale + bh * p.NB + kb;
+  };
+  auto stage_dense = [&](uint8_t* sl) {
+    const uint32_t l0 = lds_addr_of(sl);
+    if (wave == 0 && lane == 0) copy4_to_lds(st_s, 0u, l0 + kMetaOff);
+#pragma unroll
+    for (int r = 0; r < kChunks; r++) copy16_to_lds(st_k, koff[r], l0 + (r * kThreads + wave * 64) * 16);
+#pragma unroll
+    for (int r = 0; r < kChunks; r++) copy16_to_lds(st_v, voff[r], l0 + kTileBytes + (r * kThreads + wave * 64) * 16);
+    if constexpr (VSMOOTH) {
+      if (lane < kMeanLanes)
+        copy16_to_lds(p.mu_f + (bh * p.NB128 + (kb_prev >> 1)) * kHeadDim, 16u * (wave * kMeanLanes + lane),
+                      l0 + kMeanOff + wave * kMeanLanes * 16);
+    }
+    st_k += kv_dir * kTileBytes;
+    st_v += kv_dir * kBlock;
+    st_s += kv_dir;
+    kb_prev += kv_dir;
+    lc.e++;
+  };
   // Waits until only the copies of the newest staged pair may still be in flight.
   auto wait_all_but_newest = [&]() {
     if (wave == 0) wait_vmcnt<kCopies + 1>();
@@ -407,6 +441,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   v8i kop[2][2], vop[4];
   float sk_cur = 0.0f, sk_next = 0.0f;
   int lim_cur = kBlock, lim_next = kBlock;
+  const int lim_tail = static_cast<int>(p.N - (p.NB - 1) * kBlock);  // valid keys of block NB-1
   int kb_next = 0;                      // Sol: key block of the next K tile
   bool ex_cur = false, ex_next = false;  // Sol: that block is not exact for this wave's Q block
 
@@ -492,8 +527,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       // wave's own Q-block mask counts as fully masked.
       bool excluded = false;
       if constexpr (kSolPair) excluded = ex_cur;
-      if (__builtin_amdgcn_readfirstlane(lim_cur) < kBlock || excluded) {
-        int nv = excluded ? 0 : lim_cur - 32 * lh;  // valid keys among this lane's 32
+      // (dense: the one masked block is the partial last key block)
+      const int lim = (SPARSE || SOL) ? lim_cur : lim_tail;
+      if (__builtin_amdgcn_readfirstlane(lim) < kBlock || excluded) {
+        int nv = excluded ? 0 : lim - 32 * lh;  // valid keys among this lane's 32
         asm volatile("" : "+v"(nv));
 #pragma unroll
         for (int q = 0; q < 32; q++) x[q] = q < nv ? x[q] : -INFINITY;
@@ -603,7 +640,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // One key block j; `sl` is the slot of pair j+1 (read here, then refilled with pair j+4).
   // The masked copy serves blocks with fewer than 64 valid keys.
-  auto iteration = [&](auto mask_tag, int j, uint8_t* sl) {
+  // Steady (dense only): pairs j+2 and j+4 hold key blocks, so the waits and the staging need no
+  // checks and the staging is stage_dense.
+  auto iteration = [&](auto mask_tag, auto steady_tag, int j, uint8_t* sl) {
+    constexpr bool kSteady = decltype(steady_tag)::value;
     pv();         // PV of block j-1 (zero P bytes before the first block)
     read_v(sl);   // V(j)
     read_k(sl);   // K(j+1)
@@ -646,13 +686,19 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     }
     // hand-off: every read of this slot is complete, pair j+2 has landed everywhere
     wait_lgkm0();
-    if (j + 3 <= n_iter) wait_all_but_newest();
-    else wait_vmcnt<0>();
+    if constexpr (kSteady) {
+      wait_vmcnt<kCopies>();
+    } else if (j + 3 <= n_iter) {
+      wait_all_but_newest();
+    } else {
+      wait_vmcnt<0>();
+    }
     barrier_nofence();
     sk_cur = sk_next;
     lim_cur = lim_next;
     ex_cur = ex_next;
-    if (j + 4 <= n_iter) stage(j + 4, sl);
+    if constexpr (kSteady) stage_dense(sl);
+    else if (j + 4 <= n_iter) stage(j + 4, sl);
   };
 
   // ---- prologue: pairs 0..2 staged; K(0) read; QK of block 0; pair 3 staged ----
@@ -682,19 +728,41 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   using kNoMask = std::integral_constant<bool, false>;
   using kMasked = std::integral_constant<bool, true>;
   using kLoopMask = std::integral_constant<bool, SPARSE || SOL>;
+  using kGeneric = std::integral_constant<bool, false>;
+  using kSteady = std::integral_constant<bool, true>;
   const bool partial_tail = !SPARSE && !SOL && (p.N % kBlock) != 0 && has_last_block;
-  int j_begin = 0, j_end = n_iter, sidx = 1;  // sidx: slot of pair j+1
+  int j = 0, j_end = n_iter, sidx = 1;  // sidx: slot of pair j+1
   if (partial_tail && p.reverse) {
-    iteration(kMasked{}, 0, slot(1));
-    j_begin = 1;
+    iteration(kMasked{}, kGeneric{}, 0, slot(1));
+    j = 1;
     sidx = 2;
   }
   if (partial_tail && !p.reverse) j_end = n_iter - 1;
-  for (int j = j_begin; j < j_end; j++) {
-    iteration(kLoopMask{}, j, slot(sidx));
+  if constexpr (!SPARSE && !SOL) {
+    // dense: generic blocks until pair j+1 sits in slot 0, then steady blocks three at a time
+    // with constant slots while block j+2 stages a key block (j + 2 + 4 < n_iter)
+    while (j < j_end && sidx != 0) {
+      iteration(kLoopMask{}, kGeneric{}, j, slot(sidx));
+      sidx = sidx == 2 ? 0 : sidx + 1;
+      j++;
+    }
+    // (the underflow-counting variant, a debugging aid, stays on the generic path)
+    const int j_steady = STATS ? 0 : min(j_end, n_iter - 4);  // steady blocks: j < j_steady
+    if (j + 3 <= j_steady) stage_dense_init();
+    for (; j + 3 <= j_steady; j += 3) {
+      iteration(kNoMask{}, kSteady{}, j, slot(0));
+      __builtin_amdgcn_sched_barrier(0);
+      iteration(kNoMask{}, kSteady{}, j + 1, slot(1));
+      __builtin_amdgcn_sched_barrier(0);
+      iteration(kNoMask{}, kSteady{}, j + 2, slot(2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  for (; j < j_end; j++) {
+    iteration(kLoopMask{}, kGeneric{}, j, slot(sidx));
     sidx = sidx == 2 ? 0 : sidx + 1;
   }
-  if (partial_tail && !p.reverse) iteration(kMasked{}, n_iter - 1, slot(sidx));
+  if (partial_tail && !p.reverse) iteration(kMasked{}, kGeneric{}, n_iter - 1, slot(sidx));
   pv();  // PV of the last block (vop = V(n_iter - 1))
   if constexpr (VSMOOTH && EXPCAST) {
     if (rs_pend) restore_pending();  // the last block closes its V block
