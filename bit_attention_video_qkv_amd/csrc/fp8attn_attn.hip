@@ -414,6 +414,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   }
   const int64_t qblk = (q0 + 32 * wave) / kBlock;  // the wave's 32 rows lie in one Q block
   const float s_q = qblk < p.NB ? p.q_scale[bh * p.NB + qblk] : 0.0f;
+  const float sq_ls = s_q * p.logit_scale;
 
   // ---- per-wave state ----
   v16f oacc[4], sacc[2];
@@ -515,7 +516,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // E4M3 P bytes into pop and returns alpha.
   auto softmax = [&](auto mask_tag, auto&& issue_qk_half) -> float {
     constexpr bool kMask = decltype(mask_tag)::value;
-    const float cs = fmaxf(s_q * sk_cur * p.logit_scale, 1e-30f);  // log2 units per MFMA unit
+    // log2 units per MFMA unit; floored above zero where masked keys (-inf) could meet a zero
+    // scale (0 * -inf would be NaN)
+    const float cs = kMask ? fmaxf(sq_ls * sk_cur, 1e-30f) : sq_ls * sk_cur;
     float x[32];
 #pragma unroll
     for (int t = 0; t < 2; t++)
@@ -544,11 +547,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       mhi = fmax_ieee(fmax_ieee(mhi, x[q + 2]), x[q + 3]);
     }
     const float mloc = fmax_ieee(mlo, mhi);
-    // every visited block holds a valid key, so the max is finite after the first block; the
-    // guard only keeps a fully masked first block from producing NaN
+    // every dense block holds a valid key, so the max is finite from the first block on; the
+    // sparse and Sol guard keeps a fully masked first block from producing NaN
     const float xrow = xmax(mloc);
     const float m_cand = fmax_ieee(m_run, xrow * cs);
-    const float m_new = m_cand == -INFINITY ? 0.0f : m_cand;
+    const float m_new = (SPARSE || SOL) && m_cand == -INFINITY ? 0.0f : m_cand;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_cand;
     float lsum = 0.0f;
