@@ -27,7 +27,7 @@ ATTN_SRC = os.path.join(ROOT, "bit_attention_video_qkv_amd", "csrc", "fp8attn_at
 # HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) as measured by
 # rocprofv3 for the attention source whose code (comments and blank lines dropped) has this
 # sha256 prefix, per workload; see profiles/. Reported only while that code is unchanged.
-MEASURED_TRAFFIC = {("e2972fb88e7d", "wan14b"): 75029224372}
+MEASURED_TRAFFIC = {("8750fe315d64", "wan14b"): 16188853801}
 
 
 def code_sha(path):
