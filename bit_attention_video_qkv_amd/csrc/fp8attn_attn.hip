@@ -141,6 +141,9 @@ struct KvCursor {
   int bt;    // sparse: block within the KV tile
   int v;     // sparse: KV tile id col_idx[e]
   int len;   // sparse: valid tokens of tile v
+  // sparse, loaded ahead so that a tile switch waits on no load: the next tile's id and valid
+  // tokens, and the id of the tile after it (entries e + dir and e + 2 dir of the CSR row)
+  int v1, len1, v2;
 };
 
 // One workgroup owns WAVES * 32 query rows of one (b, h); each wave owns 32 of them.
@@ -253,11 +256,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     return;  // (otherwise: a query tile without key blocks has no defined output)
   }
 
+  const int edir = p.reverse ? -1 : 1;  // sparse: CSR entries in the KV order
+  auto in_row = [&](int e) -> bool { return e >= e_begin && e < e_end; };
   KvCursor lc;  // the copy engine's cursor: the next K block to stage
   lc.e = static_cast<int>(e0);
   lc.bt = 0;
   lc.v = 0;
   lc.len = 0;
+  lc.v1 = lc.len1 = lc.v2 = 0;
   if constexpr (SOL) {
     lc.v = static_cast<int>(p.reverse ? sol_prev(p.NB - 1) : sol_next(0));
   } else if constexpr (SPARSE) {
@@ -265,6 +271,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     lc.v = p.col_idx[lc.e];
     lc.len = p.tile_len[lc.v];
     lc.bt = p.reverse ? nblk_of_len(lc.len) - 1 : 0;
+    lc.v1 = in_row(lc.e + edir) ? p.col_idx[lc.e + edir] : 0;
+    lc.len1 = in_row(lc.e + edir) ? p.tile_len[lc.v1] : 0;
+    lc.v2 = in_row(lc.e + 2 * edir) ? p.col_idx[lc.e + 2 * edir] : 0;
   }
   auto block_of = [&](const KvCursor& c, int& limit) -> int64_t {
     if constexpr (SOL) {
@@ -283,21 +292,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     if constexpr (SOL) {
       c.v = static_cast<int>(p.reverse ? sol_prev(c.v - 1) : sol_next(c.v + 1));
     } else if constexpr (SPARSE) {
-      if (!p.reverse) {
-        if (++c.bt >= nblk_of_len(c.len)) {
-          c.e++;
-          c.bt = 0;
-          if (c.e < e_end) {
-            c.v = p.col_idx[c.e];
-            c.len = p.tile_len[c.v];
-          }
-        }
-      } else if (--c.bt < 0) {
-        c.e--;
-        if (c.e >= e_begin) {
-          c.v = p.col_idx[c.e];
-          c.len = p.tile_len[c.v];
-          c.bt = nblk_of_len(c.len) - 1;
+      const bool next_tile = p.reverse ? --c.bt < 0 : ++c.bt >= nblk_of_len(c.len);
+      if (next_tile) {
+        c.e += edir;
+        if (in_row(c.e)) {
+          c.v = c.v1;
+          c.len = c.len1;
+          c.bt = p.reverse ? nblk_of_len(c.len) - 1 : 0;
+          c.v1 = c.v2;
+          c.len1 = in_row(c.e + edir) ? p.tile_len[c.v1] : 0;
+          c.v2 = in_row(c.e + 2 * edir) ? p.col_idx[c.e + 2 * edir] : 0;
         }
       }
     } else {
@@ -643,8 +647,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // One key block j; `sl` is the slot of pair j+1 (read here, then refilled with pair j+4).
   // The masked copy serves blocks with fewer than 64 valid keys.
-  // Steady (dense only): pairs j+2 and j+4 hold key blocks, so the waits and the staging need no
-  // checks and the staging is stage_dense.
+  // Steady (dense and STA): pairs j+2 and j+4 hold key blocks, so the waits and the staging need
+  // no checks; dense staging is stage_dense.
   auto iteration = [&](auto mask_tag, auto steady_tag, int j, uint8_t* sl) {
     constexpr bool kSteady = decltype(steady_tag)::value;
     pv();         // PV of block j-1 (zero P bytes before the first block)
@@ -700,8 +704,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     sk_cur = sk_next;
     lim_cur = lim_next;
     ex_cur = ex_next;
-    if constexpr (kSteady) stage_dense(sl);
-    else if (j + 4 <= n_iter) stage(j + 4, sl);
+    if constexpr (kSteady) {
+      if constexpr (SPARSE) stage(j + 4, sl);  // (its key block exists: j + 4 < n_iter)
+      else stage_dense(sl);
+    } else if (j + 4 <= n_iter) {
+      stage(j + 4, sl);
+    }
   };
 
   // ---- prologue: pairs 0..2 staged; K(0) read; QK of block 0; pair 3 staged ----
@@ -741,9 +749,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     sidx = 2;
   }
   if (partial_tail && !p.reverse) j_end = n_iter - 1;
-  if constexpr (!SPARSE && !SOL) {
-    // dense: generic blocks until pair j+1 sits in slot 0, then steady blocks three at a time
-    // with constant slots while block j+2 stages a key block (j + 2 + 4 < n_iter)
+  if constexpr (!SOL) {
+    // dense and STA: generic blocks until pair j+1 sits in slot 0, then steady blocks three at a
+    // time with constant slots while block j+2 stages a key block (j + 2 + 4 < n_iter). STA
+    // blocks keep the per-block valid-key check (partial blocks end tiles anywhere).
     while (j < j_end && sidx != 0) {
       iteration(kLoopMask{}, kGeneric{}, j, slot(sidx));
       sidx = sidx == 2 ? 0 : sidx + 1;
@@ -751,13 +760,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     }
     // (the underflow-counting variant, a debugging aid, stays on the generic path)
     const int j_steady = STATS ? 0 : min(j_end, n_iter - 4);  // steady blocks: j < j_steady
-    if (j + 3 <= j_steady) stage_dense_init();
+    using kSteadyMask = std::integral_constant<bool, SPARSE>;
+    if constexpr (!SPARSE) {
+      if (j + 3 <= j_steady) stage_dense_init();
+    }
     for (; j + 3 <= j_steady; j += 3) {
-      iteration(kNoMask{}, kSteady{}, j, slot(0));
+      iteration(kSteadyMask{}, kSteady{}, j, slot(0));
       __builtin_amdgcn_sched_barrier(0);
-      iteration(kNoMask{}, kSteady{}, j + 1, slot(1));
+      iteration(kSteadyMask{}, kSteady{}, j + 1, slot(1));
       __builtin_amdgcn_sched_barrier(0);
-      iteration(kNoMask{}, kSteady{}, j + 2, slot(2));
+      iteration(kSteadyMask{}, kSteady{}, j + 2, slot(2));
       __builtin_amdgcn_sched_barrier(0);
     }
   }
