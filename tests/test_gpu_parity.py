@@ -210,6 +210,26 @@ def test_attention_expcast_small(m, orc, N, reverse):
     _compare_out(_gpu_rows(out, np.arange(N)), ref, "expcast", amb)
 
 
+@pytest.mark.parametrize("S", [256.0, 448.0])
+def test_attention_expcast_extreme_logits(m, orc, S):
+    """ExpCast with logits of order 1e4-1e5 in log2 units (Q and K scaled by 48): the byte of a
+    block's row maximum is 8 log2 S + 55.65 (at most 126.11) and must stay at or below 126 (0x7F
+    is E4M3 NaN) whatever the FP32 rounding of the per-block bias; the output is finite and
+    within tolerance of the oracle."""
+    say("expcast extreme logits", S)
+    N, H = 640, 2
+    q, k, v = workloads.make_qkv(1, N, H, seed=77)
+    q = (q.float() * 48.0).to(torch.bfloat16)
+    k = (k.float() * 48.0).to(torch.bfloat16)
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref, _, _, _, amb = orc.attention_fp8(orc.quantize(qb, kb, vb), p_scale=S, kv_reverse=True,
+                                          expcast=True, return_amb=True)
+    qz = _gpu_quantize(m, q, k, v)
+    out = _run_attn(m, qz, p_scale=S, kv_order=1, pcast=m.FP8ATTN_PCAST_EXPCAST)
+    assert torch.isfinite(out.float()).all()
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, f"expcast extreme S={S}", amb)
+
+
 @pytest.mark.parametrize("N,reverse,expcast", [(1000, True, False), (768, False, True),
                                                (300, False, False)])
 def test_attention_vsmooth_small(m, orc, N, reverse, expcast):
