@@ -186,7 +186,7 @@ size_t fp8attn_forward_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t 
                                        int32_t kv_splits) {
   if (B < 1 || N < 1 || H < 1 || D != kHeadDim || !valid_splits_arg(kv_splits)) return 0;
   const size_t bh = static_cast<size_t>(B) * H;
-  size_t n = vsmooth ? round_up(bh * cdiv(N, 128) * kHeadDim * sizeof(float)) : 0;
+  size_t n = vsmooth ? round_up(bh * cdiv(N, 128) * kHeadDim * 16) : 0;  // mean operand records
   int64_t split_blocks = 0;
   const int splits = resolve_splits(B, N, H, kv_splits, &split_blocks);
   if (splits > 1)
@@ -243,12 +243,12 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
   p.k_scale = k_scale;
   p.v_scale = v_scale;
   p.v_mean = v_mean;
-  p.mu_f = vsmooth ? static_cast<float*>(workspace) : nullptr;
+  p.mu_op = vsmooth ? static_cast<uint32_t*>(workspace) : nullptr;
   p.splits = splits;
   p.split_blocks = splits > 1 ? split_blocks : cdiv(N, 64);
   if (splits > 1) {
     const size_t bh = static_cast<size_t>(total_bh);
-    char* ws = static_cast<char*>(workspace) + (vsmooth ? round_up(bh * cdiv(N, 128) * kHeadDim * sizeof(float)) : 0);
+    char* ws = static_cast<char*>(workspace) + (vsmooth ? round_up(bh * cdiv(N, 128) * kHeadDim * 16) : 0);
     p.o_part = reinterpret_cast<float*>(ws);
     p.lse = reinterpret_cast<float*>(ws + round_up(splits * bh * N * kHeadDim * sizeof(float)));
   }

@@ -36,6 +36,8 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kTileBytes = kBlock * kHeadDim;  // 8 KB: one 64-key K tile or V tile
 
@@ -166,9 +168,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   constexpr int kRowsPerWg = WAVES * 32;
   constexpr int kChunks = 512 / kThreads;       // 16-byte chunks per thread of one 8 KB tile
   constexpr int kMetaOff = 2 * kTileBytes;      // s_k (f32) and valid keys (i32) of the K block
-  constexpr int kMeanOff = kMetaOff + 16;       // V-Smooth mean factors, 128 x f32
-  constexpr int kSlotBytes = kMeanOff + (VSMOOTH ? kHeadDim * 4 : 0);  // multiple of 16
-  constexpr int kMeanLanes = 32 / WAVES;        // V-Smooth: lanes per wave copying the factors
+  constexpr int kMeanOff = kMetaOff + 16;       // V-Smooth mean operand records, 128 x 16 B
+  constexpr int kSlotBytes = kMeanOff + (VSMOOTH ? kHeadDim * 16 : 0);  // multiple of 16
+  constexpr int kMeanLanes = 128 / WAVES;       // V-Smooth: lanes per wave copying the records
   constexpr int kCopies = 2 * kChunks + (VSMOOTH ? 1 : 0);  // copies per pair (wave 0: +1, s_k)
   __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kSlotBytes];
   auto slot = [&](int i) -> uint8_t* { return lds + i * kSlotBytes; };
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int r = 0; r < kChunks; r++) copy16_to_lds(vt, voff[r], l0 + kTileBytes + (r * kThreads + wave * 64) * 16);
     if constexpr (VSMOOTH) {
       if (lane < kMeanLanes)
-        copy16_to_lds(p.mu_f + (bh * p.NB128 + (vb >> 1)) * kHeadDim, 16u * (wave * kMeanLanes + lane),
+        copy16_to_lds(p.mu_op + (bh * p.NB128 + (vb >> 1)) * kHeadDim * 4, 16u * (wave * kMeanLanes + lane),
                       l0 + kMeanOff + wave * kMeanLanes * 16);
     }
     if (wave == 0 && lane == 0) {
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int r = 0; r < kChunks; r++) copy16_to_lds(st_v, voff[r], l0 + kTileBytes + (r * kThreads + wave * 64) * 16);
     if constexpr (VSMOOTH) {
       if (lane < kMeanLanes)
-        copy16_to_lds(p.mu_f + (bh * p.NB128 + (kb_prev >> 1)) * kHeadDim, 16u * (wave * kMeanLanes + lane),
+        copy16_to_lds(p.mu_op + (bh * p.NB128 + (kb_prev >> 1)) * kHeadDim * 4, 16u * (wave * kMeanLanes + lane),
                       l0 + kMeanOff + wave * kMeanLanes * 16);
     }
     st_k += kv_dir * kTileBytes;
@@ -436,12 +438,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   float r_cur = 0.0f;       // V-Smooth, standard cast: S-scaled row sum of the open V block
   // ExpCast: S-scaled row sums of the P codes accumulated on the matrix cores (lacc[0] in every
   // lane: the lane's whole query row), rescaled with O; with V-Smooth only since the last mean
-  // restore. The restore of a V block closed at block j waits for block j's sum, one block later
-  // (mu_pend: that V block's mean factors, rs_pend: a restore is pending).
+  // restore.
   const v8i rs_sel = rowsum_selector(lane);
   v4f lacc = {0.0f, 0.0f, 0.0f, 0.0f};
-  float mu_pend[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  bool rs_pend = false;
   unsigned long long n_under = 0;
   v8i kop[2][2], vop[4];
   float sk_cur = 0.0f, sk_next = 0.0f;
@@ -504,7 +503,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   auto pv = [&]() {
 #pragma unroll
     for (int dt = 0; dt < 4; dt++) oacc[dt] = mfma_f8(vop[dt], pop, oacc[dt]);
-    if constexpr (EXPCAST) lacc = mfma_rowsum(rs_sel, pop, lacc);
   };
 
   // Orders the QK MFMAs of key sub-tile t of the next block after the P bytes of sub-tile t of
@@ -627,22 +625,30 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     return alpha;
   };
 
-  // V-Smooth with ExpCast: rank-one mean restore O^T += mu r^T of a closed V block from its
-  // factors kept in registers and its row sum on the matrix cores (lacc), which then restarts.
-  auto keep_mean_factors = [&](const uint8_t* sl) {
-    const float* mu = reinterpret_cast<const float*>(sl + kMeanOff);
+  // V-Smooth rank-one mean restore O^T += mu r^T of a closed V block, mu = the block's mean
+  // factors (in the residual's units) and r the lanes' S-scaled row sums over its keys, on the
+  // matrix cores as one BF16 32x32x16 MFMA per 32 channels with a hi/lo split of both factors:
+  // k slots 0..2 carry mu_hi r_hi + mu_hi r_lo + mu_lo r_hi (the dropped mu_lo r_lo is below
+  // 2^-16 of the product, and the split loses below 2^-17 of each factor), exact products with
+  // FP32 accumulation. The A operand of channel 32 dt + l32 is its 16-byte record in the slot
+  // {mu_hi|mu_hi, mu_lo|0, 0, 0} (read by both lane halves); the B operand is r's split in the
+  // lanes of half 0 (k 0..7) and zero in half 1 (k 8..15).
+  auto restore_mean = [&](const uint8_t* sl, float r) {
+    const __bf16 rh = static_cast<__bf16>(r);  // round to nearest even
+    const __bf16 rl = static_cast<__bf16>(r - static_cast<float>(rh));
+    const uint32_t hi0 = __builtin_bit_cast(uint16_t, rh);                                  // r_hi | 0
+    const uint32_t hl = hi0 | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, rl)) << 16);  // r_hi | r_lo
+    v4i b;
+    b[0] = lh == 0 ? static_cast<int>(hl) : 0;
+    b[1] = lh == 0 ? static_cast<int>(hi0) : 0;
+    b[2] = 0;
+    b[3] = 0;
+    const v8bf bb = __builtin_bit_cast(v8bf, b);
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++) mu_pend[dt] = lh == 0 ? mu[32 * dt + l32] : 0.0f;
-    rs_pend = true;
-  };
-  auto restore_pending = [&]() {
-    const float r = lacc[0];
-    const float rb = lh == 0 ? r : 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < 4; dt++) oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(mu_pend[dt], rb, oacc[dt], 0, 0, 0);
-    l_part += r;
-    lacc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    rs_pend = false;
+    for (int dt = 0; dt < 4; dt++) {
+      const v4i a = *reinterpret_cast<const v4i*>(sl + kMeanOff + (32 * dt + l32) * 16);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), bb, oacc[dt], 0, 0, 0);
+    }
   };
 
   // One key block j; `sl` is the slot of pair j+1 (read here, then refilled with pair j+4).
@@ -669,26 +675,20 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         if constexpr (VSMOOTH) l_part *= alpha;
       }
     }
-    if constexpr (VSMOOTH && EXPCAST) {
-      // ExpCast: the row sum of a V block's last key block is on the matrix cores one block
-      // later, so the restore of the V block closed at block j-1 happens here (O and lacc both
-      // in the units of the running max of block j), and block j's closing is recorded
-      if (rs_pend) restore_pending();
-      if (closes_vblock(j)) keep_mean_factors(sl);
-    } else if constexpr (VSMOOTH) {
+    // ExpCast: block j's code sums, in the units of its running max like lacc by now
+    if constexpr (EXPCAST) lacc = mfma_rowsum(rs_sel, pop, lacc);
+    if constexpr (VSMOOTH) {
       if (closes_vblock(j)) {
-        // rank-one mean restore of the V block that block j closes (its factors travel in pair
-        // j+1); O holds blocks up to j-1 in the units of the running max of block j, like r
-        // as FP32 MFMAs on the matrix cores (O^T += mu r^T with K = 2, the second k slot zero:
-        // lanes of half 0 bring mu[32dt + l32] and their query's r), which keeps the VALU free
-        const float* mu = reinterpret_cast<const float*>(sl + kMeanOff);
-        const float rb = lh == 0 ? r_cur : 0.0f;
-#pragma unroll
-        for (int dt = 0; dt < 4; dt++) {
-          const float ma = lh == 0 ? mu[32 * dt + l32] : 0.0f;
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ma, rb, oacc[dt], 0, 0, 0);
+        // the V block that block j closes (its records travel in pair j+1); O holds blocks up to
+        // j-1 in the units of the running max of block j, like r
+        if constexpr (EXPCAST) {
+          restore_mean(sl, lacc[0]);
+          l_part += lacc[0];
+          lacc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        } else {
+          restore_mean(sl, r_cur);
+          r_cur = 0.0f;
         }
-        r_cur = 0.0f;
       }
     }
     // hand-off: every read of this slot is complete, pair j+2 has landed everywhere
@@ -779,9 +779,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   }
   if (partial_tail && !p.reverse) iteration(kMasked{}, kGeneric{}, n_iter - 1, slot(sidx));
   pv();  // PV of the last block (vop = V(n_iter - 1))
-  if constexpr (VSMOOTH && EXPCAST) {
-    if (rs_pend) restore_pending();  // the last block closes its V block
-  }
 
   if constexpr (STATS) {
     unsigned long long tot = n_under;
@@ -867,7 +864,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   }
 }
 
-// V-Smooth: mu_f[bh, j, d] = float(mean_hat[bh, j, d]) * (s_r[d] > 0 ? 1 / s_r[d] : 1).
+// V-Smooth: the factor mu = float(mean_hat[bh, j, d]) * (s_r[d] > 0 ? 1 / s_r[d] : 1) as the
+// restore's A-operand record mu_op[bh, j, d] = {mu_hi|mu_hi, mu_lo|0, 0, 0} (BF16 pairs, low half
+// first; mu_hi = BF16(mu), mu_lo = BF16(mu - mu_hi), both rounded to nearest even).
 __global__ __launch_bounds__(128) void vsmooth_mean_factors(AttnParams p) {
   const int64_t j = blockIdx.x;
   const int64_t bh = blockIdx.y;
@@ -875,7 +874,10 @@ __global__ __launch_bounds__(128) void vsmooth_mean_factors(AttnParams p) {
   const float sr = p.v_scale[bh * kHeadDim + d];
   const float f = sr > 0.0f ? __fdiv_rn(1.0f, sr) : 1.0f;
   const int64_t idx = (bh * p.NB128 + j) * kHeadDim + d;
-  p.mu_f[idx] = bf16_to_f32(p.v_mean[idx]) * f;
+  const float mu = bf16_to_f32(p.v_mean[idx]) * f;
+  const uint32_t hi = f32_to_bf16_rne(mu);
+  const uint32_t lo = f32_to_bf16_rne(mu - __uint_as_float(hi << 16));
+  reinterpret_cast<uint4*>(p.mu_op)[idx] = make_uint4(hi | (hi << 16), lo, 0u, 0u);
 }
 
 // Split-KV merge ([TF] long-sequence split-KV, log-sum-exp reduction): per row,

@@ -144,7 +144,8 @@ def test_workspace_sizes(m):
     assert L.fp8attn_quantize_workspace_bytes(1, 75600, 40, 128, 0) >= 40 * 591 * 128 * 4 + \
         2 * 40 * 1182 * 128 * 4   # + the smoothing block sums of K and V
     assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0, 1) == 0
-    assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1, 0) == 24 * 384 * 128 * 4
+    # V-Smooth: one 16-byte mean operand record per (b, h, 128-row block, channel)
+    assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1, 0) == 24 * 384 * 128 * 16
     # split-KV: 4096 tokens = 64 key blocks, 2 pieces of 32 blocks; 3 requested -> L = 22, 3 pieces
     assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 2) == 2 * 8 * 4096 * 129 * 4
     assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 3) == 3 * 8 * 4096 * 129 * 4
