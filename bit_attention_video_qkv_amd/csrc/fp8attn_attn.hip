@@ -21,7 +21,7 @@
 //    results take over the softmax's registers half by half. The kernel fits two waves per
 //    SIMD, so two 4-wave workgroups share every CU and cover each other's stalls.
 //  * K and V tiles (8 KB each per 64 keys) reach LDS by direct global->LDS copies, three key
-//    blocks deep; one barrier per key block. LDS chunks are XOR-swizzled so that every operand
+//    blocks deep (two for two-wave workgroups); one barrier per key block. LDS chunks are XOR-swizzled so that every operand
 //    read is free of bank conflicts.
 //  * Workgroups are mapped XCD-major so each XCD works on few heads at a time.
 #include <type_traits>
@@ -156,8 +156,8 @@ struct KvCursor {
 //   LDS:   the operands of the next block, V(j) and K(j+1), read from slot "pair j+1" after
 //          the MFMAs that consumed the previous values
 //   end:   rescale of O by alpha(j) (PV(j-1) long done), wait for pair j+2, barrier, copy
-//          pair j+4 into the slot just read.
-// Pair p (slot p % 3) holds the K tile of key block p with its s_k and valid-key count and the
+//          pair j+1+kSlots (j+4 with three slots) into the slot just read.
+// Pair p (slot p % kSlots) holds the K tile of key block p with its s_k and valid-key count and the
 // V tile of key block p-1 (for V-Smooth, with the mean factors of that block's 128-row V block).
 // QK(j+1) writes its result into the registers the softmax of block j has just consumed, so a
 // wave needs one S tile of registers; two workgroups share each CU, so every SIMD runs two such
@@ -172,7 +172,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   constexpr int kSlotBytes = kMeanOff + (VSMOOTH ? kHeadDim * 16 : 0);  // multiple of 16
   constexpr int kMeanLanes = 128 / WAVES;       // V-Smooth: lanes per wave copying the records
   constexpr int kCopies = 2 * kChunks + (VSMOOTH ? 1 : 0);  // copies per pair (wave 0: +1, s_k)
-  __shared__ __attribute__((aligned(16))) uint8_t lds[3 * kSlotBytes];
+  // LDS slots of (K, V) pairs: three, two in flight while one is read; two-wave workgroups use
+  // two (one in flight), so that four of them fit a CU's LDS instead of three
+  constexpr int kSlots = WAVES == 2 ? 2 : 3;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kSlots * kSlotBytes];
   auto slot = [&](int i) -> uint8_t* { return lds + i * kSlotBytes; };
 
   // ---- work item (XCD-major: dispatch round-robins workgroups over the 8 XCDs) ----
@@ -397,10 +400,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     kb_prev += kv_dir;
     lc.e++;
   };
-  // Waits until only the copies of the newest staged pair may still be in flight.
+  // Waits until only the copies of the newest kSlots - 2 staged pairs may still be in flight.
   auto wait_all_but_newest = [&]() {
-    if (wave == 0) wait_vmcnt<kCopies + 1>();
-    else wait_vmcnt<kCopies>();
+    if constexpr (kSlots == 2) {
+      wait_vmcnt<0>();
+    } else {
+      if (wave == 0) wait_vmcnt<kCopies + 1>();
+      else wait_vmcnt<kCopies>();
+    }
   };
 
   // ---- Q operand (B operand of S^T = K Q^T), straight from HBM ----
@@ -651,10 +658,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     }
   };
 
-  // One key block j; `sl` is the slot of pair j+1 (read here, then refilled with pair j+4).
-  // The masked copy serves blocks with fewer than 64 valid keys.
-  // Steady (dense and STA): pairs j+2 and j+4 hold key blocks, so the waits and the staging need
-  // no checks; dense staging is stage_dense.
+  // One key block j; `sl` is the slot of pair j+1 (read here, then refilled with pair
+  // j+1+kSlots). The masked copy serves blocks with fewer than 64 valid keys.
+  // Steady (dense and STA): pairs j+2 and j+1+kSlots hold key blocks, so the waits and the
+  // staging need no checks; dense staging is stage_dense.
   auto iteration = [&](auto mask_tag, auto steady_tag, int j, uint8_t* sl) {
     constexpr bool kSteady = decltype(steady_tag)::value;
     pv();         // PV of block j-1 (zero P bytes before the first block)
@@ -694,8 +701,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     // hand-off: every read of this slot is complete, pair j+2 has landed everywhere
     wait_lgkm0();
     if constexpr (kSteady) {
-      wait_vmcnt<kCopies>();
-    } else if (j + 3 <= n_iter) {
+      wait_vmcnt<(kSlots - 2) * kCopies>();
+    } else if (j + kSlots <= n_iter) {
       wait_all_but_newest();
     } else {
       wait_vmcnt<0>();
@@ -705,19 +712,23 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     lim_cur = lim_next;
     ex_cur = ex_next;
     if constexpr (kSteady) {
-      if constexpr (SPARSE) stage(j + 4, sl);  // (its key block exists: j + 4 < n_iter)
+      if constexpr (SPARSE) stage(j + 1 + kSlots, sl);  // (its key block exists: < n_iter)
       else stage_dense(sl);
-    } else if (j + 4 <= n_iter) {
-      stage(j + 4, sl);
+    } else if (j + 1 + kSlots <= n_iter) {
+      stage(j + 1 + kSlots, sl);
     }
   };
 
-  // ---- prologue: pairs 0..2 staged; K(0) read; QK of block 0; pair 3 staged ----
+  // ---- prologue: pairs 0..kSlots-1 staged; K(0) read; QK of block 0; pair kSlots staged ----
   stage(0, slot(0));
   stage(1, slot(1));
-  if (n_iter >= 2) {
-    stage(2, slot(2));
-    wait_all_but_newest();
+  if constexpr (kSlots == 3) {
+    if (n_iter >= 2) {
+      stage(2, slot(2));
+      wait_all_but_newest();
+    } else {
+      wait_vmcnt<0>();
+    }
   } else {
     wait_vmcnt<0>();
   }
@@ -731,7 +742,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   sk_cur = sk_next;
   lim_cur = lim_next;
   ex_cur = ex_next;
-  if (n_iter >= 3) stage(3, slot(0));
+  if (n_iter >= kSlots) stage(kSlots, slot(0));
 
   // ---- mainloop. Dense: the one block with fewer than 64 valid keys (the last key block, first
   // in reverse order) runs in a masked copy outside the loop. Sparse: partial blocks sit at the
@@ -746,7 +757,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   if (partial_tail && p.reverse) {
     iteration(kMasked{}, kGeneric{}, 0, slot(1));
     j = 1;
-    sidx = 2;
+    sidx = 2 % kSlots;
   }
   if (partial_tail && !p.reverse) j_end = n_iter - 1;
   if constexpr (!SOL) {
@@ -755,27 +766,29 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     // blocks keep the per-block valid-key check (partial blocks end tiles anywhere).
     while (j < j_end && sidx != 0) {
       iteration(kLoopMask{}, kGeneric{}, j, slot(sidx));
-      sidx = sidx == 2 ? 0 : sidx + 1;
+      sidx = sidx == kSlots - 1 ? 0 : sidx + 1;
       j++;
     }
     // (the underflow-counting variant, a debugging aid, stays on the generic path)
-    const int j_steady = STATS ? 0 : min(j_end, n_iter - 4);  // steady blocks: j < j_steady
+    const int j_steady = STATS ? 0 : min(j_end, n_iter - 1 - kSlots);  // steady: j < j_steady
     using kSteadyMask = std::integral_constant<bool, SPARSE>;
     if constexpr (!SPARSE) {
-      if (j + 3 <= j_steady) stage_dense_init();
+      if (j + kSlots <= j_steady) stage_dense_init();
     }
-    for (; j + 3 <= j_steady; j += 3) {
+    for (; j + kSlots <= j_steady; j += kSlots) {
       iteration(kSteadyMask{}, kSteady{}, j, slot(0));
       __builtin_amdgcn_sched_barrier(0);
       iteration(kSteadyMask{}, kSteady{}, j + 1, slot(1));
       __builtin_amdgcn_sched_barrier(0);
-      iteration(kSteadyMask{}, kSteady{}, j + 2, slot(2));
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kSlots == 3) {
+        iteration(kSteadyMask{}, kSteady{}, j + 2, slot(2));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   for (; j < j_end; j++) {
     iteration(kLoopMask{}, kGeneric{}, j, slot(sidx));
-    sidx = sidx == 2 ? 0 : sidx + 1;
+    sidx = sidx == kSlots - 1 ? 0 : sidx + 1;
   }
   if (partial_tail && !p.reverse) iteration(kMasked{}, kGeneric{}, n_iter - 1, slot(sidx));
   pv();  // PV of the last block (vop = V(n_iter - 1))
