@@ -171,7 +171,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   constexpr int kMeanOff = kMetaOff + 16;       // V-Smooth mean operand records, 128 x 16 B
   constexpr int kSlotBytes = kMeanOff + (VSMOOTH ? kHeadDim * 16 : 0);  // multiple of 16
   constexpr int kMeanLanes = 128 / WAVES;       // V-Smooth: lanes per wave copying the records
-  constexpr int kCopies = 2 * kChunks + (VSMOOTH ? 1 : 0);  // copies per pair (wave 0: +1, s_k)
+  // copies every wave issues for every pair (wave 0 adds s_k; V-Smooth pairs may add the mean
+  // records, which the waits do not count: they then wait one copy longer than they must)
+  constexpr int kCopies = 2 * kChunks;
   // LDS slots of (K, V) pairs: three, two in flight while one is read; two-wave workgroups use
   // two (one in flight), so that four of them fit a CU's LDS instead of three
   constexpr int kSlots = WAVES == 2 ? 2 : 3;
@@ -321,6 +323,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     const int64_t kn = p.reverse ? (p.NB - 2 - e) : e + 1;
     return (kb >> 1) != (kn >> 1);
   };
+  // The same for blocks that are not the last of the piece: forward, key block kb closes its V
+  // block when kb is odd; reverse, when kb is even, i.e. when e = e0 + j has the parity of NB - 1.
+  const int close_parity = p.reverse ? static_cast<int>((p.NB - 1) & 1) : 1;
+  auto closes_vblock_inner = [&](int j) -> bool { return ((static_cast<int>(e0) + j) & 1) == close_parity; };
 
   // ---- staging of pair `pidx` into slot `sl` (every thread copies its fixed 16-byte chunks;
   // per pair only the wave-uniform tile bases change) ----
@@ -390,7 +396,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int r = 0; r < kChunks; r++) copy16_to_lds(st_v, voff[r], l0 + kTileBytes + (r * kThreads + wave * 64) * 16);
     if constexpr (VSMOOTH) {
-      if (lane < kMeanLanes)
+      // only the restore of the block that closes a V block reads the records (from the slot of
+      // the next pair, which carries that block's V tile); a steady pair's V block never is the
+      // last of the piece
+      if (((kb_prev & 1) != 0) == (kv_dir > 0) && lane < kMeanLanes)
         copy16_to_lds(p.mu_op + (bh * p.NB128 + (kb_prev >> 1)) * kHeadDim * 4, 16u * (wave * kMeanLanes + lane),
                       l0 + kMeanOff + wave * kMeanLanes * 16);
     }
@@ -685,7 +694,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     // ExpCast: block j's code sums, in the units of its running max like lacc by now
     if constexpr (EXPCAST) lacc = mfma_rowsum(rs_sel, pop, lacc);
     if constexpr (VSMOOTH) {
-      if (closes_vblock(j)) {
+      if (kSteady ? closes_vblock_inner(j) : closes_vblock(j)) {
         // the V block that block j closes (its records travel in pair j+1); O holds blocks up to
         // j-1 in the units of the running max of block j, like r
         if constexpr (EXPCAST) {
