@@ -308,8 +308,8 @@ SolLayout sol_layout(int32_t B, int32_t N, int32_t H) {
   L.Mk = take(bh * kHeadDim * kHeadDim * sizeof(double));
   L.theta = take(bh * L.NB * sizeof(float));
   L.mask = take(bh * L.NB * L.W * sizeof(uint64_t));
-  L.o_part = take(2 * bh * N * kHeadDim * sizeof(float));
-  L.lse = take(2 * bh * N * sizeof(float));
+  L.o_part = take(bh * N * kHeadDim * sizeof(float));  // the summary route's normalised O
+  L.lse = take(bh * N * sizeof(float));                  // and log2 of its weight
   L.total = off;
   return L;
 }
@@ -368,8 +368,8 @@ fp8attn_status fp8attn_sol_forward(int32_t B, int32_t N, int32_t H, int32_t D, c
   sp.Mk = reinterpret_cast<double*>(ws + L.Mk);
   sp.theta = reinterpret_cast<float*>(ws + L.theta);
   sp.mask = mask;
-  sp.o_part = o_part + total_bh * N * kHeadDim;  // piece 1: the summary route
-  sp.lse = lse + total_bh * N;
+  sp.o_part = o_part;  // the summary route's piece, merged by the exact route's epilogue
+  sp.lse = lse;
   sp.N = N;
   sp.NB = L.NB;
   sp.N64 = L.NB * 64;

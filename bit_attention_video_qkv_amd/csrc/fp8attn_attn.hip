@@ -251,13 +251,20 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   }
   if (n_iter <= 0) {
     if constexpr (SOL) {
-      // no exact block: the exact route has no weight
+      // no exact block: the exact route has no weight, so O is the summary route's piece (with
+      // the sequence-mean V shift), in BF16
       for (int r = threadIdx.x; r < kRowsPerWg * (kHeadDim / 4); r += kThreads) {
         const int64_t row = q0 + r / (kHeadDim / 4);
         if (row >= p.N) continue;
-        reinterpret_cast<float4*>(p.o_part + (bh * p.N + row) * kHeadDim)[r % (kHeadDim / 4)] =
-            make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (r % (kHeadDim / 4) == 0) p.lse[bh * p.N + row] = -INFINITY;
+        const int c = 4 * (r % (kHeadDim / 4));
+        const int64_t r1 = bh * p.N + row;
+        const float4 o1 = *reinterpret_cast<const float4*>(p.o_part + r1 * kHeadDim + c);
+        float4 sh = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (p.v_shift) sh = *reinterpret_cast<const float4*>(p.v_shift + bh * kHeadDim + c);
+        uint2 o;
+        o.x = static_cast<uint32_t>(f32_to_bf16_rne(o1.x + sh.x)) | (static_cast<uint32_t>(f32_to_bf16_rne(o1.y + sh.y)) << 16);
+        o.y = static_cast<uint32_t>(f32_to_bf16_rne(o1.z + sh.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(o1.w + sh.w)) << 16);
+        *reinterpret_cast<uint2*>(p.out + ((b * p.n_out + row) * p.H + h) * kHeadDim + c) = o;
       }
     }
     return;  // (otherwise: a query tile without key blocks has no defined output)
@@ -816,7 +823,42 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   float l_tot;
   if constexpr (EXPCAST) l_tot = VSMOOTH ? l_part : lacc[0];
   else l_tot = xsum(l_part);
-  if constexpr (!SPARSE || SOL) {
+  if constexpr (SOL) {
+    // Sol: merge with the summary route's piece (o_part, lse: written before this kernel) by
+    // their log2 weights, as split_merge does for pieces, and write BF16 O directly
+    if (ok) {
+      const float lse0 = l_tot > 0.0f ? m_run + __log2f(l_tot) : -INFINITY;
+      const int64_t r1 = bh * p.N + qrow;
+      const float lse1 = p.lse[r1];
+      const float mx = fmaxf(lse0, lse1);
+      const float w0 = __builtin_amdgcn_exp2f(lse0 - mx), w1 = __builtin_amdgcn_exp2f(lse1 - mx);
+      const float inv_w = 1.0f / (w0 + w1);
+      const float a0 = l_tot > 0.0f ? w0 * inv_w / l_tot : 0.0f;  // on acc * v_scale
+      const float a1 = w1 * inv_w;
+      const float* o1 = p.o_part + r1 * kHeadDim;
+      uint16_t* orow = p.out + ((b * p.n_out + qrow) * p.H + h) * kHeadDim;
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          const int d0 = 32 * dt + 8 * g + 4 * lh;
+          const float4 sv = *reinterpret_cast<const float4*>(p.v_scale + bh * kHeadDim + d0);
+          const float4 ov = *reinterpret_cast<const float4*>(o1 + d0);
+          float4 sh = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if (p.v_shift) sh = *reinterpret_cast<const float4*>(p.v_shift + bh * kHeadDim + d0);
+          const float e0 = oacc[dt][4 * g + 0] * sv.x * a0 + ov.x * a1 + sh.x;
+          const float e1 = oacc[dt][4 * g + 1] * sv.y * a0 + ov.y * a1 + sh.y;
+          const float e2 = oacc[dt][4 * g + 2] * sv.z * a0 + ov.z * a1 + sh.z;
+          const float e3 = oacc[dt][4 * g + 3] * sv.w * a0 + ov.w * a1 + sh.w;
+          uint2 o;
+          o.x = static_cast<uint32_t>(f32_to_bf16_rne(e0)) | (static_cast<uint32_t>(f32_to_bf16_rne(e1)) << 16);
+          o.y = static_cast<uint32_t>(f32_to_bf16_rne(e2)) | (static_cast<uint32_t>(f32_to_bf16_rne(e3)) << 16);
+          *reinterpret_cast<uint2*>(orow + d0) = o;
+        }
+    }
+    return;
+  }
+  if constexpr (!SPARSE) {
     if (p.o_part) {
       // split-KV piece or Sol exact route: this piece's normalised O (FP32) and log2 of its
       // weight, m + log2(l)
@@ -962,17 +1004,12 @@ hipError_t launch_variant(AttnParams& p, hipStream_t stream) {
 
 // Sol: the exact route (two waves per 64-row Q block over its mask's blocks; the kernel also has
 // a four-wave form over the union of two Q blocks' masks, which only pays when neighbouring Q
-// blocks share most exact blocks) writes piece 0; the summary route has written piece 1; then the
-// two are merged.
+// blocks share most exact blocks) merges its result with the summary route's, which has been
+// written before, in its epilogue.
 template <bool EXPCAST>
 hipError_t launch_sol_exact(AttnParams p, hipStream_t stream) {
   p.splits = 1;
-  hipError_t e = launch_variant<2, true, EXPCAST, false, false, true>(p, stream);
-  if (e != hipSuccess) return e;
-  p.splits = 2;
-  hipLaunchKernelGGL(split_merge, dim3(static_cast<unsigned>((p.N + 7) / 8), static_cast<unsigned>(p.B * p.H)),
-                     dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return launch_variant<2, true, EXPCAST, false, false, true>(p, stream);
 }
 
 }  // namespace

@@ -458,8 +458,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     wait_lgkm0();  // every read of this slot has returned before the next barrier frees it
   }
 
-  // epilogue: the summary route's normalised output (piece 1) and log2 of its weight, in the
-  // units of the exact route (S-scaled row sums)
+  // epilogue: the summary route's normalised output and log2 of its weight, in the units of the
+  // exact route (S-scaled row sums); the exact route's epilogue merges it with its own
   if (!qvalid) return;
   auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
   const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);

@@ -192,7 +192,7 @@ def test_cluster_rejects_bad_arguments(m):
 def test_sol_rejects_bad_arguments(m):
     L = m.lib()
     need = L.fp8attn_sol_workspace_bytes(1, 1000, 2, 128)
-    assert need > 2 * 2 * 1000 * 128 * 4
+    assert need > 2 * 1000 * 128 * 4  # at least the summary route's FP32 output
     assert L.fp8attn_sol_workspace_bytes(1, 1000, 2, 64) == 0
     P = [_fake()] * 6
 
