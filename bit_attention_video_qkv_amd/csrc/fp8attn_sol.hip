@@ -154,6 +154,8 @@ __global__ __launch_bounds__(256) void sol_kmoments(SolParams p) {
   const int e0 = (threadIdx.x & 31) * 4;
   const float* ks = p.ksum + bh * p.NB * kHeadDim;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  // (unrolled so that the loads of several summaries are in flight; the sums stay in order)
+#pragma unroll 8
   for (int64_t j = 0; j < p.NB; j++) {
     const double a = static_cast<double>(ks[j * kHeadDim + d]);
     const float4 b = *reinterpret_cast<const float4*>(ks + j * kHeadDim + e0);
@@ -167,6 +169,7 @@ __global__ __launch_bounds__(256) void sol_kmoments(SolParams p) {
   for (int q = 0; q < 4; q++) p.Mk[(bh * kHeadDim + d) * kHeadDim + e0 + q] = acc[q] * inv_nb;
   if (blockIdx.y == 0 && threadIdx.x < kHeadDim) {
     double m = 0.0;
+#pragma unroll 8
     for (int64_t j = 0; j < p.NB; j++) m += static_cast<double>(ks[j * kHeadDim + threadIdx.x]);
     p.mk[bh * kHeadDim + threadIdx.x] = m * inv_nb;
   }
@@ -202,8 +205,11 @@ __global__ __launch_bounds__(128) void sol_theta(SolParams p) {
   }
   __syncthreads();
   const double sq = p.q_scale[bh * p.NB + u];
+  // over all 64 rows (rows past nq hold 0); both sums are exact in any order (the decoded codes
+  // and their squares span fewer bits than the FP64 significand)
   double csum = 0.0, csq = 0.0;
-  for (int i = 0; i < nq; i++) {
+#pragma unroll 16
+  for (int i = 0; i < 64; i++) {
     csum += c[i][e];
     csq += static_cast<double>(c[i][e]) * c[i][e];
   }
