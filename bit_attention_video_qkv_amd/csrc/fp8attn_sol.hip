@@ -184,10 +184,13 @@ __device__ __forceinline__ double block_sum_128(double v, double* red) {
   return r;
 }
 
-// 4. Threshold of Q block u. Thread e: channel e. The decoded query codes c_i (exact in FP32)
-// sit in LDS; q_i = s_q * c_i.
+// 4. Threshold of Q block u. Thread e: channel e. The query codes c_i sit in LDS (the exact
+// estimator: decoded, exact in FP32, for its M_k products; the diag estimator: the bytes, which
+// keeps a workgroup's LDS at 8 KB); q_i = s_q * c_i. Rows past N hold code 0.
+template <bool EXACT>
 __global__ __launch_bounds__(128) void sol_theta(SolParams p) {
-  __shared__ float c[64][kHeadDim + 1];
+  __shared__ float c[EXACT ? 64 : 1][kHeadDim + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t cb[EXACT ? 1 : 64][kHeadDim];
   __shared__ double red[2];
   const int64_t u = blockIdx.x, bh = blockIdx.y;
   const int e = threadIdx.x;
@@ -198,25 +201,33 @@ __global__ __launch_bounds__(128) void sol_theta(SolParams p) {
     const int L = k * 128 + e;  // 512 chunks of 16 bytes: row L / 8, bytes 16 * (L % 8) ..
     const int i = L >> 3, d0 = (L & 7) * 16;
     const uint4 w = qb[L];
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    if constexpr (EXACT) {
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int q = 0; q < 16; q++)
-      c[i][d0 + q] = i < nq ? e4m3_decode((ws[q >> 2] >> (8 * (q & 3))) & 0xFFu) : 0.0f;
+      for (int q = 0; q < 16; q++) c[i][d0 + q] = e4m3_decode((ws[q >> 2] >> (8 * (q & 3))) & 0xFFu);
+    } else {
+      *reinterpret_cast<uint4*>(&cb[i][d0]) = w;
+    }
   }
   __syncthreads();
+  auto code = [&](int i, int d) -> float {
+    if constexpr (EXACT) return c[i][d];
+    else return e4m3_decode(cb[i][d]);
+  };
   const double sq = p.q_scale[bh * p.NB + u];
   // over all 64 rows (rows past nq hold 0); both sums are exact in any order (the decoded codes
   // and their squares span fewer bits than the FP64 significand)
   double csum = 0.0, csq = 0.0;
 #pragma unroll 16
   for (int i = 0; i < 64; i++) {
-    csum += c[i][e];
-    csq += static_cast<double>(c[i][e]) * c[i][e];
+    const float v = code(i, e);
+    csum += v;
+    csq += static_cast<double>(v) * v;
   }
   // mu = ss * sq * mean_i c_i . m
   const double mu = block_sum_128(csum / nq * p.mk[bh * kHeadDim + e], red) * sq * p.softmax_scale;
   double part;
-  if (p.estimator == 0) {
+  if constexpr (!EXACT) {
     part = csq / nq * p.Mk[(bh * kHeadDim + e) * kHeadDim + e];
   } else {
     // sum_i c_i[e] (Mk c_i)[e] / nq, with (Mk c_i)[e] = sum_d Mk[d][e] c_i[d] (Mk symmetric)
@@ -227,11 +238,11 @@ __global__ __launch_bounds__(128) void sol_theta(SolParams p) {
     for (int d = 0; d < kHeadDim; d++) {
       const float m = static_cast<float>(mrow[d * kHeadDim]);
 #pragma unroll
-      for (int i = 0; i < 64; i++) y[i] = __builtin_fmaf(m, c[i][d], y[i]);
+      for (int i = 0; i < 64; i++) y[i] = __builtin_fmaf(m, code(i, d), y[i]);
     }
     double acc = 0.0;
 #pragma unroll
-    for (int i = 0; i < 64; i++) acc += static_cast<double>(c[i][e]) * y[i];
+    for (int i = 0; i < 64; i++) acc += static_cast<double>(code(i, e)) * y[i];
     part = acc / nq;
   }
   const double e2 = block_sum_128(part, red) * sq * sq * p.softmax_scale * p.softmax_scale;
@@ -500,7 +511,8 @@ hipError_t launch_sol(const SolParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(sol_kmoments, dim3(bh, kHeadDim / 8), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sol_theta, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
+  if (p.estimator == 0) hipLaunchKernelGGL(sol_theta<false>, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
+  else hipLaunchKernelGGL(sol_theta<true>, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sol_route, dim3(static_cast<unsigned>((p.NB + 1) / 2), bh), dim3(256), 0, stream, p);
