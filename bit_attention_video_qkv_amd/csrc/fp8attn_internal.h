@@ -62,10 +62,10 @@ struct AttnParams {
   // output and log2-sum-exp, which split_merge combines. splits = 1: no split, o_part null.
   int splits;
   int64_t split_blocks;
-  float* o_part;  // [splits, B*H, N, 128]
-  float* lse;     // [splits, B*H, N]
+  float* o_part;  // [splits, B*H, N, 128]; Sol: [B*H, N, 128], the summary route's output
+  float* lse;     // [splits, B*H, N]; Sol: [B*H, N], the summary route's log2 weight
   // Sol routing: exact-block mask [B*H, NB, sol_words] of the exact route (the attention then
-  // writes its partial output as piece 0), or null
+  // merges its result with the summary route's in its epilogue), or null
   const uint64_t* sol_mask;
   int64_t sol_words;
 };
