@@ -352,12 +352,16 @@ __device__ __forceinline__ float mul_rounded(float a, float b) {
 // are read back from the transpose tile.
 template <bool BIAS>
 __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim][kBlock + 16];  // [channel][token]
+  // [channel][token quad]: word w of channel c holds the codes of tokens 4w .. 4w + 3 (byte u =
+  // token 4w + u); 17 words per channel, so the 16 channel octets of a wave's stores spread over
+  // the banks (two lanes per bank at most)
+  constexpr int kTileWords = kBlock / 4 + 1;
+  __shared__ uint32_t tile[kHeadDim][kTileWords];
   const int64_t blk = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / p.H, h = bh % p.H;
-  const int chunk = threadIdx.x & 15;
-  const int row0 = threadIdx.x >> 4;
+  const int chunk = threadIdx.x & 15;  // channels 8 chunk .. + 7
+  const int row0 = threadIdx.x >> 4;   // tokens 4 row0 .. + 3
   const bool shift = p.smoothing == 2;
   float inv[8], mhat[8];
 #pragma unroll
@@ -371,9 +375,10 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
     if (threadIdx.x < 2) valid_bits[threadIdx.x] = 0u;
     __syncthreads();
   }
+  uint32_t lo4[4], hi4[4];  // per token: the codes of channels 0-3 and 4-7 of the octet
 #pragma unroll
   for (int pass = 0; pass < 4; pass++) {
-    const int t = row0 + 16 * pass;
+    const int t = 4 * row0 + pass;
     const int64_t i = blk * kBlock + t;
     const int64_t s = gather_src(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, i);
     uint32_t lo = 0, hi = 0;
@@ -398,20 +403,39 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
     if constexpr (BIAS) {
       if (chunk == 0 && s >= 0) atomicOr(&valid_bits[t >> 5], 1u << (t & 31));
     }
+    lo4[pass] = lo;
+    hi4[pass] = hi;
+  }
+  // 4 tokens x 4 channels byte transposes: first pairs of tokens interleaved per channel pair,
+  // then the two pairs joined (perm(x, y, s): byte i = byte s_i of {y: 0-3, x: 4-7})
+  auto transpose4 = [](const uint32_t (&r)[4], uint32_t (&c)[4]) {
+    const uint32_t a01 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);  // ch0 t0 t1, ch1 t0 t1
+    const uint32_t b01 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // ch2, ch3
+    const uint32_t a23 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
+    const uint32_t b23 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
+    c[0] = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
+    c[1] = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
+    c[2] = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+    c[3] = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
+  };
+  uint32_t clo[4], chi[4];
+  transpose4(lo4, clo);
+  transpose4(hi4, chi);
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      tile[chunk * 8 + q][t] = static_cast<uint8_t>(lo >> (8 * q));
-      tile[chunk * 8 + 4 + q][t] = static_cast<uint8_t>(hi >> (8 * q));
-    }
+  for (int q = 0; q < 4; q++) {
+    tile[chunk * 8 + q][row0] = clo[q];
+    tile[chunk * 8 + 4 + q][row0] = chi[q];
   }
   __syncthreads();
   // Thread t writes channel t/2, tokens 32*(t%2) .. +31 (two 16-byte stores).
   const int d = threadIdx.x >> 1;
   const int half = threadIdx.x & 1;
-  const uint4* srcp = reinterpret_cast<const uint4*>(&tile[d][32 * half]);
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) w[i] = tile[d][8 * half + i];
   uint4* dst = reinterpret_cast<uint4*>(p.v8t + (bh * kHeadDim + d) * p.N64 + blk * kBlock + 32 * half);
-  dst[0] = srcp[0];
-  dst[1] = srcp[1];
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
   if constexpr (BIAS) {
     // The rounding error of channel c, rows in ascending order (the bias correction exists only
     // with V smoothing, so V' = fl32(V - mean_V)): err = fl32(fl32(decode(code) * s_v) - V').
@@ -423,7 +447,7 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
       float acc = 0.0f;
 #pragma unroll 2
       for (int t4 = 0; t4 < kBlock; t4 += 4) {
-        const uint32_t codes = *reinterpret_cast<const uint32_t*>(&tile[c][t4]);
+        const uint32_t codes = tile[c][t4 >> 2];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
           const float r = __fsub_rn(bf16_to_f32(vin_s[t4 + u][c]), mv);
