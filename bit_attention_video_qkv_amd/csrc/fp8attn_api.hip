@@ -16,6 +16,8 @@ namespace {
 using fp8attn::kHeadDim;
 
 constexpr size_t kAlign = 256;
+// Forward workspace head: the eight per-XCD work-queue counters, padded to kAlign.
+constexpr size_t kQueueBytes = 256;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -186,7 +188,8 @@ size_t fp8attn_forward_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t 
                                        int32_t kv_splits) {
   if (B < 1 || N < 1 || H < 1 || D != kHeadDim || !valid_splits_arg(kv_splits)) return 0;
   const size_t bh = static_cast<size_t>(B) * H;
-  size_t n = vsmooth ? round_up(bh * cdiv(N, 128) * kHeadDim * 16) : 0;  // mean operand records
+  size_t n = kQueueBytes;                                                   // work queues
+  if (vsmooth) n += round_up(bh * cdiv(N, 128) * kHeadDim * 16);          // mean operand records
   int64_t split_blocks = 0;
   const int splits = resolve_splits(B, N, H, kv_splits, &split_blocks);
   if (splits > 1)
@@ -230,7 +233,7 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
   const int splits = sparse ? 1 : resolve_splits(B, N, H, o->kv_splits, &split_blocks);
   if (total_bh * cdiv(N, 64) * splits > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
   const size_t need = fp8attn_forward_workspace_bytes(B, N, H, D, vsmooth ? 1 : 0, sparse ? 1 : o->kv_splits);
-  if (need && (!workspace || !aligned(workspace, 16) || workspace_bytes < need)) return FP8ATTN_EINVAL;
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FP8ATTN_EINVAL;
   const fp8attn_status dev = check_device();
   if (dev != FP8ATTN_OK) return dev;
 
@@ -243,12 +246,15 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
   p.k_scale = k_scale;
   p.v_scale = v_scale;
   p.v_mean = v_mean;
-  p.mu_op = vsmooth ? static_cast<uint32_t*>(workspace) : nullptr;
+  // workspace: [work queues][V-Smooth mean operand records][split-KV pieces]
+  p.work_ctr = static_cast<uint32_t*>(workspace);
+  p.cus = device_cus();
+  p.mu_op = vsmooth ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kQueueBytes) : nullptr;
   p.splits = splits;
   p.split_blocks = splits > 1 ? split_blocks : cdiv(N, 64);
   if (splits > 1) {
     const size_t bh = static_cast<size_t>(total_bh);
-    char* ws = static_cast<char*>(workspace) + (vsmooth ? round_up(bh * cdiv(N, 128) * kHeadDim * 16) : 0);
+    char* ws = static_cast<char*>(workspace) + kQueueBytes + (vsmooth ? round_up(bh * cdiv(N, 128) * kHeadDim * 16) : 0);
     p.o_part = reinterpret_cast<float*>(ws);
     p.lse = reinterpret_cast<float*>(ws + round_up(splits * bh * N * kHeadDim * sizeof(float)));
   }

@@ -23,7 +23,9 @@
 //  * K and V tiles (8 KB each per 64 keys) reach LDS by direct global->LDS copies, three key
 //    blocks deep (two for two-wave workgroups); one barrier per key block. LDS chunks are XOR-swizzled so that every operand
 //    read is free of bank conflicts.
-//  * Workgroups are mapped XCD-major so each XCD works on few heads at a time.
+//  * Work items are cut into one contiguous range per XCD, so each XCD works on few heads at a
+//    time; persistent workgroups take them from per-XCD queues and, when theirs is empty, from
+//    the others.
 #include <type_traits>
 
 #include "fp8attn_common.h"
@@ -162,8 +164,10 @@ struct KvCursor {
 // QK(j+1) writes its result into the registers the softmax of block j has just consumed, so a
 // wave needs one S tile of registers; two workgroups share each CU, so every SIMD runs two such
 // waves whose barriers and dependency stalls cover each other.
+// attn_tile computes work item `work` (query tile fastest, then KV piece, then (b, h)); the
+// kernel below hands out the items.
 template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS, bool SOL>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd(AttnParams p) {
+__device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   constexpr int kThreads = WAVES * 64;
   constexpr int kRowsPerWg = WAVES * 32;
   constexpr int kChunks = 512 / kThreads;       // 16-byte chunks per thread of one 8 KB tile
@@ -180,12 +184,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   __shared__ __attribute__((aligned(16))) uint8_t lds[kSlots * kSlotBytes];
   auto slot = [&](int i) -> uint8_t* { return lds + i * kSlotBytes; };
 
-  // ---- work item (XCD-major: dispatch round-robins workgroups over the 8 XCDs) ----
-  // (work order: query tile fastest, then KV piece, then (b, h), so that the workgroups of one
-  // XCD share the K/V tiles of one piece)
-  const int per_xcd = (p.total_work + 7) / 8;
-  const int work = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (work >= p.total_work) return;
+  // ---- work item ----
   const int64_t bh = work / (p.n_qtiles * p.splits);
   const int split = (work / p.n_qtiles) % p.splits;
   const int64_t q0 = static_cast<int64_t>(work % p.n_qtiles) * kRowsPerWg;
@@ -199,12 +198,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // ---- sparse row of this query tile ----
   int e_begin = 0, e_end = 0, q_valid_len = 0;
+  int q_tile_off = 0;  // first row of the workgroup within its query tile
   if constexpr (SPARSE && !SOL) {
     const int u = static_cast<int>(q0 / p.tile_tokens);
-    e_begin = p.row_ptr[u];
-    e_end = p.row_ptr[u + 1];
-    q_valid_len = p.tile_len[u];
-    if (static_cast<int>(q0 % p.tile_tokens) >= q_valid_len) return;  // all padding rows
+    q_tile_off = static_cast<int>(q0 - static_cast<int64_t>(u) * p.tile_tokens);
+    e_begin = load_uniform(p.row_ptr, u);
+    e_end = load_uniform(p.row_ptr, u + 1);
+    q_valid_len = load_uniform(p.tile_len, u);
+    if (q_tile_off >= q_valid_len) return;  // all padding rows
   }
   const int per_tile = p.tile_tokens / kBlock;
   auto nblk_of_len = [&](int len) -> int { return min((len + kBlock - 1) / kBlock, per_tile); };
@@ -241,7 +242,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   if constexpr (SOL) {
     for (int64_t w = 0; w < p.sol_words; w++) n_iter += __builtin_popcountll(sol_word(w));
   } else if constexpr (SPARSE) {
-    for (int e = e_begin; e < e_end; e++) n_iter += nblk_of_len(p.tile_len[p.col_idx[e]]);
+    // the row's key blocks, the entries counted by the lanes in parallel (independent loads
+    // instead of a chain of dependent scalar ones)
+    int cnt = 0;
+    for (int e = e_begin + lane; e < e_end; e += 64) cnt += nblk_of_len(p.tile_len[p.col_idx[e]]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    n_iter = __builtin_amdgcn_readfirstlane(cnt);
   } else {
     const int64_t kb_lo = static_cast<int64_t>(split) * p.split_blocks;
     const int64_t kb_hi = min(p.NB, kb_lo + p.split_blocks);
@@ -282,12 +289,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     lc.v = static_cast<int>(p.reverse ? sol_prev(p.NB - 1) : sol_next(0));
   } else if constexpr (SPARSE) {
     lc.e = p.reverse ? e_end - 1 : e_begin;
-    lc.v = p.col_idx[lc.e];
-    lc.len = p.tile_len[lc.v];
+    lc.v = load_uniform(p.col_idx, lc.e);
+    lc.len = load_uniform(p.tile_len, lc.v);
     lc.bt = p.reverse ? nblk_of_len(lc.len) - 1 : 0;
-    lc.v1 = in_row(lc.e + edir) ? p.col_idx[lc.e + edir] : 0;
-    lc.len1 = in_row(lc.e + edir) ? p.tile_len[lc.v1] : 0;
-    lc.v2 = in_row(lc.e + 2 * edir) ? p.col_idx[lc.e + 2 * edir] : 0;
+    lc.v1 = in_row(lc.e + edir) ? load_uniform(p.col_idx, lc.e + edir) : 0;
+    lc.len1 = in_row(lc.e + edir) ? load_uniform(p.tile_len, lc.v1) : 0;
+    lc.v2 = in_row(lc.e + 2 * edir) ? load_uniform(p.col_idx, lc.e + 2 * edir) : 0;
   }
   auto block_of = [&](const KvCursor& c, int& limit) -> int64_t {
     if constexpr (SOL) {
@@ -314,8 +321,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
           c.len = c.len1;
           c.bt = p.reverse ? nblk_of_len(c.len) - 1 : 0;
           c.v1 = c.v2;
-          c.len1 = in_row(c.e + edir) ? p.tile_len[c.v1] : 0;
-          c.v2 = in_row(c.e + 2 * edir) ? p.col_idx[c.e + 2 * edir] : 0;
+          c.len1 = in_row(c.e + edir) ? load_uniform(p.tile_len, c.v1) : 0;
+          c.v2 = in_row(c.e + 2 * edir) ? load_uniform(p.col_idx, c.e + 2 * edir) : 0;
         }
       }
     } else {
@@ -817,7 +824,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 
   // ---- epilogue: O = acc * g_d / l', BF16, scattered to the destination rows ----
   bool ok = qrow < p.N;
-  if constexpr (SPARSE && !SOL) ok = ok && static_cast<int>(qrow % p.tile_tokens) < q_valid_len;
+  if constexpr (SPARSE && !SOL) ok = ok && q_tile_off + 32 * wave + l32 < q_valid_len;
   // the S-scaled row sum: standard cast, the two lane halves' shares; ExpCast, the matrix-core
   // sum, whole in every lane (with V-Smooth, collected per V block in l_part)
   float l_tot;
@@ -928,6 +935,53 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   }
 }
 
+// Variants whose workgroups take their items from the per-XCD queues (the others would spill
+// registers in the loop around attn_tile, or, Sol, have no queue in their workspace).
+template <bool VSMOOTH, bool STATS, bool SOL>
+constexpr bool kQueued = !VSMOOTH && !STATS && !SOL;
+
+// The work items are cut into eight contiguous ranges, one per XCD, so that the workgroups of
+// an XCD share the K/V tiles of few (b, h) in its L2. Queued variants: persistent workgroups
+// (as many as fit the device) take the items of their XCD's range one at a time from a counter
+// in the workspace, then those of the other ranges, so that an XCD that runs faster (or whose
+// items are shorter: sparse rows differ in length) takes more; the counters are zeroed by
+// attn_queue_reset before each launch. Otherwise one workgroup per item: the hardware
+// dispatches workgroup i to XCD i % 8, so workgroup i takes item (i % 8) * per_xcd + i / 8.
+template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS, bool SOL>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd(AttnParams p) {
+  const int per_xcd = (p.total_work + 7) / 8;
+  if constexpr (kQueued<VSMOOTH, STATS, SOL>) {
+    __shared__ int work_s;
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    for (;;) {
+      if (threadIdx.x == 0) {
+        int w = -1;
+        for (int k = 0; k < 8 && w < 0; k++) {
+          const int q = static_cast<int>((xcc + k) & 7u);
+          const int cnt = min(per_xcd, p.total_work - q * per_xcd);
+          if (cnt <= 0) continue;
+          const int i = static_cast<int>(atomicAdd(p.work_ctr + q, 1u));
+          if (i < cnt) w = q * per_xcd + i;
+        }
+        work_s = w;
+      }
+      __syncthreads();
+      const int work = work_s;
+      __syncthreads();  // (work_s is rewritten for the next item)
+      if (work < 0) return;
+      attn_tile<WAVES, SPARSE, EXPCAST, VSMOOTH, STATS, SOL>(p, work);
+    }
+  } else {
+    const int work = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+    if (work < p.total_work) attn_tile<WAVES, SPARSE, EXPCAST, VSMOOTH, STATS, SOL>(p, work);
+  }
+}
+
+__global__ void attn_queue_reset(uint32_t* ctr) {
+  if (threadIdx.x < 8) ctr[threadIdx.x] = 0u;
+}
+
 // V-Smooth: the factor mu = float(mean_hat[bh, j, d]) * (s_r[d] > 0 ? 1 / s_r[d] : 1) as the
 // restore's A-operand record mu_op[bh, j, d] = {mu_hi|mu_hi, mu_lo|0, 0, 0} (BF16 pairs, low half
 // first; mu_hi = BF16(mu), mu_lo = BF16(mu - mu_hi), both rounded to nearest even).
@@ -993,7 +1047,14 @@ hipError_t launch_variant(AttnParams& p, hipStream_t stream) {
   const int rows = WAVES * 32;
   p.n_qtiles = static_cast<int>((p.N + rows - 1) / rows);
   p.total_work = p.B * p.H * p.n_qtiles * p.splits;
-  const unsigned grid = static_cast<unsigned>(((p.total_work + 7) / 8) * 8);
+  unsigned grid = static_cast<unsigned>(((p.total_work + 7) / 8) * 8);
+  if constexpr (kQueued<VSMOOTH, STATS, SOL>) {
+    if (!p.work_ctr) return hipErrorInvalidValue;
+    // resident workgroups: two waves per SIMD, four SIMDs per CU
+    const int64_t slots = static_cast<int64_t>(p.cus > 0 ? p.cus : 256) * 8 / WAVES;
+    grid = static_cast<unsigned>(p.total_work < slots ? p.total_work : slots);
+    hipLaunchKernelGGL(attn_queue_reset, dim3(1), dim3(64), 0, stream, p.work_ctr);
+  }
   hipLaunchKernelGGL((attn_fwd<WAVES, SPARSE, EXPCAST, VSMOOTH, STATS, SOL>), dim3(grid), dim3(WAVES * 64), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;

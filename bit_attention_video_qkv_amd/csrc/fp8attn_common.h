@@ -75,6 +75,12 @@ __device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
   return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
+// Read of a read-only int array at a wave-uniform index as a scalar load (through the constant
+// address space). A plain load would become a vector load whose use waits on vmcnt, the
+// counter that also tracks the K/V copies in flight.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* base, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)base)[i];
+}
 __device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(gbase)),
                "s"(__builtin_amdgcn_readfirstlane(lds_addr))

@@ -68,6 +68,10 @@ struct AttnParams {
   // merges its result with the summary route's in its epilogue), or null
   const uint64_t* sol_mask;
   int64_t sol_words;
+  // per-XCD work queues: eight counters (workspace) zeroed before each launch; variants without
+  // V-Smooth, underflow counting or Sol take their work items from them
+  uint32_t* work_ctr;
+  int cus;  // compute units of the device (sizes the persistent grid)
 };
 
 // Sol routing preparation and summary route (fp8attn_sol.hip).

@@ -215,8 +215,10 @@ fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, i
  *                    partial outputs live in the workspace.
  *   out       bf16 [B, n_out, H, D]; rows a query does not own are left untouched.
  *   workspace device scratch of fp8attn_forward_workspace_bytes(B, N, H, D, vsmooth,
- *             kv_splits) bytes, 16-byte aligned (may be NULL when that is 0). With more than one
- *             piece it holds FP32 [pieces, B*H, N, D] partial outputs and [pieces, B*H, N] lse.
+ *             kv_splits) bytes (at least 256), 16-byte aligned, overwritten. It holds the work
+ *             queues of the call's workgroups (so two calls that run at the same time need two
+ *             workspaces), V-Smooth's mean operands and, with more than one piece, FP32
+ *             [pieces, B*H, N, D] partial outputs and [pieces, B*H, N] lse.
  * Errors: EINVAL on bad pointers/sizes, S outside (0, 448], sparse with V-Smooth, sparse
  *   N != n_tiles * tile_tokens or tile_tokens not a multiple of 64, ExpCast with underflow
  *   counting, kv_splits out of range or > 1 with sparse; EUNSUPPORTED on D != 128 or a device
@@ -236,7 +238,7 @@ typedef struct fp8attn_fwd_opts {
 } fp8attn_fwd_opts;
 
 /* Workspace of fp8attn_forward for the shape, V-Smooth (0/1) and kv_splits (as in the options;
- * pass 1 for a sparse call); 0 when none is needed or an argument is invalid. */
+ * pass 1 for a sparse call): at least 256 bytes; 0 when an argument is invalid. */
 size_t fp8attn_forward_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D,
                                        int32_t vsmooth, int32_t kv_splits);
 

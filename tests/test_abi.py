@@ -115,6 +115,8 @@ def test_forward_rejects_bad_arguments(m):
     sp = m._Sparse(128, 2, _fake(), _fake(), _fake())
     assert call(_opts(m, sparse=ctypes.pointer(sp), kv_splits=2)) == 1   # split-KV is dense only
     assert call(_opts(m, kv_splits=2), ws=0) == 1                         # pieces need workspace
+    assert call(_opts(m), ws=0) == 1                                      # work queues need workspace
+    assert call(_opts(m), ws=255) == 1
 
 
 @pytest.mark.parametrize("grid", [(21, 45, 80, 6, 8, 8, 1, 1, 1), (5, 7, 9, 2, 4, 8, 1, 1, 0),
@@ -143,23 +145,24 @@ def test_workspace_sizes(m):
     L = m.lib()
     assert L.fp8attn_quantize_workspace_bytes(1, 75600, 40, 128, 0) >= 40 * 591 * 128 * 4 + \
         2 * 40 * 1182 * 128 * 4   # + the smoothing block sums of K and V
-    assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0, 1) == 0
+    q = 256  # the eight work-queue counters, padded to 256 bytes
+    assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0, 1) == q
     # V-Smooth: one 16-byte mean operand record per (b, h, 128-row block, channel)
-    assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1, 0) == 24 * 384 * 128 * 16
+    assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1, 0) == q + 24 * 384 * 128 * 16
     # split-KV: 4096 tokens = 64 key blocks, 2 pieces of 32 blocks; 3 requested -> L = 22, 3 pieces
-    assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 2) == 2 * 8 * 4096 * 129 * 4
-    assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 3) == 3 * 8 * 4096 * 129 * 4
+    assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 2) == q + 2 * 8 * 4096 * 129 * 4
+    assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 3) == q + 3 * 8 * 4096 * 129 * 4
     # 5 blocks, 16 requested: L = 2, 3 pieces
     assert L.fp8attn_forward_workspace_bytes(1, 300, 1, 128, 0, 16) == \
-        -(-3 * 300 * 128 * 4 // 256) * 256 + -(-3 * 300 * 4 // 256) * 256
+        q + -(-3 * 300 * 128 * 4 // 256) * 256 + -(-3 * 300 * 4 // 256) * 256
     assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 17) == 0
     # auto (no device here: 256 compute units assumed): one piece for the large shapes and for
     # short sequences; H=1, N=75600 (591 query tiles, 1.15 rounds) -> ceil(3 * 512 / 591) = 3
     auto = m.FP8ATTN_KV_SPLITS_AUTO
-    assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0, auto) == 0
-    assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, auto) == 0
+    assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0, auto) == q
+    assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, auto) == q
     assert L.fp8attn_forward_workspace_bytes(1, 75600, 1, 128, 0, auto) == \
-        L.fp8attn_forward_workspace_bytes(1, 75600, 1, 128, 0, 3) > 0
+        L.fp8attn_forward_workspace_bytes(1, 75600, 1, 128, 0, 3) > q
     assert L.fp8attn_quantize_workspace_bytes(1, 100, 2, 64, 0) == 0
 
 
