@@ -290,7 +290,7 @@ namespace {
 
 struct SolLayout {
   int64_t NB, NBg, NBp, W;
-  size_t ksum, vsumT, kq8, kq_scale, mk, Mk, theta, mask, o_part, lse, total;
+  size_t queue, ksum, vsumT, kq8, kq_scale, mk, Mk, theta, mask, o_part, lse, total;
 };
 
 SolLayout sol_layout(int32_t B, int32_t N, int32_t H) {
@@ -306,6 +306,7 @@ SolLayout sol_layout(int32_t B, int32_t N, int32_t H) {
     off += round_up(bytes);
     return o;
   };
+  L.queue = take(kQueueBytes);  // the exact route's work queues
   L.ksum = take(bh * L.NB * kHeadDim * sizeof(float));
   L.vsumT = take(bh * kHeadDim * L.NBp * sizeof(uint16_t));
   L.kq8 = take(bh * L.NBp * kHeadDim);
@@ -418,6 +419,8 @@ fp8attn_status fp8attn_sol_forward(int32_t B, int32_t N, int32_t H, int32_t D, c
   p.lse = lse;
   p.sol_mask = mask;
   p.sol_words = L.W;
+  p.work_ctr = reinterpret_cast<uint32_t*>(ws + L.queue);
+  p.cus = device_cus();
   int variant = fp8attn::kVarSol;
   if (o->pcast == FP8ATTN_PCAST_EXPCAST) variant |= fp8attn::kVarExpCast;
   return from_hip(fp8attn::launch_attention(p, variant, stream));

@@ -936,16 +936,16 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
 }
 
 // Variants whose workgroups take their items from the per-XCD queues (the others would spill
-// registers in the loop around attn_tile, or, Sol, have no queue in their workspace).
+// registers in the loop around attn_tile).
 template <bool VSMOOTH, bool STATS, bool SOL>
-constexpr bool kQueued = !VSMOOTH && !STATS && !SOL;
+constexpr bool kQueued = !VSMOOTH && !STATS;
 
 // The work items are cut into eight contiguous ranges, one per XCD, so that the workgroups of
 // an XCD share the K/V tiles of few (b, h) in its L2. Queued variants: persistent workgroups
 // (as many as fit the device) take the items of their XCD's range one at a time from a counter
 // in the workspace, then those of the other ranges, so that an XCD that runs faster (or whose
-// items are shorter: sparse rows differ in length) takes more; the counters are zeroed by
-// attn_queue_reset before each launch. Otherwise one workgroup per item: the hardware
+// items are shorter: sparse rows and Sol masks differ in length) takes more; the counters are
+// zeroed by attn_queue_reset before each launch. Otherwise one workgroup per item: the hardware
 // dispatches workgroup i to XCD i % 8, so workgroup i takes item (i % 8) * per_xcd + i / 8.
 template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS, bool SOL>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd(AttnParams p) {

@@ -69,7 +69,7 @@ struct AttnParams {
   const uint64_t* sol_mask;
   int64_t sol_words;
   // per-XCD work queues: eight counters (workspace) zeroed before each launch; variants without
-  // V-Smooth, underflow counting or Sol take their work items from them
+  // V-Smooth or underflow counting take their work items from them
   uint32_t* work_ctr;
   int cus;  // compute units of the device (sizes the persistent grid)
 };
