@@ -637,6 +637,69 @@ def test_maximum_batch_heads(m, orc):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("sparse", [False, True])
+def test_work_queues_streams_and_reuse(m, orc, sparse):
+    """The persistent workgroups take their work items from counters in the workspace. Several
+    items per workgroup, with items taken across XCD ranges, must still write every output row
+    exactly once. The outputs start as NaN, so a skipped item shows. Calls must agree bit for bit:
+    - with a workspace full of 0xFF bytes (the counters are reset by the launch);
+    - with one workspace reused;
+    - on two streams at once with one workspace each.
+    One dense head of the first call is checked against the oracle."""
+    if sparse:
+        # 10x15x24 grid in (6,8,8) tiles: 12 tiles of 384 tokens, ragged in t and h
+        lay = m.sta_build(10, 15, 24, 6, 8, 8, 1, 1, 1)
+        Nsrc, H = 10 * 15 * 24, 40
+        N = lay["perm"].shape[0]
+        sp = m.sparse_to_device(lay, DEV)
+        perm = torch.from_numpy(lay["perm"]).to(DEV)
+    else:
+        Nsrc, H = 20000, 8
+        N, sp, perm = Nsrc, None, None
+    say("work queues", "sparse" if sparse else "dense", Nsrc, N, H)
+    g = torch.Generator(device=DEV).manual_seed(77)
+    ins = [[torch.randn((1, Nsrc, H, 128), generator=g, device=DEV).to(torch.bfloat16) for _ in range(3)]
+           for _ in range(2)]
+    qz = [m.quantize_qkv(*x, perm_q=perm, perm_kv=perm, n_layout=N) for x in ins]
+
+    def run(i, ws, stream=None):
+        out = torch.full((1, Nsrc, H, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+        kw = dict(kv_order=1, sparse=sp, out_rows=perm, n_out=Nsrc, out=out, workspace=ws)
+        if stream is None:
+            m.forward(qz[i], **kw)
+        else:
+            with torch.cuda.stream(stream):
+                m.forward(qz[i], **kw)
+        return out
+
+    def new_ws():
+        ws = m.forward_workspace(1, N, H, False, DEV, 1)
+        ws.fill_(255)
+        return ws
+
+    ref = [run(i, new_ws()) for i in range(2)]
+    torch.cuda.synchronize()
+    for r in ref:
+        assert not torch.isnan(r.float()).any(), "a work item was skipped"
+    ws = new_ws()
+    for _ in range(3):
+        assert torch.equal(run(0, ws).view(torch.int16), ref[0].view(torch.int16))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    w1, w2 = new_ws(), new_ws()
+    torch.cuda.synchronize()
+    o1, o2 = run(0, w1, s1), run(1, w2, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), ref[0].view(torch.int16))
+    assert torch.equal(o2.view(torch.int16), ref[1].view(torch.int16))
+    if not sparse:
+        h = 5
+        sl = lambda t: _bits(t[:, :, h:h + 1].contiguous().cpu())
+        ref_q = orc.quantize(*(sl(t) for t in ins[0]))
+        want, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=True, return_amb=True)
+        got = ref[0][:, :, h:h + 1].float().cpu().numpy().transpose(0, 2, 1, 3).astype(np.float64)
+        _compare_out(got, want, "work queues, head 5", amb)
+
+
 def _slice_heads(t, heads):
     return t[:, :, heads, :].contiguous()
 
