@@ -830,6 +830,25 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   float l_tot;
   if constexpr (EXPCAST) l_tot = VSMOOTH ? l_part : lacc[0];
   else l_tot = xsum(l_part);
+  // This lane's channels d0 .. d0 + 3 for output group i = 4 dt + g: d0 = 32 dt + 8 g + 4 lh.
+  // The groups are written in two halves of eight. The channel vectors of a half are loaded
+  // before any is used, so their loads overlap: two round trips instead of 16 before the
+  // stores. The sched barrier keeps the second half's loads from being hoisted, which would
+  // spill registers.
+  auto chan = [&](int i) -> int { return 32 * (i >> 2) + 8 * (i & 3) + 4 * lh; };
+  auto load8 = [&](float4 (&dst)[8], const float* src, int half) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) dst[k] = *reinterpret_cast<const float4*>(src + chan(8 * half + k));
+  };
+  auto load_scales = [&](float4 (&sv)[8], float4 (&sh)[8], int half) {
+    load8(sv, p.v_scale + bh * kHeadDim, half);
+    if (p.v_shift) {
+      load8(sh, p.v_shift + bh * kHeadDim, half);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; k++) sh[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  };
   if constexpr (SOL) {
     // Sol: merge with the summary route's piece (o_part, lse: written before this kernel) by
     // their log2 weights, as split_merge does for pieces, and write BF16 O directly
@@ -842,26 +861,26 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
       const float inv_w = 1.0f / (w0 + w1);
       const float a0 = l_tot > 0.0f ? w0 * inv_w / l_tot : 0.0f;  // on acc * v_scale
       const float a1 = w1 * inv_w;
-      const float* o1 = p.o_part + r1 * kHeadDim;
       uint16_t* orow = p.out + ((b * p.n_out + qrow) * p.H + h) * kHeadDim;
 #pragma unroll
-      for (int dt = 0; dt < 4; dt++)
+      for (int half = 0; half < 2; half++) {
+        float4 sv[8], sh[8], ov[8];
+        load_scales(sv, sh, half);
+        load8(ov, p.o_part + r1 * kHeadDim, half);
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-          const int d0 = 32 * dt + 8 * g + 4 * lh;
-          const float4 sv = *reinterpret_cast<const float4*>(p.v_scale + bh * kHeadDim + d0);
-          const float4 ov = *reinterpret_cast<const float4*>(o1 + d0);
-          float4 sh = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-          if (p.v_shift) sh = *reinterpret_cast<const float4*>(p.v_shift + bh * kHeadDim + d0);
-          const float e0 = oacc[dt][4 * g + 0] * sv.x * a0 + ov.x * a1 + sh.x;
-          const float e1 = oacc[dt][4 * g + 1] * sv.y * a0 + ov.y * a1 + sh.y;
-          const float e2 = oacc[dt][4 * g + 2] * sv.z * a0 + ov.z * a1 + sh.z;
-          const float e3 = oacc[dt][4 * g + 3] * sv.w * a0 + ov.w * a1 + sh.w;
+        for (int k = 0; k < 8; k++) {
+          const int i = 8 * half + k;
+          const float e0 = oacc[i >> 2][4 * (i & 3) + 0] * sv[k].x * a0 + ov[k].x * a1 + sh[k].x;
+          const float e1 = oacc[i >> 2][4 * (i & 3) + 1] * sv[k].y * a0 + ov[k].y * a1 + sh[k].y;
+          const float e2 = oacc[i >> 2][4 * (i & 3) + 2] * sv[k].z * a0 + ov[k].z * a1 + sh[k].z;
+          const float e3 = oacc[i >> 2][4 * (i & 3) + 3] * sv[k].w * a0 + ov[k].w * a1 + sh[k].w;
           uint2 o;
           o.x = static_cast<uint32_t>(f32_to_bf16_rne(e0)) | (static_cast<uint32_t>(f32_to_bf16_rne(e1)) << 16);
           o.y = static_cast<uint32_t>(f32_to_bf16_rne(e2)) | (static_cast<uint32_t>(f32_to_bf16_rne(e3)) << 16);
-          *reinterpret_cast<uint2*>(orow + d0) = o;
+          *reinterpret_cast<uint2*>(orow + chan(i)) = o;
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     return;
   }
@@ -875,23 +894,26 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
         const int64_t prow = (static_cast<int64_t>(split) * p.B * p.H + bh) * p.N + qrow;
         float* orow = p.o_part + prow * kHeadDim;
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++)
+        for (int half = 0; half < 2; half++) {
+          float4 sv[8], sh[8];
+          load_scales(sv, sh, half);
 #pragma unroll
-          for (int g = 0; g < 4; g++) {
-            const int d0 = 32 * dt + 8 * g + 4 * lh;
-            const float4 sv = *reinterpret_cast<const float4*>(p.v_scale + bh * kHeadDim + d0);
-            float gs[4] = {sv.x, sv.y, sv.z, sv.w};
+          for (int k = 0; k < 8; k++) {
+            const int i = 8 * half + k;
+            float gs[4] = {sv[k].x, sv[k].y, sv[k].z, sv[k].w};
             if constexpr (VSMOOTH) {
 #pragma unroll
               for (int e = 0; e < 4; e++) gs[e] = gs[e] > 0.0f ? gs[e] : 1.0f;
             }
             float4 o;
-            o.x = oacc[dt][4 * g + 0] * gs[0] * inv_l;
-            o.y = oacc[dt][4 * g + 1] * gs[1] * inv_l;
-            o.z = oacc[dt][4 * g + 2] * gs[2] * inv_l;
-            o.w = oacc[dt][4 * g + 3] * gs[3] * inv_l;
-            *reinterpret_cast<float4*>(orow + d0) = o;
+            o.x = oacc[i >> 2][4 * (i & 3) + 0] * gs[0] * inv_l;
+            o.y = oacc[i >> 2][4 * (i & 3) + 1] * gs[1] * inv_l;
+            o.z = oacc[i >> 2][4 * (i & 3) + 2] * gs[2] * inv_l;
+            o.w = oacc[i >> 2][4 * (i & 3) + 3] * gs[3] * inv_l;
+            *reinterpret_cast<float4*>(orow + chan(i)) = o;
           }
+          __builtin_amdgcn_sched_barrier(0);
+        }
         if (lh == 0) p.lse[prow] = l_tot > 0.0f ? m_run + __log2f(l_tot) : -INFINITY;
       }
       return;
@@ -904,34 +926,30 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     const float inv_l = 1.0f / l_tot;
     uint16_t* orow = p.out + ((b * p.n_out + dst) * p.H + h) * kHeadDim;
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++)
+    for (int half = 0; half < 2; half++) {
+      float4 sv[8], sh[8];
+      load_scales(sv, sh, half);
 #pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int d0 = 32 * dt + 8 * g + 4 * lh;
-        const float4 sv = *reinterpret_cast<const float4*>(p.v_scale + bh * kHeadDim + d0);
-        float gs[4] = {sv.x, sv.y, sv.z, sv.w};
+      for (int k = 0; k < 8; k++) {
+        const int i = 8 * half + k;
+        float gs[4] = {sv[k].x, sv[k].y, sv[k].z, sv[k].w};
         if constexpr (VSMOOTH) {
 #pragma unroll
           for (int e = 0; e < 4; e++) gs[e] = gs[e] > 0.0f ? gs[e] : 1.0f;
         }
-        // sequence-mean smoothing: every softmax row sums to one, so the V shift comes back
-        // as a constant vector
-        float c[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (p.v_shift) {
-          const float4 cv = *reinterpret_cast<const float4*>(p.v_shift + bh * kHeadDim + d0);
-          c[0] = cv.x;
-          c[1] = cv.y;
-          c[2] = cv.z;
-          c[3] = cv.w;
-        }
+        // sequence-mean smoothing: every softmax row sums to one, so the V shift comes back as
+        // a constant vector
+        const float c[4] = {sh[k].x, sh[k].y, sh[k].z, sh[k].w};
         float ov[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) ov[e] = oacc[dt][4 * g + e] * gs[e] * inv_l + c[e];
+        for (int e = 0; e < 4; e++) ov[e] = oacc[i >> 2][4 * (i & 3) + e] * gs[e] * inv_l + c[e];
         uint2 o;
         o.x = static_cast<uint32_t>(f32_to_bf16_rne(ov[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(ov[1])) << 16);
         o.y = static_cast<uint32_t>(f32_to_bf16_rne(ov[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(ov[3])) << 16);
-        *reinterpret_cast<uint2*>(orow + d0) = o;
+        *reinterpret_cast<uint2*>(orow + chan(i)) = o;
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
