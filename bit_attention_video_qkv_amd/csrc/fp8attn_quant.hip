@@ -353,11 +353,14 @@ __device__ __forceinline__ float mul_rounded(float a, float b) {
 template <bool BIAS>
 __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
   // [channel][token quad]: word w of channel c holds the codes of tokens 4w .. 4w + 3 (byte u =
-  // token 4w + u); 17 words per channel, so the 16 channel octets of a wave's stores spread over
-  // the banks (two lanes per bank at most)
-  constexpr int kTileWords = kBlock / 4 + 1;
+  // token 4w + u); an odd number of words per channel, so the 16 channel octets of a wave's
+  // stores spread over the banks (two lanes per bank at most).
+  // Rows per workgroup: 128, so that each channel's codes fill whole 128-byte lines of v8t; 64
+  // with the bias correction, whose error sums are per 64-row block
+  constexpr int kRows = BIAS ? kBlock : 2 * kBlock;
+  constexpr int kTileWords = kRows / 4 + 1;
   __shared__ uint32_t tile[kHeadDim][kTileWords];
-  const int64_t blk = blockIdx.x;
+  const int64_t blk = blockIdx.x;  // block of kRows rows
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / p.H, h = bh % p.H;
   const int chunk = threadIdx.x & 15;  // channels 8 chunk .. + 7
@@ -375,11 +378,13 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
     if (threadIdx.x < 2) valid_bits[threadIdx.x] = 0u;
     __syncthreads();
   }
+#pragma unroll
+  for (int hh = 0; hh < kRows / kBlock; hh++) {  // 64-row halves
   uint32_t lo4[4], hi4[4];  // per token: the codes of channels 0-3 and 4-7 of the octet
 #pragma unroll
   for (int pass = 0; pass < 4; pass++) {
-    const int t = 4 * row0 + pass;
-    const int64_t i = blk * kBlock + t;
+    const int t = kBlock * hh + 4 * row0 + pass;
+    const int64_t i = blk * kRows + t;
     const int64_t s = gather_src(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, i);
     uint32_t lo = 0, hi = 0;
     if (s >= 0) {
@@ -423,19 +428,25 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
   transpose4(hi4, chi);
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    tile[chunk * 8 + q][row0] = clo[q];
-    tile[chunk * 8 + 4 + q][row0] = chi[q];
+    tile[chunk * 8 + q][kBlock / 4 * hh + row0] = clo[q];
+    tile[chunk * 8 + 4 + q][kBlock / 4 * hh + row0] = chi[q];
+  }
   }
   __syncthreads();
-  // Thread t writes channel t/2, tokens 32*(t%2) .. +31 (two 16-byte stores).
+  // Thread t writes channel t/2, tokens kRows/2 * (t%2) .. + kRows/2 - 1 (16-byte stores); with
+  // 128 rows the second half of the last block lies beyond N64 when NB is odd.
+  constexpr int kWords = kRows / 8;
   const int d = threadIdx.x >> 1;
   const int half = threadIdx.x & 1;
-  uint32_t w[8];
+  const int64_t tok0 = blk * kRows + kRows / 2 * half;
+  if (tok0 < p.N64) {
+    uint32_t w[kWords];
 #pragma unroll
-  for (int i = 0; i < 8; i++) w[i] = tile[d][8 * half + i];
-  uint4* dst = reinterpret_cast<uint4*>(p.v8t + (bh * kHeadDim + d) * p.N64 + blk * kBlock + 32 * half);
-  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    for (int i = 0; i < kWords; i++) w[i] = tile[d][kWords * half + i];
+    uint4* dst = reinterpret_cast<uint4*>(p.v8t + (bh * kHeadDim + d) * p.N64 + tok0);
+#pragma unroll
+    for (int j = 0; j < kWords / 4; j++) dst[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+  }
   if constexpr (BIAS) {
     // The rounding error of channel c, rows in ascending order (the bias correction exists only
     // with V smoothing, so V' = fl32(V - mean_V)): err = fl32(fl32(decode(code) * s_v) - V').
@@ -501,7 +512,7 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const dim3 g_enc(static_cast<unsigned>(p.NB), bh);
   if (!p.v_bias_correction) {
-    hipLaunchKernelGGL(v_encode<false>, g_enc, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(v_encode<false>, dim3(static_cast<unsigned>(p.NB128), bh), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(v_encode<true>, g_enc, dim3(256), 0, stream, p);
