@@ -276,7 +276,9 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
  *   out        bf16 [B, N, H, D].
  *   route_mask uint64 [B*H, NB, W] (W = ceil(NB / 64); bit j % 64 of word j / 64 = KV block j
  *              exact for Q block u) or NULL.
- *   workspace  fp8attn_sol_workspace_bytes(B, N, H, D) bytes, 16-byte aligned.
+ *   workspace  fp8attn_sol_workspace_bytes(B, N, H, D) bytes, 16-byte aligned, overwritten. It
+ *              holds the summaries, thresholds and the summary route's output, and the work queues
+ *              of the exact route (two calls that run at the same time need two workspaces).
  * Errors: EINVAL on bad pointers/sizes/options; EUNSUPPORTED on D != 128 or a device other
  *   than gfx950.
  * ------------------------------------------------------------------------------------------ */
