@@ -232,8 +232,11 @@ __global__ __launch_bounds__(256) void quant_qk(QuantParams p) {
 }
 
 // 2. Per 128-row block statistics of V. Thread t: channels 8*(t%16)..+7, rows t/16 + 16*p.
+// (VS: V-Smooth; without it the FP64 column sums and their 16 KB of LDS are not needed, and
+// eight workgroups fit a CU instead of six)
+template <bool VS>
 __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
-  __shared__ double dsum[16][kHeadDim];  // [row group][channel]
+  __shared__ double dsum[VS ? 16 : 1][kHeadDim];  // [row group][channel]
   __shared__ float fmax_[16][kHeadDim];
   __shared__ float mhat_s[kHeadDim];
   __shared__ int n_valid_s;
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
   float m[8];
 #pragma unroll
   for (int q = 0; q < 8; q++) m[q] = 0.0f;
-  if (p.vsmooth) {
+  if constexpr (VS) {
     // Column sums in FP64: exact for <= 128 bf16 terms, so the summation order is irrelevant.
     double s[8];
 #pragma unroll
@@ -503,8 +506,9 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(quant_qk, g_qk, dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(v_block_stats, dim3(static_cast<unsigned>(p.NB128), static_cast<unsigned>(p.B * p.H)),
-                     dim3(256), 0, stream, p);
+  const dim3 g_stats(static_cast<unsigned>(p.NB128), static_cast<unsigned>(p.B * p.H));
+  if (p.vsmooth) hipLaunchKernelGGL(v_block_stats<true>, g_stats, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(v_block_stats<false>, g_stats, dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(v_finalize, dim3(static_cast<unsigned>(p.B * p.H), kHeadDim / 32), dim3(1024), 0, stream, p);
