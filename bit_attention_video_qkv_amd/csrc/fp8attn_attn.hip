@@ -590,19 +590,31 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     if constexpr (EXPCAST) {
       // code = clamp(rint(8 z + 56 - 0.35), 0, 126) with z = log2(S p~): one FMA per key, then
       // v_cvt_pk_u8_f32, which rounds to nearest even, saturates to [0, 255] (NaN and -inf to
-      // 0) and inserts the byte into the P word. The largest code of the block is that of the
-      // row maximum, 8 log2 S + 55.65 <= 126.11 for S <= 448, so the upper clamp is inactive;
-      // b8 is lowered only if the rounding of b8 at huge logits would carry the row maximum to
-      // 0x7F (E4M3 NaN). The row sums come from the matrix cores (pv).
+      // 0) and inserts the byte into the P word. The FMA is monotone in x, so the largest byte
+      // of a row's block is that of its maximum, 8 log2 S + 55.65 <= 126.11 for S <= 448, and
+      // the upper clamp is inactive. Only the FP32 rounding of b8 at huge logits (|m| of order
+      // 1e5 log2 units and beyond) can carry the maximum past 126.5, which would round to 0x7F
+      // (E4M3 NaN): a block where that happens in some row clamps every byte at 126 instead.
+      // The row sums come from the matrix cores (pv).
       const float c8 = 8.0f * cs;
-      float b8 = 8.0f * (p.log2S - m_new) + 55.65f;
-      b8 -= fmaxf(__builtin_fmaf(xrow, c8, b8) - 126.25f, 0.0f);
+      const float b8 = 8.0f * (p.log2S - m_new) + 55.65f;
+      if (__builtin_expect(__any(__builtin_fmaf(xrow, c8, b8) > 126.5f), 0)) {
 #pragma unroll
-      for (int w = 0; w < 8; w++) {
-        uint32_t word = static_cast<uint32_t>(pop[w]);  // every byte is overwritten
+        for (int w = 0; w < 8; w++) {
+          uint32_t word = static_cast<uint32_t>(pop[w]);
 #pragma unroll
-        for (int q = 0; q < 4; q++) word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(x[4 * w + q], c8, b8), q, word);
-        pop[w] = static_cast<int>(word);
+          for (int q = 0; q < 4; q++)
+            word = __builtin_amdgcn_cvt_pk_u8_f32(fminf(__builtin_fmaf(x[4 * w + q], c8, b8), 126.0f), q, word);
+          pop[w] = static_cast<int>(word);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 8; w++) {
+          uint32_t word = static_cast<uint32_t>(pop[w]);  // every byte is overwritten
+#pragma unroll
+          for (int q = 0; q < 4; q++) word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(x[4 * w + q], c8, b8), q, word);
+          pop[w] = static_cast<int>(word);
+        }
       }
       tie_k(0, lsum);
       tie_k(1, lsum);

@@ -551,13 +551,14 @@ int orc_sol_prepare(int B, int N, int H, int D, const uint8_t* q8, const uint8_t
 // mode) the error bound of the E4M3 matrix-core contraction on x_k and on the running max (the
 // contraction sums each group of 8 consecutive products after truncating them to
 // 2^(floor(log2 max|p|) - 14) of the group, an error below 2^-11 * sum_g max_g |p|); for ExpCast
-// the same window is applied to 8 z + 55.65 around a half-integer. Every code an evaluation
-// inside the window can give is correct: S p in [S p (1 - eta), S p (1 + eta)], or 8 z + 55.65
-// within 8 log2(e) eta (at very large logits the window spans several codes). amb_bound[d] is
-// the largest change of output channel d that the row's ambiguous codes can cause:
+// the same window is applied to 8 z + 55.65 around a half-integer. Only the nearest rounding
+// boundary is considered: an ambiguous key may take its code or the one neighbouring code across
+// that boundary (one code step), never a code further away. Where the window would span more
+// than one code (logits so large that the contraction bound exceeds a code step) no allowance
+// covers it, and parity is not claimed element by element there. amb_bound[d] is the largest
+// change of output channel d that flipping every ambiguous code of the row can cause:
 //   sum_k step_k * e^(m_k - m_final) / (S l) * (|V_kd| + [ExpCast] |O_d|),
-// step_k the largest distance from the code's value to another code value in its window, V the
-// dequantised value (V-Smooth: the
+// step_k the gap between the two candidate code values, V the dequantised value (V-Smooth: the
 // residual part plus, for ExpCast, the block mean), plus the same contraction bound for PV
 // (2^-11 * sum over groups of 8 keys of max |P8 V_d|, scaled like acc), plus the change of the
 // normalisation the logit error bound allows (2 |O_d| sum_k p_k (dx_k + dm) / l).
@@ -768,16 +769,17 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
                   const double eta = std::ldexp(1.0, -20) *
                                      (std::fabs(x[t]) + std::fabs(m_new) + std::fabs(std::log(S)) + 1.0) +
                                      dx[t] + dm_run;
-                  // the codes of the evaluations within the window around tf
-                  const double w = 8.0 * log2e * eta;
-                  const double c_lo = std::min(126.0, std::max(0.0, std::nearbyint(static_cast<double>(tf) - w)));
-                  const double c_hi = std::min(126.0, std::max(0.0, std::nearbyint(static_cast<double>(tf) + w)));
-                  const double cv = code_value[code];
-                  const double step = std::max(code_value[static_cast<int>(c_hi)] - cv,
-                                               cv - code_value[static_cast<int>(c_lo)]);
-                  if (step > 0.0) {
-                    for (int d = 0; d < D; d++) amb_v[d] += step * vabs(kb * 64 + t, d);
-                    amb_l += step;
+                  // the nearest half-integer: within the window, rint may give either side
+                  const double half = std::floor(static_cast<double>(tf)) + 0.5;
+                  if (std::fabs(static_cast<double>(tf) - half) <= 8.0 * log2e * eta) {
+                    const double c1 = std::min(126.0, std::max(0.0, half - 0.5));
+                    const double c2 = std::min(126.0, std::max(0.0, half + 0.5));
+                    const double step = std::fabs(code_value[static_cast<int>(c2)] -
+                                                  code_value[static_cast<int>(c1)]);
+                    if (step > 0.0) {
+                      for (int d = 0; d < D; d++) amb_v[d] += step * vabs(kb * 64 + t, d);
+                      amb_l += step;
+                    }
                   }
                 }
               } else {
@@ -790,13 +792,15 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
                   const double eta = std::ldexp(1.0, -20) *
                                      (std::fabs(x[t]) + std::fabs(m_new) + std::fabs(std::log(S)) + 1.0) +
                                      dx[t] + dm_run;
-                  // the codes of the evaluations within the relative window around S p
+                  // the nearest rounding boundary (midpoint to the neighbouring code on the
+                  // side of S p): within the relative window, either code may result
                   const double cv = code_value[code];
-                  const double lo = code_value[e4m3_code(static_cast<double>(sp) * (1.0 - eta))];
-                  const double hi = code_value[e4m3_code(static_cast<double>(sp) * (1.0 + eta))];
-                  const double step = std::max(hi - cv, cv - lo);
-                  if (step > 0.0)
-                    for (int d = 0; d < D; d++) amb_v[d] += step * vabs(kb * 64 + t, d);
+                  const double nb = static_cast<double>(sp) >= cv
+                                        ? (code < 0x7E ? code_value[code + 1] : cv)
+                                        : (code > 0 ? code_value[code - 1] : cv);
+                  const double mid = 0.5 * (cv + nb);
+                  if (nb != cv && std::fabs(static_cast<double>(sp) - mid) <= eta * static_cast<double>(sp))
+                    for (int d = 0; d < D; d++) amb_v[d] += std::fabs(nb - cv) * vabs(kb * 64 + t, d);
                 }
               }
             }

@@ -70,24 +70,43 @@ def _compare_quant(qz, ref):
         assert qz.v_shift is None
 
 
-def _compare_out(gpu_rows, ref_rows, what, amb=None):
-    """gpu_rows (BF16 values), ref_rows: [B, H, R, D] float64 over the compared rows.
+def _compare_out(gpu_rows, ref_rows, what, amb=None, peaked=False, wide=False):
+    """gpu_rows (BF16 values), ref_rows: [B, H, R, D] float64 over the compared rows (the
+    oracle's FP8-path output before its BF16 rounding).
 
-    Per element the GPU must be within 1e-2 of the oracle, plus half a BF16 step of the value
-    (the output is BF16, 2^-8 |O| at most), plus amb: what the documented evaluation error of
-    the kernel can explain (P codes within that error of a rounding boundary, where either code
-    is correct, and the E4M3 matrix-core truncation; see the oracle). rel-L2 over all compared
-    elements must stay below 5e-3 with no allowance."""
+    Default: every element within max-abs 1e-2 of the oracle and rel-L2 <= 5e-3, no allowance.
+    Two documented exceptions, each printing how many elements needed it:
+      wide    inputs whose outputs reach |O| >= 2 (channel offsets, token outliers): there the
+              BF16 output grid is coarser than the bar (one step is 2^-6 for |O| in [2, 4)), so
+              an element may exceed 1e-2 by half a BF16 step of its value, 2^-8 |O|;
+      peaked  rows dominated by a few keys (attention sinks, outlier channels): one P code sits
+              next to a rounding boundary within the device's evaluation error and decides a
+              visible part of the output, so an element may exceed 1e-2 by what flipping the
+              codes the oracle flags as ambiguous (each to its one neighbouring code) changes.
+    rel-L2 is never given an allowance."""
     diff = np.abs(gpu_rows - ref_rows)
-    amb = np.zeros(diff.shape) if amb is None else amb
-    bf16 = 2.0 ** -8 * np.abs(ref_rows)
-    excess = diff - (ATOL + bf16 + amb)
+    allow = np.zeros(diff.shape)
+    if wide:
+        allow = allow + 2.0 ** -8 * np.abs(ref_rows)
+    if peaked:
+        assert amb is not None
+        allow = allow + amb
     max_all = float(diff.max()) if diff.size else 0.0
-    within = float(np.mean(diff <= ATOL)) if diff.size else 1.0
+    over = diff > ATOL
     rel = float(np.linalg.norm(gpu_rows - ref_rows) / max(np.linalg.norm(ref_rows), 1e-30))
-    say(f"{what}: max_abs {max_all:.3e}, {100 * within:.3f}% of elements within 1e-2, "
-        f"max allowance used {float(np.max(diff - ATOL - bf16, initial=0)):.3e} "
-        f"(median amb {float(np.median(amb)) if amb.size else 0:.2e}), rel_l2 {rel:.3e}")
+    excess = diff - (ATOL + allow)
+    note = ""
+    if wide:
+        # elements above the bar whose GPU value is exactly the oracle's value rounded to BF16
+        ref_bf16 = torch.from_numpy(ref_rows.astype(np.float32)).to(torch.bfloat16).double().numpy()
+        note += (f" (|O| max {float(np.abs(ref_rows).max()):.2f}; half BF16 step allowed; "
+                 f"{int((over & (gpu_rows == ref_bf16)).sum())} of them equal the oracle rounded to BF16)")
+    if peaked:
+        note += f" (ambiguous-code allowance: median {float(np.median(amb)):.2e})"
+    say(f"{what}: max_abs {max_all:.3e}, rel_l2 {rel:.3e}, {int(over.sum())} of {diff.size} elements "
+        f"above 1e-2" + note)
+    if not (wide or peaked):
+        assert max_all <= ATOL, (what, max_all)
     assert np.all(excess <= 0), (what, float(excess.max()))
     assert rel <= RTOL_L2, (what, rel)
     return max_all, rel
@@ -212,22 +231,51 @@ def test_attention_expcast_small(m, orc, N, reverse):
 
 @pytest.mark.parametrize("S", [256.0, 448.0])
 def test_attention_expcast_extreme_logits(m, orc, S):
-    """ExpCast with logits of order 1e4-1e5 in log2 units (Q and K scaled by 48): the byte of a
-    block's row maximum is 8 log2 S + 55.65 (at most 126.11) and must stay at or below 126 (0x7F
-    is E4M3 NaN) whatever the FP32 rounding of the per-block bias; the output is finite and
-    within tolerance of the oracle."""
+    """ExpCast with Q and K scaled by 48 (logits of order 1e4 in log2 units). This is outside the
+    range where element-wise parity is claimed: the E4M3 matrix core's accumulation error on a
+    logit (below 2^-11 of the summed group maxima of the products) is then worth several code
+    steps, so the codes of the device and of the exact oracle differ by more than one step. What
+    is claimed there: the output is finite (no byte 0x7F, E4M3 NaN, ever reaches the PV) and it
+    stays within rel-L2 5e-3 of the oracle (the rows are nearly one-hot, and the dominant keys
+    agree)."""
     say("expcast extreme logits", S)
     N, H = 640, 2
     q, k, v = workloads.make_qkv(1, N, H, seed=77)
     q = (q.float() * 48.0).to(torch.bfloat16)
     k = (k.float() * 48.0).to(torch.bfloat16)
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
-    ref, _, _, _, amb = orc.attention_fp8(orc.quantize(qb, kb, vb), p_scale=S, kv_reverse=True,
-                                          expcast=True, return_amb=True)
+    ref, _, _, _ = orc.attention_fp8(orc.quantize(qb, kb, vb), p_scale=S, kv_reverse=True, expcast=True)
     qz = _gpu_quantize(m, q, k, v)
     out = _run_attn(m, qz, p_scale=S, kv_order=1, pcast=m.FP8ATTN_PCAST_EXPCAST)
     assert torch.isfinite(out.float()).all()
-    _compare_out(_gpu_rows(out, np.arange(N)), ref, f"expcast extreme S={S}", amb)
+    got = _gpu_rows(out, np.arange(N))
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    say(f"expcast extreme S={S}: max_abs {float(np.abs(got - ref).max()):.3e} (no element-wise claim), "
+        f"rel_l2 {rel:.3e}")
+    assert rel <= RTOL_L2
+
+
+@pytest.mark.parametrize("S", [256.0, 448.0])
+def test_attention_expcast_clamped_top_code(m, orc, S):
+    """Logits of order 1e6 in log2 units (Q and K scaled by 1024): the FP32 rounding of the
+    per-block bias can then carry the byte of a row's maximum past 126.5, which would round to
+    0x7F (E4M3 NaN); such blocks clamp every byte at 126. The output must be finite and every
+    row must be a convex combination of the dequantised V rows, whatever the codes: each output
+    channel lies within the range of that channel's V values widened by the E4M3 rounding of V
+    (2^-4 of the channel maximum) and the BF16 output rounding."""
+    say("expcast clamped top code", S)
+    N, H = 640, 2
+    q, k, v = workloads.make_qkv(1, N, H, seed=78)
+    q = (q.float() * 1024.0).to(torch.bfloat16)
+    k = (k.float() * 1024.0).to(torch.bfloat16)
+    qz = _gpu_quantize(m, q, k, v)
+    for rev in (0, 1):
+        out = _run_attn(m, qz, p_scale=S, kv_order=rev, pcast=m.FP8ATTN_PCAST_EXPCAST).float()
+        assert torch.isfinite(out).all()
+        vf = v.float().to(DEV)
+        vmax, vmin = vf.amax(dim=1, keepdim=True), vf.amin(dim=1, keepdim=True)
+        slack = 2.0 ** -4 * vf.abs().amax(dim=1, keepdim=True) + 2.0 ** -8 * vf.abs().amax()
+        assert torch.all(out <= vmax + slack) and torch.all(out >= vmin - slack)
 
 
 @pytest.mark.parametrize("N,reverse,expcast", [(1000, True, False), (768, False, True),
@@ -245,7 +293,7 @@ def test_attention_vsmooth_small(m, orc, N, reverse, expcast):
     _compare_quant(qz, ref_q)
     out = _run_attn(m, qz, kv_order=int(reverse),
                     pcast=m.FP8ATTN_PCAST_EXPCAST if expcast else m.FP8ATTN_PCAST_RNE)
-    _compare_out(_gpu_rows(out, np.arange(N)), ref, "vsmooth", amb)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, "vsmooth", amb, peaked=True, wide=True)
 
 
 def test_vsmooth_constant_value_exact(m, orc):
@@ -282,7 +330,7 @@ def _sparse_case(m, orc, grid, H, seed, reverse, expcast=False, smoothing=0, bia
     valid = perm >= 0
     got = _gpu_rows(out, perm[valid])                    # GPU wrote O in source order
     assert np.all(rv[0, 0][valid] == 1)
-    _compare_out(got, ref[:, :, valid], f"sparse {grid[:3]}", amb[:, :, valid])
+    _compare_out(got, ref[:, :, valid], f"sparse {grid[:3]}", amb[:, :, valid], wide=smoothing > 0)
 
 
 @pytest.mark.parametrize("reverse", [False, True])
@@ -368,7 +416,7 @@ def test_attention_smoothing_small(m, orc, N, smoothing, bias, reverse, expcast)
     out = _run_attn(m, qz, kv_order=int(reverse),
                     pcast=m.FP8ATTN_PCAST_EXPCAST if expcast else m.FP8ATTN_PCAST_RNE)
     got = _gpu_rows(out, np.arange(N))
-    _compare_out(got, ref, f"smoothing {smoothing} bias {bias}", amb)
+    _compare_out(got, ref, f"smoothing {smoothing} bias {bias}", amb, wide=True)
     tr = lambda a: np.ascontiguousarray(orc.bf16_decode(a).transpose(0, 2, 1, 3))
     ex, _, _ = orc.attention_ref(orc.MODE_EXACT, tr(qb), tr(kb), tr(vb))
     c = _cos(got, ex)
@@ -416,14 +464,15 @@ def test_attention_split_kv_vsmooth_and_smoothing(m, orc):
                                               kv_splits=splits)
         qz = _gpu_quantize(m, q, k, v, perm_kv=perm, vsmooth=True)
         out = _run_attn(m, qz, kv_order=int(rev), kv_splits=splits, pcast=m.FP8ATTN_PCAST_EXPCAST)
-        _compare_out(_gpu_rows(out, np.arange(N)), ref, f"split-KV {splits} vsmooth", amb)
+        _compare_out(_gpu_rows(out, np.arange(N)), ref, f"split-KV {splits} vsmooth", amb, peaked=True,
+                     wide=True)
     q, k, v = workloads.make_qkv(1, N, H, seed=82, kind="channel_offset")
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
     ref_q = orc.quantize(qb, kb, vb, smoothing=2, v_bias_correction=True)
     ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=True, return_amb=True, kv_splits=2)
     qz = _gpu_quantize(m, q, k, v, smoothing=2, bias=True)
     out = _run_attn(m, qz, kv_order=1, kv_splits=2)
-    _compare_out(_gpu_rows(out, np.arange(N)), ref, "split-KV 2 smoothing", amb)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, "split-KV 2 smoothing", amb, wide=True)
 
 
 def _auto_splits(m, B, N, H):
@@ -456,7 +505,7 @@ def test_attention_split_kv_auto(m, orc):
                                           kv_splits=splits)
     qz = _gpu_quantize(m, q, k, v)
     out = _run_attn(m, qz, kv_order=1, kv_splits=m.FP8ATTN_KV_SPLITS_AUTO)
-    _compare_out(_gpu_rows(out, rows), ref, "auto split", amb)
+    _compare_out(_gpu_rows(out, rows), ref, "auto split", amb, peaked=True, wide=True)
 
 
 @pytest.mark.parametrize("delta,S,reverse", [(9, 256.0, False), (7, 1.0, True)])
@@ -473,7 +522,7 @@ def test_attention_split_kv_sink_underflow(m, orc, delta, S, reverse):
     qz = _gpu_quantize(m, q, k, v)
     cnt = torch.zeros(H, dtype=torch.int64, device=DEV)
     out = _run_attn(m, qz, p_scale=S, kv_order=int(reverse), underflow=cnt, kv_splits=splits)
-    _compare_out(_gpu_rows(out, np.arange(N)), ref, "sink split", amb)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, "sink split", amb, peaked=True)
     g = _np(cnt).astype(np.float64)
     o = uf.sum(axis=2)[0].astype(np.float64)
     say("underflow gpu", g, "oracle", o)
@@ -518,7 +567,7 @@ def test_sol_small(m, orc, N, H, tau, est, sinks, reverse, expcast):
     sol["mask"] = _check_route_mask(orc, _np(mask), ref_sol, NB)
     ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=reverse, expcast=expcast,
                                           return_amb=True, sol=sol)
-    _compare_out(_gpu_rows(out, np.arange(N)), ref, f"sol tau={tau}", amb)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, f"sol tau={tau}", amb, peaked=True, wide=True)
 
 
 @pytest.mark.parametrize("grid,tau,reverse", [((5, 12, 16), 3.0, True), ((4, 9, 20), 2.0, False)])
@@ -537,7 +586,7 @@ def test_sol_video_local(m, orc, grid, tau, reverse):
     sol = dict(ref_sol)
     sol["mask"] = _check_route_mask(orc, _np(mask), ref_sol, -(-N // 64))
     ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=reverse, return_amb=True, sol=sol)
-    _compare_out(_gpu_rows(out, np.arange(N)), ref, f"sol video-local tau={tau}", amb)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, f"sol video-local tau={tau}", amb, peaked=True)
 
 
 def test_sol_with_smoothing(m, orc):
@@ -554,7 +603,7 @@ def test_sol_with_smoothing(m, orc):
     sol = dict(ref_sol)
     sol["mask"] = _check_route_mask(orc, _np(mask), ref_sol, -(-N // 64))
     ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=True, return_amb=True, sol=sol)
-    _compare_out(_gpu_rows(out, np.arange(N)), ref, "sol smoothing", amb)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, "sol smoothing", amb, peaked=True, wide=True)
 
 
 @pytest.mark.parametrize("delta,S,reverse", [(7, 1.0, False), (7, 256.0, True), (9, 256.0, False)])
@@ -567,7 +616,7 @@ def test_underflow_counter(m, orc, delta, S, reverse):
     qz = _gpu_quantize(m, q, k, v)
     cnt = torch.zeros(2, dtype=torch.int64, device=DEV)
     out = _run_attn(m, qz, p_scale=S, kv_order=int(reverse), underflow=cnt)
-    _compare_out(_gpu_rows(out, np.arange(4096)), ref, "sink", amb)
+    _compare_out(_gpu_rows(out, np.arange(4096)), ref, "sink", amb, peaked=True)
     g = _np(cnt).astype(np.float64)
     o = uf.sum(axis=2)[0].astype(np.float64)
     say("underflow gpu", g, "oracle", o)
@@ -736,7 +785,10 @@ def test_full_size_sampled(m, orc, name):
     ref, _, _, _, amb = orc.attention_fp8(ref_q, rows=rows, kv_reverse=True, expcast=vs,
                                           return_amb=True, kv_splits=splits)
     got = _gpu_rows(out[:, :, heads], rows)
-    _compare_out(got, ref, name, amb)
+    # outlier channels (Wan-1.3B) and outlier tokens (V-Smooth) decide outputs through single P
+    # codes and reach |O| >= 2; the channel offsets of the smoothing inputs reach |O| >= 2
+    _compare_out(got, ref, name, amb, peaked=name in ("wan13b", "vsmooth"),
+                 wide=smooth or name in ("wan13b", "vsmooth"))
 
 
 def test_full_size_sparse_sampled(m, orc):
