@@ -211,8 +211,10 @@ def attention_fp8(qz, rows=None, softmax_scale=1.0 / math.sqrt(128.0), p_scale=2
     explain. kv_splits > 1: split-KV (TeleFuser long-sequence split-KV), dense rows only: the
     key blocks are cut at multiples of 2*ceil(NB/(2*kv_splits)) blocks, each piece runs its own
     online softmax and the pieces are merged by log-sum-exp. sol: the dict of ``sol_prepare``
-    (its ``mask`` may be replaced by another valid mask): Sol routing, the exact route over the
-    masked blocks and the summary route over the others, merged by log-sum-exp."""
+    (its ``mask`` may be replaced by another valid mask): Sol routing. Every KV block is visited
+    in KV order and updates one running max, row sum and accumulator: a block whose mask bit is
+    set takes the exact FP8 step, any other block counts as n_j copies of its summary (kbar_j,
+    vbar_j) scored by the route score r_j (m' = max(m, r_j), weight n_j exp(r_j - m'))."""
     B, H, N64, D = qz["q8"].shape
     N = qz["N"]
     rows = np.arange(N, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)

@@ -676,6 +676,36 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
             for (int64_t kb = 0; kb < NB; kb++) blocks.push_back(kb);
           }
           if (kv_reverse) std::reverse(blocks.begin(), blocks.end());
+          // Sol routing: the row's exact-block bits, and per KV block the route score r_j of the
+          // query against the quantised K summary (natural-log units, like the logits) and the
+          // bound on the matrix core's contraction error of that score
+          const uint64_t* sol_mrow = nullptr;
+          std::vector<double> sol_r, sol_rb;
+          if (sol) {
+            const int64_t u = i / 64, W = ceil_div(NB, 64), NBg = ceil_div(NB, 64);
+            sol_mrow = sol->mask + (bh * NB + u) * W;
+            sol_r.assign(NB, 0.0);
+            sol_rb.assign(NB, 0.0);
+            const uint8_t* qr = q8 + (bh * N64 + i) * D;
+            for (int64_t j = 0; j < NB; j++) {
+              const uint8_t* kr = sol->kq8 + (bh * NBg * 64 + j) * D;
+              double dot = 0.0, gsum = 0.0;
+              for (int g = 0; g < D; g += 8) {
+                double gm = 0.0;
+                for (int d = g; d < std::min(D, g + 8); d++) {
+                  const double pr = code_value[qr[d]] * code_value[kr[d]];
+                  dot += pr;
+                  gm = std::max(gm, std::fabs(pr));
+                }
+                gsum += gm;
+              }
+              const double sc = static_cast<double>(q_scale[bh * NB + u]) *
+                                static_cast<double>(sol->kq_scale[bh * NBg + j / 64]) * softmax_scale;
+              sol_r[j] = dot * sc;
+              sol_rb[j] = std::ldexp(gsum, -11) * sc;
+            }
+          }
+          auto sol_exact = [&](int64_t j) { return ((sol_mrow[j / 64] >> (j % 64)) & 1ull) != 0; };
           // One streaming pass over a sequence of key blocks: the row's normalised output, its
           // running max and row sum, and the ambiguity bound of that output.
           struct Pass {
@@ -686,7 +716,9 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
           auto stream = [&](const std::vector<int64_t>& seq) -> Pass {
 
           double m = -std::numeric_limits<double>::infinity(), l = 0.0;
-          std::vector<double> acc(D, 0.0), accM(D, 0.0);
+          // accS: Sol's summary contributions, in dequantised V units (acc holds the exact blocks'
+          // S-scaled P codes times V codes); both share the running max m and the row sum l
+          std::vector<double> acc(D, 0.0), accM(D, 0.0), accS(D, 0.0);
           int64_t n_under = 0;
           // ambiguity sums per channel, in the running-max units of acc
           std::vector<double> amb_v(amb_bound ? D : 0, 0.0), amb_pv(amb_bound ? D : 0, 0.0);
@@ -721,6 +753,39 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
           bool kv_ok[64];
           double dm_run = 0.0;     // error bound of the running max
           for (const int64_t kb : seq) {
+            if (sol && !sol_exact(kb)) {
+              // Summary route ([TF] "Sol Routing": the block's compressed contribution stays in the
+              // same online-softmax state; "SM90 CuTe Mainloop": numerator, denominator and the
+              // block length are corrected together, and both routes update one row max, row sum
+              // and accumulator). The block counts as n_j copies of (kbar_j, vbar_j) with the route
+              // score r_j: m' = max(m, r_j), then l and both accumulators are rescaled by
+              // exp(m - m') and gain w = n_j exp(r_j - m') and w vbar_j.
+              const double r_j = sol_r[kb], rb = amb_bound ? sol_rb[kb] : 0.0;
+              const double n_j = static_cast<double>(std::min<int64_t>(64, N - 64 * kb));
+              if (amb_bound && r_j > m) dm_run = std::max(rb, (m > r_j - 4.0 * rb) ? dm_run : 0.0);
+              const double m_new = std::max(m, r_j);
+              const double alpha = (m == -std::numeric_limits<double>::infinity()) ? 0.0 : std::exp(m - m_new);
+              const double w = n_j * std::exp(r_j - m_new);
+              for (int d = 0; d < D; d++) {
+                acc[d] *= alpha;
+                accS[d] = alpha * accS[d] + w * bf16_value(sol->vsum[(bh * NB + kb) * D + d]);
+              }
+              l = alpha * l + w;
+              if (amb_bound) {
+                // the device evaluates r_j within rb on the matrix cores, so w within a factor
+                // exp(+-rb); its summary product runs on BF16 matrix cores with the weight split
+                // into two BF16 parts (relative error below 2^-16). In the S-scaled units of amb_v.
+                const double e = S * w * (2.0 * rb + std::ldexp(1.0, -14));
+                for (int d = 0; d < D; d++) {
+                  amb_v[d] = alpha * amb_v[d] + e * std::fabs(bf16_value(sol->vsum[(bh * NB + kb) * D + d]));
+                  amb_pv[d] *= alpha;
+                }
+                amb_l = alpha * amb_l + e;
+                amb_lx *= alpha;
+              }
+              m = m_new;
+              continue;
+            }
             double mblk = -std::numeric_limits<double>::infinity();
             for (int t = 0; t < 64; t++) {
               const int64_t kk = kb * 64 + t;
@@ -823,6 +888,7 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
               for (int t = 0; t < 64; t++)
                 if (kv_ok[t]) s += pv[t] * value(kb * 64 + t, d);
               acc[d] = alpha * acc[d] + s;
+              accS[d] *= alpha;
             }
             if (vsmooth) {
               const int64_t j = kb / 2;
@@ -837,7 +903,7 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
           for (int d = 0; d < D; d++) {
             if (mode == 3) {
               const double sv = static_cast<double>(v_scale[bh * D + d]);
-              ps.o[d] = vsmooth ? ((sv / S) * acc[d] + accM[d]) / l : acc[d] * sv / (S * l);
+              ps.o[d] = vsmooth ? ((sv / S) * acc[d] + accM[d]) / l : acc[d] * sv / (S * l) + accS[d] / l;
             } else {
               ps.o[d] = acc[d] / l;  // mode 2 already divided P by S
             }
@@ -859,73 +925,8 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
         // V blocks); each piece keeps the row's KV order; piece s gives o_s, m_s, l_s and
         // O = sum_s w_s o_s / sum_s w_s with w_s = l_s * exp(m_s - max m).
         std::vector<Pass> parts;
-        if (sol) {
-          // Sol routing: the exact route streams the row's exact blocks (in KV order); the
-          // summary route treats each other block as n_j copies of (kbar_j, vbar_j), scored with
-          // the route score; the two are merged like split-KV pieces (an empty route has no
-          // weight).
-          const int64_t u = i / 64, W = ceil_div(NB, 64), NBg = ceil_div(NB, 64);
-          const uint64_t* mrow = sol->mask + (bh * NB + u) * W;
-          auto is_exact = [&](int64_t j) { return ((mrow[j / 64] >> (j % 64)) & 1ull) != 0; };
-          std::vector<int64_t> ex;
-          for (const int64_t kb : blocks)
-            if (is_exact(kb)) ex.push_back(kb);
-          if (!ex.empty()) parts.push_back(stream(ex));
-          std::vector<double> xs(NB, 0.0), bs(NB, 0.0);
-          double mS = -std::numeric_limits<double>::infinity();
-          for (int64_t j = 0; j < NB; j++) {
-            if (is_exact(j)) continue;
-            const uint8_t* qr = q8 + (bh * N64 + i) * D;
-            const uint8_t* kr = sol->kq8 + (bh * NBg * 64 + j) * D;
-            double dot = 0.0, gsum = 0.0;
-            for (int g = 0; g < D; g += 8) {
-              double gm = 0.0;
-              for (int d = g; d < std::min(D, g + 8); d++) {
-                const double pr = code_value[qr[d]] * code_value[kr[d]];
-                dot += pr;
-                gm = std::max(gm, std::fabs(pr));
-              }
-              gsum += gm;
-            }
-            const double sc = static_cast<double>(q_scale[bh * NB + u]) *
-                              static_cast<double>(sol->kq_scale[bh * NBg + j / 64]) * softmax_scale;
-            xs[j] = dot * sc;
-            bs[j] = std::ldexp(gsum, -11) * sc;
-            mS = std::max(mS, xs[j]);
-          }
-          if (mS > -std::numeric_limits<double>::infinity()) {
-            Pass ps;
-            ps.o.assign(D, 0.0);
-            ps.amb.assign(D, 0.0);
-            double lS = 0.0, dl = 0.0;
-            std::vector<double> wj(NB, 0.0);
-            for (int64_t j = 0; j < NB; j++) {
-              if (is_exact(j)) continue;
-              wj[j] = static_cast<double>(std::min<int64_t>(64, N - 64 * j)) * std::exp(xs[j] - mS);
-              lS += wj[j];
-            }
-            for (int64_t j = 0; j < NB; j++) {
-              if (wj[j] == 0.0) continue;
-              for (int d = 0; d < D; d++)
-                ps.o[d] += wj[j] * bf16_value(sol->vsum[(bh * NB + j) * D + d]);
-              // a device evaluates the score on the matrix cores and the weight in BF16
-              dl += wj[j] * (bs[j] + std::ldexp(1.0, -9));
-            }
-            for (int d = 0; d < D; d++) ps.o[d] /= lS;
-            if (amb_bound)
-              for (int64_t j = 0; j < NB; j++) {
-                if (wj[j] == 0.0) continue;
-                const double e = wj[j] / lS * (2.0 * bs[j] + std::ldexp(1.0, -8));
-                for (int d = 0; d < D; d++)
-                  ps.amb[d] += e * (std::fabs(bf16_value(sol->vsum[(bh * NB + j) * D + d])) + std::fabs(ps.o[d]));
-              }
-            ps.m = mS;
-            ps.l = lS;
-            ps.lx = dl / lS;
-            ps.n_under = 0;
-            parts.push_back(ps);
-          }
-        } else if (kv_splits <= 1 || sparse) {
+        if (kv_splits <= 1 || sparse || sol) {
+          // (Sol: one pass over every block in KV order, exact and summary blocks alike)
           parts.push_back(stream(blocks));
         } else {
           const int64_t L = 2 * ceil_div(NB, 2 * static_cast<int64_t>(kv_splits));

@@ -10,7 +10,11 @@ two routes of the attention.
   channel is non-zero;
 * the mask is the brute-force rule "some query of the block reaches theta, or a sink block";
 * on inputs whose K and V rows are constant inside each KV block (and exactly representable),
-  the summary route is exact: all-summary Sol equals FP64 softmax attention.
+  the summary route is exact: all-summary Sol equals FP64 softmax attention;
+* both routes update one online-softmax state in KV order: where summary blocks score above
+  the exact blocks that follow them, the oracle equals an independent numpy model of that shared
+  loop (exact blocks' P codes taken against the summary-set running max) and differs from the
+  reading with two states merged by log-sum-exp.
 """
 import math
 
@@ -165,3 +169,138 @@ def test_summary_route_exact_on_block_constant_inputs(orc, N, rev):
     tr = lambda a: np.ascontiguousarray(a.transpose(0, 2, 1, 3))
     ex, _, _ = orc.attention_ref(orc.MODE_EXACT, tr(q), tr(k), tr(v), softmax_scale=ss)
     assert np.max(np.abs(out - ex)) < 1e-9 * np.max(np.abs(ex))
+
+
+# ------------------------------------------------------------------------------------------
+# One shared online-softmax state (TeleFuser blog, "Sol Routing": the summary route keeps its
+# compressed contribution in the same online-softmax state; "SM90 CuTe Mainloop": both routes
+# update one row max, row sum and output accumulator)
+# ------------------------------------------------------------------------------------------
+def _decoded(orc, qz):
+    N = qz["N"]
+    qd = orc.e4m3_decode(qz["q8"][:, :, :N]).astype(np.float64)
+    kd = orc.e4m3_decode(qz["k8"][:, :, :N]).astype(np.float64)
+    vd = orc.e4m3_decode(qz["v8t"][:, :, :, :N]).transpose(0, 1, 3, 2).astype(np.float64)
+    return qd, kd, vd
+
+
+def _logits(qz, qd, kd, b, h, i, ss):
+    """Logits of query i against every key, exact in FP64 (E4M3 products, 128-term sums)."""
+    u = i // 64
+    ks = np.repeat(qz["k_scale"][b, h].astype(np.float64), 64)[: kd.shape[2]]
+    return (kd[b, h] @ qd[b, h, i]) * float(qz["q_scale"][b, h, u]) * ks * ss
+
+
+def _route_scores(orc, qz, sol, qd, b, h, i, ss):
+    NB = -(-qz["N"] // 64)
+    kq = orc.e4m3_decode(sol["kq8"][b, h, :NB]).astype(np.float64)
+    sc = np.repeat(sol["kq_scale"][b, h].astype(np.float64), 64)[:NB]
+    return (kq @ qd[b, h, i]) * float(qz["q_scale"][b, h, i // 64]) * sc * ss
+
+
+def _sol_model(orc, qz, sol, exact, rev, S, ss, shared=True):
+    """numpy: per row, the KV blocks in KV order. shared=True: one (m, l, acc) for both routes;
+    an exact block takes m' = max(m, max x), P8 = E4M3(fl32(S exp(x - m'))), l += sum p,
+    acc += P8 . V8; a summary block takes m' = max(m, r_j), w = n_j exp(r_j - m'), l += w,
+    acc += w vbar_j. shared=False: the exact blocks run their own state, the summary blocks
+    theirs, and the two are merged by log-sum-exp (the reading this pin rules out)."""
+    B, H = qz["q8"].shape[:2]
+    N = qz["N"]
+    NB = -(-N // 64)
+    qd, kd, vd = _decoded(orc, qz)
+    out = np.zeros((B, H, N, 128))
+    order = list(range(NB))[::-1] if rev else list(range(NB))
+    for b in range(B):
+        for h in range(H):
+            vs = vd[b, h] * qz["v_scale"][b, h].astype(np.float64)[None, :]
+            vbar = orc.bf16_decode(sol["vsum"][b, h]).astype(np.float64)
+            for i in range(N):
+                x_all = _logits(qz, qd, kd, b, h, i, ss)
+                r_all = _route_scores(orc, qz, sol, qd, b, h, i, ss)
+                states = {True: [-np.inf, 0.0, np.zeros(128)], False: [-np.inf, 0.0, np.zeros(128)]}
+                for j in order:
+                    ex = bool(exact[b, h, i // 64, j])
+                    st = states[True] if shared else states[ex]
+                    m, l, acc = st
+                    if ex:
+                        xs = x_all[64 * j:min(N, 64 * j + 64)]
+                        m_new = max(m, xs.max())
+                        alpha = 0.0 if m == -np.inf else math.exp(m - m_new)
+                        p = np.exp(xs - m_new)
+                        codes = orc.e4m3_encode((S * p).astype(np.float32).astype(np.float64))
+                        pd = orc.e4m3_decode(codes).astype(np.float64) / S
+                        st[:] = [m_new, alpha * l + p.sum(), alpha * acc + pd @ vs[64 * j:64 * j + len(xs)]]
+                    else:
+                        n_j = min(64, N - 64 * j)
+                        m_new = max(m, r_all[j])
+                        alpha = 0.0 if m == -np.inf else math.exp(m - m_new)
+                        w = n_j * math.exp(r_all[j] - m_new)
+                        st[:] = [m_new, alpha * l + w, alpha * acc + w * vbar[j]]
+                if shared:
+                    m, l, acc = states[True]
+                    out[b, h, i] = acc / l
+                else:
+                    ms = [s_[0] for s_ in states.values() if s_[1] > 0]
+                    mx = max(ms)
+                    num, den = np.zeros(128), 0.0
+                    for m, l, acc in states.values():
+                        if l > 0:
+                            num += math.exp(m - mx) * acc
+                            den += math.exp(m - mx) * l
+                    out[b, h, i] = num / den
+    return out
+
+
+def _sink_block_inputs(N, H, seed, summary_blocks, delta):
+    """N(0,1) Q, K, V; channel 127 carries a bias (Q = 4, K = delta * sqrt(128) / 4 on every key
+    of the listed blocks, 0 elsewhere), so those blocks' logits, and hence their summaries'
+    route scores, sit about delta above the others."""
+    import torch
+    q, k, v = workloads.make_qkv(1, N, H, seed)
+    q = q.float()
+    k = k.float()
+    q[..., 127] = 4.0
+    k[..., 127] = 0.0
+    for j in summary_blocks:
+        k[:, 64 * j:64 * j + 64, :, 127] = delta * math.sqrt(128.0) / 4.0
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v
+
+
+@pytest.mark.parametrize("rev,S", [(False, 256.0), (True, 256.0), (False, 1.0)])
+def test_shared_state_matches_model(orc, rev, S):
+    """Summary blocks scoring about 4 above the exact blocks' logits sit before them in KV order,
+    so the exact blocks' P codes are taken against a running max that a summary set. The
+    oracle equals the shared-state model, and the two-state reading gives a different result."""
+    N, H, ss = 640, 1, 1.0 / math.sqrt(128.0)
+    NB = N // 64
+    summary = [0, 3, 4, 7, 8] if not rev else [9, 6, 5, 2, 1]
+    q, k, v = _sink_block_inputs(N, H, 61, summary, 4.0)
+    b = workloads.bits
+    qz = orc.quantize(b(q), b(k), b(v))
+    sol = dict(orc.sol_prepare(qz, tau=0.0, estimator=0, sink_blocks=0))
+    exact = np.ones((1, H, NB, NB), bool)
+    exact[..., summary] = False
+    words = np.zeros((1, H, NB, 1), np.uint64)
+    for j in range(NB):
+        words[..., 0] |= (exact[..., j].astype(np.uint64) << np.uint64(j))
+    sol["mask"] = words
+    out, _, uf, _ = orc.attention_fp8(qz, p_scale=S, kv_reverse=rev, sol=sol)
+    want = _sol_model(orc, qz, sol, exact, rev, S, ss, shared=True)
+    other = _sol_model(orc, qz, sol, exact, rev, S, ss, shared=False)
+    # the situation the pin is about: the first block visited is a summary scoring above the
+    # largest logit of the first exact block after it, for most rows
+    qd, kd, _ = _decoded(orc, qz)
+    first_ex = next(j for j in (range(NB)[::-1] if rev else range(NB)) if exact[0, 0, 0, j])
+    hits = 0
+    for i in range(0, N, 7):
+        r = _route_scores(orc, qz, sol, qd, 0, 0, i, ss)
+        x = _logits(qz, qd, kd, 0, 0, i, ss)[64 * first_ex:64 * first_ex + 64]
+        hits += r[summary[0]] > x.max()
+    assert hits >= 0.9 * len(range(0, N, 7))
+    scale = np.abs(want).max()
+    assert np.max(np.abs(out - want)) <= 1e-10 * scale
+    assert np.max(np.abs(out - other)) > 1e-3 * scale
+    if S == 1.0:
+        # with S = 1 the exact blocks' codes against the summary-set max underflow more than
+        # against their own max
+        assert uf.sum() > 0
