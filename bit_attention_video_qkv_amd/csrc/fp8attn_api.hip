@@ -290,7 +290,7 @@ namespace {
 
 struct SolLayout {
   int64_t NB, NBg, NBp, W;
-  size_t queue, ksum, vsumT, kq8, kq_scale, mk, Mk, theta, mask, o_part, lse, total;
+  size_t queue, ksum, vsumT, kq8, kq_scale, mk, Mk, theta, mask, o_part, lse, gmax, total;
 };
 
 SolLayout sol_layout(int32_t B, int32_t N, int32_t H) {
@@ -317,6 +317,7 @@ SolLayout sol_layout(int32_t B, int32_t N, int32_t H) {
   L.mask = take(bh * L.NB * L.W * sizeof(uint64_t));
   L.o_part = take(bh * N * kHeadDim * sizeof(float));  // the summary route's normalised O
   L.lse = take(bh * N * sizeof(float));                  // and log2 of its weight
+  L.gmax = take(bh * L.NBg * L.NB * 64 * sizeof(float));  // per row and group: summary max so far
   L.total = off;
   return L;
 }
@@ -390,6 +391,8 @@ fp8attn_status fp8attn_sol_forward(int32_t B, int32_t N, int32_t H, int32_t D, c
   sp.tau = o->tau;
   sp.estimator = o->estimator;
   sp.sink_blocks = o->sink_blocks;
+  sp.reverse = o->kv_order == FP8ATTN_KV_REVERSE ? 1 : 0;
+  sp.gmax = reinterpret_cast<float*>(ws + L.gmax);
   hipError_t e = fp8attn::launch_sol(sp, stream);
   if (e != hipSuccess) return FP8ATTN_EHIP;
 
@@ -419,6 +422,8 @@ fp8attn_status fp8attn_sol_forward(int32_t B, int32_t N, int32_t H, int32_t D, c
   p.lse = lse;
   p.sol_mask = mask;
   p.sol_words = L.W;
+  p.sol_gmax = sp.gmax;
+  p.sol_groups = L.NBg;
   p.work_ctr = reinterpret_cast<uint32_t*>(ws + L.queue);
   p.cus = device_cus();
   int variant = fp8attn::kVarSol;

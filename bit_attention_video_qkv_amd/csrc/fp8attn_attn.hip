@@ -96,6 +96,16 @@ __device__ __forceinline__ float xsum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Each byte of a packed word clamped to at most 126, two bytes at a time (v_pk_min_u16 on the
+// even and on the odd bytes).
+__device__ __forceinline__ uint32_t clamp_bytes_126(uint32_t w) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 lim = {126, 126};
+  const u16x2 lo = __builtin_elementwise_min(__builtin_bit_cast(u16x2, w & 0x00FF00FFu), lim);
+  const u16x2 hi = __builtin_elementwise_min(__builtin_bit_cast(u16x2, (w >> 8) & 0x00FF00FFu), lim);
+  return __builtin_bit_cast(uint32_t, lo) | (__builtin_bit_cast(uint32_t, hi) << 8);
+}
+
 __device__ __forceinline__ v8i load_op_lds(const uint8_t* base, int off0, int off1) {
   const uint4 a = *reinterpret_cast<const uint4*>(base + off0);
   const uint4 b = *reinterpret_cast<const uint4*>(base + off1);
@@ -173,7 +183,8 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   constexpr int kChunks = 512 / kThreads;       // 16-byte chunks per thread of one 8 KB tile
   constexpr int kMetaOff = 2 * kTileBytes;      // s_k (f32) and valid keys (i32) of the K block
   constexpr int kMeanOff = kMetaOff + 16;       // V-Smooth mean operand records, 128 x 16 B
-  constexpr int kSlotBytes = kMeanOff + (VSMOOTH ? kHeadDim * 16 : 0);  // multiple of 16
+  constexpr int kGmaxOff = kMeanOff;            // Sol: the K block's group summary maximum per row
+  constexpr int kSlotBytes = kMeanOff + (VSMOOTH ? kHeadDim * 16 : 0) + (SOL ? kRowsPerWg * 4 : 0);
   constexpr int kMeanLanes = 128 / WAVES;       // V-Smooth: lanes per wave copying the records
   // copies every wave issues for every pair (wave 0 adds s_k; V-Smooth pairs may add the mean
   // records, which the waits do not count: they then wait one copy longer than they must)
@@ -379,6 +390,12 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
         copy16_to_lds(p.mu_op + (bh * p.NB128 + (vb >> 1)) * kHeadDim * 4, 16u * (wave * kMeanLanes + lane),
                       l0 + kMeanOff + wave * kMeanLanes * 16);
     }
+    if constexpr (SOL) {
+      // the running summary maximum of the K block's route group, for the wave's 32 rows
+      if (lane < 32)
+        copy4_to_lds(p.sol_gmax + (bh * p.sol_groups + (kb >> 6)) * p.N64 + q0 + 32 * wave, 4u * lane,
+                     l0 + kGmaxOff + wave * 128);
+    }
     if (wave == 0 && lane == 0) {
       copy4_to_lds(p.k_scale + bh * p.NB + kb, 0u, l0 + kMetaOff);
       *reinterpret_cast<int*>(sl + kMetaOff + 4) = limit;
@@ -478,6 +495,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   const int lim_tail = static_cast<int>(p.N - (p.NB - 1) * kBlock);  // valid keys of block NB-1
   int kb_next = 0;                      // Sol: key block of the next K tile
   bool ex_cur = false, ex_next = false;  // Sol: that block is not exact for this wave's Q block
+  float gm_cur = -INFINITY, gm_next = -INFINITY;  // Sol: summary maximum so far (log2 units)
 
   // Per-lane byte offsets of the 16-byte operand chunks inside a slot (K rows in the permuted
   // order, swizzled chunks).
@@ -513,6 +531,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   auto read_meta = [&](const uint8_t* base) {
     sk_next = *reinterpret_cast<const float*>(base + kMetaOff);
     lim_next = *reinterpret_cast<const int*>(base + kMetaOff + 4);
+    if constexpr (SOL) gm_next = *reinterpret_cast<const float*>(base + kGmaxOff + (32 * wave + l32) * 4);
     if constexpr (kSolPair) {
       // looked up one block ahead, so the mask word's load has a whole block to land
       kb_next = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(base + kMetaOff + 8));
@@ -582,7 +601,8 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     // every dense block holds a valid key, so the max is finite from the first block on; the
     // sparse and Sol guard keeps a fully masked first block from producing NaN
     const float xrow = xmax(mloc);
-    const float m_cand = fmax_ieee(m_run, xrow * cs);
+    // Sol: the summary blocks of this block's route group and of the groups before it come first
+    const float m_cand = fmax_ieee(SOL ? fmax_ieee(m_run, gm_cur) : m_run, xrow * cs);
     const float m_new = (SPARSE || SOL) && m_cand == -INFINITY ? 0.0f : m_cand;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_cand;
@@ -598,23 +618,17 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
       // The row sums come from the matrix cores (pv).
       const float c8 = 8.0f * cs;
       const float b8 = 8.0f * (p.log2S - m_new) + 55.65f;
+#pragma unroll
+      for (int w = 0; w < 8; w++) {
+        uint32_t word = static_cast<uint32_t>(pop[w]);  // every byte is overwritten
+#pragma unroll
+        for (int q = 0; q < 4; q++) word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(x[4 * w + q], c8, b8), q, word);
+        pop[w] = static_cast<int>(word);
+      }
       if (__builtin_expect(__any(__builtin_fmaf(xrow, c8, b8) > 126.5f), 0)) {
+        // (rare) min(rint(t), 126) = rint(min(t, 126)): clamp the bytes themselves
 #pragma unroll
-        for (int w = 0; w < 8; w++) {
-          uint32_t word = static_cast<uint32_t>(pop[w]);
-#pragma unroll
-          for (int q = 0; q < 4; q++)
-            word = __builtin_amdgcn_cvt_pk_u8_f32(fminf(__builtin_fmaf(x[4 * w + q], c8, b8), 126.0f), q, word);
-          pop[w] = static_cast<int>(word);
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < 8; w++) {
-          uint32_t word = static_cast<uint32_t>(pop[w]);  // every byte is overwritten
-#pragma unroll
-          for (int q = 0; q < 4; q++) word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(x[4 * w + q], c8, b8), q, word);
-          pop[w] = static_cast<int>(word);
-        }
+        for (int w = 0; w < 8; w++) pop[w] = static_cast<int>(clamp_bytes_126(static_cast<uint32_t>(pop[w])));
       }
       tie_k(0, lsum);
       tie_k(1, lsum);
@@ -746,6 +760,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     sk_cur = sk_next;
     lim_cur = lim_next;
     ex_cur = ex_next;
+    gm_cur = gm_next;
     if constexpr (kSteady) {
       if constexpr (SPARSE) stage(j + 1 + kSlots, sl);  // (its key block exists: < n_iter)
       else stage_dense(sl);
@@ -777,6 +792,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   sk_cur = sk_next;
   lim_cur = lim_next;
   ex_cur = ex_next;
+  gm_cur = gm_next;
   if (n_iter >= kSlots) stage(kSlots, slot(0));
 
   // ---- mainloop. Dense: the one block with fewer than 64 valid keys (the last key block, first
@@ -862,8 +878,9 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     }
   };
   if constexpr (SOL) {
-    // Sol: merge with the summary route's piece (o_part, lse: written before this kernel) by
-    // their log2 weights, as split_merge does for pieces, and write BF16 O directly
+    // Sol: the shared state's result. The summary contributions (written before this kernel as
+    // their normalised sum o_part and log2 weight lse) and this route's accumulator are added,
+    // each rescaled to the common maximum, and O = acc / l, in BF16
     if (ok) {
       const float lse0 = l_tot > 0.0f ? m_run + __log2f(l_tot) : -INFINITY;
       const int64_t r1 = bh * p.N + qrow;
@@ -1093,10 +1110,11 @@ hipError_t launch_variant(AttnParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Sol: the exact route (two waves per 64-row Q block over its mask's blocks; the kernel also has
-// a four-wave form over the union of two Q blocks' masks, which only pays when neighbouring Q
-// blocks share most exact blocks) merges its result with the summary route's, which has been
-// written before, in its epilogue.
+// Sol: the exact blocks of the shared state (two waves per 64-row Q block over its mask's
+// blocks, each block's running max raised first by the summary maximum of its route group; the
+// kernel also has a four-wave form over the union of two Q blocks' masks, which only pays when
+// neighbouring Q blocks share most exact blocks); its epilogue adds the summary contributions,
+// which have been written before.
 template <bool EXPCAST>
 hipError_t launch_sol_exact(AttnParams p, hipStream_t stream) {
   p.splits = 1;

@@ -65,9 +65,14 @@ struct AttnParams {
   float* o_part;  // [splits, B*H, N, 128]; Sol: [B*H, N, 128], the summary route's output
   float* lse;     // [splits, B*H, N]; Sol: [B*H, N], the summary route's log2 weight
   // Sol routing: exact-block mask [B*H, NB, sol_words] of the exact route (the attention then
-  // merges its result with the summary route's in its epilogue), or null
+  // adds the summary contributions in its epilogue), or null; sol_gmax [B*H,
+  // sol_groups, N64]: per row, the running max (log2 units) of the summary route scores over the
+  // route groups of 64 KV blocks up to and including each group in KV order, which every exact
+  // block of that group takes into its running max first
   const uint64_t* sol_mask;
   int64_t sol_words;
+  const float* sol_gmax;
+  int64_t sol_groups;
   // per-XCD work queues: eight counters (workspace) zeroed before each launch; variants without
   // V-Smooth or underflow counting take their work items from them
   uint32_t* work_ctr;
@@ -92,6 +97,7 @@ struct SolParams {
   uint64_t* mask;    // [B*H, NB, W]
   float* o_part;     // piece 1 of the merge buffers: [B*H, N, 128]
   float* lse;        // [B*H, N]
+  float* gmax;       // [B*H, NBg, N64] running max of the summary scores over the groups (log2)
   int64_t N, N64, NB, NBg, NBp, W;
   int B, H;
   float softmax_scale;
@@ -99,6 +105,7 @@ struct SolParams {
   double tau;
   int estimator;
   int sink_blocks;
+  int reverse;       // KV order: groups are visited in it
 };
 
 // Summaries, quantised K summaries, moments, thresholds, then the route (mask + summary route).

@@ -16,17 +16,25 @@
 //    E2 = ss^2 * sum_{d,e} Mq[d,e] Mk[d,e] ("exact") or ss^2 * sum_d Mq[d,d] Mk[d,d] ("diag"),
 //    m and Mk the mean and second moment of the summaries, Mq the block's query second moment;
 //  * a KV block is exact for Q block u when some valid query of u has a route score >= theta_u;
-//  * the exact route runs the ordinary kernel over the exact blocks; this file computes the
-//    summary route: weights n_j * exp(r_ij - m) with r_ij the route score, applied to the V
-//    summaries; the two routes are merged by log-sum-exp like split-KV pieces.
+//  * both routes share one online-softmax state (the page's unified merge). The KV blocks are
+//    taken in route groups of 64, groups in KV order, each group's summary blocks before its
+//    exact blocks: a summary block moves the running max to max(m, r_ij) and adds
+//    n_j exp(r_ij - m') to the row sum and n_j exp(r_ij - m') vbar_j to the accumulator; an exact
+//    block then takes the ordinary FP8 step against that running max. Only the running max the
+//    exact blocks' P codes are taken against depends on the order; the summary contributions
+//    are plain sums. So sol_route accumulates them in a state of its own and writes, per row and
+//    group, the running max of the summary scores over the groups so far (gmax); the exact
+//    route (fp8attn_attn.hip) folds gmax into its running max before each group's exact blocks
+//    and adds the two accumulators in its epilogue, each rescaled to the common maximum.
 //
 // Kernels (launch order):
 //   sol_summaries  grid (NBp, B*H)         K and V summaries
 //   sol_kquant     grid (NBg, B*H)         quantised K summaries
 //   sol_kmoments   grid (B*H, 16)          mean and second moment of the summaries (FP64)
 //   sol_theta      grid (NB, B*H)          threshold per Q block
-//   sol_route      grid (ceil(NB/2), B*H), 4 waves: per group of 64 summaries staged in LDS, the
-//                  route QK (E4M3 MFMA), the exact-block mask, the summary route (BF16 MFMA)
+//   sol_route      grid (ceil(NB/2), B*H), 4 waves: per group of 64 summaries staged in LDS (the
+//                  groups in KV order), the route QK (E4M3 MFMA), the exact-block mask, the
+//                  summary contributions (BF16 MFMA) and the running summary maximum
 #include "fp8attn_common.h"
 #include "fp8attn_internal.h"
 
@@ -320,8 +328,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   // 512 chunks are the K summary tile (swizzled), the next 1024 the V summary tile (contiguous)
   const uint8_t* kq_base = p.kq8 + bh * p.NBp * kHeadDim;
   const uint8_t* vs_base = reinterpret_cast<const uint8_t*>(p.vsumT) + bh * p.NBg * (64 * kHeadDim * 2);
-  auto stage = [&](int64_t g) {
-    const uint32_t l0 = lds_addr_of(lds + (g & 1) * kSlotBytes);
+  auto stage = [&](int64_t g, int sl) {
+    const uint32_t l0 = lds_addr_of(lds + sl * kSlotBytes);
 #pragma unroll
     for (int r = 0; r < kCopiesPerThread; r++) {
       const int L = r * 256 + static_cast<int>(threadIdx.x);
@@ -344,14 +352,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     for (int r = 0; r < 16; r++) oacc[dt][r] = 0.0f;
   float m_run = -INFINITY;  // log2 units
   float l_part = 0.0f;
+  // running max of the summary route scores over the groups visited so far (log2 units)
+  float g_run = -INFINITY;
+  float* gmax_row = p.gmax + bh * p.NBg * p.N64 + (ublock ? qrow : 0);
 
-  stage(0);
-  for (int64_t g = 0; g < p.NBg; g++) {
+  // the groups in KV order (the exact route takes each group's summary maximum in that order)
+  auto group_at = [&](int64_t gi) -> int64_t { return p.reverse ? p.NBg - 1 - gi : gi; };
+  stage(group_at(0), 0);
+  for (int64_t gi = 0; gi < p.NBg; gi++) {
+    const int64_t g = group_at(gi);
     wait_vmcnt<0>();
     // group g has landed in every wave's view, and every wave is done with the other slot
     barrier_nofence();
-    if (g + 1 < p.NBg) stage(g + 1);
-    const uint8_t* ks = lds + (g & 1) * kSlotBytes;
+    if (gi + 1 < p.NBg) stage(group_at(gi + 1), static_cast<int>((gi + 1) & 1));
+    const uint8_t* ks = lds + (gi & 1) * kSlotBytes;
     const uint8_t* vsl = ks + kSlotK;
     const int64_t left = p.NB - 64 * g;  // summaries from this group on
     const uint64_t valid = left >= 64 ? ~0ull : (1ull << left) - 1ull;
@@ -417,6 +431,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
           }
         }
       }
+      // the group's largest summary score (before the block-length correction below)
+      float gm = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) gm = __builtin_elementwise_maximum(__builtin_elementwise_maximum(gm, x[t][r]), x[t][r + 1]);
+      {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(gm), __float_as_uint(gm), false, false);
+        gm = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      g_run = fmaxf(g_run, gm * kLog2e);
       if (left <= 64) {  // the last KV block weighs its token count instead of 64
         const int jl = static_cast<int>(left) - 1;
         const float dx = (lg_last - 6.0f) * kLn2;
@@ -426,20 +451,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
           for (int r = 0; r < 16; r++)
             if (32 * t + 8 * (r >> 2) + 4 * lh + (r & 3) == jl) x[t][r] += dx;
       }
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; t++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) mloc = fmaxf(mloc, x[t][r]);
-      {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
-        mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      // weight exponents score * log2 e + 6 (mloc is finite: the group has a summary-routed
-      // block). The reference point m_run moves only when some row's maximum passes it by more
-      // than kLazy, so the accumulators are rescaled a few times per row, not every group;
-      // weights stay below 2^kLazy.
-      const float ml2 = __builtin_fmaf(mloc, kLog2e, 6.0f);
+      // weight exponents score * log2 e + 6 (gm is finite: the group has a summary-routed block,
+      // and it bounds every corrected score from above). The reference point m_run moves only
+      // when some row's maximum passes it by more than kLazy, so the accumulators are rescaled a
+      // few times per row, not every group; weights stay below 2^kLazy.
+      const float ml2 = __builtin_fmaf(gm, kLog2e, 6.0f);
       if (__builtin_amdgcn_ballot_w64(ml2 > m_run + kLazy) != 0ull) {
         const float m_new = fmaxf(m_run, ml2);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on a row's first group
@@ -472,6 +488,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             oacc[dt] = mfma_bf16(av, pb[t][s2], oacc[dt]);
           }
     }
+    if (ublock && lh == 0) gmax_row[g * p.N64] = g_run;
     wait_lgkm0();  // every read of this slot has returned before the next barrier frees it
   }
 

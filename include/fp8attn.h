@@ -273,10 +273,14 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
  *   route       r_ij = (q8_i . kq8_j) s_q s_kq softmax_scale on the matrix cores; KV block j is
  *               exact for Q block u if j < sink_blocks or some valid query of u has r_ij >=
  *               theta_u; decisions within the matrix cores' rounding of theta may go either way;
- *   exact route the fp8attn_forward loop over the exact blocks in kv_order (own running max);
- *   summary     the other blocks as n_j copies of (kbar_j, vbar_j), scored by r_ij, weights in
- *               BF16 on the matrix cores;
- *   output      the two routes merged by log-sum-exp, + v_shift, BF16.
+ *   one state   both routes update one running max, row sum and accumulator ("SM90 CuTe
+ *               Mainloop", unified online-softmax merge). The KV blocks are taken in route
+ *               groups of 64 (groups in kv_order); in a group its summary blocks come first: each
+ *               counts as n_j copies of (kbar_j, vbar_j) scored by r_ij, m' = max(m, r_ij), row
+ *               sum and accumulator gain n_j exp(r_ij - m') and n_j exp(r_ij - m') vbar_j (on the
+ *               BF16 matrix cores); then the group's exact blocks take the fp8attn_forward step
+ *               against that running max, in kv_order;
+ *   output      acc / l + v_shift, BF16.
  * Arguments (device pointers unless noted):
  *   q8 .. v_scale  as written by fp8attn_quantize_qkv (vsmooth = 0).
  *   opts       host pointer: softmax_scale > 0, p_scale in (0, 448], kv_order, pcast, tau
@@ -286,8 +290,9 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
  *   route_mask uint64 [B*H, NB, W] (W = ceil(NB / 64); bit j % 64 of word j / 64 = KV block j
  *              exact for Q block u) or NULL.
  *   workspace  fp8attn_sol_workspace_bytes(B, N, H, D) bytes, 16-byte aligned, overwritten. It
- *              holds the summaries, thresholds and the summary route's output, and the work queues
- *              of the exact route (two calls that run at the same time need two workspaces).
+ *              holds the summaries, thresholds, the summary contributions and, per row and route
+ *              group, the running maximum of the summary scores, and the work queues of the exact
+ *              route (two calls that run at the same time need two workspaces).
  * Errors: EINVAL on bad pointers/sizes/options; EUNSUPPORTED on D != 128 or a device other
  *   than gfx950.
  * ------------------------------------------------------------------------------------------ */

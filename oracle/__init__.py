@@ -211,10 +211,12 @@ def attention_fp8(qz, rows=None, softmax_scale=1.0 / math.sqrt(128.0), p_scale=2
     explain. kv_splits > 1: split-KV (TeleFuser long-sequence split-KV), dense rows only: the
     key blocks are cut at multiples of 2*ceil(NB/(2*kv_splits)) blocks, each piece runs its own
     online softmax and the pieces are merged by log-sum-exp. sol: the dict of ``sol_prepare``
-    (its ``mask`` may be replaced by another valid mask): Sol routing. Every KV block is visited
-    in KV order and updates one running max, row sum and accumulator: a block whose mask bit is
-    set takes the exact FP8 step, any other block counts as n_j copies of its summary (kbar_j,
-    vbar_j) scored by the route score r_j (m' = max(m, r_j), weight n_j exp(r_j - m'))."""
+    (its ``mask`` may be replaced by another valid mask): Sol routing. One running max, row sum
+    and accumulator for both routes; the KV blocks are taken in route groups of 64, groups in KV
+    order, and inside a group first its summary blocks, then its exact blocks (each in KV order).
+    An exact block (mask bit set) takes the FP8 step; a summary block counts as n_j copies of its
+    summary (kbar_j, vbar_j) scored by the route score r_j (m' = max(m, r_j), weight
+    n_j exp(r_j - m'))."""
     B, H, N64, D = qz["q8"].shape
     N = qz["N"]
     rows = np.arange(N, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)

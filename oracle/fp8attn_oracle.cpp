@@ -754,7 +754,7 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
           double dm_run = 0.0;     // error bound of the running max
           for (const int64_t kb : seq) {
             if (sol && !sol_exact(kb)) {
-              // Summary route ([TF] "Sol Routing": the block's compressed contribution stays in the
+              // Summary block ([TF] "Sol Routing": the block's compressed contribution stays in the
               // same online-softmax state; "SM90 CuTe Mainloop": numerator, denominator and the
               // block length are corrected together, and both routes update one row max, row sum
               // and accumulator). The block counts as n_j copies of (kbar_j, vbar_j) with the route
@@ -925,8 +925,22 @@ int orc_attention(int mode, int B, int N, int H, int D, const double* qd, const 
         // V blocks); each piece keeps the row's KV order; piece s gives o_s, m_s, l_s and
         // O = sum_s w_s o_s / sum_s w_s with w_s = l_s * exp(m_s - max m).
         std::vector<Pass> parts;
-        if (kv_splits <= 1 || sparse || sol) {
-          // (Sol: one pass over every block in KV order, exact and summary blocks alike)
+        if (sol) {
+          // Sol routing ([TF] "Sol Routing" and "SM90 CuTe Mainloop"): one pass, one state. The
+          // mainloop takes the KV blocks in route groups of 64 (the K-summary groups its route QK
+          // runs on); the non-exact columns of a group's route scores are consumed as summary
+          // contributions, then the group's exact tiles run. Reading: groups in KV order, and
+          // inside a group first its summary blocks, then its exact blocks, each in KV order.
+          std::vector<int64_t> seq;
+          const int64_t NBg = ceil_div(NB, 64);
+          for (int64_t gi = 0; gi < NBg; gi++) {
+            const int64_t g = kv_reverse ? NBg - 1 - gi : gi;
+            for (int pass = 0; pass < 2; pass++)
+              for (const int64_t kb : blocks)
+                if (kb / 64 == g && sol_exact(kb) == (pass == 1)) seq.push_back(kb);
+          }
+          parts.push_back(stream(seq));
+        } else if (kv_splits <= 1 || sparse) {
           parts.push_back(stream(blocks));
         } else {
           const int64_t L = 2 * ceil_div(NB, 2 * static_cast<int64_t>(kv_splits));

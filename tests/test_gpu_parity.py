@@ -570,6 +570,75 @@ def test_sol_small(m, orc, N, H, tau, est, sinks, reverse, expcast):
     _compare_out(_gpu_rows(out, np.arange(N)), ref, f"sol tau={tau}", amb, peaked=True, wide=True)
 
 
+@pytest.mark.parametrize("N,tau,est,reverse,expcast", [
+    (1000, 1.0, 0, True, False), (2500, 2.0, 1, False, False), (4500, 1.5, 0, True, False),
+    (777, 1.0, 1, False, True), (4160, 2.5, 0, True, True)])
+def test_sol_unstructured(m, orc, N, tau, est, reverse, expcast):
+    """Sol on N(0,1) inputs, at the plain bar (max-abs 1e-2, no allowance): route masks with a
+    large share of summary blocks, one and two route groups."""
+    H = 2
+    say("sol unstructured", N, tau, est, reverse, expcast)
+    q, k, v = workloads.make_qkv(1, N, H, seed=150 + N)
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb)
+    ref_sol = orc.sol_prepare(ref_q, tau=tau, estimator=est, sink_blocks=1)
+    qz = _gpu_quantize(m, q, k, v)
+    out, mask = m.sol_forward(qz, tau=tau, estimator=est, sink_blocks=1, kv_order=int(reverse),
+                              pcast=m.FP8ATTN_PCAST_EXPCAST if expcast else m.FP8ATTN_PCAST_RNE,
+                              return_mask=True)
+    torch.cuda.synchronize()
+    sol = dict(ref_sol)
+    sol["mask"] = _check_route_mask(orc, _np(mask), ref_sol, -(-N // 64))
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, kv_reverse=reverse, expcast=expcast, return_amb=True,
+                                          sol=sol)
+    _compare_out(_gpu_rows(out, np.arange(N)), ref, f"sol unstructured tau={tau}", amb)
+
+
+@pytest.mark.parametrize("reverse,expcast", [(False, False), (True, False), (False, True)])
+def test_sol_shared_state(m, orc, reverse, expcast):
+    """Both routes in one online-softmax state. The one-key tail block (a summary block) scores
+    about 7 above every other key and shares the route group with the exact sink blocks 0 and 1
+    (V = 4 there, S = 1), so the sinks' P codes are taken against the running max that summary
+    sets, and many underflow. Device against the oracle; the reading with two states merged by
+    log-sum-exp fails the same comparison on sampled rows by a wide margin."""
+    from test_oracle_sol import _sol_model
+    N, H, S, delta = 641, 2, 1.0, 7.0
+    say("sol shared state", reverse, expcast)
+    q, k, v = workloads.make_qkv(1, N, H, 64)
+    q, k, v = q.float(), k.float(), v.float()
+    q[..., 127] = 4.0
+    k[..., 127] = 0.0
+    k[:, N - 1, :, 127] = delta * math.sqrt(128.0) / 4.0
+    v[:, :128] = 4.0
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    ref_q = orc.quantize(qb, kb, vb)
+    ref_sol = orc.sol_prepare(ref_q, tau=50.0, estimator=0, sink_blocks=2)
+    qz = _gpu_quantize(m, q, k, v)
+    _compare_quant(qz, ref_q)
+    out, mask = m.sol_forward(qz, tau=50.0, sink_blocks=2, kv_order=int(reverse), p_scale=S,
+                              pcast=m.FP8ATTN_PCAST_EXPCAST if expcast else m.FP8ATTN_PCAST_RNE,
+                              return_mask=True)
+    torch.cuda.synchronize()
+    NB = -(-N // 64)
+    sol = dict(ref_sol)
+    sol["mask"] = _check_route_mask(orc, _np(mask), ref_sol, NB)
+    exact = orc.mask_bits(sol["mask"], NB)
+    assert exact[..., :2].all() and not exact[..., 2:].any()
+    ref, _, _, _, amb = orc.attention_fp8(ref_q, p_scale=S, kv_reverse=reverse, expcast=expcast,
+                                          return_amb=True, sol=sol)
+    got = _gpu_rows(out, np.arange(N))
+    _compare_out(got, ref, "sol shared state", amb, peaked=True, wide=True)
+    if not expcast:
+        rows = np.arange(0, N, 37)
+        two = _sol_model(orc, ref_q, sol, exact, reverse, S, 1.0 / math.sqrt(128.0), shared=False,
+                         rows=rows)
+        allow = ATOL + 2.0 ** -8 * np.abs(ref[:, :, rows]) + amb[:, :, rows]
+        miss = float((np.abs(two - ref[:, :, rows]) - allow).max())
+        say(f"two-state reading: misses the same bar by up to {miss:.3e}")
+        assert miss > 0.03
+
+
 @pytest.mark.parametrize("grid,tau,reverse", [((5, 12, 16), 3.0, True), ((4, 9, 20), 2.0, False)])
 def test_sol_video_local(m, orc, grid, tau, reverse):
     """Video-like inputs (logits falling off with 3D distance): exact blocks cluster around the

@@ -11,10 +11,12 @@ two routes of the attention.
 * the mask is the brute-force rule "some query of the block reaches theta, or a sink block";
 * on inputs whose K and V rows are constant inside each KV block (and exactly representable),
   the summary route is exact: all-summary Sol equals FP64 softmax attention;
-* both routes update one online-softmax state in KV order: where summary blocks score above
-  the exact blocks that follow them, the oracle equals an independent numpy model of that shared
-  loop (exact blocks' P codes taken against the summary-set running max) and differs from the
-  reading with two states merged by log-sum-exp.
+* both routes update one online-softmax state, route group by route group of 64 KV blocks in KV
+  order, a group's summary blocks before its exact blocks: where summary blocks score above the
+  exact blocks, the oracle equals an independent numpy model of that shared loop (exact blocks'
+  P codes taken against the summary-set running max) and differs from the reading with two
+  states merged by log-sum-exp; with several groups, a group's exact blocks see the summaries of
+  that group and of the groups before it in KV order, and not those of later groups.
 """
 import math
 
@@ -198,8 +200,9 @@ def _route_scores(orc, qz, sol, qd, b, h, i, ss):
     return (kq @ qd[b, h, i]) * float(qz["q_scale"][b, h, i // 64]) * sc * ss
 
 
-def _sol_model(orc, qz, sol, exact, rev, S, ss, shared=True):
-    """numpy: per row, the KV blocks in KV order. shared=True: one (m, l, acc) for both routes;
+def _sol_model(orc, qz, sol, exact, rev, S, ss, shared=True, rows=None):
+    """numpy: per row, the KV blocks in route groups of 64 (groups in KV order; a group's summary
+    blocks, then its exact blocks, each in KV order). shared=True: one (m, l, acc) for both routes;
     an exact block takes m' = max(m, max x), P8 = E4M3(fl32(S exp(x - m'))), l += sum p,
     acc += P8 . V8; a summary block takes m' = max(m, r_j), w = n_j exp(r_j - m'), l += w,
     acc += w vbar_j. shared=False: the exact blocks run their own state, the summary blocks
@@ -208,16 +211,22 @@ def _sol_model(orc, qz, sol, exact, rev, S, ss, shared=True):
     N = qz["N"]
     NB = -(-N // 64)
     qd, kd, vd = _decoded(orc, qz)
-    out = np.zeros((B, H, N, 128))
-    order = list(range(NB))[::-1] if rev else list(range(NB))
+    rows = range(N) if rows is None else rows
+    out = np.zeros((B, H, len(rows), 128))
+    kv = list(range(NB))[::-1] if rev else list(range(NB))
+    groups = sorted({j // 64 for j in kv}, reverse=rev)
     for b in range(B):
         for h in range(H):
             vs = vd[b, h] * qz["v_scale"][b, h].astype(np.float64)[None, :]
             vbar = orc.bf16_decode(sol["vsum"][b, h]).astype(np.float64)
-            for i in range(N):
+            for ri, i in enumerate(rows):
                 x_all = _logits(qz, qd, kd, b, h, i, ss)
                 r_all = _route_scores(orc, qz, sol, qd, b, h, i, ss)
                 states = {True: [-np.inf, 0.0, np.zeros(128)], False: [-np.inf, 0.0, np.zeros(128)]}
+                u = i // 64
+                # route groups in KV order; a group's summary blocks, then its exact blocks
+                order = [j for g in groups for ex in (False, True) for j in kv
+                         if j // 64 == g and bool(exact[b, h, u, j]) == ex]
                 for j in order:
                     ex = bool(exact[b, h, i // 64, j])
                     st = states[True] if shared else states[ex]
@@ -238,7 +247,7 @@ def _sol_model(orc, qz, sol, exact, rev, S, ss, shared=True):
                         st[:] = [m_new, alpha * l + w, alpha * acc + w * vbar[j]]
                 if shared:
                     m, l, acc = states[True]
-                    out[b, h, i] = acc / l
+                    out[b, h, ri] = acc / l
                 else:
                     ms = [s_[0] for s_ in states.values() if s_[1] > 0]
                     mx = max(ms)
@@ -247,7 +256,7 @@ def _sol_model(orc, qz, sol, exact, rev, S, ss, shared=True):
                         if l > 0:
                             num += math.exp(m - mx) * acc
                             den += math.exp(m - mx) * l
-                    out[b, h, i] = num / den
+                    out[b, h, ri] = num / den
     return out
 
 
@@ -304,3 +313,31 @@ def test_shared_state_matches_model(orc, rev, S):
         # with S = 1 the exact blocks' codes against the summary-set max underflow more than
         # against their own max
         assert uf.sum() > 0
+
+
+@pytest.mark.parametrize("rev", [False, True])
+def test_shared_state_route_groups(orc, rev):
+    """70 KV blocks, two route groups. Summary block 66 (group 1) scores about 6 above every
+    other block. Forward: group 0's exact blocks run before it and are unaffected; group 1's see
+    it. Reverse: group 1 comes first, so every exact block sees it. Sampled rows of the oracle
+    equal the numpy model of the grouped shared loop, not the two-state reading."""
+    NBk = 70
+    N, H, S, ss = 64 * NBk, 1, 256.0, 1.0 / math.sqrt(128.0)
+    summary = [3, 10, 66, 68]
+    q, k, v = _sink_block_inputs(N, H, 62, [66], 6.0)
+    b = workloads.bits
+    qz = orc.quantize(b(q), b(k), b(v))
+    sol = dict(orc.sol_prepare(qz, tau=0.0, estimator=0, sink_blocks=0))
+    exact = np.ones((1, H, NBk, NBk), bool)
+    exact[..., summary] = False
+    words = np.zeros((1, H, NBk, 2), np.uint64)
+    for j in range(NBk):
+        words[..., j // 64] |= (exact[..., j].astype(np.uint64) << np.uint64(j % 64))
+    sol["mask"] = words
+    rows = np.array([0, 1, 777, 2048, 3000, N - 1], np.int32)
+    out, _, _, _ = orc.attention_fp8(qz, rows=rows, p_scale=S, kv_reverse=rev, sol=sol)
+    want = _sol_model(orc, qz, sol, exact, rev, S, ss, shared=True, rows=rows)
+    other = _sol_model(orc, qz, sol, exact, rev, S, ss, shared=False, rows=rows)
+    scale = np.abs(want).max()
+    assert np.max(np.abs(out - want)) <= 1e-10 * scale
+    assert np.max(np.abs(out - other)) > 1e-3 * scale
