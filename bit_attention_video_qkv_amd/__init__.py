@@ -73,7 +73,8 @@ _lib = None
 EXPORTED = ("fp8attn_quantize_qkv", "fp8attn_quantize_workspace_bytes", "fp8attn_forward",
             "fp8attn_forward_workspace_bytes", "fp8attn_sta_build", "fp8attn_status_string",
             "fp8attn_vsmooth_cluster", "fp8attn_vsmooth_cluster_workspace_bytes",
-            "fp8attn_sol_forward", "fp8attn_sol_workspace_bytes")
+            "fp8attn_sol_forward", "fp8attn_sol_workspace_bytes", "fp8attn_diag_e4m3_encode",
+            "fp8attn_diag_mfma_e4m3")
 
 
 def lib():
@@ -110,6 +111,10 @@ def lib():
         L.fp8attn_sol_forward.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 6 + [
             ctypes.POINTER(_SolOpts), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_size_t, ctypes.c_void_p]
+        L.fp8attn_diag_e4m3_encode.restype = ctypes.c_int
+        L.fp8attn_diag_e4m3_encode.argtypes = [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        L.fp8attn_diag_mfma_e4m3.restype = ctypes.c_int
+        L.fp8attn_diag_mfma_e4m3.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -311,3 +316,25 @@ def sol_forward(qz: Quantized, tau=3.0, estimator=0, sink_blocks=1,
         ctypes.c_size_t(ws.numel()), _stream(dev))
     _check("fp8attn_sol_forward", st)
     return (out, mask) if return_mask else out
+
+
+def diag_e4m3_encode(first_bits, n, out):
+    """fp8attn_diag_e4m3_encode: the quantiser's E4M3 codes of the FP32 bit patterns
+    first_bits .. first_bits + n - 1 into the uint8 device tensor ``out`` (n a multiple of 4)."""
+    if out.dtype != torch.uint8 or out.numel() < n:
+        raise ValueError("out must be a uint8 tensor of at least n elements")
+    _check("fp8attn_diag_e4m3_encode",
+           lib().fp8attn_diag_e4m3_encode(int(first_bits), int(n), _ptr(out), _stream(out.device)))
+    return out
+
+
+def diag_mfma_e4m3(a, bt):
+    """fp8attn_diag_mfma_e4m3: a, bt uint8 [T, 32, 64] device tensors (E4M3 codes; bt holds B
+    transposed) -> float32 [T, 32, 32], C[t] = A[t] B[t] on the matrix cores."""
+    if a.dtype != torch.uint8 or bt.dtype != torch.uint8 or a.shape != bt.shape or a.shape[1:] != (32, 64):
+        raise ValueError("a and bt must be uint8 [T, 32, 64]")
+    a, bt = a.contiguous(), bt.contiguous()
+    c = torch.empty((a.shape[0], 32, 32), dtype=torch.float32, device=a.device)
+    _check("fp8attn_diag_mfma_e4m3",
+           lib().fp8attn_diag_mfma_e4m3(_ptr(a), _ptr(bt), _ptr(c), int(a.shape[0]), _stream(a.device)))
+    return c

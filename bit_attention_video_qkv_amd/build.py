@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8attn.so")
-SOURCES = ["fp8attn_api.hip", "fp8attn_quant.hip", "fp8attn_attn.hip", "fp8attn_cluster.hip", "fp8attn_sol.hip"]
+SOURCES = ["fp8attn_api.hip", "fp8attn_quant.hip", "fp8attn_attn.hip", "fp8attn_cluster.hip", "fp8attn_sol.hip",
+           "fp8attn_diag.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -548,4 +548,23 @@ fp8attn_status fp8attn_vsmooth_cluster(int32_t B, int32_t N, int32_t H, int32_t 
   return from_hip(fp8attn::launch_cluster(p, stream));
 }
 
+fp8attn_status fp8attn_diag_e4m3_encode(uint32_t first_bits, int64_t n, uint8_t* out, hipStream_t stream) {
+  if (n < 0 || n % 4 != 0 || (n > 0 && (!out || !aligned(out, 4)))) return FP8ATTN_EINVAL;
+  if (static_cast<uint64_t>(first_bits) + static_cast<uint64_t>(n) > (1ull << 32)) return FP8ATTN_EINVAL;
+  if (n == 0) return FP8ATTN_OK;
+  const fp8attn_status dev = check_device();
+  if (dev != FP8ATTN_OK) return dev;
+  return from_hip(fp8attn::launch_diag_e4m3_encode(first_bits, n / 4, reinterpret_cast<uint32_t*>(out), stream));
+}
+
+fp8attn_status fp8attn_diag_mfma_e4m3(const uint8_t* a, const uint8_t* bt, float* c, int32_t n_tiles,
+                                      hipStream_t stream) {
+  if (n_tiles < 0) return FP8ATTN_EINVAL;
+  if (n_tiles == 0) return FP8ATTN_OK;
+  if (!a || !bt || !c || !aligned(a, 16) || !aligned(bt, 16) || !aligned(c, 4)) return FP8ATTN_EINVAL;
+  const fp8attn_status dev = check_device();
+  if (dev != FP8ATTN_OK) return dev;
+  return from_hip(fp8attn::launch_diag_mfma_e4m3(a, bt, c, n_tiles, stream));
+}
+
 }  // extern "C"

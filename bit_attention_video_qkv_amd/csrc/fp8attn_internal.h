@@ -113,6 +113,12 @@ hipError_t launch_sol(const SolParams& p, hipStream_t stream);
 
 hipError_t launch_quantize(const QuantParams& p, hipStream_t stream);
 
+// Diagnostics (fp8attn_diag.hip): the quantiser's E4M3 encoder on consecutive FP32 bit patterns,
+// and one E4M3 matrix-core product per 32 x 32 x 64 tile.
+hipError_t launch_diag_e4m3_encode(uint32_t first, int64_t n_words, uint32_t* out, hipStream_t stream);
+hipError_t launch_diag_mfma_e4m3(const uint8_t* a, const uint8_t* bt, float* c, int32_t n_tiles,
+                                 hipStream_t stream);
+
 constexpr int kMaxClusters = 32;  // V-Smooth clustering limits (registers and LDS of the kernel)
 constexpr int kMaxFeatures = 16;
 

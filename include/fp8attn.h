@@ -315,6 +315,32 @@ fp8attn_status fp8attn_sol_forward(int32_t B, int32_t N, int32_t H, int32_t D, c
                                    const fp8attn_sol_opts* opts, void* out, uint64_t* route_mask,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Diagnostics: the device arithmetic the parity contract rests on, run exactly as the
+ * production kernels run it, for tests that compare it with independent implementations.
+ *
+ * fp8attn_diag_e4m3_encode — the quantisation kernels' E4M3 encoder (round to nearest even onto
+ *   the OCP E4M3 grid; TeleFuser blog "FP8 Sol-Attn", section "面向注意力的 FP8 Preparation",
+ *   codes of x * (448 / amax)) applied to the FP32 values whose bit patterns are first_bits,
+ *   first_bits + 1, ..., first_bits + n - 1: out[i] is the code of pattern first_bits + i.
+ *   out: device uint8 [n], 4-byte aligned. The encoder is specified for |x| <= 448 * (1 + 2^-23),
+ *   the range the quantiser feeds it; outside it the codes are whatever the hardware gives.
+ *   Errors: EINVAL when n < 0, n is not a multiple of 4, out is null or misaligned, or the range
+ *   runs past pattern 2^32 - 1; EUNSUPPORTED on a device other than gfx950.
+ *
+ * fp8attn_diag_mfma_e4m3 — one matrix-core E4M3 product per tile, as the attention's QK and PV
+ *   contractions compute it (TeleFuser blog, section "SM90 CuTe Mainloop": E4M3 operands, FP32
+ *   accumulation): for t < n_tiles, C[t] = A[t] * B[t] with A[t] 32 x 64 E4M3 row-major
+ *   (2048 bytes), B[t] given as its transpose Bt[t] 32 x 64 E4M3 row-major (row j = column j of
+ *   B), C[t] 32 x 32 FP32 row-major, accumulated from zero. Device pointers; a and bt 16-byte
+ *   aligned, c 4-byte aligned. Errors: EINVAL on n_tiles < 0 or bad pointers; EUNSUPPORTED on a
+ *   device other than gfx950.
+ * ------------------------------------------------------------------------------------------ */
+fp8attn_status fp8attn_diag_e4m3_encode(uint32_t first_bits, int64_t n, uint8_t* out,
+                                        hipStream_t stream);
+fp8attn_status fp8attn_diag_mfma_e4m3(const uint8_t* a, const uint8_t* bt, float* c,
+                                      int32_t n_tiles, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fp8attn_status_string(fp8attn_status s);
 

@@ -138,6 +138,7 @@ void orc_e4m3_encode(const double* x, uint8_t* out, int64_t n) {
 }
 
 void orc_e4m3_encode_f32(const float* x, uint8_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; i++) out[i] = e4m3_code(static_cast<double>(x[i]));
 }
 

@@ -221,3 +221,18 @@ def test_sol_rejects_bad_arguments(m):
     assert call(v_shift=_fake(0x10004)) == 1
     assert L.fp8attn_sol_forward(1, 1000, 2, 128, *P, None, _fake(), None, _fake(),
                                  ctypes.c_size_t(need), None) == 1
+
+
+def test_diagnostics_argument_errors(m):
+    L = m.lib()
+    fake = ctypes.c_void_p(0x10000)
+    assert L.fp8attn_diag_e4m3_encode(0, 6, fake, None) == 1              # not a multiple of 4
+    assert L.fp8attn_diag_e4m3_encode(0, -4, fake, None) == 1
+    assert L.fp8attn_diag_e4m3_encode(0, 8, None, None) == 1
+    assert L.fp8attn_diag_e4m3_encode(0, 8, ctypes.c_void_p(0x10001), None) == 1
+    assert L.fp8attn_diag_e4m3_encode(0xFFFFFFFC, 8, fake, None) == 1     # past pattern 2^32 - 1
+    assert L.fp8attn_diag_e4m3_encode(0, 0, None, None) == 0              # nothing to do
+    assert L.fp8attn_diag_mfma_e4m3(fake, fake, fake, -1, None) == 1
+    assert L.fp8attn_diag_mfma_e4m3(None, fake, fake, 2, None) == 1
+    assert L.fp8attn_diag_mfma_e4m3(ctypes.c_void_p(0x10008), fake, fake, 2, None) == 1
+    assert L.fp8attn_diag_mfma_e4m3(None, None, None, 0, None) == 0

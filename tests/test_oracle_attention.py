@@ -396,3 +396,51 @@ def test_ambiguity_bound_flags_a_midpoint(orc):
     assert flip <= amb[0, 0, 0].min() and amb[0, 0, 0].max() <= flip * 1.03
     _, _, _, _, amb2 = orc.attention_fp8(qz, rows=rows, softmax_scale=sc * 1.3, return_amb=True)
     assert amb2[0, 0, 0].max() < 0.03 * flip              # no ambiguous code: truncation only
+
+
+def _expcast_model(orc, q, k, v, rev, S, scale, precast_l=False):
+    """numpy, per row: 64-key blocks in KV order; m' = max(m, block max); the ExpCast byte
+    c = clamp(rint(fl32(8 z + 56 - 0.35)), 0, 126) with z = (x - m') log2(e) + log2(S) (VC-Attention
+    article section 三, S folded into z); l = exp(m - m') l + sum decode(c) / S; acc = exp(m - m')
+    acc + decode(c) . V; O = acc / (S l). precast_l: l sums exp(x - m') instead (the standard
+    cast's rule, which ExpCast has no FP32 value for)."""
+    N = q.shape[0]
+    NB = -(-N // 64)
+    order = list(range(NB))[::-1] if rev else list(range(NB))
+    x_all = (q @ k.T) * scale
+    out = np.zeros_like(q)
+    for i in range(N):
+        m, l, acc = -np.inf, 0.0, np.zeros(q.shape[1])
+        for kb in order:
+            xs = x_all[i, kb * 64:min(N, kb * 64 + 64)]
+            m_new = max(m, xs.max())
+            alpha = 0.0 if m == -np.inf else math.exp(m - m_new)
+            z = (xs - m_new) / math.log(2.0) + math.log2(S)
+            c = np.clip(np.rint((8.0 * z + 56.0 - 0.35).astype(np.float32).astype(np.float64)), 0, 126)
+            pd = orc.e4m3_decode(c.astype(np.uint8)).astype(np.float64)
+            inc = np.exp(xs - m_new).sum() if precast_l else pd.sum() / S
+            l = alpha * l + inc
+            acc = alpha * acc + pd @ v[kb * 64:kb * 64 + len(xs)]
+            m = m_new
+        out[i] = acc / (S * l)
+    return out
+
+
+@pytest.mark.parametrize("N,rev,S", [(200, True, 256.0), (130, False, 448.0), (64, False, 256.0)])
+def test_expcast_loop_matches_numpy_model(orc, N, rev, S):
+    """The oracle's ExpCast path element by element against an independent model of the loop, on
+    inputs where quantisation is the identity (all scales 1, so logits are exact). The row sum
+    must be the sum of the decoded codes over S: summing the pre-cast exp(x - m) instead (as the
+    standard cast does) gives a visibly different output."""
+    rng = np.random.default_rng(300 + N)
+    H = 2
+    q, k, v = _exact_grid_inputs(orc, rng, N, H)
+    qz = orc.quantize(_bf16(q), _bf16(k), _bf16(v))
+    assert np.all(qz["q_scale"] == 1.0) and np.all(qz["k_scale"] == 1.0) and np.all(qz["v_scale"] == 1.0)
+    scale = 1.0 / 256.0      # keeps the exact-grid logits in a range where many codes are non-zero
+    out, _, _, _ = orc.attention_fp8(qz, softmax_scale=scale, p_scale=S, kv_reverse=rev, expcast=True)
+    for h in range(H):
+        want = _expcast_model(orc, q[0, :, h], k[0, :, h], v[0, :, h], rev, S, scale)
+        assert np.max(np.abs(out[0, h] - want)) <= 1e-10 * np.max(np.abs(want))
+        other = _expcast_model(orc, q[0, :, h], k[0, :, h], v[0, :, h], rev, S, scale, precast_l=True)
+        assert np.max(np.abs(out[0, h] - other)) > 1e-3 * np.max(np.abs(want))
