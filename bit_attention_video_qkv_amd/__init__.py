@@ -30,7 +30,9 @@ FP8ATTN_PCAST_RNE, FP8ATTN_PCAST_EXPCAST = 0, 1
 FP8ATTN_KV_SPLITS_AUTO, FP8ATTN_KV_SPLITS_MAX = -1, 16
 HEAD_DIM = 128
 
-_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or device", 3: "HIP runtime error"}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or device", 3: "HIP runtime error",
+           4: "shape needs more scratch than the no-allocation entry point holds"}
+FP8ATTN_ESCRATCH = 4
 
 
 class Fp8AttnError(RuntimeError):
@@ -74,7 +76,7 @@ EXPORTED = ("fp8attn_quantize_qkv", "fp8attn_quantize_workspace_bytes", "fp8attn
             "fp8attn_forward_workspace_bytes", "fp8attn_sta_build", "fp8attn_status_string",
             "fp8attn_vsmooth_cluster", "fp8attn_vsmooth_cluster_workspace_bytes",
             "fp8attn_sol_forward", "fp8attn_sol_workspace_bytes", "fp8attn_diag_e4m3_encode",
-            "fp8attn_diag_mfma_e4m3")
+            "fp8attn_diag_mfma_e4m3", "fp8attn_forward_noalloc")
 
 
 def lib():
@@ -111,6 +113,9 @@ def lib():
         L.fp8attn_sol_forward.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 6 + [
             ctypes.POINTER(_SolOpts), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_size_t, ctypes.c_void_p]
+        L.fp8attn_forward_noalloc.restype = ctypes.c_int
+        L.fp8attn_forward_noalloc.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 7 + [
+            ctypes.POINTER(_FwdOpts), ctypes.c_void_p, ctypes.c_void_p]
         L.fp8attn_diag_e4m3_encode.restype = ctypes.c_int
         L.fp8attn_diag_e4m3_encode.argtypes = [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         L.fp8attn_diag_mfma_e4m3.restype = ctypes.c_int
@@ -283,6 +288,28 @@ def forward(qz: Quantized, softmax_scale=1.0 / math.sqrt(HEAD_DIM), p_scale=256.
         _ptr(qz.k_scale), _ptr(qz.v_scale), _ptr(qz.v_mean), ctypes.byref(opts), _ptr(out),
         _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel()), _stream(dev))
     _check("fp8attn_forward", st)
+    return out
+
+
+def forward_noalloc(qz: Quantized, softmax_scale=1.0 / math.sqrt(HEAD_DIM), p_scale=256.0,
+                    kv_order=FP8ATTN_KV_REVERSE, pcast=FP8ATTN_PCAST_RNE, sparse: Sparse | None = None,
+                    out_rows=None, n_out=None, underflow=None, out=None, kv_splits=1):
+    """fp8attn_forward_noalloc: as ``forward``, with no workspace (the library's static scratch).
+    ``out`` must be given when the caller cannot allocate."""
+    B, N, H = qz.B, qz.N, qz.H
+    dev = qz.q8.device
+    if n_out is None:
+        n_out = N
+    if out is None:
+        out = torch.zeros((B, n_out, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    sp = sparse._c() if sparse is not None else None
+    opts = _FwdOpts(float(softmax_scale), float(p_scale), int(kv_order), int(pcast),
+                    ctypes.pointer(sp) if sp is not None else None, _ptr(out_rows), int(n_out),
+                    _ptr(underflow), _ptr(qz.v_shift), int(kv_splits))
+    st = lib().fp8attn_forward_noalloc(
+        B, N, H, HEAD_DIM, _ptr(qz.q8), _ptr(qz.k8), _ptr(qz.v8t), _ptr(qz.q_scale),
+        _ptr(qz.k_scale), _ptr(qz.v_scale), _ptr(qz.v_mean), ctypes.byref(opts), _ptr(out), _stream(dev))
+    _check("fp8attn_forward_noalloc", st)
     return out
 
 

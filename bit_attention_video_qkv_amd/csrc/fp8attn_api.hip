@@ -44,6 +44,26 @@ fp8attn_status check_device() {
 
 fp8attn_status from_hip(hipError_t e) { return e == hipSuccess ? FP8ATTN_OK : FP8ATTN_EHIP; }
 
+// Scratch of fp8attn_forward_noalloc: a file-scope device array (each device holds its own copy
+// from module load until the process ends). Host code never passes the array's name to a
+// kernel: its device address is looked up once per device, with that device current, and only
+// that address is used.
+static __device__ __align__(256) uint8_t scratch[FP8ATTN_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_addr[64];
+
+fp8attn_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8ATTN_EHIP;
+  if (dev < 0 || dev >= 64) return FP8ATTN_EUNSUPPORTED;
+  void* a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!a) {
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return FP8ATTN_EHIP;
+    g_scratch_addr[dev].store(a, std::memory_order_release);  // (a racing first call stores the same)
+  }
+  *out = a;
+  return FP8ATTN_OK;
+}
+
 bool valid_splits_arg(int32_t kv_splits) {
   return kv_splits == FP8ATTN_KV_SPLITS_AUTO || (kv_splits >= 0 && kv_splits <= FP8ATTN_KV_SPLITS_MAX);
 }
@@ -102,6 +122,7 @@ const char* fp8attn_status_string(fp8attn_status s) {
     case FP8ATTN_EINVAL: return "invalid argument";
     case FP8ATTN_EUNSUPPORTED: return "unsupported shape or device";
     case FP8ATTN_EHIP: return "HIP runtime error";
+    case FP8ATTN_ESCRATCH: return "shape needs more scratch than the no-allocation entry point holds";
   }
   return "unknown status";
 }
@@ -546,6 +567,27 @@ fp8attn_status fp8attn_vsmooth_cluster(int32_t B, int32_t N, int32_t H, int32_t 
   p.n_feat = n_feat;
   p.iters = iters;
   return from_hip(fp8attn::launch_cluster(p, stream));
+}
+
+fp8attn_status fp8attn_forward_noalloc(int32_t B, int32_t N, int32_t H, int32_t D, const uint8_t* q8,
+                                       const uint8_t* k8, const uint8_t* v8t, const float* q_scale,
+                                       const float* k_scale, const float* v_scale,
+                                       const uint16_t* v_mean, const fp8attn_fwd_opts* opts, void* out,
+                                       hipStream_t stream) {
+  // invalid arguments give a zero size and are reported by fp8attn_forward itself
+  const size_t need = opts ? fp8attn_forward_workspace_bytes(B, N, H, D, v_mean != nullptr ? 1 : 0,
+                                                             opts->sparse ? 1 : opts->kv_splits)
+                           : 0;
+  if (need > FP8ATTN_NOALLOC_SCRATCH_BYTES) return FP8ATTN_ESCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const fp8attn_status dev = check_device();
+    if (dev != FP8ATTN_OK) return dev;
+    const fp8attn_status st = scratch_address(&ws);
+    if (st != FP8ATTN_OK) return st;
+  }
+  return fp8attn_forward(B, N, H, D, q8, k8, v8t, q_scale, k_scale, v_scale, v_mean, opts, out, ws,
+                         FP8ATTN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 fp8attn_status fp8attn_diag_e4m3_encode(uint32_t first_bits, int64_t n, uint8_t* out, hipStream_t stream) {

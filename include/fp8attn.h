@@ -40,7 +40,8 @@ typedef enum fp8attn_status {
   FP8ATTN_OK = 0,
   FP8ATTN_EINVAL = 1,        /* bad argument, shape or pointer */
   FP8ATTN_EUNSUPPORTED = 2,  /* valid but not supported (D != 128, device not gfx950, ...) */
-  FP8ATTN_EHIP = 3           /* a HIP call or launch failed */
+  FP8ATTN_EHIP = 3,          /* a HIP call or launch failed */
+  FP8ATTN_ESCRATCH = 4       /* fp8attn_forward_noalloc: the shape needs more than its scratch */
 } fp8attn_status;
 
 typedef enum fp8attn_kv_order {
@@ -257,6 +258,30 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
                                const uint16_t* v_mean, const fp8attn_fwd_opts* opts,
                                void* out, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * fp8attn_forward_noalloc — fp8attn_forward without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). It computes exactly what fp8attn_forward computes, with the same
+ * kernels; its scratch (the work-queue counters and, with V-Smooth, the mean operand records)
+ * lives in a static device array of FP8ATTN_NOALLOC_SCRATCH_BYTES that each device holds until
+ * the process ends. The call allocates nothing: no hipMalloc, no hipFree, no allocating library
+ * routine. Every call on a device shares that device's array, and its counters are cleared by a
+ * kernel at the start of each call; calls that overlap on one device (two streams, two threads)
+ * race on it and must be serialised by the caller.
+ * Errors: those of fp8attn_forward; FP8ATTN_ESCRATCH when the call would need more scratch than
+ *   the array holds (fp8attn_forward_workspace_bytes above FP8ATTN_NOALLOC_SCRATCH_BYTES, e.g.
+ *   any split-KV with more than one piece at realistic sizes, or V-Smooth beyond
+ *   B*H*ceil(N/128) = 16383 mean records of 2 KB); nothing is enqueued then.
+ * ------------------------------------------------------------------------------------------ */
+#define FP8ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+fp8attn_status fp8attn_forward_noalloc(int32_t B, int32_t N, int32_t H, int32_t D,
+                                       const uint8_t* q8, const uint8_t* k8, const uint8_t* v8t,
+                                       const float* q_scale, const float* k_scale,
+                                       const float* v_scale, const uint16_t* v_mean,
+                                       const fp8attn_fwd_opts* opts, void* out,
+                                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * fp8attn_sol_forward — Sol routing attention (TeleFuser blog "FP8 Sol-Attn", sections "Sol
