@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 attn fwd TFLOP/s (4·N²·D·H, dense-equiv) + % of MI355X FP8 MFMA peak"
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (no sparsity)
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "bit_attention_video_qkv_amd", "csrc", "fp8attn_attn.hip")
 # HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) as measured by
 # rocprofv3 for the attention source whose code (comments and blank lines dropped) has this
@@ -235,7 +236,15 @@ def main():
     else:
         attn_flops = dense_flops
     achieved = attn_flops / (ms_attn * 1e-3) / 1e12
-    log(f"step {ms_step:.3f} ms, attention kernel {ms_attn:.3f} ms, quantize {ms_step - ms_attn:.3f} ms")
+    ms_quant = ms_step - ms_attn
+    # quantisation, algorithmic HBM bytes: each of Q, K, V read once as bf16 (2 B per source
+    # token, head and channel) and written once as E4M3 (1 B per layout position), plus the FP32
+    # scales and (V-Smooth) the bf16 means
+    nb = -(-n_layout // 64)
+    quant_bytes = (3 * 2 * B * N * H * D + 3 * B * n_layout * H * D + 4 * B * H * (2 * nb + D)
+                   + (2 * B * H * -(-n_layout // 128) * D if vs else 0))
+    log(f"step {ms_step:.3f} ms, attention kernel {ms_attn:.3f} ms, quantize {ms_quant:.3f} ms "
+        f"({quant_bytes / (ms_quant * 1e-3) / 1e9:.0f} GB/s algorithmic)")
 
     # the counters were taken on the workload's default configuration only
     default_cfg = not (args.heads or sol or args.smoothing or args.kv_splits != "1")
@@ -260,10 +269,18 @@ def main():
                    "kv_splits": args.kv_splits,
                    "sol": None if not sol else {"tau": args.sol_tau, "estimator": args.sol_estimator,
                                                  "sink_blocks": args.sol_sinks}},
-        "quantize_ms": round(ms_step - ms_attn, 4),
+        "quantize_ms": round(ms_quant, 4),
+        "quantize": {"ms": round(ms_quant, 4), "algorithmic_bytes": quant_bytes,
+                     "achieved_GBps": round(quant_bytes / (ms_quant * 1e-3) / 1e9, 1),
+                     "peak_GBps": HBM_PEAK_GBS,
+                     "frac": round(quant_bytes / (ms_quant * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "attn_fwd", "kernel_ms": round(ms_attn, 4),
+                     "traffic": traffic,
+                     "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, copy-calibrated, "
+                                        "measured on this attention source; profiles/attn_fwd_wan14b_dense.md")
+                     if traffic is not None else None,
+                     "kernel": "attn_fwd", "kernel_ms": round(ms_attn, 4),
                      "algorithmic_flop_per_launch": attn_flops},
     }
 
@@ -322,10 +339,22 @@ def cpu_baseline(args, cfg_name, sparse, vs):
     t_attn = time.time() - t1
     flops = 4.0 * rows_n * N * D            # dense-equivalent work of the sampled rows
     return {"value": round(flops / t_attn / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"1 head of {cfg_name}: quantisation of the head ({t_quant:.2f} s, not in "
-                      f"value) + attention of {rows_n} random query rows over all {N} keys "
+            "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"sampled: 1 head of {cfg_name}: quantisation of the head ({t_quant:.2f} s, not "
+                      f"in value) + attention of {rows_n} seeded random query rows over all {N} keys "
                       f"({t_attn:.2f} s); value = 4*rows*N*D / attention time"}
+
+
+def cpu_model():
+    """The host CPU's model name (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

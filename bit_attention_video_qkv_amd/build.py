@@ -27,6 +27,19 @@ def hipcc() -> str:
     return "hipcc"
 
 
+def build_issue_rates() -> str:
+    """The instruction-issue microbenchmark (csrc/issue_rates.hip), a stand-alone executable."""
+    exe = os.path.join(HERE, "issue_rates")
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", os.path.join(CSRC, "issue_rates.hip"), "-o", exe + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building issue_rates")
+    os.replace(exe + ".tmp", exe)
+    return exe
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
@@ -40,6 +53,7 @@ def build(verbose: bool = False) -> str:
     import ctypes
     ctypes.CDLL(tmp, mode=ctypes.RTLD_GLOBAL | os.RTLD_NOW)
     os.replace(tmp, LIB)
+    build_issue_rates()
     return LIB
 
 
