@@ -153,7 +153,7 @@ def main():
         n_layout = lay["perm"].shape[0]
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     del q, k, v
-    cluster_ms = None
+    cluster_ms = prepare_ms = None
     if vs:
         # The V-Smooth cluster permutation is computed once and reused across steps (VC-Attention
         # section 二), so it is timed on its own and not inside the step.
@@ -167,6 +167,20 @@ def main():
         cluster_ms = c0.elapsed_time(c1)
         assert torch.equal(perm_kv, m_perm)
         log(f"V-Smooth clustering (16 clusters, 8 channels, 10 rounds): {cluster_ms:.3f} ms, once")
+        # the whole preparation of a clustering step in one call (clustering, then the
+        # quantisation with the stable scatter fused into the V block statistics), also once
+        qz_p = fa.alloc_quantized(B, N, H, True, dev)
+        ws_p = fa.vsmooth_prepare_workspace(B, N, H, dev)
+        fa.vsmooth_prepare(qd, kd, vd, out=qz_p, workspace=ws_p)
+        torch.cuda.synchronize()
+        c0.record()
+        _, perm_p = fa.vsmooth_prepare(qd, kd, vd, out=qz_p, workspace=ws_p)
+        c1.record()
+        torch.cuda.synchronize()
+        prepare_ms = c0.elapsed_time(c1)
+        assert torch.equal(perm_p, perm_kv)
+        del qz_p, ws_p
+        log(f"V-Smooth clustering step, fused preparation (clustering + quantisation): {prepare_ms:.3f} ms, once")
     qz = fa.alloc_quantized(B, n_layout, H, vs, dev, smoothing=args.smoothing)
     ws_q = fa.quantize_workspace(B, n_layout, H, vs, dev)
     ws_f = fa.forward_workspace(B, n_layout, H, vs, dev, 1 if sparse else kv_splits)
@@ -286,6 +300,7 @@ def main():
 
     if cluster_ms is not None:
         result["vsmooth_cluster_ms_once"] = round(cluster_ms, 3)
+        result["vsmooth_prepare_ms_once"] = round(prepare_ms, 3)
     if sol:
         result["sol_exact_fraction"] = round(sol_exact_frac, 5)
         result["roofline"]["kernel"] = "fp8attn_sol_forward (all kernels)"

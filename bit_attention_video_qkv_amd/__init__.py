@@ -8,6 +8,7 @@ mirror the C ABI in ``include/fp8attn.h``:
 * ``forward``       -> ``fp8attn_forward``
 * ``sta_build``     -> ``fp8attn_sta_build`` (host helper)
 * ``vsmooth_cluster`` -> ``fp8attn_vsmooth_cluster``
+* ``vsmooth_prepare`` -> ``fp8attn_vsmooth_prepare``
 * ``sol_forward``   -> ``fp8attn_sol_forward``
 
 There is no fallback: if the library is missing or the device is not gfx950 these calls raise.
@@ -76,7 +77,8 @@ EXPORTED = ("fp8attn_quantize_qkv", "fp8attn_quantize_workspace_bytes", "fp8attn
             "fp8attn_forward_workspace_bytes", "fp8attn_sta_build", "fp8attn_status_string",
             "fp8attn_vsmooth_cluster", "fp8attn_vsmooth_cluster_workspace_bytes",
             "fp8attn_sol_forward", "fp8attn_sol_workspace_bytes", "fp8attn_diag_e4m3_encode",
-            "fp8attn_diag_mfma_e4m3", "fp8attn_forward_noalloc")
+            "fp8attn_diag_mfma_e4m3", "fp8attn_forward_noalloc", "fp8attn_vsmooth_prepare",
+            "fp8attn_vsmooth_prepare_workspace_bytes")
 
 
 def lib():
@@ -107,6 +109,11 @@ def lib():
         L.fp8attn_vsmooth_cluster.restype = ctypes.c_int
         L.fp8attn_vsmooth_cluster.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] + [ctypes.c_int32] * 3 + [
             ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
+        L.fp8attn_vsmooth_prepare_workspace_bytes.restype = ctypes.c_size_t
+        L.fp8attn_vsmooth_prepare_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+        L.fp8attn_vsmooth_prepare.restype = ctypes.c_int
+        L.fp8attn_vsmooth_prepare.argtypes = [ctypes.POINTER(_QuantArgs)] + [ctypes.c_void_p] * 3 + [
+            ctypes.c_int32] * 3 + [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p]
         L.fp8attn_sol_workspace_bytes.restype = ctypes.c_size_t
         L.fp8attn_sol_workspace_bytes.argtypes = [ctypes.c_int32] * 4
         L.fp8attn_sol_forward.restype = ctypes.c_int
@@ -232,6 +239,35 @@ def vsmooth_cluster(v, n_clusters=16, n_feat=8, iters=10, labels=False, workspac
         B, N, H, D, _ptr(v), n_clusters, n_feat, iters, _ptr(perm), _ptr(lab), _ptr(workspace),
         workspace.numel(), _stream(dev)))
     return (perm, lab) if labels else perm
+
+
+def vsmooth_prepare_workspace(B, N, H, device, n_feat=8):
+    n = lib().fp8attn_vsmooth_prepare_workspace_bytes(B, N, H, HEAD_DIM, n_feat)
+    return torch.empty(max(int(n), 256), dtype=torch.uint8, device=device)
+
+
+def vsmooth_prepare(q, k, v, n_clusters=16, n_feat=8, iters=10, perm_q=None, smoothing=0, labels=False,
+                    out=None, workspace=None):
+    """fp8attn_vsmooth_prepare: clustering and V-Smooth quantisation of one clustering step, the
+    stable scatter fused into the V block statistics. q, k, v: bf16 [B, N, H, 128]; perm_q int32
+    [N] or None; smoothing 0 or 1. Returns (Quantized, perm int32 [B, H, N]) and labels when
+    labels=True; perm is the perm_kv of quantize_qkv on the reuse steps."""
+    B, N, H, D = q.shape
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.shape != q.shape:
+            raise ValueError("q, k, v must be contiguous bf16 tensors of one shape")
+    dev = q.device
+    qz = out if out is not None else alloc_quantized(B, N, H, True, dev, smoothing)
+    perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    lab = torch.empty((B, H, N), dtype=torch.int32, device=dev) if labels else None
+    if workspace is None:
+        workspace = vsmooth_prepare_workspace(B, N, H, dev, n_feat)
+    args = _QuantArgs(B, N, N, H, D, _ptr(perm_q), None, 0, 1, int(smoothing), 0, None)
+    _check("fp8attn_vsmooth_prepare", lib().fp8attn_vsmooth_prepare(
+        ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), n_clusters, n_feat, iters, _ptr(perm), _ptr(lab),
+        _ptr(qz.q8), _ptr(qz.k8), _ptr(qz.v8t), _ptr(qz.q_scale), _ptr(qz.k_scale), _ptr(qz.v_scale),
+        _ptr(qz.v_mean), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(dev)))
+    return (qz, perm, lab) if labels else (qz, perm)
 
 
 def sta_build(T, Hg, W, tt, th, tw, rt, rh, rw):

@@ -138,11 +138,14 @@ size_t fp8attn_quantize_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t
          round_up(2 * bh * kHeadDim * sizeof(float));
 }
 
-fp8attn_status fp8attn_quantize_qkv(const fp8attn_quant_args* a, const void* q, const void* k,
-                                    const void* v, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
-                                    float* q_scale, float* k_scale, float* v_scale,
-                                    uint16_t* v_mean, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates the quantisation arguments and fills the launch parameters (no launch).
+fp8attn_status quant_setup(const fp8attn_quant_args* a, const void* q, const void* k, const void* v, uint8_t* q8,
+                           uint8_t* k8, uint8_t* v8t, float* q_scale, float* k_scale, float* v_scale,
+                           uint16_t* v_mean, void* workspace, size_t workspace_bytes, fp8attn::QuantParams* out) {
   if (!a) return FP8ATTN_EINVAL;
   if (a->B < 1 || a->N < 1 || a->H < 1 || a->N_src < 1 || a->D < 1) return FP8ATTN_EINVAL;
   if (a->D != kHeadDim) return FP8ATTN_EUNSUPPORTED;
@@ -166,7 +169,8 @@ fp8attn_status fp8attn_quantize_qkv(const fp8attn_quant_args* a, const void* q, 
   const fp8attn_status dev = check_device();
   if (dev != FP8ATTN_OK) return dev;
 
-  fp8attn::QuantParams p;
+  fp8attn::QuantParams& p = *out;
+  std::memset(&p, 0, sizeof(p));
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
@@ -202,6 +206,22 @@ fp8attn_status fp8attn_quantize_qkv(const fp8attn_quant_args* a, const void* q, 
   p.ws_cnt = reinterpret_cast<int32_t*>(ws);
   ws += round_up(bh * p.NB * sizeof(int32_t));
   p.ws_mean = reinterpret_cast<float*>(ws);
+  return FP8ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8attn_status fp8attn_quantize_qkv(const fp8attn_quant_args* a, const void* q, const void* k,
+                                    const void* v, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                                    float* q_scale, float* k_scale, float* v_scale,
+                                    uint16_t* v_mean, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  fp8attn::QuantParams p;
+  const fp8attn_status st = quant_setup(a, q, k, v, q8, k8, v8t, q_scale, k_scale, v_scale, v_mean, workspace,
+                                        workspace_bytes, &p);
+  if (st != FP8ATTN_OK) return st;
   return from_hip(fp8attn::launch_quantize(p, stream));
 }
 
@@ -496,10 +516,12 @@ fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, i
 namespace {
 
 struct ClusterLayout {
-  size_t feat, labels, part1, part2, featsel, cent, csum, ccount, total;
+  size_t feat, labels, part1, part2, featsel, cent, csum, ccount, scount, sbase, coff, total;
 };
 
-ClusterLayout cluster_layout(int32_t B, int32_t N, int32_t H, int32_t n_feat) {
+// with_index: also the scatter index of the fused preparation (sub-chunk counts, their prefix,
+// cluster offsets)
+ClusterLayout cluster_layout(int32_t B, int32_t N, int32_t H, int32_t n_feat, bool with_index = false) {
   ClusterLayout L;
   const size_t bh = static_cast<size_t>(B) * H;
   const size_t nc = static_cast<size_t>(fp8attn::cluster_chunks(N));
@@ -517,8 +539,52 @@ ClusterLayout cluster_layout(int32_t B, int32_t N, int32_t H, int32_t n_feat) {
   L.cent = take(bh * fp8attn::kMaxClusters * fp8attn::kMaxFeatures * sizeof(double));
   L.csum = take(bh * nc * fp8attn::kMaxClusters * (fp8attn::kMaxFeatures + 1) * sizeof(double));
   L.ccount = take(bh * nc * fp8attn::kMaxClusters * sizeof(int32_t));
+  L.scount = L.sbase = L.coff = 0;
+  if (with_index) {
+    const size_t ns = static_cast<size_t>(cdiv(N, fp8attn::kClusterSub));
+    L.scount = take(bh * ns * fp8attn::kMaxClusters * sizeof(int32_t));
+    L.sbase = take(bh * fp8attn::kMaxClusters * (ns + 1) * sizeof(int32_t));
+    L.coff = take(bh * (fp8attn::kMaxClusters + 1) * sizeof(int32_t));
+  }
   L.total = off;
   return L;
+}
+
+bool valid_cluster_args(int32_t n_clusters, int32_t n_feat, int32_t iters) {
+  return n_clusters >= 1 && n_clusters <= fp8attn::kMaxClusters && n_feat >= 1 && n_feat <= fp8attn::kMaxFeatures &&
+         iters >= 0 && iters <= 1000;
+}
+
+void cluster_params(fp8attn::ClusterParams* cp, const ClusterLayout& L, void* workspace, int32_t B, int32_t N,
+                    int32_t H, const void* v, int32_t n_clusters, int32_t n_feat, int32_t iters, int32_t* perm,
+                    int32_t* labels) {
+  fp8attn::ClusterParams& p = *cp;
+  std::memset(&p, 0, sizeof(p));
+  p.v = static_cast<const uint16_t*>(v);
+  p.perm = perm;
+  p.labels = labels;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_feat = reinterpret_cast<float*>(ws + L.feat);
+  p.ws_labels = reinterpret_cast<int32_t*>(ws + L.labels);
+  p.ws_part1 = reinterpret_cast<double*>(ws + L.part1);
+  p.ws_part2 = reinterpret_cast<double*>(ws + L.part2);
+  p.ws_featsel = reinterpret_cast<int32_t*>(ws + L.featsel);
+  p.ws_cent = reinterpret_cast<double*>(ws + L.cent);
+  p.ws_csum = reinterpret_cast<double*>(ws + L.csum);
+  p.ws_ccount = reinterpret_cast<int32_t*>(ws + L.ccount);
+  if (L.scount) {
+    p.ws_scount = reinterpret_cast<int32_t*>(ws + L.scount);
+    p.ws_sbase = reinterpret_cast<int32_t*>(ws + L.sbase);
+    p.ws_coff = reinterpret_cast<int32_t*>(ws + L.coff);
+  }
+  p.n_chunks = fp8attn::cluster_chunks(N);
+  p.n_sub = cdiv(N, fp8attn::kClusterSub);
+  p.N = N;
+  p.B = B;
+  p.H = H;
+  p.n_clusters = n_clusters;
+  p.n_feat = n_feat;
+  p.iters = iters;
 }
 
 }  // namespace
@@ -535,9 +601,7 @@ fp8attn_status fp8attn_vsmooth_cluster(int32_t B, int32_t N, int32_t H, int32_t 
   if (B < 1 || N < 1 || H < 1 || D < 1) return FP8ATTN_EINVAL;
   if (D != 128) return FP8ATTN_EUNSUPPORTED;
   if (static_cast<int64_t>(B) * H > 65535) return FP8ATTN_EINVAL;
-  if (n_clusters < 1 || n_clusters > fp8attn::kMaxClusters || n_feat < 1 || n_feat > fp8attn::kMaxFeatures ||
-      iters < 0 || iters > 1000)
-    return FP8ATTN_EINVAL;
+  if (!valid_cluster_args(n_clusters, n_feat, iters)) return FP8ATTN_EINVAL;
   if (!v || !perm || !aligned(v, 16) || !aligned(perm, 4)) return FP8ATTN_EINVAL;
   if (labels && !aligned(labels, 4)) return FP8ATTN_EINVAL;
   const size_t need = fp8attn_vsmooth_cluster_workspace_bytes(B, N, H, D, n_feat);
@@ -545,28 +609,50 @@ fp8attn_status fp8attn_vsmooth_cluster(int32_t B, int32_t N, int32_t H, int32_t 
   const fp8attn_status dev = check_device();
   if (dev != FP8ATTN_OK) return dev;
   fp8attn::ClusterParams p;
-  std::memset(&p, 0, sizeof(p));
-  p.v = static_cast<const uint16_t*>(v);
-  p.perm = perm;
-  p.labels = labels;
-  const ClusterLayout L = cluster_layout(B, N, H, n_feat);
-  char* ws = static_cast<char*>(workspace);
-  p.ws_feat = reinterpret_cast<float*>(ws + L.feat);
-  p.ws_labels = reinterpret_cast<int32_t*>(ws + L.labels);
-  p.ws_part1 = reinterpret_cast<double*>(ws + L.part1);
-  p.ws_part2 = reinterpret_cast<double*>(ws + L.part2);
-  p.ws_featsel = reinterpret_cast<int32_t*>(ws + L.featsel);
-  p.ws_cent = reinterpret_cast<double*>(ws + L.cent);
-  p.ws_csum = reinterpret_cast<double*>(ws + L.csum);
-  p.ws_ccount = reinterpret_cast<int32_t*>(ws + L.ccount);
-  p.n_chunks = fp8attn::cluster_chunks(N);
-  p.N = N;
-  p.B = B;
-  p.H = H;
-  p.n_clusters = n_clusters;
-  p.n_feat = n_feat;
-  p.iters = iters;
+  cluster_params(&p, cluster_layout(B, N, H, n_feat), workspace, B, N, H, v, n_clusters, n_feat, iters, perm, labels);
   return from_hip(fp8attn::launch_cluster(p, stream));
+}
+
+size_t fp8attn_vsmooth_prepare_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D, int32_t n_feat) {
+  const size_t qb = fp8attn_quantize_workspace_bytes(B, N, H, D, 1);
+  if (qb == 0 || n_feat < 1 || n_feat > fp8attn::kMaxFeatures) return 0;
+  return round_up(qb) + cluster_layout(B, N, H, n_feat, true).total;
+}
+
+fp8attn_status fp8attn_vsmooth_prepare(const fp8attn_quant_args* a, const void* q, const void* k, const void* v,
+                                       int32_t n_clusters, int32_t n_feat, int32_t iters, int32_t* perm,
+                                       int32_t* labels, uint8_t* q8, uint8_t* k8, uint8_t* v8t, float* q_scale,
+                                       float* k_scale, float* v_scale, uint16_t* v_mean, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  if (!a) return FP8ATTN_EINVAL;
+  if (a->B < 1 || a->N < 1 || a->H < 1 || a->N_src < 1 || a->D < 1) return FP8ATTN_EINVAL;
+  if (a->D != kHeadDim) return FP8ATTN_EUNSUPPORTED;
+  if (a->perm_kv || a->vsmooth != 1 || a->N != a->N_src) return FP8ATTN_EINVAL;
+  if (!valid_cluster_args(n_clusters, n_feat, iters)) return FP8ATTN_EINVAL;
+  if (!perm || !aligned(perm, 4) || (labels && !aligned(labels, 4))) return FP8ATTN_EINVAL;
+  const size_t need = fp8attn_vsmooth_prepare_workspace_bytes(a->B, a->N, a->H, a->D, n_feat);
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < need) return FP8ATTN_EINVAL;
+  // the quantisation with the permutation being written as its shared K/V gather
+  fp8attn_quant_args qa = *a;
+  qa.perm_kv = perm;
+  qa.perm_kv_per_head = 1;
+  const size_t qb = round_up(fp8attn_quantize_workspace_bytes(a->B, a->N, a->H, a->D, 1));
+  fp8attn::QuantParams qp;
+  const fp8attn_status st =
+      quant_setup(&qa, q, k, v, q8, k8, v8t, q_scale, k_scale, v_scale, v_mean, workspace, qb, &qp);
+  if (st != FP8ATTN_OK) return st;  // (includes the device check)
+  fp8attn::ClusterParams cp;
+  cluster_params(&cp, cluster_layout(a->B, a->N, a->H, n_feat, true), static_cast<char*>(workspace) + qb, a->B,
+                 a->N, a->H, v, n_clusters, n_feat, iters, perm, labels);
+  qp.sc_labels = cp.ws_labels;
+  qp.sc_sbase = cp.ws_sbase;
+  qp.sc_coff = cp.ws_coff;
+  qp.perm_out = perm;
+  qp.sc_nsub = cp.n_sub;
+  qp.sc_clusters = n_clusters;
+  const hipError_t e = fp8attn::launch_cluster(cp, stream);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(fp8attn::launch_quantize(qp, stream));
 }
 
 fp8attn_status fp8attn_forward_noalloc(int32_t B, int32_t N, int32_t H, int32_t D, const uint8_t* q8,

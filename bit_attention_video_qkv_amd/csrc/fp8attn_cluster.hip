@@ -23,6 +23,8 @@
 //   vc_gather   the selected features of every token (FP32)
 //   vc_step     assignment (+ per-chunk cluster sums, or the final per-chunk counts)
 //   vc_update   (B*H): centroids from the chunk sums          vc_scatter  stable scatter
+//   vc_index    (B*H): instead of vc_scatter, the scatter index from which the V block
+//               statistics of the quantisation place the tokens themselves
 #include "fp8attn_common.h"
 #include "fp8attn_internal.h"
 
@@ -128,16 +130,22 @@ __global__ __launch_bounds__(256) void vc_gather(ClusterParams p) {
 
 // 5. assignment of the chunk's tokens (thread i: tokens t0 + kTpt*i .. +kTpt-1). With sums: per
 // cluster, the chunk's feature sums and count (wave butterflies, then the 4 waves in order).
-// Final step (sums = 0): the chunk's count per cluster.
+// Final step (sums = 0): the chunk's count per cluster, the labels output and, for the scatter
+// index, the count per cluster of each 256-token sub-chunk (threads 32 s .. 32 s + 31 hold the
+// tokens of sub-chunk s of the chunk).
 __global__ __launch_bounds__(256) void vc_step(ClusterParams p, int sums) {
+  constexpr int kSubs = kChunk / kClusterSub;
+  static_assert(kChunk % kClusterSub == 0 && kClusterSub % kTpt == 0, "sub-chunks of whole threads");
   __shared__ double cent[kMaxClusters * kMaxFeatures];
   __shared__ double wred[4][kMaxFeatures + 1];
   __shared__ int cnt_s[kMaxClusters];
+  __shared__ int scnt_s[kSubs][kMaxClusters];
   const int64_t c = blockIdx.x, bh = blockIdx.y;
   const int K = p.n_clusters, F = p.n_feat;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < K * kMaxFeatures; i += 256) cent[i] = p.ws_cent[bh * kMaxClusters * kMaxFeatures + i];
   if (tid < kMaxClusters) cnt_s[tid] = 0;
+  if (tid < kSubs * kMaxClusters) scnt_s[tid / kMaxClusters][tid % kMaxClusters] = 0;
   __syncthreads();
   const int64_t tb = c * kChunk + static_cast<int64_t>(tid) * kTpt;
   const float* fv = p.ws_feat + bh * p.N * F;
@@ -173,11 +181,22 @@ __global__ __launch_bounds__(256) void vc_step(ClusterParams p, int sums) {
     p.ws_labels[bh * p.N + t] = best;
   }
   if (!sums) {
+    const int sub = tid / (kClusterSub / kTpt);
 #pragma unroll
-    for (int k = 0; k < kTpt; k++)
-      if (lab[k] >= 0) atomicAdd(&cnt_s[lab[k]], 1);  // integer counts: order-free
+    for (int k = 0; k < kTpt; k++) {
+      if (lab[k] < 0) continue;
+      atomicAdd(&cnt_s[lab[k]], 1);  // integer counts: order-free
+      if (p.ws_scount) atomicAdd(&scnt_s[sub][lab[k]], 1);
+      if (p.labels) p.labels[bh * p.N + tb + k] = lab[k];
+    }
     __syncthreads();
     if (tid < K) p.ws_ccount[(bh * p.n_chunks + c) * kMaxClusters + tid] = cnt_s[tid];
+    if (p.ws_scount) {
+      for (int i = tid; i < kSubs * K; i += 256) {
+        const int64_t s = c * kSubs + i / K;
+        if (s < p.n_sub) p.ws_scount[(bh * p.n_sub + s) * kMaxClusters + i % K] = scnt_s[i / K][i % K];
+      }
+    }
     return;
   }
   for (int cl = 0; cl < K; cl++) {
@@ -267,7 +286,35 @@ __global__ __launch_bounds__(256) void vc_scatter(ClusterParams p) {
   for (int k = 0; k < kTpt; k++) {
     if (lab[k] < 0) continue;
     out[pos[lab[k]]++] = static_cast<int32_t>(tb + k);
-    if (p.labels) p.labels[bh * p.N + tb + k] = lab[k];
+  }
+}
+
+// 7'. scatter index (grid B*H): per cluster, the tokens of the cluster before each sub-chunk
+// (sub-chunks in ascending order), and the first layout position of each cluster (clusters in
+// ascending order). Position off[c] + r holds the cluster's token of rank r, as in vc_scatter.
+__global__ __launch_bounds__(64) void vc_index(ClusterParams p) {
+  __shared__ int tot[kMaxClusters];
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x, K = p.n_clusters;
+  if (c < K) {
+    int32_t* sb = p.ws_sbase + (bh * K + c) * (p.n_sub + 1);
+    int run = 0;
+    for (int64_t s = 0; s < p.n_sub; s++) {
+      sb[s] = run;
+      run += p.ws_scount[(bh * p.n_sub + s) * kMaxClusters + c];
+    }
+    sb[p.n_sub] = run;
+    tot[c] = run;
+  }
+  __syncthreads();
+  if (c == 0) {
+    int32_t* off = p.ws_coff + bh * (kMaxClusters + 1);
+    int o = 0;
+    for (int cl = 0; cl < K; cl++) {
+      off[cl] = o;
+      o += tot[cl];
+    }
+    off[K] = o;
   }
 }
 
@@ -285,7 +332,8 @@ hipError_t launch_cluster(const ClusterParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(vc_update, dim3(bh), dim3(512), 0, stream, p);
   }
   hipLaunchKernelGGL(vc_step, g, dim3(256), 0, stream, p, 0);
-  hipLaunchKernelGGL(vc_scatter, g, dim3(256), 0, stream, p);
+  if (p.ws_scount) hipLaunchKernelGGL(vc_index, dim3(bh), dim3(64), 0, stream, p);
+  else hipLaunchKernelGGL(vc_scatter, g, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -32,6 +32,16 @@ struct QuantParams {
   int vsmooth;
   int smoothing;
   int v_bias_correction;
+  // V-Smooth preparation with the stable scatter fused into the V block statistics (sc_labels
+  // non-null): the statistics kernel places the tokens of each 128-row block from the cluster
+  // labels and the scatter index of the clustering and writes them to perm_out, which is then
+  // perm_kv (per head) of the other kernels
+  const int32_t* sc_labels;  // [B*H, N] cluster of each source token
+  const int32_t* sc_sbase;   // [B*H, sc_clusters, sc_nsub + 1]
+  const int32_t* sc_coff;    // [B*H, kMaxClusters + 1]
+  int32_t* perm_out;         // [B*H, N]
+  int64_t sc_nsub;
+  int sc_clusters;
 };
 
 struct AttnParams {
@@ -134,10 +144,18 @@ struct ClusterParams {
   double* ws_cent;     // [B*H, kMaxClusters, kMaxFeatures]
   double* ws_csum;     // [B*H, n_chunks, kMaxClusters, kMaxFeatures + 1] (sums, count)
   int32_t* ws_ccount;  // [B*H, n_chunks, kMaxClusters]
-  int64_t N, n_chunks;
+  // scatter index (instead of perm, for the preparation that fuses the stable scatter into the
+  // V block statistics), or null: tokens of each cluster per 256-token sub-chunk (final
+  // assignment), their exclusive prefix over the sub-chunks and the cluster offsets
+  int32_t* ws_scount;  // [B*H, n_sub, kMaxClusters]
+  int32_t* ws_sbase;   // [B*H, n_clusters, n_sub + 1]
+  int32_t* ws_coff;    // [B*H, kMaxClusters + 1]
+  int64_t N, n_chunks, n_sub;
   int B, H;
   int n_clusters, n_feat, iters;
 };
+
+constexpr int kClusterSub = 256;  // tokens per sub-chunk of the scatter index
 
 int64_t cluster_chunks(int64_t N);  // token chunks of the clustering kernels
 hipError_t launch_cluster(const ClusterParams& p, hipStream_t stream);

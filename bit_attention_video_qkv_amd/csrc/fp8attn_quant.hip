@@ -24,6 +24,10 @@
 //                    [B, H, 128, N64]; with the bias correction also the FP32 column sums of
 //                    the rounding error of the block's valid rows.
 //   5. (bias correction) the same tree over the error sums -> v_shift = mean_V - mean error.
+// V-Smooth preparation of a clustering step (VC-Attention article, section 四: the gather after
+// the clustering fused with the block mean and the quantisation): v_block_stats runs first and
+// performs the clustering's stable scatter itself (each 128-row block finds its tokens from the
+// cluster labels), writing the permutation that the other kernels then gather through.
 //
 // Every sum of the smoothing path follows one fixed order (in-block ascending, then the tree),
 // with explicitly rounded FP32 operations, so the means and v_shift are reproducible bit for bit.
@@ -231,22 +235,80 @@ __global__ __launch_bounds__(256) void quant_qk(QuantParams p) {
   }
 }
 
+// The stable scatter of the V-Smooth clustering for one 128-row block j of the layout: layout
+// position off[c] + r holds the token of rank r (in token order) among the tokens of cluster c.
+// For each cluster whose positions meet the block, the ranks ra .. rb - 1 it needs are found by
+// scanning the labels from the sub-chunk that holds rank ra (sbase: the cluster's tokens before
+// each 256-token sub-chunk), 256 tokens per step, ranks by a workgroup prefix count of the matches.
+// src_s[r] receives the token of position 128 j + r, or -1 beyond N.
+__device__ __forceinline__ void scatter_rows(const QuantParams& p, int64_t bh, int64_t j, int* src_s,
+                                             int* wtot_s, int* s0_s) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t i0 = j * kVBlock, i1 = min<int64_t>(p.N, i0 + kVBlock);
+  if (tid < kVBlock) src_s[tid] = -1;
+  const int32_t* coff = p.sc_coff + bh * (kMaxClusters + 1);
+  const int32_t* lab = p.sc_labels + bh * p.N;
+  for (int c = 0; c < p.sc_clusters; c++) {
+    const int64_t oc = coff[c];
+    const int64_t lo = max<int64_t>(i0, oc), hi = min<int64_t>(i1, static_cast<int64_t>(coff[c + 1]));
+    if (lo >= hi) continue;  // (uniform: every thread reads the same offsets)
+    const int ra = static_cast<int>(lo - oc), rb = static_cast<int>(hi - oc);
+    const int32_t* sb = p.sc_sbase + (bh * p.sc_clusters + c) * (p.sc_nsub + 1);
+    __syncthreads();  // (s0_s and wtot_s of the previous cluster are read)
+    if (tid == 0) *s0_s = static_cast<int>(p.sc_nsub);
+    __syncthreads();
+    for (int64_t s = tid; s < p.sc_nsub; s += 256)
+      if (sb[s] <= ra && ra < sb[s + 1]) *s0_s = static_cast<int>(s);  // (one sub-chunk matches)
+    __syncthreads();
+    const int64_t s0 = *s0_s;
+    int base = s0 < p.sc_nsub ? sb[s0] : rb;
+    for (int64_t t0 = s0 * kClusterSub; base < rb && t0 < p.N; t0 += 256) {
+      const int64_t t = t0 + tid;
+      const bool m = t < p.N && lab[t] == c;
+      const uint64_t bal = __ballot(m);
+      if (lane == 0) wtot_s[wave] = __popcll(bal);
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        const int n = wtot_s[w];
+        before += w < wave ? n : 0;
+        total += n;
+      }
+      const int rank = base + before + __popcll(bal & ((1ull << lane) - 1ull));
+      if (m && rank >= ra && rank < rb) src_s[oc + rank - i0] = static_cast<int>(t);
+      base += total;
+      __syncthreads();  // (wtot_s is rewritten by the next step)
+    }
+  }
+  __syncthreads();
+}
+
 // 2. Per 128-row block statistics of V. Thread t: channels 8*(t%16)..+7, rows t/16 + 16*p.
 // (VS: V-Smooth; without it the FP64 column sums and their 16 KB of LDS are not needed, and
-// eight workgroups fit a CU instead of six)
-template <bool VS>
+// eight workgroups fit a CU instead of six.) SCATTER: the block's tokens come from the fused
+// stable scatter of the clustering, and the block writes them to perm_out.
+template <bool VS, bool SCATTER>
 __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
   __shared__ double dsum[VS ? 16 : 1][kHeadDim];  // [row group][channel]
   __shared__ float fmax_[16][kHeadDim];
   __shared__ float mhat_s[kHeadDim];
   __shared__ int n_valid_s;
+  __shared__ int src_s[SCATTER ? kVBlock : 1];
+  __shared__ int wtot_s[4], s0_s;
   const int64_t j = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / p.H, h = bh % p.H;
   const int chunk = threadIdx.x & 15;
   const int rg = threadIdx.x >> 4;
   if (threadIdx.x == 0) n_valid_s = 0;
-  __syncthreads();
+  if constexpr (SCATTER) {
+    scatter_rows(p, bh, j, src_s, wtot_s, &s0_s);  // (ends with a barrier)
+    const int64_t i = j * kVBlock + threadIdx.x;
+    if (threadIdx.x < kVBlock && i < p.N) p.perm_out[bh * p.N + i] = src_s[threadIdx.x];
+  } else {
+    __syncthreads();
+  }
   // V' = fl32(V - mean_V) on valid rows under smoothing 2 (never together with V-Smooth)
   const bool shift = p.smoothing == 2;
   float mv[8];
@@ -259,7 +321,9 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
 #pragma unroll
   for (int pass = 0; pass < 8; pass++) {
     const int64_t i = j * kVBlock + rg + 16 * pass;
-    const int64_t s = gather_src(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, i);
+    int64_t s;
+    if constexpr (SCATTER) s = src_s[rg + 16 * pass];
+    else s = gather_src(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, i);
     valid[pass] = s >= 0;
     my_valid += (chunk == 0 && valid[pass]) ? 1 : 0;
     if (valid[pass]) {
@@ -494,6 +558,14 @@ static hipError_t launch_seq_means(const QuantParams& p, int z_first, int nz, in
 hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
   const unsigned bh = static_cast<unsigned>(p.B * p.H);
   hipError_t e;
+  const dim3 g_stats(static_cast<unsigned>(p.NB128), static_cast<unsigned>(p.B * p.H));
+  if (p.sc_labels) {
+    // fused stable scatter: the V statistics place the tokens and write the permutation, which
+    // the other kernels then read as perm_kv
+    hipLaunchKernelGGL((v_block_stats<true, true>), g_stats, dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (p.smoothing >= 1) {
     hipLaunchKernelGGL(seq_block_sums, dim3(static_cast<unsigned>(p.NB), bh, static_cast<unsigned>(p.smoothing)),
                        dim3(256), 0, stream, p);
@@ -506,11 +578,12 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(quant_qk, g_qk, dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 g_stats(static_cast<unsigned>(p.NB128), static_cast<unsigned>(p.B * p.H));
-  if (p.vsmooth) hipLaunchKernelGGL(v_block_stats<true>, g_stats, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(v_block_stats<false>, g_stats, dim3(256), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!p.sc_labels) {
+    if (p.vsmooth) hipLaunchKernelGGL((v_block_stats<true, false>), g_stats, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((v_block_stats<false, false>), g_stats, dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(v_finalize, dim3(static_cast<unsigned>(p.B * p.H), kHeadDim / 32), dim3(1024), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

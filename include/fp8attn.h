@@ -160,6 +160,36 @@ fp8attn_status fp8attn_vsmooth_cluster(int32_t B, int32_t N, int32_t H, int32_t 
                                        size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * fp8attn_vsmooth_prepare — the V-Smooth preparation of a clustering step in one call, with the
+ * clustering's stable scatter fused into the gather, block mean and residual quantisation
+ * (VC-Attention article, section 四 and Fig. 7: the gather after the clustering, the block
+ * mean, the scale and the quantisation fused, so the permuted tensors never pass through HBM;
+ * section 二: the permutation is then reused across the steps of a window).
+ * Computes exactly what fp8attn_vsmooth_cluster followed by fp8attn_quantize_qkv with
+ * perm_kv = perm (perm_kv_per_head = 1) computes, bit for bit, but no kernel writes the
+ * permutation before the quantisation: the V block statistics place each 128-row block's
+ * tokens from the cluster labels (position off[c] + r holds the token of rank r among the
+ * tokens of cluster c) and write perm as they go, for the other kernels and for the reuse
+ * steps, which call fp8attn_quantize_qkv with it.
+ * Arguments: args as for fp8attn_quantize_qkv with perm_kv = NULL, vsmooth = 1 and
+ *   N == N_src (perm_q, smoothing 0/1 allowed); q, k, v, q8 .. v_mean as there; n_clusters,
+ *   n_feat, iters, perm (out, int32 [B, H, N]) and labels (out or NULL) as for
+ *   fp8attn_vsmooth_cluster; workspace of at least fp8attn_vsmooth_prepare_workspace_bytes(...)
+ *   bytes, 16-byte aligned, overwritten.
+ * Errors: those of the two calls it replaces; EINVAL also on perm_kv != NULL, vsmooth != 1 or
+ *   N != N_src.
+ * ------------------------------------------------------------------------------------------ */
+size_t fp8attn_vsmooth_prepare_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t D,
+                                               int32_t n_feat);
+fp8attn_status fp8attn_vsmooth_prepare(const fp8attn_quant_args* args, const void* q,
+                                       const void* k, const void* v, int32_t n_clusters,
+                                       int32_t n_feat, int32_t iters, int32_t* perm,
+                                       int32_t* labels, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                                       float* q_scale, float* k_scale, float* v_scale,
+                                       uint16_t* v_mean, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * fp8attn_sta_build — HOST helper that lays a raster latent grid (T, Hg, W) out in tiles
  * (tt, th, tw) (the grid is padded up to whole tiles; tiles numbered in raster order over the
  * tile grid; inside a tile valid tokens first in raster order, then padding) and lists, for

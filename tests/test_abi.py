@@ -192,6 +192,37 @@ def test_cluster_rejects_bad_arguments(m):
     assert call(ws=None) == EINVAL and call(wsb=need - 1) == EINVAL
 
 
+def test_vsmooth_prepare_rejects_bad_arguments(m):
+    L = m.lib()
+    A = m._QuantArgs
+    need = L.fp8attn_vsmooth_prepare_workspace_bytes(1, 1000, 2, 128, 8)
+    assert need >= L.fp8attn_quantize_workspace_bytes(1, 1000, 2, 128, 1) + \
+        L.fp8attn_vsmooth_cluster_workspace_bytes(1, 1000, 2, 128, 8)
+    assert L.fp8attn_vsmooth_prepare_workspace_bytes(1, 1000, 2, 64, 8) == 0
+    assert L.fp8attn_vsmooth_prepare_workspace_bytes(1, 1000, 2, 128, 17) == 0
+
+    def call(a, K=16, F=8, it=10, perm=_fake(), lab=None, ws=_fake(), wsb=need, qkv=(_fake(),) * 3):
+        return L.fp8attn_vsmooth_prepare(ctypes.byref(a), *qkv, K, F, it, perm, lab, *([_fake()] * 7), ws,
+                                         ctypes.c_size_t(wsb), None)
+    EINVAL, EUNSUPPORTED = 1, 2
+    good = lambda **kw: A(**dict(dict(B=1, N_src=1000, N=1000, H=2, D=128, perm_q=None, perm_kv=None,
+                                      perm_kv_per_head=0, vsmooth=1, smoothing=0, v_bias_correction=0,
+                                      v_shift=None), **kw))
+    assert L.fp8attn_vsmooth_prepare(None, *([_fake()] * 3), 16, 8, 10, _fake(), None, *([_fake()] * 7),
+                                     _fake(), ctypes.c_size_t(need), None) == EINVAL
+    assert call(good(D=64)) == EUNSUPPORTED
+    assert call(good(B=0)) == EINVAL
+    assert call(good(perm_kv=_fake().value)) == EINVAL                 # the clustering supplies perm_kv
+    assert call(good(vsmooth=0)) == EINVAL
+    assert call(good(N=999)) == EINVAL                                 # N != N_src
+    assert call(good(smoothing=2)) == EINVAL                           # smoothing 2 excludes V-Smooth
+    assert call(good(), K=0) == EINVAL and call(good(), K=33) == EINVAL
+    assert call(good(), F=0) == EINVAL and call(good(), it=1001) == EINVAL
+    assert call(good(), perm=None) == EINVAL and call(good(), lab=_fake(0x10002)) == EINVAL
+    assert call(good(), ws=None) == EINVAL and call(good(), wsb=need - 1) == EINVAL
+    assert call(good(), qkv=(None, _fake(), _fake())) == EINVAL
+
+
 def test_sol_rejects_bad_arguments(m):
     L = m.lib()
     need = L.fp8attn_sol_workspace_bytes(1, 1000, 2, 128)

@@ -729,6 +729,47 @@ def test_vsmooth_cluster_matches_oracle(m, orc, N, H, K, F, iters):
     assert np.array_equal(perm_g, perm_o)
 
 
+@pytest.mark.parametrize("B,N,H,K,F,iters,smoothing,rev_q", [
+    (1, 49152, 2, 16, 8, 10, 0, False), (2, 1000, 3, 16, 8, 10, 0, False), (1, 37, 1, 16, 8, 3, 0, False),
+    (1, 5, 1, 16, 4, 2, 0, False), (1, 3000, 1, 32, 16, 0, 0, False), (1, 4099, 2, 1, 8, 2, 0, False),
+    (1, 2000, 2, 16, 8, 4, 1, True)])
+def test_vsmooth_prepare_fused_scatter(m, orc, B, N, H, K, F, iters, smoothing, rev_q):
+    """The fused preparation (stable scatter inside the V block statistics) against the two-call
+    path (clustering, then quantisation through its permutation): every output bit-exact, the
+    permutation and labels equal; both against the oracle's clustering and quantisation. Covers
+    a full V-Smooth head pair, B = 2, fewer tokens than one 256-token sub-chunk, fewer tokens
+    than clusters, 32 clusters, one cluster (identity permutation), K smoothing with a query
+    permutation."""
+    say("vsmooth prepare", B, N, H, K, F, iters, smoothing, rev_q)
+    if N == 49152:
+        q, k, v = workloads.workload("vsmooth", heads=H)
+    else:
+        q, k, v = workloads.make_qkv(B, N, H, seed=N + 7 * K, kind="token_outliers", n_outlier_channels=8)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    perm_q = np.arange(N - 1, -1, -1, dtype=np.int32) if rev_q else None
+    pq = None if perm_q is None else torch.from_numpy(perm_q).to(DEV)
+    qz, perm, lab = m.vsmooth_prepare(qd, kd, vd, n_clusters=K, n_feat=F, iters=iters, perm_q=pq,
+                                      smoothing=smoothing, labels=True)
+    perm2, lab2 = m.vsmooth_cluster(vd, n_clusters=K, n_feat=F, iters=iters, labels=True)
+    qz2 = m.quantize_qkv(qd, kd, vd, perm_q=pq, perm_kv=perm2, vsmooth=True, smoothing=smoothing)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(perm), _np(perm2)), "perm"
+    assert np.array_equal(_np(lab), _np(lab2)), "labels"
+    for key in ("q8", "k8", "v8t", "q_scale", "k_scale", "v_scale", "v_mean"):
+        a, b = _np(getattr(qz, key)), _np(getattr(qz2, key))
+        assert a.dtype == b.dtype and np.array_equal(a.view(np.uint8), b.view(np.uint8)), key
+    perm_np, lab_np = _np(perm), _np(lab)
+    _check_perm_valid(perm_np, lab_np)
+    if N <= 4099:
+        perm_o = orc.vsmooth_perm(_bits(v), n_clusters=K, n_feat=F, iters=iters)
+        assert np.array_equal(perm_np, perm_o)
+        ref = orc.quantize(_bits(q), _bits(k), _bits(v), perm_q=perm_q, perm_kv=perm_o, vsmooth=True,
+                           smoothing=smoothing)
+        _compare_quant(qz, ref)
+    if K == 1:
+        assert np.array_equal(perm_np, np.broadcast_to(np.arange(N, dtype=np.int32), perm_np.shape))
+
+
 # ------------------------------------------------------------------------------------------
 # Full-size workloads (benchmark launch configuration), sampled heads and rows
 # ------------------------------------------------------------------------------------------
