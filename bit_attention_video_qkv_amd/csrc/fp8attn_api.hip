@@ -516,7 +516,7 @@ fp8attn_status fp8attn_sta_build(int32_t T, int32_t Hg, int32_t W, int32_t tt, i
 namespace {
 
 struct ClusterLayout {
-  size_t feat, labels, part1, part2, featsel, cent, csum, ccount, scount, sbase, coff, total;
+  size_t feat, labels, part1, part2, featsel, cent, csum, ccount, lab8, scount, sbase, ctot, total;
 };
 
 // with_index: also the scatter index of the fused preparation (sub-chunk counts, their prefix,
@@ -539,12 +539,13 @@ ClusterLayout cluster_layout(int32_t B, int32_t N, int32_t H, int32_t n_feat, bo
   L.cent = take(bh * fp8attn::kMaxClusters * fp8attn::kMaxFeatures * sizeof(double));
   L.csum = take(bh * nc * fp8attn::kMaxClusters * (fp8attn::kMaxFeatures + 1) * sizeof(double));
   L.ccount = take(bh * nc * fp8attn::kMaxClusters * sizeof(int32_t));
-  L.scount = L.sbase = L.coff = 0;
+  L.lab8 = L.scount = L.sbase = L.ctot = 0;
   if (with_index) {
     const size_t ns = static_cast<size_t>(cdiv(N, fp8attn::kClusterSub));
-    L.scount = take(bh * ns * fp8attn::kMaxClusters * sizeof(int32_t));
+    L.lab8 = take(bh * static_cast<size_t>(cdiv(N, 16) * 16));
+    L.scount = take(bh * fp8attn::kMaxClusters * ns * sizeof(int32_t));
     L.sbase = take(bh * fp8attn::kMaxClusters * (ns + 1) * sizeof(int32_t));
-    L.coff = take(bh * (fp8attn::kMaxClusters + 1) * sizeof(int32_t));
+    L.ctot = take(bh * fp8attn::kMaxClusters * sizeof(int32_t));
   }
   L.total = off;
   return L;
@@ -573,12 +574,14 @@ void cluster_params(fp8attn::ClusterParams* cp, const ClusterLayout& L, void* wo
   p.ws_csum = reinterpret_cast<double*>(ws + L.csum);
   p.ws_ccount = reinterpret_cast<int32_t*>(ws + L.ccount);
   if (L.scount) {
+    p.ws_lab8 = reinterpret_cast<uint8_t*>(ws + L.lab8);
     p.ws_scount = reinterpret_cast<int32_t*>(ws + L.scount);
     p.ws_sbase = reinterpret_cast<int32_t*>(ws + L.sbase);
-    p.ws_coff = reinterpret_cast<int32_t*>(ws + L.coff);
+    p.ws_ctot = reinterpret_cast<int32_t*>(ws + L.ctot);
   }
   p.n_chunks = fp8attn::cluster_chunks(N);
   p.n_sub = cdiv(N, fp8attn::kClusterSub);
+  p.lab_stride = cdiv(N, 16) * 16;
   p.N = N;
   p.B = B;
   p.H = H;
@@ -644,11 +647,12 @@ fp8attn_status fp8attn_vsmooth_prepare(const fp8attn_quant_args* a, const void* 
   fp8attn::ClusterParams cp;
   cluster_params(&cp, cluster_layout(a->B, a->N, a->H, n_feat, true), static_cast<char*>(workspace) + qb, a->B,
                  a->N, a->H, v, n_clusters, n_feat, iters, perm, labels);
-  qp.sc_labels = cp.ws_labels;
+  qp.sc_labels = cp.ws_lab8;
   qp.sc_sbase = cp.ws_sbase;
-  qp.sc_coff = cp.ws_coff;
+  qp.sc_ctot = cp.ws_ctot;
   qp.perm_out = perm;
   qp.sc_nsub = cp.n_sub;
+  qp.sc_lab_stride = cp.lab_stride;
   qp.sc_clusters = n_clusters;
   const hipError_t e = fp8attn::launch_cluster(cp, stream);
   if (e != hipSuccess) return from_hip(e);

@@ -23,7 +23,7 @@
 //   vc_gather   the selected features of every token (FP32)
 //   vc_step     assignment (+ per-chunk cluster sums, or the final per-chunk counts)
 //   vc_update   (B*H): centroids from the chunk sums          vc_scatter  stable scatter
-//   vc_index    (B*H): instead of vc_scatter, the scatter index from which the V block
+//   vc_index    (n_clusters, B*H): instead of vc_scatter, the scatter index from which the V block
 //               statistics of the quantisation place the tokens themselves
 #include "fp8attn_common.h"
 #include "fp8attn_internal.h"
@@ -186,15 +186,19 @@ __global__ __launch_bounds__(256) void vc_step(ClusterParams p, int sums) {
     for (int k = 0; k < kTpt; k++) {
       if (lab[k] < 0) continue;
       atomicAdd(&cnt_s[lab[k]], 1);  // integer counts: order-free
-      if (p.ws_scount) atomicAdd(&scnt_s[sub][lab[k]], 1);
       if (p.labels) p.labels[bh * p.N + tb + k] = lab[k];
+      if (p.ws_scount) {
+        atomicAdd(&scnt_s[sub][lab[k]], 1);
+        p.ws_lab8[bh * p.lab_stride + tb + k] = static_cast<uint8_t>(lab[k]);
+      }
     }
     __syncthreads();
     if (tid < K) p.ws_ccount[(bh * p.n_chunks + c) * kMaxClusters + tid] = cnt_s[tid];
     if (p.ws_scount) {
       for (int i = tid; i < kSubs * K; i += 256) {
-        const int64_t s = c * kSubs + i / K;
-        if (s < p.n_sub) p.ws_scount[(bh * p.n_sub + s) * kMaxClusters + i % K] = scnt_s[i / K][i % K];
+        const int cl = i / kSubs;
+        const int64_t s = c * kSubs + i % kSubs;
+        if (s < p.n_sub) p.ws_scount[(bh * kMaxClusters + cl) * p.n_sub + s] = scnt_s[i % kSubs][cl];
       }
     }
     return;
@@ -289,32 +293,41 @@ __global__ __launch_bounds__(256) void vc_scatter(ClusterParams p) {
   }
 }
 
-// 7'. scatter index (grid B*H): per cluster, the tokens of the cluster before each sub-chunk
-// (sub-chunks in ascending order), and the first layout position of each cluster (clusters in
-// ascending order). Position off[c] + r holds the cluster's token of rank r, as in vc_scatter.
-__global__ __launch_bounds__(64) void vc_index(ClusterParams p) {
-  __shared__ int tot[kMaxClusters];
-  const int64_t bh = blockIdx.x;
-  const int c = threadIdx.x, K = p.n_clusters;
-  if (c < K) {
-    int32_t* sb = p.ws_sbase + (bh * K + c) * (p.n_sub + 1);
-    int run = 0;
-    for (int64_t s = 0; s < p.n_sub; s++) {
-      sb[s] = run;
-      run += p.ws_scount[(bh * p.n_sub + s) * kMaxClusters + c];
+// 7'. scatter index, grid (n_clusters, B*H): the tokens of cluster c before each sub-chunk
+// (exclusive prefix over the sub-chunks in ascending order, 256 at a time: wave scans, then the
+// four waves in order) and the cluster's total.
+__global__ __launch_bounds__(256) void vc_index(ClusterParams p) {
+  __shared__ int wsum[4];
+  const int c = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* cnt = p.ws_scount + (bh * kMaxClusters + c) * p.n_sub;
+  int32_t* sb = p.ws_sbase + (bh * kMaxClusters + c) * (p.n_sub + 1);
+  int carry = 0;
+  for (int64_t s0 = 0; s0 < p.n_sub; s0 += 256) {
+    const int64_t s = s0 + tid;
+    const int v = s < p.n_sub ? cnt[s] : 0;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      incl += lane >= d ? y : 0;
     }
-    sb[p.n_sub] = run;
-    tot[c] = run;
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      before += w < wave ? wsum[w] : 0;
+      total += wsum[w];
+    }
+    if (s < p.n_sub) sb[s] = carry + before + incl - v;
+    carry += total;
+    __syncthreads();  // (wsum is rewritten by the next pass)
   }
-  __syncthreads();
-  if (c == 0) {
-    int32_t* off = p.ws_coff + bh * (kMaxClusters + 1);
-    int o = 0;
-    for (int cl = 0; cl < K; cl++) {
-      off[cl] = o;
-      o += tot[cl];
-    }
-    off[K] = o;
+  if (tid == 0) {
+    sb[p.n_sub] = carry;
+    p.ws_ctot[bh * kMaxClusters + c] = carry;
   }
 }
 
@@ -332,7 +345,7 @@ hipError_t launch_cluster(const ClusterParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(vc_update, dim3(bh), dim3(512), 0, stream, p);
   }
   hipLaunchKernelGGL(vc_step, g, dim3(256), 0, stream, p, 0);
-  if (p.ws_scount) hipLaunchKernelGGL(vc_index, dim3(bh), dim3(64), 0, stream, p);
+  if (p.ws_scount) hipLaunchKernelGGL(vc_index, dim3(static_cast<unsigned>(p.n_clusters), bh), dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(vc_scatter, g, dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -36,11 +36,11 @@ struct QuantParams {
   // non-null): the statistics kernel places the tokens of each 128-row block from the cluster
   // labels and the scatter index of the clustering and writes them to perm_out, which is then
   // perm_kv (per head) of the other kernels
-  const int32_t* sc_labels;  // [B*H, N] cluster of each source token
-  const int32_t* sc_sbase;   // [B*H, sc_clusters, sc_nsub + 1]
-  const int32_t* sc_coff;    // [B*H, kMaxClusters + 1]
+  const uint8_t* sc_labels;  // [B*H, sc_lab_stride] cluster of each source token (a byte)
+  const int32_t* sc_sbase;   // [B*H, kMaxClusters, sc_nsub + 1]
+  const int32_t* sc_ctot;    // [B*H, kMaxClusters] tokens per cluster
   int32_t* perm_out;         // [B*H, N]
-  int64_t sc_nsub;
+  int64_t sc_nsub, sc_lab_stride;
   int sc_clusters;
 };
 
@@ -145,12 +145,13 @@ struct ClusterParams {
   double* ws_csum;     // [B*H, n_chunks, kMaxClusters, kMaxFeatures + 1] (sums, count)
   int32_t* ws_ccount;  // [B*H, n_chunks, kMaxClusters]
   // scatter index (instead of perm, for the preparation that fuses the stable scatter into the
-  // V block statistics), or null: tokens of each cluster per 256-token sub-chunk (final
-  // assignment), their exclusive prefix over the sub-chunks and the cluster offsets
-  int32_t* ws_scount;  // [B*H, n_sub, kMaxClusters]
-  int32_t* ws_sbase;   // [B*H, n_clusters, n_sub + 1]
-  int32_t* ws_coff;    // [B*H, kMaxClusters + 1]
-  int64_t N, n_chunks, n_sub;
+  // V block statistics), or null: the labels as bytes, the tokens of each cluster per 256-token
+  // sub-chunk (final assignment), their exclusive prefix over the sub-chunks and their total
+  uint8_t* ws_lab8;    // [B*H, lab_stride] (lab_stride = N rounded up to 16)
+  int32_t* ws_scount;  // [B*H, kMaxClusters, n_sub]
+  int32_t* ws_sbase;   // [B*H, kMaxClusters, n_sub + 1]
+  int32_t* ws_ctot;    // [B*H, kMaxClusters]
+  int64_t N, n_chunks, n_sub, lab_stride;
   int B, H;
   int n_clusters, n_feat, iters;
 };

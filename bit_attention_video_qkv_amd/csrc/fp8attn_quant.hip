@@ -236,24 +236,34 @@ __global__ __launch_bounds__(256) void quant_qk(QuantParams p) {
 }
 
 // The stable scatter of the V-Smooth clustering for one 128-row block j of the layout: layout
-// position off[c] + r holds the token of rank r (in token order) among the tokens of cluster c.
-// For each cluster whose positions meet the block, the ranks ra .. rb - 1 it needs are found by
-// scanning the labels from the sub-chunk that holds rank ra (sbase: the cluster's tokens before
-// each 256-token sub-chunk), 256 tokens per step, ranks by a workgroup prefix count of the matches.
+// position off[c] + r holds the token of rank r (in token order) among the tokens of cluster c,
+// off[c] = the tokens of the clusters below c. For each cluster whose positions meet the block,
+// the ranks ra .. rb - 1 it needs are found by scanning the byte labels from the 256-token
+// sub-chunk that holds rank ra (sbase: the cluster's tokens before each sub-chunk), 4096 labels
+// per step (16 per thread), ranks by a workgroup prefix count of the matches.
 // src_s[r] receives the token of position 128 j + r, or -1 beyond N.
-__device__ __forceinline__ void scatter_rows(const QuantParams& p, int64_t bh, int64_t j, int* src_s,
+__device__ __forceinline__ void scatter_rows(const QuantParams& p, int64_t bh, int64_t j, int* src_s, int* off_s,
                                              int* wtot_s, int* s0_s) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t i0 = j * kVBlock, i1 = min<int64_t>(p.N, i0 + kVBlock);
+  const int K = p.sc_clusters;
   if (tid < kVBlock) src_s[tid] = -1;
-  const int32_t* coff = p.sc_coff + bh * (kMaxClusters + 1);
-  const int32_t* lab = p.sc_labels + bh * p.N;
-  for (int c = 0; c < p.sc_clusters; c++) {
-    const int64_t oc = coff[c];
-    const int64_t lo = max<int64_t>(i0, oc), hi = min<int64_t>(i1, static_cast<int64_t>(coff[c + 1]));
+  if (tid == 0) {
+    int o = 0;
+    for (int c = 0; c < K; c++) {
+      off_s[c] = o;
+      o += p.sc_ctot[bh * kMaxClusters + c];
+    }
+    off_s[K] = o;
+  }
+  __syncthreads();
+  const uint8_t* lab = p.sc_labels + bh * p.sc_lab_stride;
+  for (int c = 0; c < K; c++) {
+    const int64_t oc = off_s[c];
+    const int64_t lo = max<int64_t>(i0, oc), hi = min<int64_t>(i1, static_cast<int64_t>(off_s[c + 1]));
     if (lo >= hi) continue;  // (uniform: every thread reads the same offsets)
     const int ra = static_cast<int>(lo - oc), rb = static_cast<int>(hi - oc);
-    const int32_t* sb = p.sc_sbase + (bh * p.sc_clusters + c) * (p.sc_nsub + 1);
+    const int32_t* sb = p.sc_sbase + (bh * kMaxClusters + c) * (p.sc_nsub + 1);
     __syncthreads();  // (s0_s and wtot_s of the previous cluster are read)
     if (tid == 0) *s0_s = static_cast<int>(p.sc_nsub);
     __syncthreads();
@@ -262,21 +272,39 @@ __device__ __forceinline__ void scatter_rows(const QuantParams& p, int64_t bh, i
     __syncthreads();
     const int64_t s0 = *s0_s;
     int base = s0 < p.sc_nsub ? sb[s0] : rb;
-    for (int64_t t0 = s0 * kClusterSub; base < rb && t0 < p.N; t0 += 256) {
-      const int64_t t = t0 + tid;
-      const bool m = t < p.N && lab[t] == c;
-      const uint64_t bal = __ballot(m);
-      if (lane == 0) wtot_s[wave] = __popcll(bal);
+    for (int64_t t0 = s0 * kClusterSub; base < rb && t0 < p.N; t0 += 16 * 256) {
+      // this thread's 16 labels (the row is padded to 16 bytes, so a load that starts below N
+      // stays inside it)
+      const int64_t tb = t0 + 16 * tid;
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (tb < p.N) w = *reinterpret_cast<const uint4*>(lab + tb);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      uint32_t mbits = 0;  // bit k: label tb + k is cluster c
+#pragma unroll
+      for (int k = 0; k < 16; k++)
+        mbits |= (tb + k < p.N && ((ww[k >> 2] >> (8 * (k & 3))) & 0xFFu) == static_cast<uint32_t>(c)) ? 1u << k : 0u;
+      const int cnt = __popc(mbits);
+      int incl = cnt;  // inclusive prefix over the wave's lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        incl += lane >= d ? y : 0;
+      }
+      if (lane == 63) wtot_s[wave] = incl;
       __syncthreads();
       int before = 0, total = 0;
 #pragma unroll
-      for (int w = 0; w < 4; w++) {
-        const int n = wtot_s[w];
-        before += w < wave ? n : 0;
-        total += n;
+      for (int q = 0; q < 4; q++) {
+        before += q < wave ? wtot_s[q] : 0;
+        total += wtot_s[q];
       }
-      const int rank = base + before + __popcll(bal & ((1ull << lane) - 1ull));
-      if (m && rank >= ra && rank < rb) src_s[oc + rank - i0] = static_cast<int>(t);
+      int rank = base + before + incl - cnt;
+      while (mbits) {
+        const int k = __ffs(mbits) - 1;
+        mbits &= mbits - 1u;
+        if (rank >= ra && rank < rb) src_s[oc + rank - i0] = static_cast<int>(tb + k);
+        rank++;
+      }
       base += total;
       __syncthreads();  // (wtot_s is rewritten by the next step)
     }
@@ -295,6 +323,7 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
   __shared__ float mhat_s[kHeadDim];
   __shared__ int n_valid_s;
   __shared__ int src_s[SCATTER ? kVBlock : 1];
+  __shared__ int off_s[SCATTER ? kMaxClusters + 1 : 1];
   __shared__ int wtot_s[4], s0_s;
   const int64_t j = blockIdx.x;
   const int64_t bh = blockIdx.y;
@@ -303,7 +332,7 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
   const int rg = threadIdx.x >> 4;
   if (threadIdx.x == 0) n_valid_s = 0;
   if constexpr (SCATTER) {
-    scatter_rows(p, bh, j, src_s, wtot_s, &s0_s);  // (ends with a barrier)
+    scatter_rows(p, bh, j, src_s, off_s, wtot_s, &s0_s);  // (ends with a barrier)
     const int64_t i = j * kVBlock + threadIdx.x;
     if (threadIdx.x < kVBlock && i < p.N) p.perm_out[bh * p.N + i] = src_s[threadIdx.x];
   } else {
