@@ -28,7 +28,7 @@ ATTN_SRC = os.path.join(ROOT, "bit_attention_video_qkv_amd", "csrc", "fp8attn_at
 # HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) as measured by
 # rocprofv3 for the attention source whose code (comments and blank lines dropped) has this
 # sha256 prefix, per workload; see profiles/. Reported only while that code is unchanged.
-MEASURED_TRAFFIC = {("6cb74686cb9c", "wan14b"): 17006662916}
+MEASURED_TRAFFIC = {("f28753a2c890", "wan14b"): 17644241715}
 
 
 def code_sha(path):
@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--sol-estimator", type=int, default=0, choices=(0, 1),
                     help="Sol threshold estimator: 0 diag, 1 exact")
     ap.add_argument("--sol-sinks", type=int, default=1, help="Sol: leading KV blocks always exact")
+    ap.add_argument("--pcast", default="default", choices=("default", "rne", "expcast"),
+                    help="P cast: the standard E4M3 RNE cast of S*exp, or the ExpCast codes "
+                         "(default: ExpCast with V-Smooth, as the V-Smooth configuration, else RNE)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -113,6 +116,9 @@ def main():
         return
 
     cfg_name, sparse, vs, desc = WORKLOADS[args.workload]
+    expcast = vs if args.pcast == "default" else args.pcast == "expcast"
+    if expcast != vs:
+        desc += "; ExpCast P codes" if expcast else "; standard P cast"
     kv_splits = fa.FP8ATTN_KV_SPLITS_AUTO if args.kv_splits == "auto" else int(args.kv_splits)
     if sparse and kv_splits > 1:
         print("split-KV is for dense workloads", file=sys.stderr)
@@ -185,7 +191,7 @@ def main():
     ws_q = fa.quantize_workspace(B, n_layout, H, vs, dev)
     ws_f = fa.forward_workspace(B, n_layout, H, vs, dev, 1 if sparse else kv_splits)
     out = torch.zeros((B, n_out, H, D), dtype=torch.bfloat16, device=dev)
-    pcast = fa.FP8ATTN_PCAST_EXPCAST if vs else fa.FP8ATTN_PCAST_RNE
+    pcast = fa.FP8ATTN_PCAST_EXPCAST if expcast else fa.FP8ATTN_PCAST_RNE
 
     ws_sol = fa.sol_workspace(B, n_layout, H, dev) if sol else None
 
@@ -280,7 +286,7 @@ def main():
         "config": {"workload": desc, "global_batch": B, "seq_len": N, "heads": H, "head_dim": D,
                    "parallelism": "none (one GPU)", "name": args.workload,
                    "smoothing": args.smoothing, "v_bias_correction": args.bias_correction,
-                   "kv_splits": args.kv_splits,
+                   "kv_splits": args.kv_splits, "pcast": "expcast" if expcast else "rne",
                    "sol": None if not sol else {"tau": args.sol_tau, "estimator": args.sol_estimator,
                                                  "sink_blocks": args.sol_sinks}},
         "quantize_ms": round(ms_quant, 4),
@@ -306,7 +312,7 @@ def main():
         result["roofline"]["kernel"] = "fp8attn_sol_forward (all kernels)"
         result["roofline"]["traffic"] = None
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(args, cfg_name, sparse, vs)
+        result["cpu_baseline"] = cpu_baseline(args, cfg_name, sparse, vs, expcast)
     print(json.dumps(result), flush=True)
 
 
@@ -322,7 +328,7 @@ def calibrate_copy(torch, nbytes=1 << 30, reps=3):
     print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def cpu_baseline(args, cfg_name, sparse, vs):
+def cpu_baseline(args, cfg_name, sparse, vs, expcast):
     """The oracle as it stands on the host cores: quantisation of one head plus the attention
     of a bounded sample of that head's query rows, scaled to TFLOP/s."""
     import numpy as np
@@ -350,7 +356,7 @@ def cpu_baseline(args, cfg_name, sparse, vs):
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(Nl, rows_n, replace=False)).astype(np.int32)
     t1 = time.time()
-    oracle.attention_fp8(qz, rows=rows, kv_reverse=True, expcast=vs, sparse=lay)
+    oracle.attention_fp8(qz, rows=rows, kv_reverse=True, expcast=expcast, sparse=lay)
     t_attn = time.time() - t1
     flops = 4.0 * rows_n * N * D            # dense-equivalent work of the sampled rows
     return {"value": round(flops / t_attn / 1e12, 6), "unit": "TFLOP/s",
