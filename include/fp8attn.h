@@ -14,8 +14,12 @@
  *  - V-Smooth and ExpCast: VC-Attention article, sections 二 and 三.
  *
  * Conventions shared by every entry point:
- *  - Device pointers are caller-owned device memory; the library never allocates device
- *    memory, never synchronises, and keeps no mutable global state (thread-safe).
+ *  - Device pointers are caller-owned device memory; no call allocates device memory or
+ *    synchronises. The only global state is write-once per device and held in atomics: the
+ *    result of the gfx950 check and the device address of fp8attn_forward_noalloc's scratch
+ *    array (a module array the loader places on each device). Every entry point is
+ *    thread-safe; calls of fp8attn_forward_noalloc that overlap on one device race on its
+ *    scratch.
  *  - Work is enqueued on the caller's `stream`; outputs are valid when the stream reaches it.
  *  - Argument checks are synchronous and happen before any launch: on error nothing is
  *    enqueued and FP8ATTN_EINVAL / FP8ATTN_EUNSUPPORTED is returned. A failed launch returns
