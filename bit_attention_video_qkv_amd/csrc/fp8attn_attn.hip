@@ -618,23 +618,30 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
       // The row sums come from the matrix cores (pv).
       const float c8 = 8.0f * cs;
       const float b8 = 8.0f * (p.log2S - m_new) + 55.65f;
+      // key half by key half, as in the standard cast: the QK MFMAs of the next block's key
+      // half t take over half t's registers once its bytes exist and run beside the other
+      // half's codes
 #pragma unroll
-      for (int w = 0; w < 8; w++) {
-        uint32_t word = static_cast<uint32_t>(pop[w]);  // every byte is overwritten
+      for (int t = 0; t < 2; t++) {
 #pragma unroll
-        for (int q = 0; q < 4; q++) word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(x[4 * w + q], c8, b8), q, word);
-        pop[w] = static_cast<int>(word);
+        for (int w = 4 * t; w < 4 * t + 4; w++) {
+          uint32_t word = static_cast<uint32_t>(pop[w]);  // every byte is overwritten
+#pragma unroll
+          for (int q = 0; q < 4; q++) word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(x[4 * w + q], c8, b8), q, word);
+          pop[w] = static_cast<int>(word);
+        }
+        tie_k(t, lsum);
+        if (t == 0) interleave_region1();
+        else interleave_region2();
+        issue_qk_half(t);
       }
       if (__builtin_expect(__any(__builtin_fmaf(xrow, c8, b8) > 126.5f), 0)) {
-        // (rare) min(rint(t), 126) = rint(min(t, 126)): clamp the bytes themselves
+        // (rare) min(rint(t), 126) = rint(min(t, 126)): clamp the bytes themselves (after the
+        // QK issue, so that the branch does not split the scheduling regions; only the row-sum
+        // and PV MFMAs, later, read the bytes)
 #pragma unroll
         for (int w = 0; w < 8; w++) pop[w] = static_cast<int>(clamp_bytes_126(static_cast<uint32_t>(pop[w])));
       }
-      tie_k(0, lsum);
-      tie_k(1, lsum);
-      interleave_region1();
-      issue_qk_half(0);
-      issue_qk_half(1);
     } else {
       const float bias = p.log2S - m_new;
       // key sub-tile by key sub-tile (t = 0: x[0..15], t = 1: x[16..31]), so that the QK MFMAs of
