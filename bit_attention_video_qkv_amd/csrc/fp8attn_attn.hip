@@ -618,6 +618,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
       // The row sums come from the matrix cores (pv).
       const float c8 = 8.0f * cs;
       const float b8 = 8.0f * (p.log2S - m_new) + 55.65f;
+      const bool clamp = __builtin_expect(__any(__builtin_fmaf(xrow, c8, b8) > 126.5f), 0);  // (uniform)
       // key half by key half, as in the standard cast: the QK MFMAs of the next block's key
       // half t take over half t's registers once its bytes exist and run beside the other
       // half's codes
@@ -635,7 +636,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
         else interleave_region2();
         issue_qk_half(t);
       }
-      if (__builtin_expect(__any(__builtin_fmaf(xrow, c8, b8) > 126.5f), 0)) {
+      if (clamp) {
         // (rare) min(rint(t), 126) = rint(min(t, 126)): clamp the bytes themselves (after the
         // QK issue, so that the branch does not split the scheduling regions; only the row-sum
         // and PV MFMAs, later, read the bytes)
@@ -989,10 +990,10 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   }
 }
 
-// Variants whose workgroups take their items from the per-XCD queues (the others would spill
-// registers in the loop around attn_tile).
+// Variants whose workgroups take their items from the per-XCD queues (the underflow-counting
+// debugging variant would spill registers in the loop around attn_tile).
 template <bool VSMOOTH, bool STATS, bool SOL>
-constexpr bool kQueued = !VSMOOTH && !STATS;
+constexpr bool kQueued = !STATS;
 
 // The work items are cut into eight contiguous ranges, one per XCD, so that the workgroups of
 // an XCD share the K/V tiles of few (b, h) in its L2. Queued variants: persistent workgroups
