@@ -519,12 +519,12 @@ struct ClusterLayout {
   size_t feat, labels, part1, part2, featsel, cent, csum, ccount, lab8, scount, sbase, ctot, total;
 };
 
-// with_index: also the scatter index of the fused preparation (sub-chunk counts, their prefix,
-// cluster offsets)
+// with_index: also the byte labels of the fused preparation
 ClusterLayout cluster_layout(int32_t B, int32_t N, int32_t H, int32_t n_feat, bool with_index = false) {
   ClusterLayout L;
   const size_t bh = static_cast<size_t>(B) * H;
   const size_t nc = static_cast<size_t>(fp8attn::cluster_chunks(N));
+  const size_t nsc = static_cast<size_t>(fp8attn::cluster_step_chunks(N));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -537,16 +537,13 @@ ClusterLayout cluster_layout(int32_t B, int32_t N, int32_t H, int32_t n_feat, bo
   L.part2 = take(bh * nc * kHeadDim * sizeof(double));
   L.featsel = take(bh * fp8attn::kMaxFeatures * sizeof(int32_t));
   L.cent = take(bh * fp8attn::kMaxClusters * fp8attn::kMaxFeatures * sizeof(double));
-  L.csum = take(bh * nc * fp8attn::kMaxClusters * (fp8attn::kMaxFeatures + 1) * sizeof(double));
-  L.ccount = take(bh * nc * fp8attn::kMaxClusters * sizeof(int32_t));
-  L.lab8 = L.scount = L.sbase = L.ctot = 0;
-  if (with_index) {
-    const size_t ns = static_cast<size_t>(cdiv(N, fp8attn::kClusterSub));
-    L.lab8 = take(bh * static_cast<size_t>(cdiv(N, 16) * 16));
-    L.scount = take(bh * fp8attn::kMaxClusters * ns * sizeof(int32_t));
-    L.sbase = take(bh * fp8attn::kMaxClusters * (ns + 1) * sizeof(int32_t));
-    L.ctot = take(bh * fp8attn::kMaxClusters * sizeof(int32_t));
-  }
+  L.csum = take(bh * nsc * fp8attn::kMaxClusters * (fp8attn::kMaxFeatures + 1) * sizeof(double));
+  L.ccount = take(bh * nsc * fp8attn::kMaxClusters * sizeof(int32_t));
+  const size_t ns = static_cast<size_t>(cdiv(N, fp8attn::kClusterSub));
+  L.scount = take(bh * fp8attn::kMaxClusters * ns * sizeof(int32_t));
+  L.sbase = take(bh * fp8attn::kMaxClusters * (ns + 1) * sizeof(int32_t));
+  L.ctot = take(bh * fp8attn::kMaxClusters * sizeof(int32_t));
+  L.lab8 = with_index ? take(bh * static_cast<size_t>(cdiv(N, 16) * 16)) : 0;
   L.total = off;
   return L;
 }
@@ -573,13 +570,12 @@ void cluster_params(fp8attn::ClusterParams* cp, const ClusterLayout& L, void* wo
   p.ws_cent = reinterpret_cast<double*>(ws + L.cent);
   p.ws_csum = reinterpret_cast<double*>(ws + L.csum);
   p.ws_ccount = reinterpret_cast<int32_t*>(ws + L.ccount);
-  if (L.scount) {
-    p.ws_lab8 = reinterpret_cast<uint8_t*>(ws + L.lab8);
-    p.ws_scount = reinterpret_cast<int32_t*>(ws + L.scount);
-    p.ws_sbase = reinterpret_cast<int32_t*>(ws + L.sbase);
-    p.ws_ctot = reinterpret_cast<int32_t*>(ws + L.ctot);
-  }
+  p.ws_scount = reinterpret_cast<int32_t*>(ws + L.scount);
+  p.ws_sbase = reinterpret_cast<int32_t*>(ws + L.sbase);
+  p.ws_ctot = reinterpret_cast<int32_t*>(ws + L.ctot);
+  p.ws_lab8 = L.lab8 ? reinterpret_cast<uint8_t*>(ws + L.lab8) : nullptr;
   p.n_chunks = fp8attn::cluster_chunks(N);
+  p.n_schunks = fp8attn::cluster_step_chunks(N);
   p.n_sub = cdiv(N, fp8attn::kClusterSub);
   p.lab_stride = cdiv(N, 16) * 16;
   p.N = N;

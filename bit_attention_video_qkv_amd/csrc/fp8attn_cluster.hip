@@ -11,20 +11,25 @@
 //     in FP64, ties to the lower cluster id; an empty cluster keeps its centroid;
 //   * perm = the head's tokens stably sorted by cluster id.
 //
-// Work is split into chunks of kChunk tokens (many workgroups per head); partial results are
-// combined in ascending chunk order, so every result is deterministic. The features are bf16
-// values: sums of them in FP64 are exact for any realistic value range (fewer than 2^21 tokens
-// of 8-bit mantissas spanning under 24 binades), which makes the means and centroids independent
-// of the summation order. Distances are formed with separately rounded products (never fused).
+// Work is split into chunks of tokens (many workgroups per head): kChunk tokens for the channel
+// statistics and the gather, kStepChunk for the assignment and the scatter. Partial results are
+// combined in ascending chunk order, and a cluster's sums inside a chunk in token order, so every
+// result is deterministic. The features are bf16 values: sums of them in FP64 are exact for any
+// realistic value range (fewer than 2^21 tokens of 8-bit mantissas spanning under 24 binades),
+// which makes the means and centroids independent of the summation order. Distances are formed
+// with separately rounded products (never fused).
 //
 // Kernels per head (b, h), grids (chunks, B*H) unless noted:
 //   vc_colsum   channel sums per chunk                     vc_sqdev  centred sums of squares
 //   vc_select   (B*H): variances, feature choice, initial centroids
 //   vc_gather   the selected features of every token (FP32)
-//   vc_step     assignment (+ per-chunk cluster sums, or the final per-chunk counts)
-//   vc_update   (B*H): centroids from the chunk sums          vc_scatter  stable scatter
-//   vc_index    (n_clusters, B*H): instead of vc_scatter, the scatter index from which the V block
-//               statistics of the quantisation place the tokens themselves
+//   vc_step     (step chunks) assignment (+ per-chunk cluster sums, or the final per-chunk and
+//               per-sub-chunk counts)
+//   vc_update   (B*H): centroids from the chunk sums
+//   vc_index    (n_clusters, B*H): the scatter index (per cluster, the tokens before each
+//               256-token sub-chunk, and the total)
+//   vc_scatter  (step chunks) stable scatter into perm; the fused preparation skips it, and the
+//               V block statistics of the quantisation place the tokens from the index
 #include "fp8attn_common.h"
 #include "fp8attn_internal.h"
 
@@ -32,14 +37,13 @@ namespace fp8attn {
 
 namespace {
 
-constexpr int kChunk = 2048;  // tokens per chunk
-constexpr int kTpt = kChunk / 256;  // tokens per thread in vc_step / vc_scatter (contiguous)
+constexpr int kChunk = 2048;     // tokens per chunk of the channel statistics and the gather
+constexpr int kStepChunk = 512;  // tokens per chunk of the assignment and the scatter (2 per thread)
 
-__device__ __forceinline__ double dmul_rounded(double a, double b) {
-  double p = a * b;
-  asm volatile("" : "+v"(p));
-  return p;
-}
+// fl(a * b), rounded on its own: an FMA with an exact zero addend rounds the exact product once,
+// and the compiler neither drops it nor fuses it with the add that follows (as it would fuse a
+// plain product), so no scheduling barrier is needed.
+__device__ __forceinline__ double dmul_rounded(double a, double b) { return __builtin_fma(a, b, 0.0); }
 
 __device__ __forceinline__ float vval(const ClusterParams& p, int64_t bh, int64_t t, int d) {
   const int64_t b = bh / p.H, h = bh % p.H;
@@ -80,7 +84,8 @@ __global__ __launch_bounds__(256) void vc_sqdev(ClusterParams p) {
   if (half == 0) p.ws_part2[(bh * p.n_chunks + c) * kHeadDim + d] = acc + red[d];
 }
 
-// 3. variances -> the n_feat largest (first channel on ties), ascending; initial centroids.
+// 3. variances -> the n_feat largest (the lower channel first on ties), ascending; initial
+// centroids.
 __global__ __launch_bounds__(kHeadDim) void vc_select(ClusterParams p) {
   __shared__ double var[kHeadDim];
   __shared__ int feat[kMaxFeatures];
@@ -90,23 +95,22 @@ __global__ __launch_bounds__(kHeadDim) void vc_select(ClusterParams p) {
   double s = 0.0;
   for (int64_t k = 0; k < p.n_chunks; k++) s += p.ws_part2[(bh * p.n_chunks + k) * kHeadDim + d];
   var[d] = s / static_cast<double>(p.N);
-  taken[d] = false;
   __syncthreads();
-  if (d == 0) {
-    for (int f = 0; f < p.n_feat; f++) {
-      int best = -1;
-      for (int c = 0; c < kHeadDim; c++)
-        if (!taken[c] && (best < 0 || var[c] > var[best])) best = c;
-      taken[best] = true;
-      feat[f] = best;
-    }
-    for (int i = 1; i < p.n_feat; i++)  // insertion sort, ascending
-      for (int j = i; j > 0 && feat[j - 1] > feat[j]; j--) {
-        const int tmp = feat[j];
-        feat[j] = feat[j - 1];
-        feat[j - 1] = tmp;
-      }
-    for (int f = 0; f < p.n_feat; f++) p.ws_featsel[bh * kMaxFeatures + f] = feat[f];
+  // channel d is chosen when fewer than n_feat channels rank above it (a larger variance, or an
+  // equal one at a lower channel); the chosen ones take their places in ascending channel order
+  int rank = 0;
+  const double vd = var[d];
+  for (int c = 0; c < kHeadDim; c++) {
+    const double vc = var[c];
+    rank += (vc > vd || (vc == vd && c < d)) ? 1 : 0;
+  }
+  taken[d] = rank < p.n_feat;
+  __syncthreads();
+  if (taken[d]) {
+    int pos = 0;
+    for (int c = 0; c < d; c++) pos += taken[c] ? 1 : 0;
+    feat[pos] = d;
+    p.ws_featsel[bh * kMaxFeatures + pos] = d;
   }
   __syncthreads();
   for (int i = d; i < p.n_clusters * p.n_feat; i += kHeadDim) {
@@ -128,106 +132,117 @@ __global__ __launch_bounds__(256) void vc_gather(ClusterParams p) {
   }
 }
 
-// 5. assignment of the chunk's tokens (thread i: tokens t0 + kTpt*i .. +kTpt-1). With sums: per
-// cluster, the chunk's feature sums and count (wave butterflies, then the 4 waves in order).
-// Final step (sums = 0): the chunk's count per cluster, the labels output and, for the scatter
-// index, the count per cluster of each 256-token sub-chunk (threads 32 s .. 32 s + 31 hold the
-// tokens of sub-chunk s of the chunk).
+// 5. assignment of a step chunk's tokens (thread i: tokens i and i + 256 of the chunk), the
+// clusters visited in ascending order with each centroid read once per thread. With sums: the
+// chunk's feature sums and count per cluster, each by one thread that walks the chunk's tokens in
+// order (labels and features staged in LDS), so a cluster's sums accumulate in token order.
+// Final step (sums = 0): the chunk's count per cluster, the labels output, the count per cluster
+// of each 256-token sub-chunk and, for the fused preparation, the labels as bytes.
+// KF: the feature count when fixed at compile time (8, the default), else 0 (n_feat, up to 16).
+template <int KF>
 __global__ __launch_bounds__(256) void vc_step(ClusterParams p, int sums) {
-  constexpr int kSubs = kChunk / kClusterSub;
-  static_assert(kChunk % kClusterSub == 0 && kClusterSub % kTpt == 0, "sub-chunks of whole threads");
+  constexpr int kSubs = kStepChunk / kClusterSub;
+  constexpr int kFM = KF ? KF : kMaxFeatures;  // feature slots
+  static_assert(kStepChunk == 2 * 256 && kStepChunk % kClusterSub == 0, "two tokens per thread");
   __shared__ double cent[kMaxClusters * kMaxFeatures];
-  __shared__ double wred[4][kMaxFeatures + 1];
+  __shared__ float feat_s[kStepChunk][kFM + 1];  // (+1: column walks stay conflict-free)
+  __shared__ __attribute__((aligned(16))) int lab_s[kStepChunk];
   __shared__ int cnt_s[kMaxClusters];
   __shared__ int scnt_s[kSubs][kMaxClusters];
   const int64_t c = blockIdx.x, bh = blockIdx.y;
-  const int K = p.n_clusters, F = p.n_feat;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = p.n_clusters, F = KF ? KF : p.n_feat;
+  const int tid = threadIdx.x;
   for (int i = tid; i < K * kMaxFeatures; i += 256) cent[i] = p.ws_cent[bh * kMaxClusters * kMaxFeatures + i];
   if (tid < kMaxClusters) cnt_s[tid] = 0;
   if (tid < kSubs * kMaxClusters) scnt_s[tid / kMaxClusters][tid % kMaxClusters] = 0;
-  __syncthreads();
-  const int64_t tb = c * kChunk + static_cast<int64_t>(tid) * kTpt;
+  const int64_t t0 = c * kStepChunk;
   const float* fv = p.ws_feat + bh * p.N * F;
-  // the thread's tokens' features, loaded once (zero beyond n_feat and past N)
-  float fx[kTpt][kMaxFeatures];
+  // the thread's two tokens' features: every load is unconditional (addresses clamped into the
+  // head's features; a token past N reads the last one, and its label is dropped), so all are in
+  // flight before any is used; the features beyond n_feat are multiplied to zero
+  float fx[2][kFM];
 #pragma unroll
-  for (int k = 0; k < kTpt; k++)
+  for (int k = 0; k < 2; k++) {
+    const int64_t t = t0 + tid + 256 * k;
+    const int64_t tc = t < p.N ? t : p.N - 1;
 #pragma unroll
-    for (int f = 0; f < kMaxFeatures; f++) fx[k][f] = (tb + k < p.N && f < F) ? fv[(tb + k) * F + f] : 0.0f;
-  int lab[kTpt];
+    for (int f = 0; f < kFM; f++) {
+      if constexpr (KF != 0) fx[k][f] = fv[tc * F + f];
+      else fx[k][f] = fv[tc * F + (f < F ? f : F - 1)] * (f < F ? 1.0f : 0.0f);
+    }
+  }
+  if (sums) {
 #pragma unroll
-  for (int k = 0; k < kTpt; k++) {
-    const int64_t t = tb + k;
-    lab[k] = -1;
-    if (t >= p.N) continue;
-    int best = 0;
-    double bd = INFINITY;
-    for (int cl = 0; cl < K; cl++) {
+    for (int k = 0; k < 2; k++)
+#pragma unroll
+      for (int f = 0; f < kFM; f++) feat_s[tid + 256 * k][f] = fx[k][f];
+  }
+  __syncthreads();
+  // squared distances with separately rounded products, features in ascending order; the first
+  // cluster of the smallest distance wins
+  int best[2] = {0, 0};
+  double bd[2] = {INFINITY, INFINITY};
+  for (int cl = 0; cl < K; cl++) {
+    double cv[kFM];
+#pragma unroll
+    for (int f = 0; f < kFM; f++) cv[f] = f < F ? cent[cl * kMaxFeatures + f] : 0.0;
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      // (a feature beyond n_feat adds +0 to the sum, which starts at +0: no effect)
       double dist = 0.0;
 #pragma unroll
-      for (int f = 0; f < kMaxFeatures; f++) {
-        if (f < F) {
-          const double diff = static_cast<double>(fx[k][f]) - cent[cl * kMaxFeatures + f];
-          dist += dmul_rounded(diff, diff);
-        }
+      for (int f = 0; f < kFM; f++) {
+        const double diff = static_cast<double>(fx[k][f]) - cv[f];
+        dist += dmul_rounded(diff, diff);
       }
-      if (dist < bd) {
-        bd = dist;
-        best = cl;
+      if (dist < bd[k]) {
+        bd[k] = dist;
+        best[k] = cl;
       }
     }
-    lab[k] = best;
-    p.ws_labels[bh * p.N + t] = best;
   }
-  if (!sums) {
-    const int sub = tid / (kClusterSub / kTpt);
 #pragma unroll
-    for (int k = 0; k < kTpt; k++) {
-      if (lab[k] < 0) continue;
-      atomicAdd(&cnt_s[lab[k]], 1);  // integer counts: order-free
-      if (p.labels) p.labels[bh * p.N + tb + k] = lab[k];
-      if (p.ws_scount) {
-        atomicAdd(&scnt_s[sub][lab[k]], 1);
-        p.ws_lab8[bh * p.lab_stride + tb + k] = static_cast<uint8_t>(lab[k]);
-      }
+  for (int k = 0; k < 2; k++) {
+    const int lt = tid + 256 * k;
+    const int64_t t = t0 + lt;
+    const int lab = t < p.N ? best[k] : -1;
+    lab_s[lt] = lab;
+    if (lab < 0) continue;
+    p.ws_labels[bh * p.N + t] = lab;
+    if (!sums) {
+      atomicAdd(&cnt_s[lab], 1);  // integer counts: order-free
+      atomicAdd(&scnt_s[lt / kClusterSub][lab], 1);
+      if (p.labels) p.labels[bh * p.N + t] = lab;
+      if (p.ws_lab8) p.ws_lab8[bh * p.lab_stride + t] = static_cast<uint8_t>(lab);
     }
-    __syncthreads();
-    if (tid < K) p.ws_ccount[(bh * p.n_chunks + c) * kMaxClusters + tid] = cnt_s[tid];
-    if (p.ws_scount) {
-      for (int i = tid; i < kSubs * K; i += 256) {
-        const int cl = i / kSubs;
-        const int64_t s = c * kSubs + i % kSubs;
-        if (s < p.n_sub) p.ws_scount[(bh * kMaxClusters + cl) * p.n_sub + s] = scnt_s[i % kSubs][cl];
-      }
+  }
+  __syncthreads();
+  if (!sums) {
+    if (tid < K) p.ws_ccount[(bh * p.n_schunks + c) * kMaxClusters + tid] = cnt_s[tid];
+    for (int i = tid; i < kSubs * K; i += 256) {
+      const int cl = i / kSubs;
+      const int64_t sub = c * kSubs + i % kSubs;
+      if (sub < p.n_sub) p.ws_scount[(bh * kMaxClusters + cl) * p.n_sub + sub] = scnt_s[i % kSubs][cl];
     }
     return;
   }
-  for (int cl = 0; cl < K; cl++) {
-    double part[kMaxFeatures + 1];
+  // one (cluster, feature or count) per thread, the chunk's tokens in order; eight tokens' labels
+  // and values are read before their adds, and a token of another cluster adds +0 (the sum
+  // starts at +0 and so is never -0, so that leaves it unchanged)
+  for (int i = tid; i < K * (F + 1); i += 256) {
+    const int cl = i / (F + 1), f = i % (F + 1);
+    double acc = 0.0;
+    for (int lt = 0; lt < kStepChunk; lt += 8) {
+      const int4 la = *reinterpret_cast<const int4*>(&lab_s[lt]);
+      const int4 lb = *reinterpret_cast<const int4*>(&lab_s[lt + 4]);
+      const int l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+      float v8[8];
 #pragma unroll
-    for (int f = 0; f <= kMaxFeatures; f++) part[f] = 0.0;
+      for (int u = 0; u < 8; u++) v8[u] = f < F ? feat_s[lt + u][f] : 1.0f;
 #pragma unroll
-    for (int k = 0; k < kTpt; k++) {
-      if (lab[k] != cl) continue;
-#pragma unroll
-      for (int f = 0; f < kMaxFeatures; f++) part[f] += static_cast<double>(fx[k][f]);
-      part[kMaxFeatures] += 1.0;
+      for (int u = 0; u < 8; u++) acc += l8[u] == cl ? static_cast<double>(v8[u]) : 0.0;
     }
-#pragma unroll
-    for (int f = 0; f <= kMaxFeatures; f++) {
-      if (f < F || f == kMaxFeatures) {
-        double x = part[f];
-        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-        if (lane == 0) wred[wave][f == kMaxFeatures ? F : f] = x;
-      }
-    }
-    __syncthreads();
-    if (tid <= F) {
-      const double tot = ((wred[0][tid] + wred[1][tid]) + wred[2][tid]) + wred[3][tid];
-      p.ws_csum[((bh * p.n_chunks + c) * kMaxClusters + cl) * (kMaxFeatures + 1) + tid] = tot;
-    }
-    __syncthreads();
+    p.ws_csum[((bh * p.n_schunks + c) * kMaxClusters + cl) * (kMaxFeatures + 1) + f] = acc;
   }
 }
 
@@ -239,35 +254,48 @@ __global__ __launch_bounds__(512) void vc_update(ClusterParams p) {
   if (i >= p.n_clusters * F) return;
   const int cl = i / F, f = i % F;
   double s = 0.0, n = 0.0;
-  for (int64_t k = 0; k < p.n_chunks; k++) {
-    const double* row = p.ws_csum + ((bh * p.n_chunks + k) * kMaxClusters + cl) * (kMaxFeatures + 1);
-    s += row[f];
-    n += row[F];
+  const int64_t stride = kMaxClusters * (kMaxFeatures + 1);
+  const double* col = p.ws_csum + (bh * p.n_schunks * kMaxClusters + cl) * (kMaxFeatures + 1);
+  for (int64_t k0 = 0; k0 < p.n_schunks; k0 += 8) {  // eight chunks' loads in flight, adds in order
+    double a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int64_t k = k0 + u < p.n_schunks ? k0 + u : p.n_schunks - 1;
+      a[u] = col[k * stride + f];
+      b[u] = col[k * stride + F];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      if (k0 + u < p.n_schunks) {
+        s += a[u];
+        n += b[u];
+      }
+    }
   }
   if (n > 0.0) p.ws_cent[(bh * kMaxClusters + cl) * kMaxFeatures + f] = s / n;
 }
 
-// 7. stable scatter: positions ordered by (cluster, token). Base of (cluster, chunk) = tokens of
-// lower clusters + tokens of this cluster in earlier chunks; inside the chunk, thread i's
-// contiguous tokens come after those of threads < i.
+// 7. stable scatter: positions ordered by (cluster, token). The base of (cluster, step chunk) is
+// the tokens of the lower clusters plus this cluster's tokens before the chunk (the scatter
+// index: cluster totals and the prefix at the chunk's first sub-chunk); inside the chunk, thread
+// i's two consecutive tokens come after those of threads < i.
 __global__ __launch_bounds__(256) void vc_scatter(ClusterParams p) {
+  constexpr int kSubs = kStepChunk / kClusterSub;
   __shared__ int base[kMaxClusters];
   __shared__ int scan[kMaxClusters][257];
   const int64_t c = blockIdx.x, bh = blockIdx.y;
   const int K = p.n_clusters, tid = threadIdx.x;
   if (tid < K) {
     int before = 0;
-    for (int cl = 0; cl < tid; cl++)
-      for (int64_t k = 0; k < p.n_chunks; k++) before += p.ws_ccount[(bh * p.n_chunks + k) * kMaxClusters + cl];
-    for (int64_t k = 0; k < c; k++) before += p.ws_ccount[(bh * p.n_chunks + k) * kMaxClusters + tid];
-    base[tid] = before;
+    for (int cl = 0; cl < tid; cl++) before += p.ws_ctot[bh * kMaxClusters + cl];
+    base[tid] = before + p.ws_sbase[(bh * kMaxClusters + tid) * (p.n_sub + 1) + c * kSubs];
   }
-  const int64_t tb = c * kChunk + static_cast<int64_t>(tid) * kTpt;
-  int lab[kTpt];
+  const int64_t tb = c * kStepChunk + 2 * static_cast<int64_t>(tid);
+  int lab[2];
   int my[kMaxClusters];
   for (int cl = 0; cl < K; cl++) my[cl] = 0;
 #pragma unroll
-  for (int k = 0; k < kTpt; k++) {
+  for (int k = 0; k < 2; k++) {
     const int64_t t = tb + k;
     lab[k] = t < p.N ? p.ws_labels[bh * p.N + t] : -1;
     for (int cl = 0; cl < K; cl++) my[cl] += lab[k] == cl ? 1 : 0;
@@ -287,7 +315,7 @@ __global__ __launch_bounds__(256) void vc_scatter(ClusterParams p) {
   for (int cl = 0; cl < K; cl++) pos[cl] = base[cl] + scan[cl][tid];
   int32_t* out = p.perm + bh * p.N;
 #pragma unroll
-  for (int k = 0; k < kTpt; k++) {
+  for (int k = 0; k < 2; k++) {
     if (lab[k] < 0) continue;
     out[pos[lab[k]]++] = static_cast<int32_t>(tb + k);
   }
@@ -335,21 +363,27 @@ __global__ __launch_bounds__(256) void vc_index(ClusterParams p) {
 
 hipError_t launch_cluster(const ClusterParams& p, hipStream_t stream) {
   const unsigned bh = static_cast<unsigned>(p.B * p.H), nc = static_cast<unsigned>(p.n_chunks);
-  const dim3 g(nc, bh);
+  const dim3 g(nc, bh), gs(static_cast<unsigned>(p.n_schunks), bh);
   hipLaunchKernelGGL(vc_colsum, g, dim3(256), 0, stream, p);
   hipLaunchKernelGGL(vc_sqdev, g, dim3(256), 0, stream, p);
   hipLaunchKernelGGL(vc_select, dim3(bh), dim3(kHeadDim), 0, stream, p);
   hipLaunchKernelGGL(vc_gather, g, dim3(256), 0, stream, p);
+  auto step = [&](int sums) {
+    if (p.n_feat == 8) hipLaunchKernelGGL(vc_step<8>, gs, dim3(256), 0, stream, p, sums);
+    else hipLaunchKernelGGL(vc_step<0>, gs, dim3(256), 0, stream, p, sums);
+  };
   for (int it = 0; it < p.iters; it++) {
-    hipLaunchKernelGGL(vc_step, g, dim3(256), 0, stream, p, 1);
+    step(1);
     hipLaunchKernelGGL(vc_update, dim3(bh), dim3(512), 0, stream, p);
   }
-  hipLaunchKernelGGL(vc_step, g, dim3(256), 0, stream, p, 0);
-  if (p.ws_scount) hipLaunchKernelGGL(vc_index, dim3(static_cast<unsigned>(p.n_clusters), bh), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(vc_scatter, g, dim3(256), 0, stream, p);
+  step(0);
+  hipLaunchKernelGGL(vc_index, dim3(static_cast<unsigned>(p.n_clusters), bh), dim3(256), 0, stream, p);
+  // the fused preparation places the tokens in the V block statistics instead
+  if (!p.ws_lab8) hipLaunchKernelGGL(vc_scatter, gs, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 int64_t cluster_chunks(int64_t N) { return (N + kChunk - 1) / kChunk; }
+int64_t cluster_step_chunks(int64_t N) { return (N + kStepChunk - 1) / kStepChunk; }
 
 }  // namespace fp8attn

@@ -142,23 +142,25 @@ struct ClusterParams {
   double* ws_part2;    // [B*H, n_chunks, 128] centred sums of squares per chunk
   int32_t* ws_featsel; // [B*H, kMaxFeatures]
   double* ws_cent;     // [B*H, kMaxClusters, kMaxFeatures]
-  double* ws_csum;     // [B*H, n_chunks, kMaxClusters, kMaxFeatures + 1] (sums, count)
-  int32_t* ws_ccount;  // [B*H, n_chunks, kMaxClusters]
-  // scatter index (instead of perm, for the preparation that fuses the stable scatter into the
-  // V block statistics), or null: the labels as bytes, the tokens of each cluster per 256-token
-  // sub-chunk (final assignment), their exclusive prefix over the sub-chunks and their total
-  uint8_t* ws_lab8;    // [B*H, lab_stride] (lab_stride = N rounded up to 16)
+  double* ws_csum;     // [B*H, n_schunks, kMaxClusters, kMaxFeatures + 1] (sums, count at n_feat)
+  int32_t* ws_ccount;  // [B*H, n_schunks, kMaxClusters]
+  // scatter index: the tokens of each cluster per 256-token sub-chunk (final assignment), their
+  // exclusive prefix over the sub-chunks and their total; and, for the preparation that fuses
+  // the stable scatter into the V block statistics, the labels as bytes (else null, and
+  // vc_scatter writes perm)
+  uint8_t* ws_lab8;    // [B*H, lab_stride] (lab_stride = N rounded up to 16) or null
   int32_t* ws_scount;  // [B*H, kMaxClusters, n_sub]
   int32_t* ws_sbase;   // [B*H, kMaxClusters, n_sub + 1]
   int32_t* ws_ctot;    // [B*H, kMaxClusters]
-  int64_t N, n_chunks, n_sub, lab_stride;
+  int64_t N, n_chunks, n_schunks, n_sub, lab_stride;
   int B, H;
   int n_clusters, n_feat, iters;
 };
 
 constexpr int kClusterSub = 256;  // tokens per sub-chunk of the scatter index
 
-int64_t cluster_chunks(int64_t N);  // token chunks of the clustering kernels
+int64_t cluster_chunks(int64_t N);       // token chunks of the channel statistics and the gather
+int64_t cluster_step_chunks(int64_t N);  // token chunks of the assignment and the scatter
 hipError_t launch_cluster(const ClusterParams& p, hipStream_t stream);
 
 enum AttnVariant : int {
