@@ -322,10 +322,16 @@ def calibrate_copy(torch, nbytes=1 << 30, reps=3):
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(reps):
         dst.copy_(src)
+    e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps}), flush=True)
+    ms = e0.elapsed_time(e1) / reps
+    # (the copy's own rate, read + write bytes: what a plain streaming kernel reaches on this HBM)
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps, "ms_per_copy": round(ms, 4),
+                      "copy_GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(args, cfg_name, sparse, vs, expcast):

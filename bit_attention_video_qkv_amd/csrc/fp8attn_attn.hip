@@ -194,6 +194,8 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   constexpr int kSlots = WAVES == 2 ? 2 : 3;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kSlots * kSlotBytes];
   auto slot = [&](int i) -> uint8_t* { return lds + i * kSlotBytes; };
+  // the head's V channel scales and output shift, copied in the prologue for the epilogue
+  __shared__ __attribute__((aligned(16))) float vsc_s[2 * kHeadDim];
 
   // ---- work item ----
   const int64_t bh = work / (p.n_qtiles * p.splits);
@@ -468,6 +470,9 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   const int64_t qblk = (q0 + 32 * wave) / kBlock;  // the wave's 32 rows lie in one Q block
   const float s_q = qblk < p.NB ? p.q_scale[bh * p.NB + qblk] : 0.0f;
   const float sq_ls = s_q * p.logit_scale;
+  // the output row of the scatter, loaded now so that the epilogue waits on no load
+  int32_t out_row = 0;
+  if (p.out_rows && qrow < p.N) out_row = p.out_rows[qrow];
 
   // ---- per-wave state ----
   v16f oacc[4], sacc[2];
@@ -778,6 +783,13 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   };
 
   // ---- prologue: pairs 0..kSlots-1 staged; K(0) read; QK of block 0; pair kSlots staged ----
+  // (first the V scales and shift for the epilogue: the oldest copies, so the prologue's waits
+  // for the first pairs cover them; a workgroup only reaches here after every wave left the
+  // previous item's epilogue)
+  if (lane < 32) {
+    if (wave == 0) copy16_to_lds(p.v_scale + bh * kHeadDim, 16u * lane, lds_addr_of(reinterpret_cast<const uint8_t*>(vsc_s)));
+    if (wave == 1 && p.v_shift) copy16_to_lds(p.v_shift + bh * kHeadDim, 16u * lane, lds_addr_of(reinterpret_cast<const uint8_t*>(vsc_s + kHeadDim)));
+  }
   stage(0, slot(0));
   stage(1, slot(1));
   if constexpr (kSlots == 3) {
@@ -867,19 +879,18 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   if constexpr (EXPCAST) l_tot = VSMOOTH ? l_part : lacc[0];
   else l_tot = xsum(l_part);
   // This lane's channels d0 .. d0 + 3 for output group i = 4 dt + g: d0 = 32 dt + 8 g + 4 lh.
-  // The groups are written in two halves of eight. The channel vectors of a half are loaded
-  // before any is used, so their loads overlap: two round trips instead of 16 before the
-  // stores. The sched barrier keeps the second half's loads from being hoisted, which would
-  // spill registers.
+  // The groups are written in two halves of eight, their V scales and shifts read from the
+  // prologue's copy in LDS. The sched barrier keeps the second half's reads from being hoisted,
+  // which would spill registers.
   auto chan = [&](int i) -> int { return 32 * (i >> 2) + 8 * (i & 3) + 4 * lh; };
   auto load8 = [&](float4 (&dst)[8], const float* src, int half) {
 #pragma unroll
     for (int k = 0; k < 8; k++) dst[k] = *reinterpret_cast<const float4*>(src + chan(8 * half + k));
   };
   auto load_scales = [&](float4 (&sv)[8], float4 (&sh)[8], int half) {
-    load8(sv, p.v_scale + bh * kHeadDim, half);
+    load8(sv, vsc_s, half);
     if (p.v_shift) {
-      load8(sh, p.v_shift + bh * kHeadDim, half);
+      load8(sh, vsc_s + kHeadDim, half);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; k++) sh[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -957,7 +968,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     }
   }
   int64_t dst = qrow;
-  if (ok && p.out_rows) dst = p.out_rows[qrow];
+  if (ok && p.out_rows) dst = out_row;
   ok = ok && dst >= 0 && dst < p.n_out;
   if (ok) {
     const float inv_l = 1.0f / l_tot;
