@@ -60,6 +60,29 @@ def test_mean_over_valid_tokens(sta):
     assert np.all(np.abs(qz["v_shift"][0] - want) <= bound)
 
 
+@pytest.mark.parametrize("sta", [False, True])
+def test_mean_exact_when_every_partial_sum_is_exact(sta):
+    # Values k/8 with |k| <= 64 over 3000 tokens: every partial sum of them, in any order, is a
+    # multiple of 1/8 below 2^15 and so exact in FP32. The mean is then the plain definition's
+    # value bit for bit: the exact sum over the valid tokens divided by their count, rounded once
+    # (a dropped or doubled token, a padding row counted, or a wrong count fails this).
+    N, H = 3000, 2
+    g = torch.Generator("cpu").manual_seed(78)
+    kk = torch.randint(-64, 65, (1, N, H, 128), generator=g).float() / 8.0
+    v = kk.to(torch.bfloat16)
+    assert torch.equal(v.float(), kk)
+    q, k, _ = workloads.make_qkv(1, N, H, seed=79)
+    perm = None
+    if sta:
+        lay = oracle.sta_layout(15, 10, 20, 6, 8, 8, 1, 1, 1)  # 3000 tokens, padded tiles
+        perm = lay["perm"]
+        assert (perm >= 0).sum() == N and perm.shape[0] > N
+    qz = oracle.quantize(_bits(q), _bits(k), _bits(v), perm_q=perm, perm_kv=perm, smoothing=2)
+    exact_sum = kk[0].double().sum(dim=0).numpy()  # [H, 128], exact
+    want = (exact_sum.astype(np.float32) / np.float32(N)).astype(np.float32)
+    assert np.array_equal(qz["v_shift"][0].view(np.uint32), want.view(np.uint32))
+
+
 def _offset_error(which, smoothing):
     B, N, H = 1, 2048, 2
     q, k, v = workloads.make_qkv(B, N, H, seed=74)
