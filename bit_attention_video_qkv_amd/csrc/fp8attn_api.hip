@@ -18,6 +18,9 @@ using fp8attn::kHeadDim;
 constexpr size_t kAlign = 256;
 // Forward workspace head: the eight per-XCD work-queue counters, padded to kAlign.
 constexpr size_t kQueueBytes = 256;
+// The attention kernels copy a head's channel-major V tile rows (128 rows of N64 bytes) with
+// 32-bit offsets from a per-block base: 127 * N64 + 48 must stay below 2^32.
+constexpr int64_t kMaxAttnTokens = int64_t{1} << 25;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -246,7 +249,7 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
   if (!o || B < 1 || N < 1 || H < 1 || D < 1) return FP8ATTN_EINVAL;
   if (D != kHeadDim) return FP8ATTN_EUNSUPPORTED;
   const int64_t total_bh = static_cast<int64_t>(B) * H;
-  if (total_bh > 65535) return FP8ATTN_EUNSUPPORTED;
+  if (total_bh > 65535 || cdiv(N, 64) * 64 > kMaxAttnTokens) return FP8ATTN_EUNSUPPORTED;
   const void* p16[] = {q8, k8, v8t, v_scale};
   for (const void* ptr : p16)
     if (!ptr || !aligned(ptr, 16)) return FP8ATTN_EINVAL;
@@ -378,7 +381,8 @@ fp8attn_status fp8attn_sol_forward(int32_t B, int32_t N, int32_t H, int32_t D, c
   if (!o || B < 1 || N < 1 || H < 1 || D < 1) return FP8ATTN_EINVAL;
   if (D != kHeadDim) return FP8ATTN_EUNSUPPORTED;
   const int64_t total_bh = static_cast<int64_t>(B) * H;
-  if (total_bh > 65535 || total_bh * cdiv(N, 64) > INT32_MAX) return FP8ATTN_EUNSUPPORTED;
+  if (total_bh > 65535 || total_bh * cdiv(N, 64) > INT32_MAX || cdiv(N, 64) * 64 > kMaxAttnTokens)
+    return FP8ATTN_EUNSUPPORTED;
   const void* p16[] = {q8, k8, v8t, v_scale, out, workspace};
   for (const void* ptr : p16)
     if (!ptr || !aligned(ptr, 16)) return FP8ATTN_EINVAL;

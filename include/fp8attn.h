@@ -26,7 +26,10 @@
  *    FP8ATTN_EHIP. No call ever falls back to another implementation.
  *  - Shapes: B batch, N tokens in the layout order, H heads, D = 128 channels.
  *    NB = ceil(N / 64), N64 = 64 * NB, NB128 = ceil(N / 128).
- *  - Indices and offsets are 64-bit inside the library; B*H*N64*128 may exceed 2^31.
+ *  - Indices and offsets are 64-bit inside the library; B*H*N64*128 may exceed 2^31. The
+ *    attention entry points (fp8attn_forward, fp8attn_forward_noalloc, fp8attn_sol_forward)
+ *    address one head's channel-major V with 32-bit offsets and take N64 <= 2^25 (33,554,432
+ *    tokens per head); a larger N returns FP8ATTN_EUNSUPPORTED.
  */
 #ifndef FP8ATTN_H_
 #define FP8ATTN_H_

@@ -117,6 +117,9 @@ def test_forward_rejects_bad_arguments(m):
     assert call(_opts(m, kv_splits=2), ws=0) == 1                         # pieces need workspace
     assert call(_opts(m), ws=0) == 1                                      # work queues need workspace
     assert call(_opts(m), ws=255) == 1
+    big = (1 << 25) + 1                                                   # N64 > 2^25 tokens per head
+    assert call(_opts(m, n_out=big), N=big, ws=1 << 40) == 2
+    assert call(_opts(m, n_out=(1 << 25) - 63), N=(1 << 25) - 63, ws=0) == 1   # N64 = 2^25 is accepted
 
 
 @pytest.mark.parametrize("grid", [(21, 45, 80, 6, 8, 8, 1, 1, 1), (5, 7, 9, 2, 4, 8, 1, 1, 0),
@@ -241,6 +244,9 @@ def test_sol_rejects_bad_arguments(m):
 
     assert call(D=64) == 2
     assert call(ws=need - 1) == 1
+    opts = m._SolOpts(0.088, 256.0, 1, 0, 3.0, 0, 1, None)
+    assert L.fp8attn_sol_forward(1, (1 << 25) + 1, 2, 128, *P, ctypes.byref(opts), _fake(), None,
+                                 _fake(), ctypes.c_size_t(1 << 40), None) == 2   # N64 > 2^25
     assert call(estimator=2) == 1
     assert call(sink_blocks=-1) == 1
     assert call(tau=float("nan")) == 1
