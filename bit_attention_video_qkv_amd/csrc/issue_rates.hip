@@ -22,6 +22,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 #define MUL(r) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(r) : "v"(c1));
 #define EXP(r) asm volatile("v_exp_f32 %0, %0" : "+v"(r));
 #define MAX3(r, a, b) asm volatile("v_maximum3_f32 %0, %0, %1, %2" : "+v"(r) : "v"(a), "v"(b));
+#define MAX3L(r, a, b) asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(r) : "v"(a), "v"(b));
 #define CVT(d, a, b) asm volatile("v_cvt_pk_fp8_f32 %0, %1, %2" : "+v"(d) : "v"(a), "v"(b));
 #define CVTU8(d, a) asm volatile("v_cvt_pk_u8_f32 %0, %1, 1, %0" : "+v"(d) : "v"(a));
 #define SB __builtin_amdgcn_sched_barrier(0);
@@ -30,17 +31,19 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 enum Kind {
   kFma, kAdd, kMul, kMax3, kExp, kCvtFp8, kCvtU8, kExpFma, kCvtFma, kMfma, kMfmaFma,
-  kBlock, kBlockValuOnly, kBlockPlainSlowOps, kBlockExpCast, kBlockExpCastValuOnly, kBlockExpCastEven, kNumKinds
+  kBlock, kBlockValuOnly, kBlockPlainSlowOps, kBlockExpCast, kBlockExpCastValuOnly, kBlockExpCastEven,
+  kMax3Legacy, kNumKinds
 };
 static const char* kNames[] = {
     "v_fma_f32",           "v_add_f32",           "v_mul_f32",        "v_maximum3_f32",
     "v_exp_f32",           "v_cvt_pk_fp8_f32",    "v_cvt_pk_u8_f32",  "exp + fma alternating",
     "cvt_pk_fp8 + fma alternating", "mfma 32x32x64 f8",   "mfma + 16 fma each",
     "attention block mix", "block mix, VALU part only", "block mix, exp/cvt replaced by fma",
-    "ExpCast block mix", "ExpCast mix, VALU part only", "ExpCast mix, MFMAs spread evenly"};
+    "ExpCast block mix", "ExpCast mix, VALU part only", "ExpCast mix, MFMAs spread evenly",
+    "v_max3_f32"};
 // per wave and iteration: VALU instructions, MFMAs
-static const int kValu[] = {32, 32, 32, 16, 32, 16, 16, 32, 16, 0, 64, 136, 136, 136, 88, 88, 88};
-static const int kMfmas[] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 4, 4, 8, 0, 8, 9, 0, 9};
+static const int kValu[] = {32, 32, 32, 16, 32, 16, 16, 32, 16, 0, 64, 136, 136, 136, 88, 88, 88, 16};
+static const int kMfmas[] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 4, 4, 8, 0, 8, 9, 0, 9, 0};
 
 template <int KIND, int WPS>
 __global__ __launch_bounds__(256 * WPS) void probe(unsigned long long* out, int iters, float c1, float c2) {
@@ -81,6 +84,9 @@ __global__ __launch_bounds__(256 * WPS) void probe(unsigned long long* out, int 
     } else if constexpr (KIND == kMax3) {
 #pragma unroll
       for (int i = 0; i < 16; i++) MAX3(x[i], x[16 + i], x[(i + 7) & 31])
+    } else if constexpr (KIND == kMax3Legacy) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) MAX3L(x[i], x[16 + i], x[(i + 7) & 31])
     } else if constexpr (KIND == kExp) {
 #pragma unroll
       for (int i = 0; i < 32; i++) EXP(x[i])
@@ -397,6 +403,7 @@ void run_all(int ncu, unsigned long long* dout) {
   run<kAdd, WPS>(ncu, dout);
   run<kMul, WPS>(ncu, dout);
   run<kMax3, WPS>(ncu, dout);
+  run<kMax3Legacy, WPS>(ncu, dout);
   run<kExp, WPS>(ncu, dout);
   run<kCvtFp8, WPS>(ncu, dout);
   run<kCvtU8, WPS>(ncu, dout);
