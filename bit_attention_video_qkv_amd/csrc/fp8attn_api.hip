@@ -27,6 +27,8 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// V-Smooth mean operand records: 32 bytes per channel for each group of four 128-row V blocks
+size_t mean_record_bytes(size_t bh, int64_t N) { return bh * cdiv(cdiv(N, 128), 4) * kHeadDim * 32; }
 
 // Per-device result of the gfx950 check (0 unknown, 1 gfx950, 2 other). Written once per device.
 std::atomic<int> g_arch_ok[64];
@@ -233,7 +235,7 @@ size_t fp8attn_forward_workspace_bytes(int32_t B, int32_t N, int32_t H, int32_t 
   if (B < 1 || N < 1 || H < 1 || D != kHeadDim || !valid_splits_arg(kv_splits)) return 0;
   const size_t bh = static_cast<size_t>(B) * H;
   size_t n = kQueueBytes;                                                   // work queues
-  if (vsmooth) n += round_up(bh * cdiv(N, 128) * kHeadDim * 16);          // mean operand records
+  if (vsmooth) n += round_up(mean_record_bytes(bh, N));                   // mean operand records
   int64_t split_blocks = 0;
   const int splits = resolve_splits(B, N, H, kv_splits, &split_blocks);
   if (splits > 1)
@@ -298,7 +300,7 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
   p.split_blocks = splits > 1 ? split_blocks : cdiv(N, 64);
   if (splits > 1) {
     const size_t bh = static_cast<size_t>(total_bh);
-    char* ws = static_cast<char*>(workspace) + kQueueBytes + (vsmooth ? round_up(bh * cdiv(N, 128) * kHeadDim * 16) : 0);
+    char* ws = static_cast<char*>(workspace) + kQueueBytes + (vsmooth ? round_up(mean_record_bytes(bh, N)) : 0);
     p.o_part = reinterpret_cast<float*>(ws);
     p.lse = reinterpret_cast<float*>(ws + round_up(splits * bh * N * kHeadDim * sizeof(float)));
   }

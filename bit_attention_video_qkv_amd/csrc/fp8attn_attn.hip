@@ -128,24 +128,20 @@ __device__ __forceinline__ void copy4_to_lds(const void* gbase, uint32_t voff, u
 // is followed by a run of VALU work long enough to cover its 64-cycle issue on the matrix
 // core, so the wave never queues behind its own MFMAs while it has VALU work left.
 __device__ __forceinline__ void interleave_region1() {
-#ifndef FP8ATTN_NO_IGLP
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (PV)
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS read
     __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // VALU
   }
-#endif
   __builtin_amdgcn_sched_barrier(0);
 }
 __device__ __forceinline__ void interleave_region2() {
-#ifndef FP8ATTN_NO_IGLP
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (QK, first key half)
     __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // VALU
   }
-#endif
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -182,10 +178,13 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   constexpr int kRowsPerWg = WAVES * 32;
   constexpr int kChunks = 512 / kThreads;       // 16-byte chunks per thread of one 8 KB tile
   constexpr int kMetaOff = 2 * kTileBytes;      // s_k (f32) and valid keys (i32) of the K block
-  constexpr int kMeanOff = kMetaOff + 16;       // V-Smooth mean operand records, 128 x 16 B
+  // V-Smooth: the mean operand records of a group of four 128-row V blocks, 128 channels x 32 B
+  constexpr int kMeanOff = kMetaOff + 16;
+  constexpr int kMeanBytes = VSMOOTH ? kHeadDim * 32 : 0;
   constexpr int kGmaxOff = kMeanOff;            // Sol: the K block's group summary maximum per row
-  constexpr int kSlotBytes = kMeanOff + (VSMOOTH ? kHeadDim * 16 : 0) + (SOL ? kRowsPerWg * 4 : 0);
-  constexpr int kMeanLanes = 128 / WAVES;       // V-Smooth: lanes per wave copying the records
+  constexpr int kSlotBytes = kMeanOff + kMeanBytes + (SOL ? kRowsPerWg * 4 : 0);
+  constexpr int kMeanLanes = kMeanBytes / 16 / WAVES;  // V-Smooth: lanes per wave copying them
+  static_assert(kMeanLanes <= 64, "one 16-byte record chunk per lane");
   // copies every wave issues for every pair (wave 0 adds s_k; V-Smooth pairs may add the mean
   // records, which the waits do not count: they then wait one copy longer than they must)
   constexpr int kCopies = 2 * kChunks;
@@ -354,6 +353,24 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   // block when kb is odd; reverse, when kb is even, i.e. when e = e0 + j has the parity of NB - 1.
   const int close_parity = p.reverse ? static_cast<int>((p.NB - 1) & 1) : 1;
   auto closes_vblock_inner = [&](int j) -> bool { return ((static_cast<int>(e0) + j) & 1) == close_parity; };
+  // The mean restore runs once per group of four V blocks (eight key blocks, kb / 8): block j
+  // closes its group when the next block lies in another group or j is the piece's last block;
+  // in the steady state, when kb % 8 is 7 (forward) or 0 (reverse), i.e. when e = e0 + j has the
+  // phase of NB - 1 in reverse.
+  auto closes_group = [&](int j) -> bool {
+    if (j + 1 >= n_iter) return true;
+    const int64_t e = e0 + j;
+    const int64_t kb = p.reverse ? (p.NB - 1 - e) : e;
+    const int64_t kn = p.reverse ? (p.NB - 2 - e) : e + 1;
+    return (kb >> 3) != (kn >> 3);
+  };
+  const int group_phase = p.reverse ? static_cast<int>((p.NB - 1) & 7) : 7;
+  auto closes_group_inner = [&](int j) -> bool { return ((static_cast<int>(e0) + j) & 7) == group_phase; };
+  // position of block j's V block in its group (the records' and pending sums' index)
+  auto vpos_of = [&](int j) -> int {
+    const int64_t e = e0 + j;
+    return static_cast<int>(((p.reverse ? (p.NB - 1 - e) : e) >> 1) & 3);
+  };
 
   // ---- staging of pair `pidx` into slot `sl` (every thread copies its fixed 16-byte chunks;
   // per pair only the wave-uniform tile bases change) ----
@@ -389,8 +406,8 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     for (int r = 0; r < kChunks; r++) copy16_to_lds(vt, voff[r], l0 + kTileBytes + (r * kThreads + wave * 64) * 16);
     if constexpr (VSMOOTH) {
       if (lane < kMeanLanes)
-        copy16_to_lds(p.mu_op + (bh * p.NB128 + (vb >> 1)) * kHeadDim * 4, 16u * (wave * kMeanLanes + lane),
-                      l0 + kMeanOff + wave * kMeanLanes * 16);
+        copy16_to_lds(p.mu_op + (bh * ((p.NB128 + 3) >> 2) + (vb >> 3)) * (kMeanBytes / 4),
+                      16u * (wave * kMeanLanes + lane), l0 + kMeanOff + wave * kMeanLanes * 16);
     }
     if constexpr (SOL) {
       // the running summary maximum of the K block's route group, for the wave's 32 rows
@@ -429,12 +446,12 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
 #pragma unroll
     for (int r = 0; r < kChunks; r++) copy16_to_lds(st_v, voff[r], l0 + kTileBytes + (r * kThreads + wave * 64) * 16);
     if constexpr (VSMOOTH) {
-      // only the restore of the block that closes a V block reads the records (from the slot of
-      // the next pair, which carries that block's V tile); a steady pair's V block never is the
-      // last of the piece
-      if (((kb_prev & 1) != 0) == (kv_dir > 0) && lane < kMeanLanes)
-        copy16_to_lds(p.mu_op + (bh * p.NB128 + (kb_prev >> 1)) * kHeadDim * 4, 16u * (wave * kMeanLanes + lane),
-                      l0 + kMeanOff + wave * kMeanLanes * 16);
+      // only the restore of the block that closes a group of V blocks reads the records (from
+      // the slot of the next pair, which carries that block's V tile); a steady pair's V block
+      // never is the last of the piece
+      if ((kb_prev & 7) == (kv_dir > 0 ? 7 : 0) && lane < kMeanLanes)
+        copy16_to_lds(p.mu_op + (bh * ((p.NB128 + 3) >> 2) + (kb_prev >> 3)) * (kMeanBytes / 4),
+                      16u * (wave * kMeanLanes + lane), l0 + kMeanOff + wave * kMeanLanes * 16);
     }
     st_k += kv_dir * kTileBytes;
     st_v += kv_dir * kBlock;
@@ -488,6 +505,10 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   // S-scaled sum over the closed V blocks (V-Smooth), else unused.
   float l_part = 0.0f;
   float r_cur = 0.0f;       // V-Smooth, standard cast: S-scaled row sum of the open V block
+  // V-Smooth: S-scaled row sums of the closed V blocks of the open group that this lane half
+  // feeds to the restore (positions 2 lh and 2 lh + 1 in the group), rescaled with O until the
+  // group's restore
+  float r_pa = 0.0f, r_pb = 0.0f;
   // ExpCast: S-scaled row sums of the P codes accumulated on the matrix cores (lacc[0] in every
   // lane: the lane's whole query row), rescaled with O; with V-Smooth only since the last mean
   // restore.
@@ -694,30 +715,39 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     return alpha;
   };
 
-  // V-Smooth rank-one mean restore O^T += mu r^T of a closed V block, mu = the block's mean
-  // factors (in the residual's units) and r the lanes' S-scaled row sums over its keys, on the
-  // matrix cores as one BF16 32x32x16 MFMA per 32 channels with a hi/lo split of both factors:
-  // k slots 0..2 carry mu_hi r_hi + mu_hi r_lo + mu_lo r_hi (the dropped mu_lo r_lo is below
-  // 2^-16 of the product, and the split loses below 2^-17 of each factor), exact products with
-  // FP32 accumulation. The A operand of channel 32 dt + l32 is its 16-byte record in the slot
-  // {mu_hi|mu_hi, mu_lo|0, 0, 0} (read by both lane halves); the B operand is r's split in the
-  // lanes of half 0 (k 0..7) and zero in half 1 (k 8..15).
-  auto restore_mean = [&](const uint8_t* sl, float r) {
+  // V-Smooth rank-one mean restores O^T += sum_v mu_v r_v^T of the (up to four) V blocks v of a
+  // group, mu_v = the block's mean factors (in the residual's units) and r_v the lanes' S-scaled
+  // row sums over its keys, on the matrix cores as one BF16 32x32x16 MFMA per 32 channels with a
+  // hi/lo split of both factors: per block, three k slots carry mu_hi r_hi + mu_hi r_lo +
+  // mu_lo r_hi (the dropped mu_lo r_lo is below 2^-16 of the product, and the split loses below
+  // 2^-17 of each factor), exact products with FP32 accumulation. Lane half h holds k slots
+  // 8h..8h+7 for the group's blocks 2h (slots 0..2) and 2h+1 (slots 3..5): the A operand of
+  // channel 32 dt + l32 is its 16-byte record {hiA|hiA, loA|hiB, hiB|loB, 0} at byte 16 h of the
+  // channel's 32 bytes in the slot, the B operand {rhA|rlA, rhA|rhB, rlB|rhB, 0}. Blocks that do
+  // not exist or were not visited have zero sums (and zero factors past the sequence).
+  auto split_bf16 = [](float r, uint32_t& hi, uint32_t& lo) {
     const __bf16 rh = static_cast<__bf16>(r);  // round to nearest even
     const __bf16 rl = static_cast<__bf16>(r - static_cast<float>(rh));
-    const uint32_t hi0 = __builtin_bit_cast(uint16_t, rh);                                  // r_hi | 0
-    const uint32_t hl = hi0 | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, rl)) << 16);  // r_hi | r_lo
+    hi = __builtin_bit_cast(uint16_t, rh);
+    lo = __builtin_bit_cast(uint16_t, rl);
+  };
+  auto restore_group = [&](const uint8_t* sl) {
+    uint32_t ha, la, hb, lb;
+    split_bf16(r_pa, ha, la);
+    split_bf16(r_pb, hb, lb);
     v4i b;
-    b[0] = lh == 0 ? static_cast<int>(hl) : 0;
-    b[1] = lh == 0 ? static_cast<int>(hi0) : 0;
-    b[2] = 0;
+    b[0] = static_cast<int>(ha | (la << 16));
+    b[1] = static_cast<int>(ha | (hb << 16));
+    b[2] = static_cast<int>(lb | (hb << 16));
     b[3] = 0;
     const v8bf bb = __builtin_bit_cast(v8bf, b);
 #pragma unroll
     for (int dt = 0; dt < 4; dt++) {
-      const v4i a = *reinterpret_cast<const v4i*>(sl + kMeanOff + (32 * dt + l32) * 16);
+      const v4i a = *reinterpret_cast<const v4i*>(sl + kMeanOff + (32 * dt + l32) * 32 + 16 * lh);
       oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), bb, oacc[dt], 0, 0, 0);
     }
+    r_pa = 0.0f;
+    r_pb = 0.0f;
   };
 
   // One key block j; `sl` is the slot of pair j+1 (read here, then refilled with pair
@@ -743,21 +773,33 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
         lacc[0] *= alpha;  // the only register of the sum that is read
         if constexpr (VSMOOTH) l_part *= alpha;
       }
+      if constexpr (VSMOOTH) {
+        r_pa *= alpha;
+        r_pb *= alpha;
+      }
     }
     // ExpCast: block j's code sums, in the units of its running max like lacc by now
     if constexpr (EXPCAST) lacc = mfma_rowsum(rs_sel, pop, lacc);
     if constexpr (VSMOOTH) {
       if (kSteady ? closes_vblock_inner(j) : closes_vblock(j)) {
-        // the V block that block j closes (its records travel in pair j+1); O holds blocks up to
-        // j-1 in the units of the running max of block j, like r
+        // the V block that block j closes: its row sum joins the group's pending sums, in the
+        // units of the running max of block j like O (which holds blocks up to j-1)
+        float r;
         if constexpr (EXPCAST) {
-          restore_mean(sl, lacc[0]);
-          l_part += lacc[0];
+          r = lacc[0];
+          l_part += r;
           lacc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         } else {
-          restore_mean(sl, r_cur);
+          r = r_cur;
           r_cur = 0.0f;
         }
+        const int pos = vpos_of(j);  // (uniform)
+        if ((pos >> 1) == lh) {
+          if (pos & 1) r_pb = r;
+          else r_pa = r;
+        }
+        // the group's records travel in pair j+1 when block j closes the group
+        if (kSteady ? closes_group_inner(j) : closes_group(j)) restore_group(sl);
       }
     }
     // hand-off: every read of this slot is complete, pair j+2 has landed everywhere
@@ -1048,20 +1090,30 @@ __global__ void attn_queue_reset(uint32_t* ctr) {
   if (threadIdx.x < 8) ctr[threadIdx.x] = 0u;
 }
 
-// V-Smooth: the factor mu = float(mean_hat[bh, j, d]) * (s_r[d] > 0 ? 1 / s_r[d] : 1) as the
-// restore's A-operand record mu_op[bh, j, d] = {mu_hi|mu_hi, mu_lo|0, 0, 0} (BF16 pairs, low half
-// first; mu_hi = BF16(mu), mu_lo = BF16(mu - mu_hi), both rounded to nearest even).
+// V-Smooth: the factors mu_v = float(mean_hat[bh, v, d]) * (s_r[d] > 0 ? 1 / s_r[d] : 1) of the
+// four V blocks v = 4 g .. 4 g + 3 of group g (0 past the sequence), split as mu_hi = BF16(mu),
+// mu_lo = BF16(mu - mu_hi) (both rounded to nearest even), written as the restore's A-operand
+// records of channel d: mu_op[bh, g, d] = {hiA|hiA, loA|hiB, hiB|loB, 0} for blocks (A, B) =
+// (4g, 4g+1), then for (4g+2, 4g+3) (BF16 pairs, low half first; 32 bytes).
 __global__ __launch_bounds__(128) void vsmooth_mean_factors(AttnParams p) {
-  const int64_t j = blockIdx.x;
+  const int64_t g = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int d = threadIdx.x;
   const float sr = p.v_scale[bh * kHeadDim + d];
   const float f = sr > 0.0f ? __fdiv_rn(1.0f, sr) : 1.0f;
-  const int64_t idx = (bh * p.NB128 + j) * kHeadDim + d;
-  const float mu = bf16_to_f32(p.v_mean[idx]) * f;
-  const uint32_t hi = f32_to_bf16_rne(mu);
-  const uint32_t lo = f32_to_bf16_rne(mu - __uint_as_float(hi << 16));
-  reinterpret_cast<uint4*>(p.mu_op)[idx] = make_uint4(hi | (hi << 16), lo, 0u, 0u);
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int64_t v = 4 * g + k;
+    const float mu = v < p.NB128 ? bf16_to_f32(p.v_mean[(bh * p.NB128 + v) * kHeadDim + d]) * f : 0.0f;
+    hi[k] = f32_to_bf16_rne(mu);
+    lo[k] = f32_to_bf16_rne(mu - __uint_as_float(hi[k] << 16));
+  }
+  uint4* rec = reinterpret_cast<uint4*>(p.mu_op) + ((bh * ((p.NB128 + 3) >> 2) + g) * kHeadDim + d) * 2;
+#pragma unroll
+  for (int h = 0; h < 2; h++)
+    rec[h] = make_uint4(hi[2 * h] | (hi[2 * h] << 16), lo[2 * h] | (hi[2 * h + 1] << 16),
+                        hi[2 * h + 1] | (lo[2 * h + 1] << 16), 0u);
 }
 
 // Split-KV merge ([TF] long-sequence split-KV, log-sum-exp reduction): per row,
@@ -1147,7 +1199,7 @@ hipError_t launch_attention(AttnParams p, int variant, hipStream_t stream) {
              st = variant & kVarStats;
   if (variant & kVarSol) return ec ? launch_sol_exact<true>(p, stream) : launch_sol_exact<false>(p, stream);
   if (vs) {
-    hipLaunchKernelGGL(vsmooth_mean_factors, dim3(static_cast<unsigned>(p.NB128), static_cast<unsigned>(p.B * p.H)),
+    hipLaunchKernelGGL(vsmooth_mean_factors, dim3(static_cast<unsigned>((p.NB128 + 3) / 4), static_cast<unsigned>(p.B * p.H)),
                        dim3(kHeadDim), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -53,7 +53,7 @@ struct AttnParams {
   const float* v_scale;
   const uint16_t* v_mean;   // V-Smooth block means (bf16) or null
   const float* v_shift;     // [B*H, 128] added to every output row before BF16, or null
-  uint32_t* mu_op;          // V-Smooth: [B*H, NB128, 128] x 16 B mean operand records (workspace)
+  uint32_t* mu_op;          // V-Smooth: [B*H, ceil(NB128 / 4), 128] x 32 B mean operand records (workspace)
   uint16_t* out;            // bf16 [B, n_out, H, 128]
   const int32_t* out_rows;  // [N] or null
   unsigned long long* underflow;  // [B*H] or null

@@ -309,7 +309,7 @@ fp8attn_status fp8attn_forward(int32_t B, int32_t N, int32_t H, int32_t D, const
  * Errors: those of fp8attn_forward; FP8ATTN_ESCRATCH when the call would need more scratch than
  *   the array holds (fp8attn_forward_workspace_bytes above FP8ATTN_NOALLOC_SCRATCH_BYTES, e.g.
  *   any split-KV with more than one piece at realistic sizes, or V-Smooth beyond
- *   B*H*ceil(N/128) = 16383 mean records of 2 KB); nothing is enqueued then.
+ *   B*H*ceil(N/512) = 8191 groups of mean records of 4 KB); nothing is enqueued then.
  * ------------------------------------------------------------------------------------------ */
 #define FP8ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
 

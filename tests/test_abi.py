@@ -150,8 +150,9 @@ def test_workspace_sizes(m):
         2 * 40 * 1182 * 128 * 4   # + the smoothing block sums of K and V
     q = 256  # the eight work-queue counters, padded to 256 bytes
     assert L.fp8attn_forward_workspace_bytes(1, 75600, 40, 128, 0, 1) == q
-    # V-Smooth: one 16-byte mean operand record per (b, h, 128-row block, channel)
-    assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1, 0) == q + 24 * 384 * 128 * 16
+    # V-Smooth: one 32-byte mean operand record per (b, h, group of four 128-row blocks, channel)
+    assert L.fp8attn_forward_workspace_bytes(1, 49152, 24, 128, 1, 0) == q + 24 * 96 * 128 * 32
+    assert L.fp8attn_forward_workspace_bytes(1, 129, 1, 128, 1, 0) == q + 128 * 32   # 2 blocks, one group
     # split-KV: 4096 tokens = 64 key blocks, 2 pieces of 32 blocks; 3 requested -> L = 22, 3 pieces
     assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 2) == q + 2 * 8 * 4096 * 129 * 4
     assert L.fp8attn_forward_workspace_bytes(1, 4096, 8, 128, 0, 3) == q + 3 * 8 * 4096 * 129 * 4
