@@ -279,8 +279,12 @@ def test_attention_expcast_clamped_top_code(m, orc, S):
 
 
 @pytest.mark.parametrize("N,reverse,expcast", [(1000, True, False), (768, False, True),
-                                               (300, False, False)])
+                                               (300, False, False), (300, True, True),
+                                               (1100, True, True), (1100, False, False)])
 def test_attention_vsmooth_small(m, orc, N, reverse, expcast):
+    """V-Smooth against the oracle. The restore runs per group of four 128-row V blocks (eight
+    key blocks): the sizes cover an odd block count (300: 5 blocks, one partial group) and a
+    group cut by the sequence end in both orders (1100: 18 blocks, groups of 8, 8 and 2)."""
     say("vsmooth", N, reverse, expcast)
     H = 2
     q, k, v = workloads.make_qkv(1, N, H, seed=21 + N, kind="token_outliers")
