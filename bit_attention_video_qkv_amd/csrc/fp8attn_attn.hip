@@ -601,21 +601,6 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     for (int t = 0; t < 2; t++)
 #pragma unroll
       for (int r = 0; r < 16; r++) x[16 * t + r] = sacc[t][r];
-    if constexpr (kMask) {
-      // only blocks with padding keys pay for the selects; the empty asm keeps the compiler from
-      // hoisting the per-key compares out of the (uniform) branch. Sol: a block outside this
-      // wave's own Q-block mask counts as fully masked.
-      bool excluded = false;
-      if constexpr (kSolPair) excluded = ex_cur;
-      // (dense: the one masked block is the partial last key block)
-      const int lim = (SPARSE || SOL) ? lim_cur : lim_tail;
-      if (__builtin_amdgcn_readfirstlane(lim) < kBlock || excluded) {
-        int nv = excluded ? 0 : lim - 32 * lh;  // valid keys among this lane's 32
-        asm volatile("" : "+v"(nv));
-#pragma unroll
-        for (int q = 0; q < 32; q++) x[q] = q < nv ? x[q] : -INFINITY;
-      }
-    }
     // two chains of three-input maxima, first over the first key half (whose QK finished first)
     float mlo = fmax_ieee(x[0], x[1]), mhi = fmax_ieee(x[2], x[3]);
 #pragma unroll
@@ -750,12 +735,33 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     r_pb = 0.0f;
   };
 
+  // Keys past a block's valid count get S = -inf, in blocks with padding keys only. This runs
+  // at the start of the block, before its PV MFMAs, so that the branch leaves the common path's
+  // interleave of PV MFMAs, operand reads and softmax intact; the empty asm keeps the compiler
+  // from hoisting the per-key compares out of the (uniform) branch. Sol: a block outside this
+  // wave's own Q-block mask counts as fully masked. (Dense: the one masked block is the partial
+  // last key block.)
+  auto mask_block = [&]() {
+    bool excluded = false;
+    if constexpr (kSolPair) excluded = ex_cur;
+    const int lim = (SPARSE || SOL) ? lim_cur : lim_tail;
+    if (__builtin_amdgcn_readfirstlane(lim) < kBlock || excluded) {
+      int nv = excluded ? 0 : lim - 32 * lh;  // valid keys among this lane's 32
+      asm volatile("" : "+v"(nv));
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) sacc[t][r] = 16 * t + r < nv ? sacc[t][r] : -INFINITY;
+    }
+  };
+
   // One key block j; `sl` is the slot of pair j+1 (read here, then refilled with pair
   // j+1+kSlots). The masked copy serves blocks with fewer than 64 valid keys.
   // Steady (dense and STA): pairs j+2 and j+1+kSlots hold key blocks, so the waits and the
   // staging need no checks; dense staging is stage_dense.
   auto iteration = [&](auto mask_tag, auto steady_tag, int j, uint8_t* sl) {
     constexpr bool kSteady = decltype(steady_tag)::value;
+    if constexpr (decltype(mask_tag)::value) mask_block();
     pv();         // PV of block j-1 (zero P bytes before the first block)
     read_v(sl);   // V(j)
     read_k(sl);   // K(j+1)
