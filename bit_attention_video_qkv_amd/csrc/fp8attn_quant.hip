@@ -38,14 +38,23 @@ namespace fp8attn {
 
 namespace {
 
-// Source row index of layout position i for head bh, or -1 (padding, beyond N, or an
-// out-of-range permutation entry, which is treated as padding).
-__device__ __forceinline__ int64_t gather_src(const int32_t* perm, int per_head, int64_t bh,
-                                              int64_t N, int64_t Nsrc, int64_t i) {
-  if (i >= N) return -1;
-  if (perm == nullptr) return i;
-  const int64_t s = per_head ? perm[bh * N + i] : perm[i];
-  return (s >= 0 && s < Nsrc) ? s : -1;
+// Source row indices of the layout positions pos[k] for head bh, or -1 (padding, beyond N, or
+// an out-of-range permutation entry, which is treated as padding). The permutation entries are
+// read at clamped indices (N >= 1) with no per-row branch, so that they load together.
+template <int R>
+__device__ __forceinline__ void gather_srcs(const int32_t* perm, int per_head, int64_t bh, int64_t N, int64_t Nsrc,
+                                            const int64_t (&pos)[R], int64_t (&src)[R]) {
+  if (perm == nullptr) {  // (uniform)
+#pragma unroll
+    for (int k = 0; k < R; k++) src[k] = pos[k] < N ? pos[k] : -1;
+  } else {
+    const int32_t* row = per_head ? perm + bh * N : perm;
+    int32_t e[R];
+#pragma unroll
+    for (int k = 0; k < R; k++) e[k] = row[pos[k] < N ? pos[k] : N - 1];
+#pragma unroll
+    for (int k = 0; k < R; k++) src[k] = (pos[k] < N && e[k] >= 0 && e[k] < Nsrc) ? e[k] : -1;
+  }
 }
 
 // Byte offset-free pointer to the 128-channel bf16 row (b, src, h) of the source layout.
@@ -54,12 +63,24 @@ __device__ __forceinline__ const uint16_t* src_row(const uint16_t* base, int64_t
   return base + ((b * Nsrc + src) * H + h) * kHeadDim;
 }
 
+// The 16 bytes of channels 8 chunk .. + 7 of source row s of head (b, h), zeros for s < 0. The
+// load always issues (row 0, which exists since N_src >= 1, stands in for a padding row), so a
+// thread's row loads are in flight together instead of each one waiting behind a branch.
+__device__ __forceinline__ uint4 load_row16(const uint16_t* base, int64_t b, int64_t s, int64_t h,
+                                            int64_t Nsrc, int64_t H, int chunk) {
+  // an opaque all-ones or zero mask: with a plain select the compiler turns the load back into
+  // a predicated one, which it then waits for inside its branch
+  uint32_t keep = s >= 0 ? 0xFFFFFFFFu : 0u;
+  asm volatile("" : "+v"(keep));
+  const uint4 raw = *reinterpret_cast<const uint4*>(src_row(base, b, s >= 0 ? s : 0, h, Nsrc, H) + chunk * 8);
+  return make_uint4(raw.x & keep, raw.y & keep, raw.z & keep, raw.w & keep);
+}
+
 struct Bf16x8 {
   float v[8];
 };
 
-__device__ __forceinline__ Bf16x8 load8(const uint16_t* p) {
-  const uint4 raw = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ Bf16x8 unpack8(const uint4 raw) {
   Bf16x8 r;
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -96,14 +117,18 @@ __global__ __launch_bounds__(256) void seq_block_sums(QuantParams p) {
   const uint16_t* src = z == 0 ? p.k : p.v;
   const int chunk = threadIdx.x & 15;
   const int row0 = threadIdx.x >> 4;
+  int64_t pos[4], s[4];
+  uint4 raw[4];
+#pragma unroll
+  for (int pass = 0; pass < 4; pass++) pos[pass] = blk * kBlock + row0 + 16 * pass;
+  gather_srcs(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, pos, s);
+#pragma unroll
+  for (int pass = 0; pass < 4; pass++) raw[pass] = load_row16(src, b, s[pass], h, p.Nsrc, p.H, chunk);
 #pragma unroll
   for (int pass = 0; pass < 4; pass++) {
     const int r = row0 + 16 * pass;
-    const int64_t s = gather_src(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, blk * kBlock + r);
-    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-    if (s >= 0) raw = *reinterpret_cast<const uint4*>(src_row(src, b, s, h, p.Nsrc, p.H) + chunk * 8);
-    *reinterpret_cast<uint4*>(&tile[r][chunk * 8]) = raw;
-    if (chunk == 0 && s >= 0) atomicOr(&valid_bits[r >> 5], 1u << (r & 31));
+    *reinterpret_cast<uint4*>(&tile[r][chunk * 8]) = raw[pass];
+    if (chunk == 0 && s[pass] >= 0) atomicOr(&valid_bits[r >> 5], 1u << (r & 31));
   }
   __syncthreads();
   const int d = threadIdx.x;
@@ -201,21 +226,21 @@ __global__ __launch_bounds__(256) void quant_qk(QuantParams p) {
   float mk[8];
 #pragma unroll
   for (int j = 0; j < 8; j++) mk[j] = shift ? p.ws_mean[bh * kHeadDim + chunk * 8 + j] : 0.0f;
+  int64_t pos[4], s[4];
+  uint4 raw[4];
+#pragma unroll
+  for (int pass = 0; pass < 4; pass++) pos[pass] = blk * kBlock + row0 + 16 * pass;
+  gather_srcs(perm, per_head, bh, p.N, p.Nsrc, pos, s);
+#pragma unroll
+  for (int pass = 0; pass < 4; pass++) raw[pass] = load_row16(src, b, s[pass], h, p.Nsrc, p.H, chunk);
   Bf16x8 x[4];
   float amax = 0.0f;
 #pragma unroll
   for (int pass = 0; pass < 4; pass++) {
-    const int64_t i = blk * kBlock + row0 + 16 * pass;
-    const int64_t s = gather_src(perm, per_head, bh, p.N, p.Nsrc, i);
-    if (s >= 0) {
-      x[pass] = load8(src_row(src, b, s, h, p.Nsrc, p.H) + chunk * 8);
-      if (shift)
+    x[pass] = unpack8(raw[pass]);  // padding rows are zeros and stay zeros
+    if (shift)
 #pragma unroll
-        for (int j = 0; j < 8; j++) x[pass].v[j] = __fsub_rn(x[pass].v[j], mk[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; j++) x[pass].v[j] = 0.0f;
-    }
+      for (int j = 0; j < 8; j++) x[pass].v[j] = s[pass] >= 0 ? __fsub_rn(x[pass].v[j], mk[j]) : 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(x[pass].v[j]));
   }
@@ -344,26 +369,30 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
 #pragma unroll
   for (int q = 0; q < 8; q++) mv[q] = shift ? p.ws_mean[(p.B * p.H + bh) * kHeadDim + chunk * 8 + q] : 0.0f;
 
+  int64_t srow[8];
+  uint4 raw[8];
+  if constexpr (SCATTER) {
+#pragma unroll
+    for (int pass = 0; pass < 8; pass++) srow[pass] = src_s[rg + 16 * pass];
+  } else {
+    int64_t pos[8];
+#pragma unroll
+    for (int pass = 0; pass < 8; pass++) pos[pass] = j * kVBlock + rg + 16 * pass;
+    gather_srcs(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, pos, srow);
+  }
+#pragma unroll
+  for (int pass = 0; pass < 8; pass++) raw[pass] = load_row16(p.v, b, srow[pass], h, p.Nsrc, p.H, chunk);
   Bf16x8 x[8];
   bool valid[8];
   int my_valid = 0;  // rows counted once, by the chunk-0 thread of each row
 #pragma unroll
   for (int pass = 0; pass < 8; pass++) {
-    const int64_t i = j * kVBlock + rg + 16 * pass;
-    int64_t s;
-    if constexpr (SCATTER) s = src_s[rg + 16 * pass];
-    else s = gather_src(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, i);
-    valid[pass] = s >= 0;
+    valid[pass] = srow[pass] >= 0;
     my_valid += (chunk == 0 && valid[pass]) ? 1 : 0;
-    if (valid[pass]) {
-      x[pass] = load8(src_row(p.v, b, s, h, p.Nsrc, p.H) + chunk * 8);
-      if (shift)
+    x[pass] = unpack8(raw[pass]);  // padding rows are zeros and stay zeros
+    if (shift)
 #pragma unroll
-        for (int q = 0; q < 8; q++) x[pass].v[q] = __fsub_rn(x[pass].v[q], mv[q]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; q++) x[pass].v[q] = 0.0f;
-    }
+      for (int q = 0; q < 8; q++) x[pass].v[q] = valid[pass] ? __fsub_rn(x[pass].v[q], mv[q]) : 0.0f;
   }
 
   float m[8];
@@ -474,35 +503,42 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
     if (threadIdx.x < 2) valid_bits[threadIdx.x] = 0u;
     __syncthreads();
   }
+  // every row of the workgroup loaded before the first is used (then the V-Smooth mean)
+  constexpr int kHalves = kRows / kBlock;
+  int64_t pos[4 * kHalves], srow[4 * kHalves];  // row 4 hh + pass
+  uint4 raw[4 * kHalves];
 #pragma unroll
-  for (int hh = 0; hh < kRows / kBlock; hh++) {  // 64-row halves
+  for (int k = 0; k < 4 * kHalves; k++) pos[k] = blk * kRows + kBlock * (k >> 2) + 4 * row0 + (k & 3);
+  gather_srcs(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, pos, srow);
+#pragma unroll
+  for (int k = 0; k < 4 * kHalves; k++) raw[k] = load_row16(p.v, b, srow[k], h, p.Nsrc, p.H, chunk);
+  // V-Smooth: the block mean of the workgroup's rows (one 128-row V block holds all of them)
+  if (p.vsmooth) {
+    const uint4 mraw = *reinterpret_cast<const uint4*>(p.v_mean + (bh * p.NB128 + blk * kRows / kVBlock) * kHeadDim + chunk * 8);
+    const Bf16x8 m = unpack8(mraw);
+#pragma unroll
+    for (int q = 0; q < 8; q++) mhat[q] = m.v[q];
+  }
+#pragma unroll
+  for (int hh = 0; hh < kHalves; hh++) {  // 64-row halves
   uint32_t lo4[4], hi4[4];  // per token: the codes of channels 0-3 and 4-7 of the octet
 #pragma unroll
   for (int pass = 0; pass < 4; pass++) {
     const int t = kBlock * hh + 4 * row0 + pass;
-    const int64_t i = blk * kRows + t;
-    const int64_t s = gather_src(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, i);
-    uint32_t lo = 0, hi = 0;
-    if (s >= 0) {
-      const uint16_t* row = src_row(p.v, b, s, h, p.Nsrc, p.H) + chunk * 8;
-      const Bf16x8 x = load8(row);
-      if constexpr (BIAS) *reinterpret_cast<uint4*>(&vin_s[t][chunk * 8]) = *reinterpret_cast<const uint4*>(row);
-      if (p.vsmooth) {
-        const uint16_t* mrow = p.v_mean + (bh * p.NB128 + i / kVBlock) * kHeadDim + chunk * 8;
+    const bool valid = srow[4 * hh + pass] >= 0;
+    if constexpr (BIAS) *reinterpret_cast<uint4*>(&vin_s[t][chunk * 8]) = raw[4 * hh + pass];
+    const Bf16x8 x = unpack8(raw[4 * hh + pass]);
+    float r[8], y[8];
 #pragma unroll
-        for (int q = 0; q < 8; q++) mhat[q] = bf16_to_f32(mrow[q]);
-      }
-      float r[8], y[8];
-#pragma unroll
-      for (int q = 0; q < 8; q++) {
-        r[q] = __fsub_rn(x.v[q], mhat[q]);
-        y[q] = r[q] * inv[q];
-      }
-      lo = e4m3x4(y[0], y[1], y[2], y[3]);
-      hi = e4m3x4(y[4], y[5], y[6], y[7]);
+    for (int q = 0; q < 8; q++) {
+      r[q] = __fsub_rn(x.v[q], mhat[q]);
+      y[q] = r[q] * inv[q];
     }
+    // padding rows: code 0
+    const uint32_t lo = valid ? e4m3x4(y[0], y[1], y[2], y[3]) : 0u;
+    const uint32_t hi = valid ? e4m3x4(y[4], y[5], y[6], y[7]) : 0u;
     if constexpr (BIAS) {
-      if (chunk == 0 && s >= 0) atomicOr(&valid_bits[t >> 5], 1u << (t & 31));
+      if (chunk == 0 && valid) atomicOr(&valid_bits[t >> 5], 1u << (t & 31));
     }
     lo4[pass] = lo;
     hi4[pass] = hi;

@@ -99,7 +99,7 @@ typedef enum fp8attn_pcast {
  *   q8, k8    E4M3 [B, H, N64, D]; rows >= N are written as code 0.
  *   v8t       E4M3 [B, H, D, N64]; columns >= N and padding positions are code 0.
  *   q_scale, k_scale   FP32 [B, H, NB].      v_scale   FP32 [B, H, D].
- *   v_mean    bf16 [B, H, NB128, D] when vsmooth, else ignored (may be NULL).
+ *   v_mean    bf16 [B, H, NB128, D] (16-byte aligned) when vsmooth, else ignored (may be NULL).
  *   workspace device scratch of at least fp8attn_quantize_workspace_bytes(...) bytes,
  *             16-byte aligned; its contents are overwritten. The size covers every option.
  * Errors: EINVAL on null/misaligned pointers, non-positive sizes, N != N_src without
