@@ -43,10 +43,10 @@ namespace {
 // read at clamped indices (N >= 1) with no per-row branch, so that they load together.
 template <int R>
 __device__ __forceinline__ void gather_srcs(const int32_t* perm, int per_head, int64_t bh, int64_t N, int64_t Nsrc,
-                                            const int64_t (&pos)[R], int64_t (&src)[R]) {
+                                            const int64_t (&pos)[R], int32_t (&src)[R]) {
   if (perm == nullptr) {  // (uniform)
 #pragma unroll
-    for (int k = 0; k < R; k++) src[k] = pos[k] < N ? pos[k] : -1;
+    for (int k = 0; k < R; k++) src[k] = pos[k] < N ? static_cast<int32_t>(pos[k]) : -1;
   } else {
     const int32_t* row = per_head ? perm + bh * N : perm;
     int32_t e[R];
@@ -57,22 +57,23 @@ __device__ __forceinline__ void gather_srcs(const int32_t* perm, int per_head, i
   }
 }
 
-// Byte offset-free pointer to the 128-channel bf16 row (b, src, h) of the source layout.
-__device__ __forceinline__ const uint16_t* src_row(const uint16_t* base, int64_t b, int64_t src,
-                                                   int64_t h, int64_t Nsrc, int64_t H) {
-  return base + ((b * Nsrc + src) * H + h) * kHeadDim;
+// Row s of head (b, h) starts at head_base(...) + s * H * 128 elements.
+__device__ __forceinline__ const uint16_t* head_base(const uint16_t* base, int64_t b, int64_t h, int64_t Nsrc,
+                                                     int64_t H) {
+  return base + (b * Nsrc * H + h) * kHeadDim;
 }
 
-// The 16 bytes of channels 8 chunk .. + 7 of source row s of head (b, h), zeros for s < 0. The
-// load always issues (row 0, which exists since N_src >= 1, stands in for a padding row), so a
-// thread's row loads are in flight together instead of each one waiting behind a branch.
-__device__ __forceinline__ uint4 load_row16(const uint16_t* base, int64_t b, int64_t s, int64_t h,
-                                            int64_t Nsrc, int64_t H, int chunk) {
+// The 16 bytes of channels 8 chunk .. + 7 of source row s of a head (hb = head_base, rstride =
+// H * 128), zeros for s < 0. The load always issues (row 0, which exists since N_src >= 1,
+// stands in for a padding row), so a thread's row loads are in flight together instead of each
+// one waiting behind a branch.
+__device__ __forceinline__ uint4 load_row16(const uint16_t* hb, int64_t rstride, int32_t s, int chunk) {
   // an opaque all-ones or zero mask: with a plain select the compiler turns the load back into
   // a predicated one, which it then waits for inside its branch
   uint32_t keep = s >= 0 ? 0xFFFFFFFFu : 0u;
   asm volatile("" : "+v"(keep));
-  const uint4 raw = *reinterpret_cast<const uint4*>(src_row(base, b, s >= 0 ? s : 0, h, Nsrc, H) + chunk * 8);
+  const int64_t row = s >= 0 ? s : 0;
+  const uint4 raw = *reinterpret_cast<const uint4*>(hb + row * rstride + chunk * 8);
   return make_uint4(raw.x & keep, raw.y & keep, raw.z & keep, raw.w & keep);
 }
 
@@ -117,13 +118,15 @@ __global__ __launch_bounds__(256) void seq_block_sums(QuantParams p) {
   const uint16_t* src = z == 0 ? p.k : p.v;
   const int chunk = threadIdx.x & 15;
   const int row0 = threadIdx.x >> 4;
-  int64_t pos[4], s[4];
+  int64_t pos[4];
+  int32_t s[4];
   uint4 raw[4];
 #pragma unroll
   for (int pass = 0; pass < 4; pass++) pos[pass] = blk * kBlock + row0 + 16 * pass;
   gather_srcs(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, pos, s);
+  const uint16_t* hb = head_base(src, b, h, p.Nsrc, p.H);
 #pragma unroll
-  for (int pass = 0; pass < 4; pass++) raw[pass] = load_row16(src, b, s[pass], h, p.Nsrc, p.H, chunk);
+  for (int pass = 0; pass < 4; pass++) raw[pass] = load_row16(hb, p.H * kHeadDim, s[pass], chunk);
 #pragma unroll
   for (int pass = 0; pass < 4; pass++) {
     const int r = row0 + 16 * pass;
@@ -226,13 +229,15 @@ __global__ __launch_bounds__(256) void quant_qk(QuantParams p) {
   float mk[8];
 #pragma unroll
   for (int j = 0; j < 8; j++) mk[j] = shift ? p.ws_mean[bh * kHeadDim + chunk * 8 + j] : 0.0f;
-  int64_t pos[4], s[4];
+  int64_t pos[4];
+  int32_t s[4];
   uint4 raw[4];
 #pragma unroll
   for (int pass = 0; pass < 4; pass++) pos[pass] = blk * kBlock + row0 + 16 * pass;
   gather_srcs(perm, per_head, bh, p.N, p.Nsrc, pos, s);
+  const uint16_t* hb = head_base(src, b, h, p.Nsrc, p.H);
 #pragma unroll
-  for (int pass = 0; pass < 4; pass++) raw[pass] = load_row16(src, b, s[pass], h, p.Nsrc, p.H, chunk);
+  for (int pass = 0; pass < 4; pass++) raw[pass] = load_row16(hb, p.H * kHeadDim, s[pass], chunk);
   Bf16x8 x[4];
   float amax = 0.0f;
 #pragma unroll
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
 #pragma unroll
   for (int q = 0; q < 8; q++) mv[q] = shift ? p.ws_mean[(p.B * p.H + bh) * kHeadDim + chunk * 8 + q] : 0.0f;
 
-  int64_t srow[8];
+  int32_t srow[8];
   uint4 raw[8];
   if constexpr (SCATTER) {
 #pragma unroll
@@ -380,25 +385,24 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
     for (int pass = 0; pass < 8; pass++) pos[pass] = j * kVBlock + rg + 16 * pass;
     gather_srcs(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, pos, srow);
   }
+  const uint16_t* vhb = head_base(p.v, b, h, p.Nsrc, p.H);
 #pragma unroll
-  for (int pass = 0; pass < 8; pass++) raw[pass] = load_row16(p.v, b, srow[pass], h, p.Nsrc, p.H, chunk);
-  Bf16x8 x[8];
-  bool valid[8];
-  int my_valid = 0;  // rows counted once, by the chunk-0 thread of each row
-#pragma unroll
-  for (int pass = 0; pass < 8; pass++) {
-    valid[pass] = srow[pass] >= 0;
-    my_valid += (chunk == 0 && valid[pass]) ? 1 : 0;
-    x[pass] = unpack8(raw[pass]);  // padding rows are zeros and stay zeros
-    if (shift)
-#pragma unroll
-      for (int q = 0; q < 8; q++) x[pass].v[q] = valid[pass] ? __fsub_rn(x[pass].v[q], mv[q]) : 0.0f;
-  }
-
+  for (int pass = 0; pass < 8; pass++) raw[pass] = load_row16(vhb, p.H * kHeadDim, srow[pass], chunk);
   float m[8];
 #pragma unroll
   for (int q = 0; q < 8; q++) m[q] = 0.0f;
   if constexpr (VS) {
+    bool valid[8];
+    int my_valid = 0;  // rows counted once, by the chunk-0 thread of each row
+#pragma unroll
+    for (int pass = 0; pass < 8; pass++) {
+      valid[pass] = srow[pass] >= 0;
+      my_valid += (chunk == 0 && valid[pass]) ? 1 : 0;
+    }
+    // (no V shift: sequence-mean smoothing of V is rejected together with V-Smooth)
+    Bf16x8 x[8];
+#pragma unroll
+    for (int pass = 0; pass < 8; pass++) x[pass] = unpack8(raw[pass]);  // padding rows are zeros
     // Column sums in FP64: exact for <= 128 bf16 terms, so the summation order is irrelevant.
     double s[8];
 #pragma unroll
@@ -427,10 +431,16 @@ __global__ __launch_bounds__(256) void v_block_stats(QuantParams p) {
 #pragma unroll
         for (int q = 0; q < 8; q++) m[q] = fmaxf(m[q], fabsf(x[pass].v[q] - mhat_s[chunk * 8 + q]));
   } else {
+    // each row folded in as it arrives; padding rows are zeros and stay zeros
 #pragma unroll
-    for (int pass = 0; pass < 8; pass++)
+    for (int pass = 0; pass < 8; pass++) {
+      const Bf16x8 x = unpack8(raw[pass]);
 #pragma unroll
-      for (int q = 0; q < 8; q++) m[q] = fmaxf(m[q], fabsf(x[pass].v[q]));
+      for (int q = 0; q < 8; q++) {
+        const float v = shift ? (srow[pass] >= 0 ? __fsub_rn(x.v[q], mv[q]) : 0.0f) : x.v[q];
+        m[q] = fmaxf(m[q], fabsf(v));
+      }
+    }
   }
 #pragma unroll
   for (int q = 0; q < 8; q++) fmax_[rg][chunk * 8 + q] = m[q];
@@ -505,13 +515,15 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
   }
   // every row of the workgroup loaded before the first is used (then the V-Smooth mean)
   constexpr int kHalves = kRows / kBlock;
-  int64_t pos[4 * kHalves], srow[4 * kHalves];  // row 4 hh + pass
+  int64_t pos[4 * kHalves];  // row 4 hh + pass
+  int32_t srow[4 * kHalves];
   uint4 raw[4 * kHalves];
 #pragma unroll
   for (int k = 0; k < 4 * kHalves; k++) pos[k] = blk * kRows + kBlock * (k >> 2) + 4 * row0 + (k & 3);
   gather_srcs(p.perm_kv, p.perm_kv_per_head, bh, p.N, p.Nsrc, pos, srow);
+  const uint16_t* vhb = head_base(p.v, b, h, p.Nsrc, p.H);
 #pragma unroll
-  for (int k = 0; k < 4 * kHalves; k++) raw[k] = load_row16(p.v, b, srow[k], h, p.Nsrc, p.H, chunk);
+  for (int k = 0; k < 4 * kHalves; k++) raw[k] = load_row16(vhb, p.H * kHeadDim, srow[k], chunk);
   // V-Smooth: the block mean of the workgroup's rows (one 128-row V block holds all of them)
   if (p.vsmooth) {
     const uint4 mraw = *reinterpret_cast<const uint4*>(p.v_mean + (bh * p.NB128 + blk * kRows / kVBlock) * kHeadDim + chunk * 8);

@@ -143,10 +143,13 @@ def test_quantize_bit_exact(m, orc, name, c, vsmooth):
 
 
 @pytest.mark.parametrize("per_head", [False, True])
-def test_quantize_gather_bit_exact(m, orc, per_head):
-    say("quantize gather, per_head", per_head)
+@pytest.mark.parametrize("N", [384, 350])
+def test_quantize_gather_bit_exact(m, orc, per_head, N):
+    """Permutations with entries past the source (padding rows); N = 350 also leaves layout
+    positions past N inside the last 64- and 128-row blocks."""
+    say("quantize gather, per_head", per_head, "N", N)
     rng = np.random.default_rng(5)
-    Nsrc, N, H = 300, 384, 2
+    Nsrc, H = 300, 2
     q, k, v = workloads.make_qkv(1, Nsrc, H, 7, kind="token_outliers")
     perm_q = rng.permutation(N).astype(np.int32)
     perm_q = np.where(perm_q >= Nsrc, -1, perm_q).astype(np.int32)
