@@ -202,7 +202,7 @@ def _run_attn(m, qz, **kw):
 @pytest.mark.parametrize("N,H,reverse,S", [
     (512, 2, True, 256.0), (512, 2, False, 256.0), (512, 2, False, 1.0), (512, 2, True, 448.0),
     (1000, 3, True, 256.0), (1000, 3, False, 448.0), (37, 2, False, 256.0), (64, 1, True, 1.0),
-    (2500, 2, False, 256.0)])
+    (2500, 2, False, 256.0), (1, 2, True, 256.0), (65, 2, False, 256.0), (65, 1, True, 448.0)])
 def test_attention_dense_small(m, orc, N, H, reverse, S):
     say("dense", N, H, "reverse" if reverse else "forward", S)
     q, k, v = workloads.make_qkv(1, N, H, seed=N + H)
