@@ -220,7 +220,7 @@ def test_attention_dense_small(m, orc, N, H, reverse, S):
     assert c >= COS_MIN
 
 
-@pytest.mark.parametrize("N,reverse", [(512, True), (1000, False)])
+@pytest.mark.parametrize("N,reverse", [(512, True), (1000, False), (1, True), (65, False)])
 def test_attention_expcast_small(m, orc, N, reverse):
     say("expcast", N, reverse)
     q, k, v = workloads.make_qkv(1, N, 2, seed=11 + N)
