@@ -645,6 +645,9 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
         tie_k(t, lsum);
         if (t == 0) interleave_region1();
         else interleave_region2();
+        // the rest of the block (QK MFMAs, second half's codes, row sum) runs at raised wave
+        // priority, the PV MFMAs and operand reads at the normal one (see iteration)
+        if (t == 0) __builtin_amdgcn_s_setprio(1);
         issue_qk_half(t);
       }
       if (clamp) {
@@ -762,6 +765,11 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   auto iteration = [&](auto mask_tag, auto steady_tag, int j, uint8_t* sl) {
     constexpr bool kSteady = decltype(steady_tag)::value;
     if constexpr (decltype(mask_tag)::value) mask_block();
+    // ExpCast, whose loop the matrix cores bound: the two waves of a SIMD arbitrate by phase,
+    // a wave in the QK half of its block ahead of one in the PV half. (Measured faster on every
+    // ExpCast variant; the standard cast, bound by its VALU work, ran slower with any such
+    // arrangement and keeps one priority throughout.)
+    if constexpr (EXPCAST) __builtin_amdgcn_s_setprio(0);
     pv();         // PV of block j-1 (zero P bytes before the first block)
     read_v(sl);   // V(j)
     read_k(sl);   // K(j+1)
