@@ -176,6 +176,10 @@ template <int WAVES, bool SPARSE, bool EXPCAST, bool VSMOOTH, bool STATS, bool S
 __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   constexpr int kThreads = WAVES * 64;
   constexpr int kRowsPerWg = WAVES * 32;
+  // Loops whose waves take turns by phase at the SIMD (see iteration): ExpCast, bound by the
+  // matrix cores, and the sparse paths, whose waves wait more; the dense standard cast, bound by
+  // its VALU work, ran slower with any such arrangement and keeps one priority throughout.
+  constexpr bool kPhasePrio = EXPCAST || SPARSE;
   constexpr int kChunks = 512 / kThreads;       // 16-byte chunks per thread of one 8 KB tile
   constexpr int kMetaOff = 2 * kTileBytes;      // s_k (f32) and valid keys (i32) of the K block
   // V-Smooth: the mean operand records of a group of four 128-row V blocks, 128 channels x 32 B
@@ -647,7 +651,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
         else interleave_region2();
         // the rest of the block (QK MFMAs, second half's codes, row sum) runs at raised wave
         // priority, the PV MFMAs and operand reads at the normal one (see iteration)
-        if (t == 0) __builtin_amdgcn_s_setprio(1);
+        if (kPhasePrio && t == 0) __builtin_amdgcn_s_setprio(1);
         issue_qk_half(t);
       }
       if (clamp) {
@@ -693,6 +697,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
         // QK of the next block's key half t takes over this half's registers
         if (t == 0) interleave_region1();
         else interleave_region2();
+        if (kPhasePrio && t == 0) __builtin_amdgcn_s_setprio(1);  // (as in the ExpCast branch)
         issue_qk_half(t);
       }
     }
@@ -765,11 +770,10 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   auto iteration = [&](auto mask_tag, auto steady_tag, int j, uint8_t* sl) {
     constexpr bool kSteady = decltype(steady_tag)::value;
     if constexpr (decltype(mask_tag)::value) mask_block();
-    // ExpCast, whose loop the matrix cores bound: the two waves of a SIMD arbitrate by phase,
-    // a wave in the QK half of its block ahead of one in the PV half. (Measured faster on every
-    // ExpCast variant; the standard cast, bound by its VALU work, ran slower with any such
-    // arrangement and keeps one priority throughout.)
-    if constexpr (EXPCAST) __builtin_amdgcn_s_setprio(0);
+    // Phase priority: the two waves of a SIMD arbitrate by phase, a wave in the QK part of its
+    // block (from the first QK MFMAs on) ahead of one in the PV part (PV MFMAs, operand reads,
+    // row maximum, first half's P bytes).
+    if constexpr (kPhasePrio) __builtin_amdgcn_s_setprio(0);
     pv();         // PV of block j-1 (zero P bytes before the first block)
     read_v(sl);   // V(j)
     read_k(sl);   // K(j+1)
