@@ -370,6 +370,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int64_t left = p.NB - 64 * g;  // summaries from this group on
     const uint64_t valid = left >= 64 ? ~0ull : (1ull << left) - 1ull;
 
+    // the route scores and the mask run at a raised wave priority, the summary route at the
+    // normal one, so that the waves of a SIMD take turns by phase (measured faster)
+    __builtin_amdgcn_s_setprio(1);
     // route scores
     const float cs = sq * kqs[g] * p.softmax_scale;
     float x[2][16];
@@ -416,6 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     if (sink_end > 0) word |= sink_end >= 64 ? ~0ull : ((1ull << sink_end) - 1ull);
     if (ublock && (wave & 1) == 0 && lane == 0) p.mask[(bh * p.NB + u) * p.W + g] = word;
 
+    __builtin_amdgcn_s_setprio(0);
     // summary route over the group's non-exact summaries
     const uint64_t sbits = valid & ~word;
     if (ublock && sbits != 0ull) {
