@@ -177,9 +177,10 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
   constexpr int kThreads = WAVES * 64;
   constexpr int kRowsPerWg = WAVES * 32;
   // Loops whose waves take turns by phase at the SIMD (see iteration): ExpCast, bound by the
-  // matrix cores, and the sparse paths, whose waves wait more; the dense standard cast, bound by
-  // its VALU work, ran slower with any such arrangement and keeps one priority throughout.
-  constexpr bool kPhasePrio = EXPCAST || SPARSE;
+  // matrix cores, and the sparse and V-Smooth paths, whose waves wait more; the plain dense
+  // standard cast, bound by its VALU work, ran slower with any such arrangement and keeps one
+  // priority throughout.
+  constexpr bool kPhasePrio = EXPCAST || SPARSE || VSMOOTH;
   constexpr int kChunks = 512 / kThreads;       // 16-byte chunks per thread of one 8 KB tile
   constexpr int kMetaOff = 2 * kTileBytes;      // s_k (f32) and valid keys (i32) of the K block
   // V-Smooth: the mean operand records of a group of four 128-row V blocks, 128 channels x 32 B
