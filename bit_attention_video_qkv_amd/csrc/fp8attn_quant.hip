@@ -577,19 +577,19 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
   }
   }
   __syncthreads();
-  // Thread t writes channel t/2, tokens kRows/2 * (t%2) .. + kRows/2 - 1 (16-byte stores); with
-  // 128 rows the second half of the last block lies beyond N64 when NB is odd.
-  constexpr int kWords = kRows / 8;
-  const int d = threadIdx.x >> 1;
-  const int half = threadIdx.x & 1;
-  const int64_t tok0 = blk * kRows + kRows / 2 * half;
-  if (tok0 < p.N64) {
-    uint32_t w[kWords];
+  // 16-token chunks of the channels' code rows: chunk q = 256 i + t is chunk q % kCh of channel
+  // q / kCh, so the lanes of a wave write whole 128-byte lines of consecutive channels; with 128
+  // rows the second half of the last block lies beyond N64 when NB is odd.
+  constexpr int kCh = kRows / 16;  // chunks per channel
 #pragma unroll
-    for (int i = 0; i < kWords; i++) w[i] = tile[d][kWords * half + i];
-    uint4* dst = reinterpret_cast<uint4*>(p.v8t + (bh * kHeadDim + d) * p.N64 + tok0);
-#pragma unroll
-    for (int j = 0; j < kWords / 4; j++) dst[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+  for (int i = 0; i < kHeadDim * kCh / 256; i++) {
+    const int q = 256 * i + threadIdx.x;
+    const int d = q / kCh, k = q % kCh;
+    const int64_t tok0 = blk * kRows + 16 * k;
+    if (tok0 < p.N64) {
+      const uint4 w = make_uint4(tile[d][4 * k], tile[d][4 * k + 1], tile[d][4 * k + 2], tile[d][4 * k + 3]);
+      *reinterpret_cast<uint4*>(p.v8t + (bh * kHeadDim + d) * p.N64 + tok0) = w;
+    }
   }
   if constexpr (BIAS) {
     // The rounding error of channel c, rows in ascending order (the bias correction exists only
