@@ -726,6 +726,9 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     lo = __builtin_bit_cast(uint16_t, rl);
   };
   auto restore_group = [&](const uint8_t* sl) {
+    v4i a[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) a[dt] = *reinterpret_cast<const v4i*>(sl + kMeanOff + (32 * dt + l32) * 32 + 16 * lh);
     uint32_t ha, la, hb, lb;
     split_bf16(r_pa, ha, la);
     split_bf16(r_pb, hb, lb);
@@ -736,9 +739,14 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, const int work) {
     b[3] = 0;
     const v8bf bb = __builtin_bit_cast(v8bf, b);
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++) {
-      const v4i a = *reinterpret_cast<const v4i*>(sl + kMeanOff + (32 * dt + l32) * 32 + 16 * lh);
-      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), bb, oacc[dt], 0, 0, 0);
+    for (int dt = 0; dt < 4; dt++)
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a[dt]), bb, oacc[dt], 0, 0, 0);
+    if constexpr (EXPCAST) {
+      // the four record reads in flight together (left to itself the compiler, short of
+      // registers here, reads one record per MFMA and waits for each)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 1);  // VALU (the row sums' split)
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);   // MFMA
     }
     r_pa = 0.0f;
     r_pb = 0.0f;
