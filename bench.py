@@ -28,7 +28,7 @@ ATTN_SRC = os.path.join(ROOT, "bit_attention_video_qkv_amd", "csrc", "fp8attn_at
 # HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) as measured by
 # rocprofv3 for the attention source whose code (comments and blank lines dropped) has this
 # sha256 prefix, per workload; see profiles/. Reported only while that code is unchanged.
-MEASURED_TRAFFIC = {("bb3bb11a3ae7", "wan14b"): 15626508113}
+MEASURED_TRAFFIC = {("e51e0f02b9d9", "wan14b"): 16029482546}
 
 
 def code_sha(path):
