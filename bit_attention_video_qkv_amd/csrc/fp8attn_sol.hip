@@ -30,7 +30,7 @@
 // Kernels (launch order):
 //   sol_summaries  grid (NBp, B*H)         K and V summaries
 //   sol_kquant     grid (NBg, B*H)         quantised K summaries
-//   sol_kmoments   grid (B*H, 16)          mean and second moment of the summaries (FP64)
+//   sol_kmoments   grid (B*H) or (B*H, 16) mean and second moment of the summaries (FP64)
 //   sol_theta      grid (NB, B*H)          threshold per Q block
 //   sol_route      grid (ceil(NB/2), B*H), 4 waves: per group of 64 summaries staged in LDS (the
 //                  groups in KV order), the route QK (E4M3 MFMA), the exact-block mask, the
@@ -66,6 +66,19 @@ __device__ __forceinline__ int64_t vsum_index(const SolParams& p, int64_t bh, in
   return ((((bh * p.NBg + g) * 2 + t) * 2 + s) * 4 + dt) * 512 + lane * 8 + e;
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// E4M3 codes to FP32 on the conversion unit: one byte, or the two bytes of one half of a word.
+// gfx950's FP8 conversions use the OCP E4M3 format, the one the quantisation kernels write with
+// their encoder; the quantised tensors hold no NaN code.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(c), 0);
+}
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w, bool high) {
+  return high ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true)
+              : __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+}
+
 // 1. Summaries of KV block j (grid over the padded count NBp: padding summaries get a zero V
 // summary, which the summary PV multiplies by p = 0). Threads 0..127: K channel d; 128..255: V
 // channel d. Rows and positions past N hold code 0 (the quantisation contract), so all 64 are
@@ -90,7 +103,7 @@ __global__ __launch_bounds__(256) void sol_summaries(SolParams p) {
     const int d = threadIdx.x;
     float s = 0.0f;
 #pragma unroll 16
-    for (int r = 0; r < 64; r++) s += e4m3_decode(kt[r][d]);
+    for (int r = 0; r < 64; r++) s += e4m3_to_f32(kt[r][d]);
     const float prod = s * p.k_scale[bh * p.NB + j];
     p.ksum[(bh * p.NB + j) * kHeadDim + d] = __fdiv_rn(prod, static_cast<float>(n));
   } else {
@@ -102,9 +115,13 @@ __global__ __launch_bounds__(256) void sol_summaries(SolParams p) {
       const uint4 w = vp[c];
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int q = 0; q < 4; q++)
-#pragma unroll
-        for (int b = 0; b < 4; b++) s += e4m3_decode((ws[q] >> (8 * b)) & 0xFFu);
+      for (int q = 0; q < 4; q++) {
+        const f32x2 lo = e4m3x2_to_f32(ws[q], false), hi = e4m3x2_to_f32(ws[q], true);
+        s += lo.x;
+        s += lo.y;
+        s += hi.x;
+        s += hi.y;
+      }
     }
     const float prod = s * p.v_scale[bh * kHeadDim + d];
     p.vsumT[vsum_index(p, bh, j, d)] = f32_to_bf16_rne(__fdiv_rn(prod, static_cast<float>(n)));
@@ -153,34 +170,71 @@ __global__ __launch_bounds__(256) void sol_kquant(SolParams p) {
   }
 }
 
-// 3. Mean and second moment of the summaries (FP64, ascending j). grid (B*H, 16): workgroup y
-// computes rows 8y..8y+7 of Mk (thread t: row 8y + t/32, columns 4*(t%32)..+3); y = 0 also the
-// mean.
+// 3. Mean and second moment of the summaries (FP64, ascending j). FULL (the exact estimator):
+// grid (B*H, 16), workgroup y computes rows 8y..8y+7 of Mk (thread t: row 8y + t/32, columns
+// 4*(t%32)..+3); otherwise (the diag estimator, which reads only the diagonal): grid (B*H),
+// thread d computes Mk[d][d]. The thread that owns row d's first columns also sums the mean of
+// channel d. Each thread holds the next batch of summaries in registers while it folds the
+// current one in, so that many loads are in flight while the sums stay in order.
+template <bool FULL>
 __global__ __launch_bounds__(256) void sol_kmoments(SolParams p) {
+  constexpr int kBatch = FULL ? 16 : 32;
   const int64_t bh = blockIdx.x;
-  const int d = blockIdx.y * 8 + (threadIdx.x >> 5);
-  const int e0 = (threadIdx.x & 31) * 4;
+  const int d = FULL ? static_cast<int>(blockIdx.y) * 8 + static_cast<int>(threadIdx.x >> 5)
+                     : static_cast<int>(threadIdx.x);
+  const int e0 = FULL ? static_cast<int>(threadIdx.x & 31) * 4 : d;
   const float* ks = p.ksum + bh * p.NB * kHeadDim;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  // (unrolled so that the loads of several summaries are in flight; the sums stay in order)
-#pragma unroll 8
-  for (int64_t j = 0; j < p.NB; j++) {
-    const double a = static_cast<double>(ks[j * kHeadDim + d]);
-    const float4 b = *reinterpret_cast<const float4*>(ks + j * kHeadDim + e0);
-    acc[0] += a * static_cast<double>(b.x);
-    acc[1] += a * static_cast<double>(b.y);
-    acc[2] += a * static_cast<double>(b.z);
-    acc[3] += a * static_cast<double>(b.w);
+  double acc[4] = {0.0, 0.0, 0.0, 0.0}, msum = 0.0;
+  auto load = [&](int64_t j, float& a, float4& b) {
+    a = ks[j * kHeadDim + d];
+    if constexpr (FULL) b = *reinterpret_cast<const float4*>(ks + j * kHeadDim + e0);
+  };
+  auto fold = [&](float a, const float4& b) {
+    const double ad = static_cast<double>(a);
+    msum += ad;
+    if constexpr (FULL) {
+      acc[0] += ad * static_cast<double>(b.x);
+      acc[1] += ad * static_cast<double>(b.y);
+      acc[2] += ad * static_cast<double>(b.z);
+      acc[3] += ad * static_cast<double>(b.w);
+    } else {
+      acc[0] += ad * ad;
+    }
+  };
+  const int64_t n_full = p.NB / kBatch * kBatch;
+  float a_cur[kBatch], a_nxt[kBatch];
+  float4 b_cur[kBatch], b_nxt[kBatch];
+  if (n_full > 0) {
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) load(u, a_cur[u], b_cur[u]);
+  }
+  for (int64_t j = 0; j < n_full; j += kBatch) {
+    if (j + kBatch < n_full) {
+#pragma unroll
+      for (int u = 0; u < kBatch; u++) load(j + kBatch + u, a_nxt[u], b_nxt[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) fold(a_cur[u], b_cur[u]);
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      a_cur[u] = a_nxt[u];
+      b_cur[u] = b_nxt[u];
+    }
+  }
+  for (int64_t j = n_full; j < p.NB; j++) {
+    float a;
+    float4 b;
+    load(j, a, b);
+    fold(a, b);
   }
   const double inv_nb = 1.0 / static_cast<double>(p.NB);
+  if constexpr (FULL) {
 #pragma unroll
-  for (int q = 0; q < 4; q++) p.Mk[(bh * kHeadDim + d) * kHeadDim + e0 + q] = acc[q] * inv_nb;
-  if (blockIdx.y == 0 && threadIdx.x < kHeadDim) {
-    double m = 0.0;
-#pragma unroll 8
-    for (int64_t j = 0; j < p.NB; j++) m += static_cast<double>(ks[j * kHeadDim + threadIdx.x]);
-    p.mk[bh * kHeadDim + threadIdx.x] = m * inv_nb;
+    for (int q = 0; q < 4; q++) p.Mk[(bh * kHeadDim + d) * kHeadDim + e0 + q] = acc[q] * inv_nb;
+  } else {
+    p.Mk[(bh * kHeadDim + d) * kHeadDim + d] = acc[0] * inv_nb;
   }
+  if (!FULL || (threadIdx.x & 31) == 0) p.mk[bh * kHeadDim + d] = msum * inv_nb;
 }
 
 __device__ __forceinline__ double block_sum_128(double v, double* red) {
@@ -203,6 +257,10 @@ __global__ __launch_bounds__(128) void sol_theta(SolParams p) {
   const int64_t u = blockIdx.x, bh = blockIdx.y;
   const int e = threadIdx.x;
   const int nq = static_cast<int>(min<int64_t>(64, p.N - 64 * u));
+  // (issued before the block's codes, so that their latencies overlap)
+  const double sq = p.q_scale[bh * p.NB + u];
+  const double mk_e = p.mk[bh * kHeadDim + e];
+  const double mk_ee = EXACT ? 0.0 : p.Mk[(bh * kHeadDim + e) * kHeadDim + e];
   const uint4* qb = reinterpret_cast<const uint4*>(p.q8 + (bh * p.N64 + 64 * u) * kHeadDim);
 #pragma unroll
   for (int k = 0; k < 4; k++) {
@@ -212,7 +270,7 @@ __global__ __launch_bounds__(128) void sol_theta(SolParams p) {
     if constexpr (EXACT) {
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int q = 0; q < 16; q++) c[i][d0 + q] = e4m3_decode((ws[q >> 2] >> (8 * (q & 3))) & 0xFFu);
+      for (int q = 0; q < 16; q++) c[i][d0 + q] = e4m3_to_f32((ws[q >> 2] >> (8 * (q & 3))) & 0xFFu);
     } else {
       *reinterpret_cast<uint4*>(&cb[i][d0]) = w;
     }
@@ -220,23 +278,24 @@ __global__ __launch_bounds__(128) void sol_theta(SolParams p) {
   __syncthreads();
   auto code = [&](int i, int d) -> float {
     if constexpr (EXACT) return c[i][d];
-    else return e4m3_decode(cb[i][d]);
+    else return e4m3_to_f32(cb[i][d]);
   };
-  const double sq = p.q_scale[bh * p.NB + u];
-  // over all 64 rows (rows past nq hold 0); both sums are exact in any order (the decoded codes
-  // and their squares span fewer bits than the FP64 significand)
-  double csum = 0.0, csq = 0.0;
+  // over all 64 rows (rows past nq hold 0). Both sums are exact in any order: a decoded code is
+  // a multiple of 2^-9 below 2^9, so 64 of them sum exactly in FP32 (24 bits); its square (at
+  // most 8 significant bits) is exact in FP32, and 64 squares sum exactly in FP64.
+  float csum = 0.0f;
+  double csq = 0.0;
 #pragma unroll 16
   for (int i = 0; i < 64; i++) {
     const float v = code(i, e);
     csum += v;
-    csq += static_cast<double>(v) * v;
+    csq += static_cast<double>(v * v);
   }
   // mu = ss * sq * mean_i c_i . m
-  const double mu = block_sum_128(csum / nq * p.mk[bh * kHeadDim + e], red) * sq * p.softmax_scale;
+  const double mu = block_sum_128(static_cast<double>(csum) / nq * mk_e, red) * sq * p.softmax_scale;
   double part;
   if constexpr (!EXACT) {
-    part = csq / nq * p.Mk[(bh * kHeadDim + e) * kHeadDim + e];
+    part = csq / nq * mk_ee;
   } else {
     // sum_i c_i[e] (Mk c_i)[e] / nq, with (Mk c_i)[e] = sum_d Mk[d][e] c_i[d] (Mk symmetric)
     float y[64];
@@ -529,7 +588,8 @@ hipError_t launch_sol(const SolParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(sol_kquant, dim3(static_cast<unsigned>(p.NBg), bh), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sol_kmoments, dim3(bh, kHeadDim / 8), dim3(256), 0, stream, p);
+  if (p.estimator == 0) hipLaunchKernelGGL(sol_kmoments<false>, dim3(bh), dim3(kHeadDim), 0, stream, p);
+  else hipLaunchKernelGGL(sol_kmoments<true>, dim3(bh, kHeadDim / 8), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.estimator == 0) hipLaunchKernelGGL(sol_theta<false>, dim3(static_cast<unsigned>(p.NB), bh), dim3(128), 0, stream, p);
