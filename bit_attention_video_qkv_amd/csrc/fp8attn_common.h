@@ -34,11 +34,19 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
-// Exact value of an OCP E4M3 byte (finite codes; the encoders saturate, so 0x7F/0xFF never occur).
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float mag = e == 0 ? static_cast<float>(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (c & 0x80u) ? -mag : mag;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// The two E4M3 bytes of one half of a packed word (high: bytes 2 and 3) as FP32, on the
+// conversion unit (OCP E4M3, the format of the encoders above; the encoders saturate, so the
+// NaN codes 0x7F/0xFF never occur).
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w, bool high) {
+  return high ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true)
+              : __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+}
+
+// One E4M3 byte (bits 0..7 of c) as FP32, on the conversion unit.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(c), 0);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -603,10 +603,12 @@ __global__ __launch_bounds__(256) void v_encode(QuantParams p) {
 #pragma unroll 2
       for (int t4 = 0; t4 < kBlock; t4 += 4) {
         const uint32_t codes = tile[c][t4 >> 2];
+        const f32x2 lo = e4m3x2_to_f32(codes, false), hi = e4m3x2_to_f32(codes, true);
+        const float dec[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
         for (int u = 0; u < 4; u++) {
           const float r = __fsub_rn(bf16_to_f32(vin_s[t4 + u][c]), mv);
-          const float e = __fsub_rn(mul_rounded(e4m3_decode((codes >> (8 * u)) & 0xFFu), svc), r);
+          const float e = __fsub_rn(mul_rounded(dec[u], svc), r);
           const float sum = __fadd_rn(acc, e);
           acc = ((vm >> (t4 + u)) & 1u) ? sum : acc;
         }

@@ -66,19 +66,6 @@ __device__ __forceinline__ int64_t vsum_index(const SolParams& p, int64_t bh, in
   return ((((bh * p.NBg + g) * 2 + t) * 2 + s) * 4 + dt) * 512 + lane * 8 + e;
 }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// E4M3 codes to FP32 on the conversion unit: one byte, or the two bytes of one half of a word.
-// gfx950's FP8 conversions use the OCP E4M3 format, the one the quantisation kernels write with
-// their encoder; the quantised tensors hold no NaN code.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(c), 0);
-}
-__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w, bool high) {
-  return high ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true)
-              : __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-}
-
 // 1. Summaries of KV block j (grid over the padded count NBp: padding summaries get a zero V
 // summary, which the summary PV multiplies by p = 0). Threads 0..127: K channel d; 128..255: V
 // channel d. Rows and positions past N hold code 0 (the quantisation contract), so all 64 are
