@@ -77,7 +77,7 @@ EXPORTED = ("fp8attn_quantize_qkv", "fp8attn_quantize_workspace_bytes", "fp8attn
             "fp8attn_forward_workspace_bytes", "fp8attn_sta_build", "fp8attn_status_string",
             "fp8attn_vsmooth_cluster", "fp8attn_vsmooth_cluster_workspace_bytes",
             "fp8attn_sol_forward", "fp8attn_sol_workspace_bytes", "fp8attn_diag_e4m3_encode",
-            "fp8attn_diag_mfma_e4m3", "fp8attn_forward_noalloc", "fp8attn_vsmooth_prepare",
+            "fp8attn_diag_e4m3_decode", "fp8attn_diag_mfma_e4m3", "fp8attn_forward_noalloc", "fp8attn_vsmooth_prepare",
             "fp8attn_vsmooth_prepare_workspace_bytes")
 
 
@@ -125,6 +125,8 @@ def lib():
             ctypes.POINTER(_FwdOpts), ctypes.c_void_p, ctypes.c_void_p]
         L.fp8attn_diag_e4m3_encode.restype = ctypes.c_int
         L.fp8attn_diag_e4m3_encode.argtypes = [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        L.fp8attn_diag_e4m3_decode.restype = ctypes.c_int
+        L.fp8attn_diag_e4m3_decode.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         L.fp8attn_diag_mfma_e4m3.restype = ctypes.c_int
         L.fp8attn_diag_mfma_e4m3.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32, ctypes.c_void_p]
         _lib = L
@@ -388,6 +390,19 @@ def diag_e4m3_encode(first_bits, n, out):
         raise ValueError("out must be a uint8 tensor of at least n elements")
     _check("fp8attn_diag_e4m3_encode",
            lib().fp8attn_diag_e4m3_encode(int(first_bits), int(n), _ptr(out), _stream(out.device)))
+    return out
+
+
+def diag_e4m3_decode(codes):
+    """fp8attn_diag_e4m3_decode: uint8 device tensor of n codes (n a multiple of 4) -> float32
+    [2, n]: row 0 decoded two codes per conversion, row 1 one code per conversion."""
+    if codes.dtype != torch.uint8 or codes.dim() != 1 or codes.numel() % 4 != 0:
+        raise ValueError("codes must be a 1-D uint8 tensor whose length is a multiple of 4")
+    codes = codes.contiguous()
+    n = codes.numel()
+    out = torch.empty((2, n), dtype=torch.float32, device=codes.device)
+    _check("fp8attn_diag_e4m3_decode",
+           lib().fp8attn_diag_e4m3_decode(_ptr(codes), n, _ptr(out), _stream(codes.device)))
     return out
 
 

@@ -691,6 +691,15 @@ fp8attn_status fp8attn_diag_e4m3_encode(uint32_t first_bits, int64_t n, uint8_t*
   return from_hip(fp8attn::launch_diag_e4m3_encode(first_bits, n / 4, reinterpret_cast<uint32_t*>(out), stream));
 }
 
+fp8attn_status fp8attn_diag_e4m3_decode(const uint8_t* codes, int64_t n, float* out, hipStream_t stream) {
+  if (n < 0 || n % 4 != 0 || n > (int64_t{1} << 40)) return FP8ATTN_EINVAL;
+  if (n == 0) return FP8ATTN_OK;
+  if (!codes || !out || !aligned(codes, 4) || !aligned(out, 16)) return FP8ATTN_EINVAL;
+  const fp8attn_status dev = check_device();
+  if (dev != FP8ATTN_OK) return dev;
+  return from_hip(fp8attn::launch_diag_e4m3_decode(reinterpret_cast<const uint32_t*>(codes), n / 4, out, stream));
+}
+
 fp8attn_status fp8attn_diag_mfma_e4m3(const uint8_t* a, const uint8_t* bt, float* c, int32_t n_tiles,
                                       hipStream_t stream) {
   if (n_tiles < 0) return FP8ATTN_EINVAL;

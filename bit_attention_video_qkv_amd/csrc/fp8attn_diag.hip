@@ -5,6 +5,9 @@
 //    compare it with an independent encoder over every input the quantiser can produce
 //    (TeleFuser blog "FP8 Sol-Attn", section "面向注意力的 FP8 Preparation": codes of x / s with
 //    s = amax / 448, so |x / s| <= 448 up to one FP32 rounding);
+//  * the E4M3 decoders of the Sol preparation and the V bias correction (e4m3x2_to_f32 and
+//    e4m3_to_f32 on the conversion unit), applied to given codes, so that a test can compare them
+//    with the exact values of every finite code;
 //  * one E4M3 x E4M3 -> FP32 matrix-core product (v_mfma_scale_f32_32x32x64_f8f6f4, the QK and
 //    PV contraction of the attention kernel) per 32 x 32 x 64 tile, so that a test can bound how
 //    far the hardware's sum of exact E4M3 products lies from the exact sum.
@@ -25,6 +28,20 @@ __global__ __launch_bounds__(256) void diag_e4m3_encode(uint32_t first, int64_t 
   if (i >= n_words) return;
   const uint32_t b = first + 4u * static_cast<uint32_t>(i);
   out[i] = e4m3x4(__uint_as_float(b), __uint_as_float(b + 1u), __uint_as_float(b + 2u), __uint_as_float(b + 3u));
+}
+
+// out[4i + k] = code 4i + k decoded two codes per conversion (e4m3x2_to_f32, as the bias
+// correction and the V summaries decode); out[n + 4i + k] = the same code decoded alone
+// (e4m3_to_f32, as the K summaries and the thresholds decode), i < n_words.
+__global__ __launch_bounds__(256) void diag_e4m3_decode(const uint32_t* codes, int64_t n_words, float* out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n_words) return;
+  const uint32_t w = codes[i];
+  const f32x2 lo = e4m3x2_to_f32(w, false), hi = e4m3x2_to_f32(w, true);
+  *reinterpret_cast<float4*>(out + 4 * i) = make_float4(lo.x, lo.y, hi.x, hi.y);
+  *reinterpret_cast<float4*>(out + 4 * n_words + 4 * i) =
+      make_float4(e4m3_to_f32(w & 0xFFu), e4m3_to_f32((w >> 8) & 0xFFu), e4m3_to_f32((w >> 16) & 0xFFu),
+                  e4m3_to_f32(w >> 24));
 }
 
 // One wave per tile t: C[t] (32 x 32 FP32, row-major) = A[t] (32 x 64 E4M3, row-major) times the
@@ -55,6 +72,12 @@ __global__ __launch_bounds__(64) void diag_mfma_e4m3(const uint8_t* a, const uin
 hipError_t launch_diag_e4m3_encode(uint32_t first, int64_t n_words, uint32_t* out, hipStream_t stream) {
   hipLaunchKernelGGL(diag_e4m3_encode, dim3(static_cast<unsigned>((n_words + 255) / 256)), dim3(256), 0, stream,
                      first, n_words, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_diag_e4m3_decode(const uint32_t* codes, int64_t n_words, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(diag_e4m3_decode, dim3(static_cast<unsigned>((n_words + 255) / 256)), dim3(256), 0, stream,
+                     codes, n_words, out);
   return hipGetLastError();
 }
 

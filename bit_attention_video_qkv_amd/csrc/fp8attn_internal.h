@@ -126,6 +126,7 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t stream);
 // Diagnostics (fp8attn_diag.hip): the quantiser's E4M3 encoder on consecutive FP32 bit patterns,
 // and one E4M3 matrix-core product per 32 x 32 x 64 tile.
 hipError_t launch_diag_e4m3_encode(uint32_t first, int64_t n_words, uint32_t* out, hipStream_t stream);
+hipError_t launch_diag_e4m3_decode(const uint32_t* codes, int64_t n_words, float* out, hipStream_t stream);
 hipError_t launch_diag_mfma_e4m3(const uint8_t* a, const uint8_t* bt, float* c, int32_t n_tiles,
                                  hipStream_t stream);
 

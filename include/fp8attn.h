@@ -390,6 +390,15 @@ fp8attn_status fp8attn_sol_forward(int32_t B, int32_t N, int32_t H, int32_t D, c
  *   Errors: EINVAL when n < 0, n is not a multiple of 4, out is null or misaligned, or the range
  *   runs past pattern 2^32 - 1; EUNSUPPORTED on a device other than gfx950.
  *
+ * fp8attn_diag_e4m3_decode — the E4M3 decoders of the Sol preparation and the V bias
+ *   correction (FPSAttention write-up, section 2.1: the dequantised value of a code is its OCP
+ *   E4M3 value times its scale) applied to n codes: out[i] is code i decoded two codes per
+ *   conversion, out[n + i] the same code decoded alone. codes: device uint8 [n], 4-byte aligned;
+ *   out: device float [2 n], 16-byte aligned. The decoders are specified for the finite codes
+ *   (all but 0x7F and 0xFF, which the encoders never write). Errors: EINVAL when n < 0, n is not
+ *   a multiple of 4 or above 2^40, or a pointer is null or misaligned; EUNSUPPORTED on a device
+ *   other than gfx950.
+ *
  * fp8attn_diag_mfma_e4m3 — one matrix-core E4M3 product per tile, as the attention's QK and PV
  *   contractions compute it (TeleFuser blog, section "SM90 CuTe Mainloop": E4M3 operands, FP32
  *   accumulation): for t < n_tiles, C[t] = A[t] * B[t] with A[t] 32 x 64 E4M3 row-major
@@ -399,6 +408,8 @@ fp8attn_status fp8attn_sol_forward(int32_t B, int32_t N, int32_t H, int32_t D, c
  *   device other than gfx950.
  * ------------------------------------------------------------------------------------------ */
 fp8attn_status fp8attn_diag_e4m3_encode(uint32_t first_bits, int64_t n, uint8_t* out,
+                                        hipStream_t stream);
+fp8attn_status fp8attn_diag_e4m3_decode(const uint8_t* codes, int64_t n, float* out,
                                         hipStream_t stream);
 fp8attn_status fp8attn_diag_mfma_e4m3(const uint8_t* a, const uint8_t* bt, float* c,
                                       int32_t n_tiles, hipStream_t stream);

@@ -270,6 +270,11 @@ def test_diagnostics_argument_errors(m):
     assert L.fp8attn_diag_e4m3_encode(0, 8, ctypes.c_void_p(0x10001), None) == 1
     assert L.fp8attn_diag_e4m3_encode(0xFFFFFFFC, 8, fake, None) == 1     # past pattern 2^32 - 1
     assert L.fp8attn_diag_e4m3_encode(0, 0, None, None) == 0              # nothing to do
+    assert L.fp8attn_diag_e4m3_decode(fake, 6, fake, None) == 1              # not a multiple of 4
+    assert L.fp8attn_diag_e4m3_decode(fake, -4, fake, None) == 1
+    assert L.fp8attn_diag_e4m3_decode(None, 8, fake, None) == 1
+    assert L.fp8attn_diag_e4m3_decode(fake, 8, ctypes.c_void_p(0x10004), None) == 1  # out misaligned
+    assert L.fp8attn_diag_e4m3_decode(None, 0, None, None) == 0              # nothing to do
     assert L.fp8attn_diag_mfma_e4m3(fake, fake, fake, -1, None) == 1
     assert L.fp8attn_diag_mfma_e4m3(None, fake, fake, 2, None) == 1
     assert L.fp8attn_diag_mfma_e4m3(ctypes.c_void_p(0x10008), fake, fake, 2, None) == 1

@@ -56,6 +56,21 @@ def test_e4m3_encoder_exhaustive(m, orc):
     assert total == 2 * top
 
 
+def test_e4m3_decoder_every_finite_code(m, orc):
+    # every finite code (the encoders never write 0x7F / 0xFF), in an order that puts each code
+    # at each byte position of a word; both device decoders against the oracle's exact values,
+    # sign of zero included
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    codes = np.concatenate([np.roll(finite, k) for k in range(4)])
+    codes = np.concatenate([codes, np.zeros((-codes.size) % 4, np.uint8)])
+    got = m.diag_e4m3_decode(torch.from_numpy(codes).to(DEV)).cpu().numpy()
+    want = orc.e4m3_decode(codes).astype(np.float32)
+    for row, how in enumerate(("two codes per conversion", "one code per conversion")):
+        bad = np.flatnonzero(got[row].view(np.uint32) != want.view(np.uint32))
+        assert bad.size == 0, (how, hex(int(codes[bad[0]])), float(got[row][bad[0]]), float(want[bad[0]]))
+    say(f"{codes.size} codes decoded equal to the oracle's values by both decoders")
+
+
 def _tiles(orc, rng, kind, T):
     finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
     if kind == "all_codes":
